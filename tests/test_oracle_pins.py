@@ -1,0 +1,400 @@
+"""Pins of the fp64 CPU oracle against what the pages and the mathematics fix.
+
+Every pin here checks the oracle against something other than itself: exact identities,
+closed forms derived by hand (``tests/golden``), library routines (scipy's logsumexp,
+numpy means), brute force on tiny inputs, and invariants the definitions imply.
+Citations: "Block Sparse Attention with Log-Linear Complexity", agihunt.info summary
+(pyramid paragraph; LSE and forced-block paragraph; kernels/GQA paragraph) and rcap.io
+explainer (tree/pooling paragraph; top-down walk paragraph with the g*K bound; scoring
+paragraph with the Jensen remark; the paragraph on Appendix A's sandwich).
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp
+
+import oracle
+from block_selection_pyramid_amd import synth
+
+from walk_np import select_one
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32, BF16 = oracle.F32, oracle.BF16
+
+
+def rng_arrays(seed, shape):
+    return np.random.default_rng(seed).standard_normal(shape).astype(np.float32)
+
+
+# --------------------------------------------------------------- LSE identities
+
+def test_lse_identities():
+    r = np.random.default_rng(0)
+    for n in [1, 2, 3, 17, 64]:
+        x = r.standard_normal(n) * 5
+        c = float(r.standard_normal() * 10)
+        assert oracle.lse([x[0]]) == x[0]
+        assert math.isclose(oracle.lse(x + c), oracle.lse(x) + c, rel_tol=0, abs_tol=1e-12)
+        a, b = x[: n // 2], x[n // 2:]
+        if len(a) and len(b):
+            assert math.isclose(oracle.lse(x), oracle.lse([oracle.lse(a), oracle.lse(b)]), abs_tol=1e-12)
+        assert math.isclose(oracle.lse(np.full(n, x[0])), x[0] + math.log(n), abs_tol=1e-12)
+        assert x.max() <= oracle.lse(x) <= x.max() + math.log(n) + 1e-12
+        # library routine
+        assert math.isclose(oracle.lse(x), float(logsumexp(x)), abs_tol=1e-12)
+    assert oracle.lse([-math.inf, 1.0]) == 1.0
+    assert oracle.lse([-math.inf]) == -math.inf
+    assert oracle.lse([1000.0, 1000.0]) == pytest.approx(1000.0 + math.log(2), abs=1e-12)
+
+
+# ----------------------------------------------------------------- level table
+
+@pytest.mark.parametrize("N,K,expect", [
+    (1024, 4, [16, 8]),
+    (4096, 8, [64, 32, 16]),
+    (16384, 32, [256, 128, 64]),
+    (65536, 8, [1024, 512, 256, 128, 64, 32, 16]),
+    (131072, 8, [2048, 1024, 512, 256, 128, 64, 32, 16]),
+    (262144, 8, [4096, 2048, 1024, 512, 256, 128, 64, 32, 16]),
+])
+def test_level_tables(N, K, expect):
+    assert oracle.levels(N, 64, K, 2)[1:] == expect
+
+
+def test_level_count_closed_form():
+    # L = 1 + ceil(log_g(n_1 / (g K))) once n_1 > g K (pyramid paragraph: O(log N) levels)
+    for e in range(10, 19):
+        N = 2 ** e
+        for K in (4, 8, 32):
+            n1 = N // 64
+            L = len(oracle.levels(N, 64, K, 2)) - 1
+            want = 1 if n1 <= 2 * K else 1 + math.ceil(math.log2(n1 / (2 * K)))
+            assert L == want
+    assert oracle.levels(1000, 64, 8, 2)[1:] == [16]
+    assert oracle.levels(5000, 64, 8, 3)[1:] == [79, 27, 9]
+
+
+# --------------------------------------------------------------------- pyramid
+
+def test_pyramid_is_direct_mean_on_full_trees():
+    p = oracle.Problem(1, 64 * 64, 1, 2, 16, 64, 4, 2, dtype=F32)
+    k = rng_arrays(1, (1, 2, p.seq_len, 16))
+    pyr = oracle.build_pyramid(p, k)
+    sizes = oracle.levels(p.seq_len, 64, 4, 2)
+    off = 0
+    for l in range(1, len(sizes)):
+        span = 64 * 2 ** (l - 1)
+        for h in range(2):
+            direct = k[0, h].astype(np.float64).reshape(sizes[l], span, 16).mean(axis=1)
+            np.testing.assert_allclose(pyr[0, h, off: off + sizes[l]], direct, rtol=0, atol=1e-12)
+        off += sizes[l]
+    assert off == pyr.shape[2]
+
+
+def test_pyramid_ragged_tail_and_odd_levels():
+    # N = 5*64 + 7: the last leaf averages its 7 present keys; odd counts leave
+    # single-child nodes whose mean is that child.
+    N, K, g = 5 * 64 + 7, 3, 2
+    p = oracle.Problem(1, N, 1, 1, 4, 64, K, g, dtype=F32)
+    k = rng_arrays(2, (1, 1, N, 4))
+    pyr = oracle.build_pyramid(p, k)[0, 0]
+    sizes = oracle.levels(N, 64, K, g)
+    assert sizes[1:] == [6]  # n1 = 6 <= g*K = 6 -> L = 1
+    kd = k[0, 0].astype(np.float64)
+    np.testing.assert_allclose(pyr[5], kd[320:327].mean(axis=0), atol=1e-12)
+    p2 = oracle.Problem(1, N, 1, 1, 4, 64, 3, 2, dtype=F32)
+    N2 = 13 * 64 + 1  # n1 = 14 -> 7 -> L=2 with K=3 (gK = 6 < 7?) -> n = [14, 7, 4]
+    p2 = oracle.Problem(1, N2, 1, 1, 4, 64, 3, 2, dtype=F32)
+    k2 = rng_arrays(3, (1, 1, N2, 4))
+    pyr2 = oracle.build_pyramid(p2, k2)[0, 0]
+    s2 = oracle.levels(N2, 64, 3, 2)
+    assert s2[1:] == [14, 7, 4]
+    kd2 = k2[0, 0].astype(np.float64)
+    np.testing.assert_allclose(pyr2[13], kd2[832:833].mean(axis=0), atol=1e-12)
+    lv2 = pyr2[14:21]
+    np.testing.assert_allclose(lv2[6], (pyr2[12] + pyr2[13]) / 2, atol=1e-12)
+    lv3 = pyr2[21:25]
+    np.testing.assert_allclose(lv3[3], lv2[6], atol=1e-12)  # single child
+    np.testing.assert_allclose(lv3[0], kd2[0:256].mean(axis=0), atol=1e-12)
+
+
+def test_bf16_inputs_are_read_exactly():
+    x = rng_arrays(4, (1, 1, 128, 8))
+    bits = synth.to_bf16_bits(x)
+    vals = synth.bf16_bits_to_f32(bits).astype(np.float64)
+    p = oracle.Problem(1, 128, 1, 1, 8, 64, 3, 2, dtype=BF16)
+    pyr = oracle.build_pyramid(p, bits)
+    np.testing.assert_allclose(pyr[0, 0, 0], vals[0, 0, :64].mean(axis=0), atol=1e-15)
+    # bf16 rounding is nearest-even on the float value
+    assert np.all(np.abs(vals - x) <= np.abs(x) * 2.0 ** -8 + 1e-30)
+
+
+# ---------------------------------------------------------- golden hand cases
+
+def _golden_inputs(g):
+    P = g["problem"]
+    p = oracle.Problem(P["batch"], P["seq_len"], P["n_q_heads"], P["n_kv_heads"], P["head_dim"], P["block"],
+                       P["top_k"], P["branch"], scale=P.get("scale", 0.0), dtype=F32)
+    return p
+
+
+def test_golden_zero_keys():
+    g = json.load(open(os.path.join(GOLDEN, "zero_keys.json")))
+    p = _golden_inputs(g)
+    assert oracle.levels(p.seq_len, p.block, p.top_k, p.branch) == g["levels"]
+    q = rng_arrays(5, (1, p.n_q_heads, p.seq_len, p.head_dim))
+    k = np.zeros((1, 1, p.seq_len, p.head_dim), dtype=np.float32)
+    rows = [c["i"] for c in g["cases"]]
+    idx, sc = oracle.select(p, q, k, rows=rows)
+    for t, c in enumerate(g["cases"]):
+        assert idx[t].tolist() == c["idx"], c
+        want = [p.group * math.log(n) if n else -math.inf for n in c["keys_seen"]]
+        for a, b in zip(sc[t], want):
+            assert (a == b) if math.isinf(b) else abs(a - b) < 1e-12
+
+
+def test_golden_monotone_keys_equal_brute_force():
+    g = json.load(open(os.path.join(GOLDEN, "monotone_keys.json")))
+    p = _golden_inputs(g)
+    N, C, d = p.seq_len, p.block, p.head_dim
+    q = np.zeros((1, p.n_q_heads, N, d), dtype=np.float32)
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, d), dtype=np.float32)
+    k[0, 0, :, 0] = 8.0 * (np.arange(N) // C)
+    rows = [c["i"] for c in g["cases"]]
+    idx, sc = oracle.select(p, q, k, rows=rows)
+    for t, c in enumerate(g["cases"]):
+        assert idx[t].tolist() == c["idx"], (c, idx[t])
+        for j, n, s in zip(c["idx"], c["keys_seen"], sc[t]):
+            if j < 0:
+                assert s == -math.inf
+            else:
+                assert abs(s - p.group * (2 * j + math.log(n))) < 1e-9
+    # and for every row: {0} u [max(1, b-K+2), b]
+    allidx, _ = oracle.select(p, q, k)
+    for i in range(0, N, 37):
+        b = i // C
+        want = sorted({0} | set(range(max(1, b - p.top_k + 2), b + 1)))
+        assert allidx[i].tolist() == want + [-1] * (p.top_k - len(want))
+
+
+# ---------------------------------------------------------- leaf and causal
+
+def test_leaf_score_closed_forms():
+    p = oracle.Problem(1, 1024, 4, 2, 32, 64, 4, 2, dtype=F32)
+    q = rng_arrays(6, (1, 4, 1024, 32))
+    k = rng_arrays(7, (1, 2, 1024, 32))
+    s = p.s
+    for h in range(2):
+        for b in (0, 3, 15):
+            i = 64 * b
+            row = h * 1024 + i
+            tot, ph = oracle.leaf_score(p, q, k, row, b)
+            want = [s * float(q[0, h * 2 + r, i].astype(np.float64) @ k[0, h, i].astype(np.float64))
+                    for r in range(2)]
+            np.testing.assert_allclose(ph, want, atol=1e-12)
+            assert abs(tot - sum(want)) < 1e-12
+            i2 = i + 1
+            _, ph2 = oracle.leaf_score(p, q, k, h * 1024 + i2, b)
+            for r in range(2):
+                x = [s * float(q[0, h * 2 + r, i2].astype(np.float64) @ k[0, h, t].astype(np.float64))
+                     for t in (i, i + 1)]
+                assert abs(ph2[r] - float(logsumexp(x))) < 1e-12
+
+
+def _prefill(seed, N, Hq, Hkv, d, K, dtype=F32, g=2, needles=2, B=1):
+    w = synth.custom(batch=B, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K, branch=g,
+                     dtype=dtype, seed=seed, needles=needles)
+    q, k, _ = synth.make_inputs(w)
+    p = oracle.Problem(B, N, Hq, Hkv, d, 64, K, g, dtype=dtype)
+    return p, q, k
+
+
+@pytest.mark.parametrize("N,K,G", [(1024, 4, 1), (3000, 8, 2), (4096 + 37, 3, 4), (777, 5, 1)])
+def test_selection_invariants(N, K, G):
+    p, q, k = _prefill(10 + N, N, 2 * G, 2, 16, K, B=2)
+    idx, sc = oracle.select(p, q, k)
+    idx = idx.reshape(2, 2, N, K)
+    sc = sc.reshape(2, 2, N, K)
+    for i in range(N):
+        b = i // 64
+        for bb in range(2):
+            for h in range(2):
+                row = idx[bb, h, i]
+                n = int((row >= 0).sum())
+                assert n == min(K, b + 1)
+                sel = row[:n]
+                assert np.all(np.diff(sel) > 0) and sel.max() <= b and sel.min() >= 0
+                assert np.all(row[n:] == -1) and np.all(np.isneginf(sc[bb, h, i, n:]))
+                for f in {0, b - 1, b}:
+                    if f >= 0:
+                        assert f in sel
+
+
+# ------------------------------------------------------ reduces to brute force
+
+def brute_force(p, q, k, row):
+    """F u TopK_{K-|F|} over every causal leaf block by raw-key LSE (numpy/scipy)."""
+    N, C, G = p.seq_len, p.block, p.group
+    bh, i = divmod(row, N)
+    b, h = divmod(bh, p.n_kv_heads)
+    qr = q[b, h * G:(h + 1) * G, i].astype(np.float64)
+    kk = k[b, h].astype(np.float64)
+    bq = i // C
+    scores = {}
+    for j in range(bq + 1):
+        hi = min(j * C + C, N, i + 1)
+        scores[j] = float(logsumexp(p.s * (qr @ kk[j * C:hi].T), axis=1).sum())
+    F = sorted({0, bq - 1, bq} & set(range(bq + 1)))
+    rest = sorted([j for j in scores if j not in F], key=lambda j: (-scores[j], j))
+    sel = sorted(F + rest[: p.top_k - len(F)])
+    return sel, [scores[j] for j in sel]
+
+
+def test_L1_regime_equals_brute_force():
+    # n_1 = 16 <= g*K = 16: the walk starts at the leaf level and scores every causal block
+    p, q, k = _prefill(21, 1024, 2, 1, 32, 8)
+    assert len(oracle.levels(1024, 64, 8, 2)) - 1 == 1
+    idx, sc = oracle.select(p, q, k)
+    for i in range(0, 1024, 7):
+        sel, s = brute_force(p, q, k, i)
+        assert idx[i, : len(sel)].tolist() == sel
+        np.testing.assert_allclose(sc[i, : len(sel)], s, atol=1e-9)
+
+
+def test_K_at_least_blocks_selects_every_causal_block():
+    p, q, k = _prefill(22, 1024, 1, 1, 64, 16)
+    idx, _ = oracle.select(p, q, k)
+    for i in range(1024):
+        b = i // 64
+        assert idx[i, : b + 1].tolist() == list(range(b + 1))
+        assert np.all(idx[i, b + 1:] == -1)
+
+
+# ------------------------------------------------- Jensen sandwich (Appendix A)
+
+def test_jensen_sandwich_intermediate_scores():
+    # log g + s<q, P_l[j]>  <=  S_h(l, j)  <=  LSE over node j's raw keys - log(C g^(l-2))
+    N, C, g, K, d = 64 * 64, 64, 2, 4, 16
+    p, q, k = _prefill(23, N, 2, 1, d, K)
+    pyr = oracle.build_pyramid(p, k)
+    sizes = oracle.levels(N, C, K, g)
+    offs = np.cumsum([0] + sizes[1:])
+    kd = k[0, 0].astype(np.float64)
+    i = N - 1
+    for l in range(2, len(sizes)):
+        for j in range(sizes[l]):
+            _, ph = oracle.node_score(p, q, pyr, i, l, j)
+            node_mean = pyr[0, 0, offs[l - 1] + j]
+            span = C * g ** (l - 1)
+            raw = kd[j * span:(j + 1) * span]
+            for r in range(2):
+                qq = q[0, r, i].astype(np.float64)
+                lower = math.log(g) + p.s * float(qq @ node_mean)
+                upper = float(logsumexp(p.s * (raw @ qq))) - math.log(C * g ** (l - 2))
+                assert lower - 1e-9 <= ph[r] <= upper + 1e-9
+
+
+# ------------------------------------------------------------ O(log N) counts
+
+def test_candidates_bounded_and_work_logarithmic():
+    C, K, g, d = 64, 8, 2, 8
+    seen = []
+    for e in range(11, 20, 2):
+        N = 2 ** e
+        p, q, k = _prefill(30 + e, N, 1, 1, d, K, needles=0)
+        rows = [N - 1, N // 2 + 5, N - 200]
+        _, _, st = oracle.select(p, q, k, rows=rows, stats=True)
+        L = len(oracle.levels(N, C, K, g)) - 1
+        assert np.all(st["max_cand"] <= g * K)
+        assert np.all(st["levels"] == L)
+        bound = (L - 1) * g * g * K + (g * K + 3) * C
+        assert np.all(st["dots"] <= bound)
+        brute = (N - 1) // C * C + 1
+        if e >= 15:
+            assert st["dots"][0] < brute / 4
+        seen.append((int(st["dots"][0]), brute))
+    # per-query work stays within a constant band while a full scan grows 128x
+    work = [w for w, _ in seen]
+    assert max(work) / min(work) < 1.6 and seen[-1][1] / seen[0][1] > 100
+
+
+# ------------------------------------------------------------------- GQA rule
+
+def test_gqa_identical_heads_scale_scores():
+    # G identical query heads give the single-head selection, scores times G
+    N, d, K = 4096, 16, 8
+    p1, q1, k = _prefill(40, N, 1, 1, d, K)
+    G = 4
+    qG = np.ascontiguousarray(np.repeat(q1, G, axis=1))
+    pG = oracle.Problem(1, N, G, 1, d, 64, K, 2, dtype=F32)
+    rows = list(range(0, N, 13))
+    i1, s1 = oracle.select(p1, q1, k, rows=rows)
+    iG, sG = oracle.select(pG, qG, k, rows=rows)
+    assert np.array_equal(i1, iG)
+    fin = i1 >= 0
+    np.testing.assert_allclose(sG[fin], G * s1[fin], rtol=1e-12)
+
+
+def test_gqa_group_is_sum_of_heads():
+    N, d, K = 2048, 16, 8
+    p, q, k = _prefill(41, N, 4, 2, d, K)
+    pyr = oracle.build_pyramid(p, k)
+    for row in (5, N + 700, 2 * N - 1):
+        tot, ph = oracle.leaf_score(p, q, k, row, 0)
+        assert abs(tot - ph.sum()) < 1e-12
+        tot2, ph2 = oracle.node_score(p, q, pyr, row, 2, 0)
+        assert abs(tot2 - ph2.sum()) < 1e-12
+
+
+# ----------------------------------------------------------- decode == prefill
+
+def test_decode_equals_last_prefill_row():
+    N, K = 4096 + 11, 8
+    p, q, k = _prefill(50, N, 4, 2, 16, K, B=2)
+    pyr = oracle.build_pyramid(p, k)
+    qdec = np.ascontiguousarray(q[:, :, N - 1, :])
+    idd, sd = oracle.select(p, qdec, k, pyr, decode=True)
+    rows = [(b * 2 + h) * N + N - 1 for b in range(2) for h in range(2)]
+    ip, sp = oracle.select(p, q, k, pyr, rows=rows)
+    assert np.array_equal(idd, ip)
+    np.testing.assert_array_equal(sd, sp)
+
+
+# --------------------------------------------------- independent second walk
+
+@pytest.mark.parametrize("N,K,G,g", [(1024, 4, 1, 2), (2048 + 50, 4, 2, 2), (3000, 3, 1, 3)])
+def test_matches_independent_numpy_walk(N, K, G, g):
+    p, q, k = _prefill(60 + N, N, G, 1, 16, K, g=g)
+    pyr = oracle.build_pyramid(p, k)
+    rows = list(range(0, N, 29)) + [N - 1]
+    idx, sc = oracle.select(p, q, k, pyr, rows=rows)
+    kd = k[0, 0].astype(np.float64)
+    for t, i in enumerate(rows):
+        wi, ws = select_one(q[0, :, i].astype(np.float64), kd, i, 64, K, g, p.s)
+        if idx[t].tolist() != wi:
+            # only acceptable where the two fp64 orders of summation tie-break differently
+            st, _ = oracle.check(p, q, k, pyr, [i], np.array([wi]), np.array([ws], dtype=np.float32),
+                                 tau=1e-9, rtol=1e-9)
+            assert st[0] == 0, (i, idx[t], wi)
+        else:
+            np.testing.assert_allclose(sc[t][np.isfinite(sc[t])], np.array(ws)[np.isfinite(ws)], rtol=1e-12)
+
+
+# --------------------------------------------------------- strong needle found
+
+def test_dominant_needle_is_found():
+    # a key aligned to query i with a huge norm dominates every LSE on its path
+    N, d, K = 8192, 16, 8
+    p, q, k = _prefill(70, N, 1, 1, d, K, needles=0)
+    r = np.random.default_rng(3)
+    for _ in range(6):
+        i = int(r.integers(1000, N))
+        pos = int(r.integers(0, i - 200))
+        kk = k.copy()
+        kk[0, 0, pos] = 4000.0 * q[0, 0, i] / np.linalg.norm(q[0, 0, i])
+        idx, _ = oracle.select(p, q, kk, rows=[i])
+        assert pos // 64 in idx[0].tolist()
