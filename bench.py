@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of libpisa's pyramid Top-K block selector on one MI355X.
+
+Headline (one "step"): pyramid build + prefill selection at 256K tokens, C=64, K=8, g=2,
+16 query / 4 KV heads, d=128, bf16 (the pages' selection-latency workload, synthetic
+inputs resident in HBM).  Also timed in the same run: the same step at 64K, and one
+decode step (32 sequences x 262144-token cache, precomputed pyramid; cold: each step
+follows a 1 GiB write that evicts L2 and MALL; warm: back to back).
+
+Prints one JSON line.  Per-stage times come from HIP events recorded by the library on
+the stream its kernels run on (pisa_select_prefill_staged) and around pisa_build_pyramid.
+The roofline entry is for the stage with the largest average time; its algorithmic work
+per launch is stated in the design notes.  ``cpu_baseline`` times the fp64 CPU oracle
+(test infrastructure) on a bounded sample of the 256K workload and scales it to the
+whole workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+METRIC = "pyramid selection latency ms @64K/256K prefill (C=64,K=8); decode µs/step"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+VALU_FP32_PEAK_TFLOPS = 157.3
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-64k", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=6144)
+    ap.add_argument("--only", choices=["256k", "64k", "decode"], default=None,
+                    help="time one workload only (profiling runs)")
+    return ap.parse_args()
+
+
+def dev(torch, a):
+    t = torch.from_numpy(a)
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.cuda()
+
+
+def visible(n_l, bq, shift):
+    return np.minimum(n_l, (bq >> shift) + 1)
+
+
+def routing_dots_per_query(levels, K, bq):
+    """Child dot products one query (one head) scores over the routing levels L..2.
+
+    Candidates at the top level are its visible nodes; below, the visible children of at
+    most K kept nodes (2K slots).  Exact except that a kept frontier node may have one
+    visible child instead of two (at most one dot per level less)."""
+    L = len(levels) - 1
+    if L == 1:
+        return np.zeros_like(bq)
+    dots = np.zeros_like(bq)
+    cand = visible(levels[L], bq, L - 1)
+    for l in range(L, 1, -1):
+        vis_child = visible(levels[l - 1], bq, l - 2)
+        all_vis = cand == visible(levels[l], bq, l - 1)
+        d = np.where(all_vis, vis_child, np.minimum(2 * cand, vis_child))
+        dots += d
+        cand = np.where(cand <= K, d, np.minimum(2 * K, vis_child))
+    return dots
+
+
+def forced_keys_per_query(N, C):
+    i = np.arange(N)
+    bq = i // C
+    keys = np.minimum(C, i + 1)                       # block 0 (causal if bq == 0)
+    keys = keys + np.where(bq >= 2, C, 0)             # previous block b-1 > 0
+    keys = keys + np.where(bq >= 1, i - bq * C + 1, 0)  # current block b > 0
+    return keys
+
+
+class Prefill:
+    def __init__(self, torch, pisa, synth, name):
+        self.torch, self.pisa = torch, pisa
+        self.w = w = synth.WORKLOADS[name]
+        t = time.time()
+        q, k, _ = synth.make_inputs(w)
+        log(f"{name}: inputs generated in {time.time() - t:.1f}s")
+        self.q, self.k = dev(torch, q), dev(torch, k)
+        del q, k
+        self.p = p = pisa.Problem(**w.shape())
+        self.pyr = torch.empty(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+        self.ws = pisa.workspace(p)
+        shape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+        self.oi = torch.empty(shape, dtype=torch.int32, device="cuda")
+        self.os = torch.empty(shape, dtype=torch.float32, device="cuda")
+
+    def step(self, ev=None):
+        pisa = self.pisa
+        if ev is None:
+            pisa.build_pyramid(self.p, self.k, self.pyr)
+            pisa.select_prefill(self.p, self.q, self.k, self.pyr, self.ws, self.oi, self.os)
+            return
+        ev[0].record()
+        pisa.build_pyramid(self.p, self.k, self.pyr)
+        pisa.select_prefill_staged(self.p, self.q, self.k, self.pyr, self.ws, self.oi, self.os, ev[1:6])
+
+    def run(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        for e in evs:  # torch creates the HIP event on first record; the library records them later
+            for x in e:
+                x.record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(steps):
+            self.step(evs[s])
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        names = ["build", "route", "group", "leaf", "final"]
+        stage = {n: [] for n in names}
+        for e in evs:
+            for j, n in enumerate(names):
+                stage[n].append(e[j].elapsed_time(e[j + 1]))
+        total = [e[0].elapsed_time(e[5]) for e in evs]
+        return wall_ms, {n: statistics.mean(v) for n, v in stage.items()}, statistics.median(total)
+
+    def work(self):
+        """Algorithmic work of each stage for one step (see the design notes)."""
+        p, w = self.p, self.w
+        d, G, C, K = p.head_dim, p.n_q_heads // p.n_kv_heads, p.block, p.top_k
+        L, levels, offs = self.pisa.levels(p)
+        T = offs[-1]
+        BH = p.batch * p.n_kv_heads
+        bq = np.arange(p.seq_len) // C
+        rdots = int(routing_dots_per_query(levels, K, bq).sum())
+        pairs = self.pisa.routed_pairs(p, self.ws)
+        fkeys = int(forced_keys_per_query(p.seq_len, C).sum())
+        return {
+            "build": ("hbm", BH * (p.seq_len * d * 2 + T * d * 4), "GB/s"),
+            "route": ("alu", BH * rdots * G * 2 * d, "TFLOP/s"),
+            "leaf": ("mfma", pairs * G * C * 2 * d, "TFLOP/s"),
+            "final": ("mfma", BH * fkeys * G * 2 * d, "TFLOP/s"),
+            "group": ("hbm", BH * p.seq_len * 2 * K * 4 * 4, "GB/s"),
+            "_pairs": pairs,
+            "_route_dots": BH * rdots,
+        }
+
+
+def roofline(stage_ms, work):
+    dom = max((n for n in stage_ms if n in work), key=lambda n: stage_ms[n])
+    bound, amount, unit = work[dom]
+    t = stage_ms[dom] * 1e-3
+    if unit == "GB/s":
+        achieved, peak = amount / t / 1e9, HBM_PEAK_GBS
+    else:
+        achieved = amount / t / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else VALU_FP32_PEAK_TFLOPS
+    return dom, {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                 "frac": round(achieved / peak, 4), "traffic": None}
+
+
+def time_decode(torch, pisa, synth, steps):
+    w = synth.WORKLOADS["decode"]
+    t = time.time()
+    q, k, _ = synth.make_inputs(w)
+    log(f"decode: inputs generated in {time.time() - t:.1f}s")
+    qd, kd = dev(torch, q), dev(torch, k)
+    del q, k
+    p = pisa.Problem(**w.shape())
+    pyr = pisa.build_pyramid(p, kd)
+    oi = torch.empty((p.batch, p.n_kv_heads, p.top_k), dtype=torch.int32, device="cuda")
+    os_ = torch.empty((p.batch, p.n_kv_heads, p.top_k), dtype=torch.float32, device="cuda")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > L2 + MALL
+    for _ in range(5):
+        pisa.select_decode(p, qd, kd, pyr, None, oi, os_)
+    torch.cuda.synchronize()
+    cold = []
+    for _ in range(steps):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pisa.select_decode(p, qd, kd, pyr, None, oi, os_)
+        b.record()
+        b.synchronize()
+        cold.append(a.elapsed_time(b) * 1e3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        pisa.select_decode(p, qd, kd, pyr, None, oi, os_)
+    b.record()
+    b.synchronize()
+    warm = a.elapsed_time(b) * 1e3 / steps
+    return statistics.median(cold), warm
+
+
+def cpu_baseline(synth, sample_rows):
+    import oracle
+    w = synth.WORKLOADS["256k"]
+    q, k, _ = synth.make_inputs(w)
+    op = oracle.Problem(**w.shape())
+    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    pyr = oracle.build_pyramid(op, k)
+    t1 = time.perf_counter()
+    total_rows = w.batch * w.n_kv_heads * w.seq_len
+    rows = np.sort(np.random.default_rng(0).choice(total_rows, sample_rows, replace=False))
+    oracle.select(op, q, k, pyr, rows=rows)
+    t2 = time.perf_counter()
+    est_ms = ((t1 - t0) + (t2 - t1) * total_rows / sample_rows) * 1e3
+    return {"value": round(est_ms, 1), "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": "fp64 C oracle: full pyramid build + selection of %d random query groups of %d "
+                      "(256K prefill, 16/4 heads), select time scaled by %d/%d; measured %.1fs" % (
+                          sample_rows, total_rows, total_rows, sample_rows, t2 - t0)}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py: this build runs on one GPU only (the selector shards by (batch, KV head) "
+              "with no exchange; multi-GPU runs are not part of it); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from block_selection_pyramid_amd import pisa, synth
+    pisa.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    out = {"metric": METRIC}
+    extra = {}
+    head = None
+    if a.only in (None, "256k"):
+        b = Prefill(torch, pisa, synth, "256k")
+        wall_ms, stage_ms, ev_ms = b.run(a.steps, a.warmup)
+        work = b.work()
+        dom, roof = roofline(stage_ms, work)
+        head = (b.w, wall_ms, stage_ms, ev_ms, dom, roof, work)
+        log("256k: wall %.3f ms/step, events %.3f ms; stages %s" % (
+            wall_ms, ev_ms, {k: round(v, 3) for k, v in stage_ms.items()}))
+        del b
+        torch.cuda.empty_cache()
+    if a.only in (None, "64k") and not a.no_64k:
+        b = Prefill(torch, pisa, synth, "64k")
+        wall64, stage64, ev64 = b.run(a.steps, a.warmup)
+        extra["prefill_64k_ms"] = round(wall64, 4)
+        extra["prefill_64k_stages_ms"] = {k: round(v, 4) for k, v in stage64.items()}
+        log("64k: wall %.3f ms/step; stages %s" % (wall64, extra["prefill_64k_stages_ms"]))
+        del b
+        torch.cuda.empty_cache()
+    if a.only in (None, "decode") and not a.no_decode:
+        cold, warm = time_decode(torch, pisa, synth, a.decode_steps)
+        extra["decode_us_per_step"] = round(cold, 2)
+        extra["decode_us_per_step_warm"] = round(warm, 2)
+        log("decode: cold %.2f us, warm %.2f us" % (cold, warm))
+        torch.cuda.empty_cache()
+    if head is None:
+        print(json.dumps(extra))
+        return
+    w, wall_ms, stage_ms, ev_ms, dom, roof, work = head
+    out.update({
+        "value": round(wall_ms, 4), "unit": "ms", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(wall_ms, 4), "higher_is_better": False, "scaling": "strong", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill-256k (pyramid build + selection)", "batch": w.batch, "seq_len": w.seq_len,
+                   "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
+                   "block": w.block, "top_k": w.top_k, "branch": w.branch, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "roofline_kernel": dom,
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "event_ms_per_step": round(ev_ms, 4),
+        "routed_pairs": work["_pairs"],
+    })
+    out.update(extra)
+    if not a.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(synth, a.cpu_sample_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

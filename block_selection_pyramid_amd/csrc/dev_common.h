@@ -1,0 +1,70 @@
+// Device helpers shared by the libpisa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pisa_internal.h"
+
+namespace pisa {
+
+using bf16 = uint16_t;  // raw bfloat16 bits
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Load 16 bytes of input starting at element e of row r and widen to float.
+// bf16: 8 elements, fp32: 4 elements.
+template <typename T>
+struct Vec;
+template <>
+struct Vec<bf16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void load(const bf16* p, float* out) {
+    uint4 u = *reinterpret_cast<const uint4*>(p);
+    out[0] = bf2f(u.x & 0xFFFFu); out[1] = bf2f(u.x >> 16);
+    out[2] = bf2f(u.y & 0xFFFFu); out[3] = bf2f(u.y >> 16);
+    out[4] = bf2f(u.z & 0xFFFFu); out[5] = bf2f(u.z >> 16);
+    out[6] = bf2f(u.w & 0xFFFFu); out[7] = bf2f(u.w >> 16);
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void load(const float* p, float* out) {
+    float4 v = *reinterpret_cast<const float4*>(p);
+    out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+  }
+};
+
+// Orders LDS traffic among the lanes of one wavefront.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Forced leaf blocks of a query in leaf block bq: {0, bq-1, bq} that exist, ascending.
+__device__ __forceinline__ int forced_blocks(int bq, int* f) {
+  int m = 0;
+  f[m++] = 0;
+  if (bq - 1 > 0) f[m++] = bq - 1;
+  if (bq > 0) f[m++] = bq;
+  return m;
+}
+__device__ __forceinline__ bool is_forced(int j, int bq) { return j == 0 || j == bq || j == bq - 1; }
+
+}  // namespace pisa

@@ -1,0 +1,84 @@
+// Leaf grouping: "groups queries that need the same leaf block and scores them together"
+// ("Block Sparse Attention with Log-Linear Complexity", rcap.io explainer, kernel
+// paragraph).  A counting sort over leaf blocks: the routing kernel histograms the
+// candidates per (batch, KV head, leaf block); here an exclusive scan turns the counts
+// into list offsets and into offsets of fixed-size work chunks, and a scatter writes each
+// (query, slot) candidate into its block's list.  Order inside a list does not affect any
+// result: every entry's score is computed on its own and written back to its slot.
+#include "dev_common.h"
+
+namespace pisa {
+
+namespace {
+
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __restrict__ cnt, int32_t M, int32_t qc,
+                                                            int32_t* __restrict__ off, int32_t* __restrict__ choff) {
+  __shared__ int32_t s_e[kScanThreads], s_c[kScanThreads];
+  const int t = threadIdx.x;
+  const int per = (M + kScanThreads - 1) / kScanThreads;
+  const int lo = min(M, t * per), hi = min(M, lo + per);
+  int se = 0, sc = 0;
+  for (int x = lo; x < hi; ++x) {
+    const int c = cnt[x];
+    se += c;
+    sc += (c + qc - 1) / qc;
+  }
+  s_e[t] = se;
+  s_c[t] = sc;
+  __syncthreads();
+  // inclusive Hillis-Steele scan of the per-thread sums
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int ae = t >= o ? s_e[t - o] : 0;
+    const int ac = t >= o ? s_c[t - o] : 0;
+    __syncthreads();
+    s_e[t] += ae;
+    s_c[t] += ac;
+    __syncthreads();
+  }
+  int be = s_e[t] - se, bc = s_c[t] - sc;  // exclusive prefix of this thread's segment
+  for (int x = lo; x < hi; ++x) {
+    off[x] = be;
+    choff[x] = bc;
+    const int c = cnt[x];
+    be += c;
+    bc += (c + qc - 1) / qc;
+  }
+  if (t == kScanThreads - 1) {
+    off[M] = s_e[t];
+    choff[M] = s_c[t];
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ cand, int64_t slots, int32_t N,
+                                                      int32_t twoK, int32_t n1, const int32_t* __restrict__ off,
+                                                      int32_t* __restrict__ cursor, int32_t* __restrict__ entries) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= slots) return;
+  const int leaf = cand[t];
+  if (leaf < 0) return;
+  const int slot = (int)(t % twoK);
+  const int64_t qg = t / twoK;  // bh * N + i
+  const int bh = (int)(qg / N), i = (int)(qg % N);
+  const int list = bh * n1 + leaf;
+  const int pos = off[list] + atomicAdd(&cursor[list], 1);
+  entries[pos] = (i << 6) | slot;
+}
+
+}  // namespace
+
+int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st) {
+  scan_kernel<<<1, kScanThreads, 0, st>>>(cnt, M, qc, off, choff);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
+                   hipStream_t st) {
+  const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
+  scatter_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(cand, slots, g.N, 2 * g.K, g.n1, off, cursor,
+                                                                   entries);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+}  // namespace pisa

@@ -1,0 +1,264 @@
+// Leaf scoring on the matrix cores (stage two of the two-stage prefill) and the forced
+// local blocks plus final Top-K.
+//
+// "Block Sparse Attention with Log-Linear Complexity": rcap.io explainer, kernel
+// paragraph (stage two groups queries that need the same leaf block so that each leaf key
+// tile is loaded once and reused); agihunt.info summary, LSE and forced-block paragraph
+// (leaf LSE over raw keys; first, previous and current blocks forced in) and kernels
+// paragraph (GQA heads share the selection).
+//
+// The pages reuse a key tile across up to four queries.  Here a workgroup stages one
+// 64 x d bf16 key tile in LDS and streams the (query, slot) entries of that block's list
+// through v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from LDS, B = 16 dims x 32
+// columns where a column is one (query, head) pair of a listed entry (32/G entries per
+// wavefront), so every MFMA is dense.  The epilogue takes a 64-key LSE per column in
+// registers (one cross-lane exchange), sums the G heads of an entry with shuffles and
+// writes the score to the entry's slot.
+//
+// MFMA operand layout (v_mfma_f32_32x32x16_bf16, wave64): lane l supplies row (l & 31)
+// of A and column (l & 31) of B, each with the 8 consecutive k of group (l >> 5); the
+// 16 results of lane l are column (l & 31), rows 8*(v/4) + 4*(l >> 5) + (v & 3).  The
+// head dimension is walked as k-step s, group hh -> d = hh*(d/2) + 8s .. 8s+7, the same
+// map for A and B, so each lane reads one contiguous half row of its query.
+#include "final_dev.h"
+
+namespace pisa {
+
+namespace {
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int acc_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
+
+// Stages rows [row0, row0 + 64) of one (b,h)'s keys into LDS (zero past N).
+template <int D>
+__device__ __forceinline__ void stage_tile(const bf16* __restrict__ kb, int row0, int N, bf16* kt) {
+  constexpr int LDSR = D + 8;
+  constexpr int TPR = D / 8;
+  for (int t = threadIdx.x; t < kLeaf * TPR; t += 256) {
+    const int r = t / TPR, c = (t % TPR) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row0 + r < N) v = *reinterpret_cast<const uint4*>(kb + (int64_t)(row0 + r) * D + c);
+    *reinterpret_cast<uint4*>(kt + r * LDSR + c) = v;
+  }
+}
+
+// 64 keys (LDS tile) x 32 columns (B fragments) -> two 32x32 accumulators.
+template <int D>
+__device__ __forceinline__ void tile_mfma(const bf16* kt, const bf16x8* bq, int col, int hh, f32x16& acc0,
+                                          f32x16& acc1) {
+  constexpr int LDSR = D + 8;
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    acc0[v] = 0.f;
+    acc1[v] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + hh * (D / 2) + s * 8);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + hh * (D / 2) + s * 8);
+    acc0 = mfma32(a0, bq[s], acc0);
+    acc1 = mfma32(a1, bq[s], acc1);
+  }
+}
+
+// Per-column LSE over the 64 rows held by this lane and its partner lane (l ^ 32),
+// in units of the scaled dot product.  Masked rows hold -inf; at least one row is live.
+__device__ __forceinline__ float column_lse(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(a0[v], a1[v]));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float sum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    sum += __builtin_amdgcn_exp2f((a0[v] - m) * s_log2e) + __builtin_amdgcn_exp2f((a1[v] - m) * s_log2e);
+  sum += __shfl_xor(sum, 32);
+  return s * m + logf(sum);
+}
+
+template <int D>
+__device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool valid, bf16x8* bq) {
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (valid) {
+      bq[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 8);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
+    }
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                        Geo geo, const int32_t* __restrict__ off,
+                                                        const int32_t* __restrict__ choff,
+                                                        const int32_t* __restrict__ entries, int32_t M,
+                                                        float* __restrict__ lscore) {
+  constexpr int EW = 32 / G;   // entries per wavefront
+  constexpr int QC = 4 * EW;   // entries per chunk (workgroup)
+  constexpr int KS = D / 16;
+  __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
+
+  const int c = blockIdx.x;
+  if (c >= choff[M]) return;  // uniform: grid is an upper bound on the chunk count
+  int lo = 0, hi = M;         // largest list whose first chunk is <= c
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (choff[mid] <= c) lo = mid; else hi = mid;
+  }
+  const int list = lo;
+  const int bh = list / geo.n1, j = list % geo.n1;
+  const int e0 = off[list] + (c - choff[list]) * QC;
+  const int e1 = min(e0 + QC, off[list + 1]);
+
+  stage_tile<D>(k + (int64_t)bh * geo.N * D, j * kLeaf, geo.N, kt);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const int e = e0 + wave * EW + col / G;
+  const int r = col % G;
+  const bool valid = e < e1;
+  const int ent = valid ? entries[e] : 0;
+  const int i = ent >> 6, slot = ent & 63;
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+
+  bf16x8 bq[KS];
+  load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D + hh * (D / 2), valid, bq);
+  f32x16 acc0, acc1;
+  tile_mfma<D>(kt, bq, col, hh, acc0, acc1);
+
+  // Routed blocks lie before the query's previous block, so all 64 keys exist and are
+  // causal; a short tail block is still masked for safety.
+  const int live = min(kLeaf, geo.N - j * kLeaf);
+  if (live < kLeaf) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      if (acc_row(v, hh) >= live) acc0[v] = -INFINITY;
+      if (32 + acc_row(v, hh) >= live) acc1[v] = -INFINITY;
+    }
+  }
+  float lse = column_lse(acc0, acc1, geo.s, geo.s_log2e);
+#pragma unroll
+  for (int o = 1; o < G; o <<= 1) lse += __shfl_xor(lse, o);
+  if (hh == 0 && r == 0 && valid) lscore[((int64_t)bh * geo.N + i) * (2 * geo.K) + slot] = lse;
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                           Geo geo, const int32_t* __restrict__ cand,
+                                                           const float* __restrict__ lscore,
+                                                           int32_t* __restrict__ out_idx,
+                                                           float* __restrict__ out_score) {
+  constexpr int KS = D / 16;
+  constexpr int LDSR = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 kt[3][kLeaf * LDSR];
+  __shared__ float fs[kLeaf][4];
+
+  const int bq = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  int F[3];
+  const int nf = forced_blocks(bq, F);
+  const bf16* kb = k + (int64_t)bh * geo.N * D;
+  for (int f = 0; f < nf; ++f) stage_tile<D>(kb, F[f] * kLeaf, geo.N, kt[f]);
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  // 64 queries x G heads = 2G groups of 32 columns
+  for (int cg = wave; cg < 2 * G; cg += 4) {
+    const int gc = cg * 32 + col;
+    const int ql = gc / G, r = gc % G;
+    const int i = bq * kLeaf + ql;
+    const bool valid = i < geo.N;
+    bf16x8 bfr[KS];
+    load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D + hh * (D / 2), valid, bfr);
+    for (int f = 0; f < nf; ++f) {
+      f32x16 acc0, acc1;
+      tile_mfma<D>(kt[f], bfr, col, hh, acc0, acc1);
+      const int t0 = F[f] * kLeaf;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int ta = t0 + acc_row(v, hh), tb = ta + 32;
+        if (ta > i || ta >= geo.N) acc0[v] = -INFINITY;
+        if (tb > i || tb >= geo.N) acc1[v] = -INFINITY;
+      }
+      // columns past N (last query block only) still see live keys, so no NaN arises
+      float lse = column_lse(acc0, acc1, geo.s, geo.s_log2e);
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) lse += __shfl_xor(lse, o);
+      if (hh == 0 && r == 0 && valid) fs[ql][f] = lse;
+    }
+  }
+  __syncthreads();
+
+  const int twoK = 2 * geo.K;
+  for (int ql = wave; ql < kLeaf; ql += 4) {
+    const int i = bq * kLeaf + ql;
+    if (i >= geo.N) break;
+    const int64_t row = (int64_t)bh * geo.N + i;
+    const int leaf = lane < twoK ? cand[row * twoK + lane] : -1;
+    const float sc = leaf >= 0 ? lscore[row * twoK + lane] : -INFINITY;
+    finalize_row(leaf, sc, F, nf, fs[ql], geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
+  }
+}
+
+template <int D>
+int leaf_d(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
+           const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
+  const int qc = chunk_entries(g.G);
+  const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
+  const int64_t grid = (slots + qc - 1) / qc + M;  // bound on sum over lists of ceil(count/qc)
+  const bf16* qq = (const bf16*)q;
+  const bf16* kk = (const bf16*)k;
+  switch (g.G) {
+    case 1: leaf_mfma_kernel<D, 1><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 2: leaf_mfma_kernel<D, 2><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 4: leaf_mfma_kernel<D, 4><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 8: leaf_mfma_kernel<D, 8><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 16: leaf_mfma_kernel<D, 16><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    default: return PISA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <int D>
+int forced_d(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore, int32_t* oi,
+             float* os, hipStream_t st) {
+  dim3 grid(g.n1, g.B * g.Hkv);
+  const bf16* qq = (const bf16*)q;
+  const bf16* kk = (const bf16*)k;
+  switch (g.G) {
+    case 1: forced_final_kernel<D, 1><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
+    case 2: forced_final_kernel<D, 2><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
+    case 4: forced_final_kernel<D, 4><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
+    case 8: forced_final_kernel<D, 8><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
+    case 16: forced_final_kernel<D, 16><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
+    default: return PISA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
+                     const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
+  if (g.d == 128) return leaf_d<128>(g, q, k, off, choff, entries, M, lscore, st);
+  if (g.d == 64) return leaf_d<64>(g, q, k, off, choff, entries, M, lscore, st);
+  return PISA_ERR_UNSUPPORTED;
+}
+
+int launch_forced_final(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore,
+                        int32_t* out_idx, float* out_score, hipStream_t st) {
+  if (g.d == 128) return forced_d<128>(g, q, k, cand, lscore, out_idx, out_score, st);
+  if (g.d == 64) return forced_d<64>(g, q, k, cand, lscore, out_idx, out_score, st);
+  return PISA_ERR_UNSUPPORTED;
+}
+
+}  // namespace pisa

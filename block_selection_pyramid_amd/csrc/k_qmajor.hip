@@ -1,0 +1,165 @@
+// Query-major leaf scoring and the fused decode kernel.
+//
+// Query-major: one wavefront per query group gathers each of its candidate leaf tiles and
+// the forced tiles and scores them on the VALU (lane = key).  This is the fp32-input
+// prefill path (MFMA has no fp32 x fp32 form at the needed rate; fp32 inputs are the
+// small correctness workloads).
+//
+// Decode ("Block Sparse Attention with Log-Linear Complexity", agihunt.info summary,
+// kernels paragraph: a single-stage kernel for decode avoids launch overhead; rcap.io
+// explainer: one query at a time leaves no cross-query tile reuse): one workgroup per
+// (sequence, KV head) walks the pyramid for the new query at position N-1 (wavefront 0),
+// then all four wavefronts score the candidate and forced tiles, and wavefront 0 writes
+// the selection.  Everything stays in LDS and registers; one launch per step.
+#include "final_dev.h"
+#include "route_dev.h"
+
+namespace pisa {
+
+namespace {
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void qmajor_kernel(const T* __restrict__ q, const T* __restrict__ k, Geo geo,
+                                                     const int32_t* __restrict__ cand, int32_t* __restrict__ out_idx,
+                                                     float* __restrict__ out_score) {
+  __shared__ float qs_all[4][G * (D + kQPad)];
+  __shared__ float sc_all[4][kMaxCand + 4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + wave;
+  const int bh = blockIdx.y;
+  if (i >= geo.N) return;  // whole wavefront; no workgroup barrier follows
+  float* qs = qs_all[wave];
+  float* scs = sc_all[wave];
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  const T* rows[G];
+#pragma unroll
+  for (int r = 0; r < G; ++r) rows[r] = q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D;
+  load_qrows<T, D, G>(rows, qs, lane);
+  wave_sync();
+
+  const int bq = i / geo.C;
+  int F[3];
+  const int nf = forced_blocks(bq, F);
+  const int twoK = 2 * geo.K;
+  const int64_t row = (int64_t)bh * geo.N + i;
+  const int leaf = lane < twoK ? cand[row * twoK + lane] : -1;
+  const T* keys = k + (int64_t)bh * geo.N * D;
+  for (int t = 0; t < twoK + nf; ++t) {
+    const int j = t < twoK ? __shfl(leaf, t) : F[t - twoK];
+    if (j < 0) continue;  // uniform across the wavefront
+    const float s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
+    if (lane == 0) scs[t] = s;
+  }
+  wave_sync();
+  const float sc = leaf >= 0 ? scs[lane] : -INFINITY;
+  finalize_row(leaf, sc, F, nf, scs + twoK, geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                     const float* __restrict__ pyr, Geo geo,
+                                                     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  __shared__ float qs[G * (D + kQPad)];
+  __shared__ WalkLds wl;
+  __shared__ int32_t tj[kMaxCand + 4];
+  __shared__ float tsc[kMaxCand + 4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int bh = blockIdx.x;
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  const int i = geo.N - 1;
+  const int bq = i / geo.C;
+  int F[3];
+  const int nf = forced_blocks(bq, F);
+  const int twoK = 2 * geo.K;
+  int leaf = -1;
+  if (wave == 0) {
+    const T* rows[G];
+#pragma unroll
+    for (int r = 0; r < G; ++r) rows[r] = q + ((int64_t)b * geo.Hq + h * G + r) * D;
+    load_qrows<T, D, G>(rows, qs, lane);
+    wave_sync();
+    const int nx = route_walk<D, G>(geo, pyr + (int64_t)bh * geo.T * D, qs, bq, &wl, lane);
+    if (lane < twoK) {
+      leaf = lane < nx ? wl.X[lane] : -1;
+      if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
+      tj[lane] = leaf;
+    }
+    if (lane < nf) tj[twoK + lane] = lane == 0 ? F[0] : (lane == 1 ? F[1] : F[2]);
+  }
+  __syncthreads();
+  const T* keys = k + (int64_t)bh * geo.N * D;
+  for (int t = wave; t < twoK + nf; t += 4) {
+    const int j = tj[t];
+    if (j < 0) continue;
+    const float s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
+    if (lane == 0) tsc[t] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float sc = leaf >= 0 ? tsc[lane] : -INFINITY;
+    finalize_row(leaf, sc, F, nf, tsc + twoK, geo.K, twoK, lane, out_idx + (int64_t)bh * geo.K,
+                 out_score + (int64_t)bh * geo.K);
+  }
+}
+
+template <typename T, int D>
+int qmajor_g(const Geo& g, const void* q, const void* k, const int32_t* cand, int32_t* oi, float* os,
+             hipStream_t st) {
+  dim3 grid((g.N + 3) / 4, g.B * g.Hkv);
+  const T* qq = (const T*)q;
+  const T* kk = (const T*)k;
+  switch (g.G) {
+    case 1: qmajor_kernel<T, D, 1><<<grid, 256, 0, st>>>(qq, kk, g, cand, oi, os); break;
+    case 2: qmajor_kernel<T, D, 2><<<grid, 256, 0, st>>>(qq, kk, g, cand, oi, os); break;
+    case 4: qmajor_kernel<T, D, 4><<<grid, 256, 0, st>>>(qq, kk, g, cand, oi, os); break;
+    case 8: qmajor_kernel<T, D, 8><<<grid, 256, 0, st>>>(qq, kk, g, cand, oi, os); break;
+    case 16: qmajor_kernel<T, D, 16><<<grid, 256, 0, st>>>(qq, kk, g, cand, oi, os); break;
+    default: return PISA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <typename T, int D>
+int decode_g(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* oi, float* os,
+             hipStream_t st) {
+  const unsigned grid = g.B * g.Hkv;
+  const T* qq = (const T*)q;
+  const T* kk = (const T*)k;
+  switch (g.G) {
+    case 1: decode_kernel<T, D, 1><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
+    case 2: decode_kernel<T, D, 2><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
+    case 4: decode_kernel<T, D, 4><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
+    case 8: decode_kernel<T, D, 8><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
+    case 16: decode_kernel<T, D, 16><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
+    default: return PISA_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+}  // namespace
+
+int launch_qmajor(const Geo& g, int dtype, const void* q, const void* k, const int32_t* cand, int32_t* out_idx,
+                  float* out_score, hipStream_t st) {
+  if (dtype == PISA_BF16) {
+    if (g.d == 128) return qmajor_g<bf16, 128>(g, q, k, cand, out_idx, out_score, st);
+    if (g.d == 64) return qmajor_g<bf16, 64>(g, q, k, cand, out_idx, out_score, st);
+  } else {
+    if (g.d == 128) return qmajor_g<float, 128>(g, q, k, cand, out_idx, out_score, st);
+    if (g.d == 64) return qmajor_g<float, 64>(g, q, k, cand, out_idx, out_score, st);
+  }
+  return PISA_ERR_UNSUPPORTED;
+}
+
+int launch_decode(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* out_idx,
+                  float* out_score, hipStream_t st) {
+  if (dtype == PISA_BF16) {
+    if (g.d == 128) return decode_g<bf16, 128>(g, q, k, pyr, out_idx, out_score, st);
+    if (g.d == 64) return decode_g<bf16, 64>(g, q, k, pyr, out_idx, out_score, st);
+  } else {
+    if (g.d == 128) return decode_g<float, 128>(g, q, k, pyr, out_idx, out_score, st);
+    if (g.d == 64) return decode_g<float, 64>(g, q, k, pyr, out_idx, out_score, st);
+  }
+  return PISA_ERR_UNSUPPORTED;
+}
+
+}  // namespace pisa

@@ -1,0 +1,54 @@
+// Internal declarations of libpisa: problem geometry, workspace layout, kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pisa.h"
+
+namespace pisa {
+
+constexpr int kMaxLevels = PISA_MAX_LEVELS;
+constexpr int kWave = 64;
+constexpr int kLeaf = 64;     // C supported by the kernels
+constexpr int kMaxCand = 64;  // g*K <= 64 candidates per level (one per lane)
+
+// Geometry of one problem, passed by value to every kernel.
+struct Geo {
+  int32_t B, Hq, Hkv, G, N, d, C, K, g, L, n1, T;
+  float s;        // scale applied to every dot product
+  float s_log2e;  // s * log2(e), for exp2-based LSE
+  int32_t n[kMaxLevels + 2];    // n[0] = N, n[l] nodes at level l (1..L)
+  int32_t off[kMaxLevels + 2];  // node offset of level l in one (b, h) pyramid
+};
+
+// Prefill workspace carve-up (byte offsets, 256-aligned).
+struct PrefillWs {
+  size_t cand, lscore, cnt, cursor, off, choff, entries, total;
+  int64_t slots;  // B*Hkv*N*2K
+  int32_t M;      // B*Hkv*n1 leaf lists
+};
+
+int make_geo(const pisa_problem* p, Geo* g);  // PISA_OK or PISA_ERR_INVALID_ARG
+int supported(const Geo& g, int dtype, int mode);
+PrefillWs prefill_ws(const Geo& g);
+inline int chunk_entries(int G) { return 128 / G; }  // leaf entries (query groups) per chunk
+
+// ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
+int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
+int launch_zero(int32_t* a, int64_t n, hipStream_t st);
+int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* cand, int32_t* cnt,
+                 hipStream_t st);
+int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
+int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
+                   hipStream_t st);
+int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
+                     const int32_t* entries, int32_t M, float* lscore, hipStream_t st);
+int launch_forced_final(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore,
+                        int32_t* out_idx, float* out_score, hipStream_t st);
+int launch_qmajor(const Geo& g, int dtype, const void* q, const void* k, const int32_t* cand, int32_t* out_idx,
+                  float* out_score, hipStream_t st);
+int launch_decode(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* out_idx,
+                  float* out_score, hipStream_t st);
+
+}  // namespace pisa

@@ -1,0 +1,255 @@
+"""Python binding of libpisa (argument marshalling only).
+
+Every step of the selection runs in the HIP kernels of ``libpisa.so``; this module checks
+tensor placement/dtype/contiguity, allocates outputs and workspace with torch when the
+caller does not pass them, and calls the C ABI declared in ``include/pisa.h`` on torch's
+current HIP stream.  There is no CPU fallback: if the library is missing or fails to load,
+every call raises.
+
+Names follow the C ABI: ``build_pyramid``, ``select_prefill``, ``select_decode``,
+``levels``, ``pyramid_bytes``, ``workspace_bytes``, ``supported``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+from . import build as _build
+
+F32, BF16 = 0, 1
+PREFILL, DECODE = 0, 1
+MAX_LEVELS = 32
+LIB_PATH = _build.OUT
+
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error",
+           5: "internal error"}
+
+
+class PisaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class _CProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("seq_len", ctypes.c_int32),
+        ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("top_k", ctypes.c_int32),
+        ("branch", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+@dataclass(frozen=True)
+class Problem:
+    batch: int
+    seq_len: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    block: int = 64
+    top_k: int = 8
+    branch: int = 2
+    scale: float = 0.0
+    dtype: int = BF16
+
+    def c(self) -> _CProblem:
+        return _CProblem(self.batch, self.seq_len, self.n_q_heads, self.n_kv_heads, self.head_dim, self.block,
+                         self.top_k, self.branch, self.scale, self.dtype)
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == F32 else torch.bfloat16
+
+    @property
+    def s(self) -> float:
+        return self.scale if self.scale > 0 else 1.0 / math.sqrt(self.head_dim)
+
+
+_lib = None
+
+EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
+           "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs", "pisa_select_decode",
+           "pisa_status_string", "pisa_version")
+
+
+def load(path: str | None = None):
+    """Loads libpisa.so (building it first only if no build exists)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        _build.build(force=True)
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(_CProblem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.pisa_levels.argtypes = [P, vp, vp, vp]
+    lib.pisa_supported.argtypes = [P, ctypes.c_int]
+    lib.pisa_pyramid_bytes.argtypes = [P]
+    lib.pisa_pyramid_bytes.restype = sz
+    lib.pisa_workspace_bytes.argtypes = [P, ctypes.c_int]
+    lib.pisa_workspace_bytes.restype = sz
+    lib.pisa_build_pyramid.argtypes = [P, vp, vp, vp]
+    lib.pisa_select_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.pisa_select_prefill_staged.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp, ctypes.c_int32, vp]
+    lib.pisa_prefill_routed_pairs.argtypes = [P, vp, sz, vp, vp]
+    lib.pisa_select_decode.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.pisa_status_string.argtypes = [ctypes.c_int]
+    lib.pisa_status_string.restype = ctypes.c_char_p
+    lib.pisa_version.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise PisaError(rc, what)
+
+
+def levels(p: Problem):
+    """(L, [n_0..n_L], [offset of level 1..L+1])."""
+    n = (ctypes.c_int32)()
+    nodes = (ctypes.c_int64 * (MAX_LEVELS + 2))()
+    offs = (ctypes.c_int64 * (MAX_LEVELS + 2))()
+    _check(load().pisa_levels(ctypes.byref(p.c()), ctypes.byref(n), nodes, offs), "pisa_levels")
+    L = n.value
+    return L, list(nodes[: L + 1]), list(offs[1: L + 2])
+
+
+def supported(p: Problem, mode: int = PREFILL) -> int:
+    return load().pisa_supported(ctypes.byref(p.c()), mode)
+
+
+def pyramid_bytes(p: Problem) -> int:
+    return load().pisa_pyramid_bytes(ctypes.byref(p.c()))
+
+
+def workspace_bytes(p: Problem, mode: int = PREFILL) -> int:
+    return load().pisa_workspace_bytes(ctypes.byref(p.c()), mode)
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape=None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def pyramid_shape(p: Problem):
+    L, nodes, offs = levels(p)
+    return (p.batch, p.n_kv_heads, offs[-1], p.head_dim)
+
+
+def build_pyramid(p: Problem, k: torch.Tensor, pyramid: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    shape = pyramid_shape(p)
+    kp = _dev(k, "k", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    if pyramid is None:
+        pyramid = torch.empty(shape, dtype=torch.float32, device=k.device)
+    pp = _dev(pyramid, "pyramid", torch.float32, shape)
+    _check(load().pisa_build_pyramid(ctypes.byref(p.c()), kp, pp, _stream(stream)), "pisa_build_pyramid")
+    return pyramid
+
+
+def workspace(p: Problem, mode: int = PREFILL, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(p, mode)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def select_prefill(p: Problem, q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tensor,
+                   ws: torch.Tensor | None = None, out_idx: torch.Tensor | None = None,
+                   out_score: torch.Tensor | None = None, stream=None):
+    """Returns (idx int32 [B, Hkv, N, K], score fp32 [B, Hkv, N, K])."""
+    oshape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+    qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.seq_len, p.head_dim))
+    kp = _dev(k, "k", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    if ws is None:
+        ws = workspace(p, PREFILL, q.device)
+    if out_idx is None:
+        out_idx = torch.empty(oshape, dtype=torch.int32, device=q.device)
+    if out_score is None:
+        out_score = torch.empty(oshape, dtype=torch.float32, device=q.device)
+    wp = _dev(ws, "workspace", torch.uint8)
+    ip = _dev(out_idx, "out_idx", torch.int32, oshape)
+    sp = _dev(out_score, "out_score", torch.float32, oshape)
+    _check(load().pisa_select_prefill(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, _stream(stream)),
+           "pisa_select_prefill")
+    return out_idx, out_score
+
+
+def select_prefill_staged(p: Problem, q, k, pyramid, ws, out_idx, out_score, events, stream=None):
+    """pisa_select_prefill recording 5 torch.cuda.Event (enable_timing=True) at its stage
+    boundaries (route | group | leaf | forced+final)."""
+    oshape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+    qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.seq_len, p.head_dim))
+    kp = _dev(k, "k", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    wp = _dev(ws, "workspace", torch.uint8)
+    ip = _dev(out_idx, "out_idx", torch.int32, oshape)
+    sp = _dev(out_score, "out_score", torch.float32, oshape)
+    if len(events) != 5:
+        raise ValueError("need 5 events")
+    arr = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
+    _check(load().pisa_select_prefill_staged(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, arr, 5,
+                                             _stream(stream)), "pisa_select_prefill_staged")
+    return out_idx, out_score
+
+
+def routed_pairs(p: Problem, ws: torch.Tensor, stream=None) -> int:
+    """Blocking diagnostic: (query group, leaf block) pairs routed to leaf scoring."""
+    out = ctypes.c_int64()
+    _check(load().pisa_prefill_routed_pairs(ctypes.byref(p.c()), _dev(ws, "workspace", torch.uint8), ws.numel(),
+                                            ctypes.byref(out), _stream(stream)), "pisa_prefill_routed_pairs")
+    return out.value
+
+
+def select_decode(p: Problem, q: torch.Tensor, k_cache: torch.Tensor, pyramid: torch.Tensor,
+                  ws: torch.Tensor | None = None, out_idx: torch.Tensor | None = None,
+                  out_score: torch.Tensor | None = None, stream=None):
+    """Returns (idx int32 [B, Hkv, K], score fp32 [B, Hkv, K]) for the query at N-1."""
+    oshape = (p.batch, p.n_kv_heads, p.top_k)
+    qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.head_dim))
+    kp = _dev(k_cache, "k_cache", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    nws = workspace_bytes(p, DECODE)
+    wp, wn = None, 0
+    if ws is not None:
+        wp, wn = _dev(ws, "workspace", torch.uint8), ws.numel()
+    elif nws:
+        ws = workspace(p, DECODE, q.device)
+        wp, wn = ws.data_ptr(), ws.numel()
+    if out_idx is None:
+        out_idx = torch.empty(oshape, dtype=torch.int32, device=q.device)
+    if out_score is None:
+        out_score = torch.empty(oshape, dtype=torch.float32, device=q.device)
+    ip = _dev(out_idx, "out_idx", torch.int32, oshape)
+    sp = _dev(out_score, "out_score", torch.float32, oshape)
+    _check(load().pisa_select_decode(ctypes.byref(p.c()), qp, kp, pp, wp, wn, ip, sp, _stream(stream)),
+           "pisa_select_decode")
+    return out_idx, out_score
+
+
+def version() -> str:
+    return load().pisa_version().decode()

@@ -1,0 +1,174 @@
+/*
+ * pisa.h -- C ABI of libpisa, PISA's pyramid Top-K block selector on MI355X (gfx950).
+ *
+ * The method ("Block Sparse Attention with Log-Linear Complexity", as summarised on
+ * agihunt.info and explained on rcap.io) picks, for each query of a block-sparse
+ * attention layer, the K leaf key blocks (tiles of C consecutive keys) it will attend to:
+ *
+ *   - keys are mean-pooled into a pyramid: level 1 holds one mean per leaf block of C
+ *     keys, each coarser level holds the mean of g adjacent nodes of the level below
+ *     (agihunt.info, pyramid paragraph; rcap.io, "think of the keys as leaves of a tree");
+ *   - the walk starts at the coarsest stored level, scores each candidate node by the
+ *     LogSumExp over its children of the scaled dot products q.child, keeps the Top-K and
+ *     expands only their children, so each level scores at most g*K candidates (rcap.io,
+ *     top-down walk and scoring-rule paragraphs);
+ *   - at the leaf level the LSE runs over the block's raw keys, causally masked, and the
+ *     first, previous and current leaf blocks are forced in (agihunt.info, LSE and
+ *     forced-block paragraph);
+ *   - the query heads of one GQA group share one selection (agihunt.info, kernels
+ *     paragraph).
+ *
+ * Readings fixed by this library where the pages are silent:
+ *   - the stored pyramid stops at the first level L with at most g*K nodes (every coarser
+ *     level would hold <= K nodes, all of which a walk from a root keeps);
+ *   - one pyramid per (batch, KV head); the group's score of a node is the SUM over its G
+ *     query heads of the per-head LSE; Top-K orders by score descending, then block index
+ *     ascending (lower index wins ties);
+ *   - causality above the leaves is node-granular: a node covering leaf blocks starting at
+ *     f is visible to a query in leaf block b iff f <= b; its full stored mean is used;
+ *   - forced blocks F = {0, b-1, b} (those that exist) count inside K: the output is
+ *     F u TopK_{K-|F|}(leaf candidates \ F), so K >= 3 and |selection| = min(K, b+1);
+ *   - the scale s (default 1/sqrt(d)) multiplies each dot product in fp32; inputs are
+ *     read exactly and every dot product and LSE is accumulated in fp32.
+ *
+ * Layouts (all row-major, contiguous, 16-byte aligned device memory on the current
+ * device; query head hq belongs to KV head hq / G with G = n_q_heads / n_kv_heads):
+ *   q (prefill)   [B, Hq, N, d]     dtype of the problem (fp32 or bf16)
+ *   q (decode)    [B, Hq, d]        the new token's query, at position N-1
+ *   k / k_cache   [B, Hkv, N, d]    dtype of the problem
+ *   pyramid       [B, Hkv, T, d]    fp32, T = sum of level sizes, level 1 (leaves) first;
+ *                                   see pisa_levels for the level offsets
+ *   out_idx       [B, Hkv, N, K] (prefill) or [B, Hkv, K] (decode), int32: selected leaf
+ *                 block ids in ascending order, padded with -1
+ *   out_score     same shape, fp32: each selected block's group-summed causal leaf LSE,
+ *                 padded with -inf
+ *
+ * Ownership and execution: the caller allocates every buffer (inputs, pyramid, workspace,
+ * outputs); the library allocates nothing and keeps no pointer after a call returns.
+ * Compute calls are asynchronous: they validate their arguments on the host (returning an
+ * error before any HIP call), enqueue kernels on `stream` and return without
+ * synchronising.  Faults inside kernels surface at the caller's next synchronisation.
+ * Calls on one stream are ordered; concurrent calls must not share a workspace.  The
+ * library keeps no state between calls and no C++ exception crosses this interface.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t is `struct ihipStream_t*`; NULL means the default stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* pisa_stream_t;
+
+#define PISA_MAX_LEVELS 32
+
+enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 };
+
+enum pisa_mode { PISA_PREFILL = 0, PISA_DECODE = 1 };
+
+enum pisa_status {
+  PISA_OK = 0,
+  PISA_ERR_INVALID_ARG = 1, /* bad shape, null pointer, misalignment */
+  PISA_ERR_UNSUPPORTED = 2, /* valid problem outside the kernels' support matrix */
+  PISA_ERR_WORKSPACE = 3,   /* workspace smaller than pisa_workspace_bytes() */
+  PISA_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  PISA_ERR_INTERNAL = 5
+};
+
+typedef struct {
+  int32_t batch;      /* B >= 1 */
+  int32_t seq_len;    /* N >= 1: prefill length; decode: key-cache length incl. the new token */
+  int32_t n_q_heads;  /* Hq, a multiple of n_kv_heads */
+  int32_t n_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;   /* d */
+  int32_t block;      /* C, keys per leaf block */
+  int32_t top_k;      /* K >= 3 (the three forced blocks count inside K) */
+  int32_t branch;     /* g >= 2, children per pyramid node */
+  float scale;        /* s; <= 0 selects 1/sqrt(d) */
+  int32_t dtype;      /* enum pisa_dtype, of q and k */
+} pisa_problem;
+
+/*
+ * Level table.  level_nodes[l] (l = 0..L) holds n_l with n_0 = N, n_1 = ceil(N/C),
+ * n_l = ceil(n_{l-1}/g), L = first level with n_L <= g*K.  level_offset[l] (l = 1..L+1) is
+ * the node offset of level l inside one (batch, KV head) pyramid (level_offset[1] = 0,
+ * level_offset[L+1] = T).  Both arrays must hold PISA_MAX_LEVELS + 2 entries; either may
+ * be NULL.  Returns PISA_OK or PISA_ERR_INVALID_ARG.
+ */
+int pisa_levels(const pisa_problem* p, int32_t* n_levels, int64_t* level_nodes, int64_t* level_offset);
+
+/* PISA_OK if the kernels support this problem in this mode, else the error code. */
+int pisa_supported(const pisa_problem* p, int mode);
+
+/* Bytes of the fp32 pyramid [B, Hkv, T, d]; 0 for an invalid problem. */
+size_t pisa_pyramid_bytes(const pisa_problem* p);
+
+/* Bytes of device workspace a call in `mode` needs (may be 0); 0 for an invalid problem. */
+size_t pisa_workspace_bytes(const pisa_problem* p, int mode);
+
+/*
+ * Builds the pyramid of k [B, Hkv, N, d] into `pyramid` (agihunt.info, pyramid paragraph:
+ * level 1 = mean of each leaf block's keys, a short last block averaging the keys it has;
+ * level l = unweighted mean of the g (or fewer, at the end) level l-1 nodes below it).
+ * One pass over k in HBM; the result is reused by every prefill or decode call on k.
+ */
+int pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyramid, pisa_stream_t stream);
+
+/*
+ * Prefill selection for every query position i in [0, N) of every (batch, KV head):
+ * routing walk over levels L..2, leaf LSE scoring of the candidates, forced blocks and
+ * Top-K as described above.  `pyramid` must hold pisa_build_pyramid's result for k.
+ * Writes out_idx / out_score [B, Hkv, N, K].
+ */
+int pisa_select_prefill(const pisa_problem* p, const void* q, const void* k, const float* pyramid,
+                        void* workspace, size_t workspace_bytes, int32_t* out_idx, float* out_score,
+                        pisa_stream_t stream);
+
+/*
+ * Decode selection for one new query per sequence, at position N-1 of a key cache of
+ * length N that already holds the new token's key; one fused kernel (agihunt.info,
+ * kernels paragraph: single-stage decode).  Equal to row N-1 of pisa_select_prefill on
+ * the same keys.  Writes out_idx / out_score [B, Hkv, K].
+ */
+int pisa_select_decode(const pisa_problem* p, const void* q, const void* k_cache, const float* pyramid,
+                       void* workspace, size_t workspace_bytes, int32_t* out_idx, float* out_score,
+                       pisa_stream_t stream);
+
+/*
+ * Same as pisa_select_prefill, and additionally records caller-created HIP events
+ * (hipEvent_t handles, e.g. from hipEventCreate) on `stream` at the stage boundaries:
+ * events[0] before the first kernel, events[1] after routing (counter clearing + the
+ * routing walk), events[2] after leaf grouping (scan + scatter), events[3] after leaf
+ * scoring, events[4] after forced blocks + final Top-K.  n_events must be 5.  Stages a
+ * problem does not use (fp32 inputs score leaves query-major in stage 3) record their
+ * boundary events back to back.  For per-kernel timing of the prefill path.
+ */
+int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void* k, const float* pyramid,
+                               void* workspace, size_t workspace_bytes, int32_t* out_idx, float* out_score,
+                               void* const* events, int32_t n_events, pisa_stream_t stream);
+
+/*
+ * Diagnostic, blocking: after a bf16 pisa_select_prefill on `stream` with `workspace`,
+ * waits for the stream and reports how many (query group, leaf block) pairs the routing
+ * walk sent to leaf scoring (forced blocks excluded).  fp32 problems report the number of
+ * non-empty routed candidate slots the same way.
+ */
+int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size_t workspace_bytes,
+                              int64_t* routed_pairs, pisa_stream_t stream);
+
+/* Static description of a status code. */
+const char* pisa_status_string(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char* pisa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PISA_H_ */

@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/pisa.h
+declares, and rejects bad arguments on the host before any HIP call (no compute call
+here ever passes validation, so nothing touches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from block_selection_pyramid_amd import build as pbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pisa.h")
+
+
+@pytest.fixture(scope="module")
+def pisa():
+    from block_selection_pyramid_amd import pisa as m
+    m.load()
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pisa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_three_entry_points():
+    fns = declared_functions()
+    for f in ("pisa_build_pyramid", "pisa_select_prefill", "pisa_select_decode"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(pisa):
+    lib = pisa.load()
+    for f in declared_functions():
+        assert hasattr(lib, f), f
+    assert set(pisa.EXPORTS) == set(declared_functions())
+    # exported names are plain C symbols (extern "C")
+    out = os.popen("nm -D --defined-only %s" % pbuild.OUT).read()
+    for f in declared_functions():
+        assert re.search(r"\bT %s$" % f, out, flags=re.M), f
+
+
+def test_status_strings_and_version(pisa):
+    lib = pisa.load()
+    assert lib.pisa_status_string(0) == b"ok"
+    assert lib.pisa_status_string(3) == b"workspace too small"
+    assert re.match(r"^\d+\.\d+\.\d+$", pisa.version())
+
+
+@pytest.mark.parametrize("N,K", [(1024, 4), (4096, 8), (16384, 32), (65536, 8), (262144, 8), (1000, 3),
+                                 (4096 + 37, 5), (1, 8), (64 * 17, 4)])
+def test_level_table_matches_oracle(pisa, N, K):
+    p = pisa.Problem(1, N, 4, 1, 128, 64, K, 2)
+    L, nodes, offs = pisa.levels(p)
+    assert nodes == oracle.levels(N, 64, K, 2)
+    assert offs[0] == 0 and offs[-1] == sum(nodes[1:])
+    assert pisa.pyramid_bytes(p) == 4 * offs[-1] * 128
+
+
+def test_sizes(pisa):
+    p = pisa.Problem(1, 262144, 16, 4, 128, 64, 8, 2)
+    assert pisa.pyramid_bytes(p) == 4 * 4 * 8176 * 128
+    ws = pisa.workspace_bytes(p, pisa.PREFILL)
+    slots = 4 * 262144 * 16
+    assert ws >= slots * 12 and ws < slots * 12 + 4 * 4 * 4096 * 4 + 4096
+    assert pisa.workspace_bytes(p, pisa.DECODE) == 0
+
+
+def _call_prefill(pisa, p, ws_bytes=1 << 40, q=0x1000, k=0x1000, pyr=0x1000, ws=0x1000, oi=0x1000, os_=0x1000):
+    lib = pisa.load()
+    return lib.pisa_select_prefill(ctypes.byref(p.c()), q, k, pyr, ws, ws_bytes, oi, os_, None)
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("seq_len", 0), ("n_q_heads", 6), ("n_kv_heads", 0),
+                                         ("top_k", 2), ("branch", 1), ("head_dim", 0), ("block", 0),
+                                         ("dtype", 7)])
+def test_invalid_arguments(pisa, field, value):
+    base = dict(batch=1, seq_len=4096, n_q_heads=16, n_kv_heads=4, head_dim=128)
+    base[field] = value
+    p = pisa.Problem(**base)
+    assert pisa.supported(p) == 1
+    assert pisa.pyramid_bytes(p) == 0 and pisa.workspace_bytes(p) == 0
+    assert _call_prefill(pisa, p) == 1
+    lib = pisa.load()
+    assert lib.pisa_build_pyramid(ctypes.byref(p.c()), 0x1000, 0x1000, None) == 1
+    assert lib.pisa_select_decode(ctypes.byref(p.c()), 0x1000, 0x1000, 0x1000, None, 0, 0x1000, 0x1000, None) == 1
+
+
+def test_null_and_misaligned_pointers(pisa):
+    p = pisa.Problem(1, 4096, 16, 4, 128)
+    assert _call_prefill(pisa, p, q=0) == 1
+    assert _call_prefill(pisa, p, oi=0) == 1
+    assert _call_prefill(pisa, p, k=0x1004) == 1
+    lib = pisa.load()
+    assert lib.pisa_build_pyramid(ctypes.byref(p.c()), 0x1002, 0x1000, None) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=96), dict(block=32), dict(branch=3), dict(top_k=33),
+                                dict(n_q_heads=12, n_kv_heads=4), dict(n_q_heads=64, n_kv_heads=2)])
+def test_unsupported_problems(pisa, kw):
+    base = dict(batch=1, seq_len=4096, n_q_heads=16, n_kv_heads=4, head_dim=128)
+    base.update(kw)
+    p = pisa.Problem(**base)
+    assert pisa.supported(p) == 2
+    assert _call_prefill(pisa, p) == 2
+
+
+def test_workspace_too_small(pisa):
+    p = pisa.Problem(1, 4096, 16, 4, 128)
+    need = pisa.workspace_bytes(p)
+    assert _call_prefill(pisa, p, ws_bytes=need - 1) == 3
+
+
+def test_binding_rejects_host_tensors(pisa):
+    import torch
+    p = pisa.Problem(1, 128, 4, 1, 64)
+    k = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pisa.build_pyramid(p, k, torch.zeros(1, 1, 3, 64))
