@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-64k", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=6144)
+    ap.add_argument("--cpu-sample-rows", type=int, default=262144)
     ap.add_argument("--only", choices=["256k", "64k", "decode"], default=None,
                     help="time one workload only (profiling runs)")
     return ap.parse_args()
