@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=262144)
     ap.add_argument("--only", choices=["256k", "64k", "decode"], default=None,
                     help="time one workload only (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
     return ap.parse_args()
 
 
@@ -151,7 +153,7 @@ class Prefill:
         pairs = self.pisa.routed_pairs(p, self.ws)
         fkeys = int(forced_keys_per_query(p.seq_len, C).sum())
         return {
-            "build": ("hbm", BH * (p.seq_len * d * 2 + T * d * 4), "GB/s"),
+            "build": ("hbm", BH * (p.seq_len * d * 2 + T * d * 8), "GB/s"),
             "route": ("alu", BH * rdots * G * 2 * d, "TFLOP/s"),
             "leaf": ("mfma", pairs * G * C * 2 * d, "TFLOP/s"),
             "final": ("mfma", BH * fkeys * G * 2 * d, "TFLOP/s"),
@@ -243,6 +245,12 @@ def main():
         sys.exit(1)
     out = {"metric": METRIC}
     extra = {}
+    if a.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     head = None
     if a.only in (None, "256k"):
         b = Prefill(torch, pisa, synth, "256k")

@@ -15,6 +15,27 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
+// float -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f2bf_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Routing copy of the pyramid: node n of one (b, h) occupies 2*D bf16 as D/32 chunks of
+// [hi(32 dims) | lo(32 dims)] (128 bytes, one cache line each) with hi = bf16(P) and
+// lo = bf16(P - hi).  It follows the fp32 means in the pyramid buffer.
+__device__ __forceinline__ int64_t rcopy_index(int64_t node, int e, int D) {
+  return node * 2 * D + (e >> 5) * 64 + (e & 31);
+}
+template <int D>
+__device__ __forceinline__ void store_rcopy(bf16* R, int64_t node, int e, float v) {
+  const uint32_t hi = f2bf_rne(v);
+  const float rest = v - bf2f(hi);
+  const int64_t i = rcopy_index(node, e, D);
+  R[i] = (bf16)hi;
+  R[i + 32] = (bf16)f2bf_rne(rest);
+}
+
 // Load 16 bytes of input starting at element e of row r and widen to float.
 // bf16: 8 elements, fp32: 4 elements.
 template <typename T>

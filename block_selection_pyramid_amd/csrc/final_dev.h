@@ -52,11 +52,15 @@ __device__ float score_tile_valu(const T* __restrict__ keys /* this (b,h) */, in
 __device__ __forceinline__ void finalize_row(int leaf, float sc, const int* F, int nf, const float* fsc, int K,
                                              int twoK, int lane, int32_t* __restrict__ oi,
                                              float* __restrict__ os) {
+  // Rank on a total order of (score desc, index asc): ranks are distinct even for scores
+  // that compare unordered, so at most K - |F| candidates are kept.
+  const uint32_t u = __float_as_uint(sc);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint64_t my = leaf >= 0 ? (((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)leaf)) : 0ull;
   int rank = 0;
   for (int y = 0; y < twoK; ++y) {
-    const int oy = __shfl(leaf, y);
-    const float so = __shfl(sc, y);
-    rank += oy >= 0 && (so > sc || (so == sc && oy < leaf));
+    const uint64_t oy = __shfl(my, y);
+    rank += oy > my;
   }
   const int kept = leaf >= 0 && rank < K - nf;
   // ascending output position: selected entries (kept or forced) with a smaller index
@@ -72,11 +76,11 @@ __device__ __forceinline__ void finalize_row(int leaf, float sc, const int* F, i
     pos += F[f] < leaf;
     pf += F[f] < fj;
   }
-  if (kept) {
+  if (kept && pos < K) {
     oi[pos] = leaf;
     os[pos] = sc;
   }
-  if (lane < nf) {
+  if (lane < nf && pf < K) {
     oi[pf] = fj;
     os[pf] = fsc[lane];
   }

@@ -66,6 +66,44 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   entries[pos] = (i << 6) | slot;
 }
 
+// Workgroup = kLeafQueries consecutive queries of one (b, h): count its candidates per
+// leaf block in LDS, reserve one range per non-empty block with a single returning global
+// add, then place each entry with an LDS counter.
+__global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __restrict__ cand, int32_t N, int32_t BH,
+                                                           int32_t twoK, int32_t n1, const int32_t* __restrict__ off,
+                                                           int32_t* __restrict__ cursor,
+                                                           int32_t* __restrict__ entries) {
+  extern __shared__ int lds[];
+  int* hist = lds;        // n1 counts, then reserved bases
+  int* lcur = lds + n1;   // n1 local cursors
+  const int bh = blockIdx.x % BH;
+  const int q0 = (blockIdx.x / BH) * kLeafQueries;
+  const int q1 = min(N, q0 + kLeafQueries);
+  for (int t = threadIdx.x; t < n1; t += 256) {
+    hist[t] = 0;
+    lcur[t] = 0;
+  }
+  __syncthreads();
+  const int32_t* c = cand + ((int64_t)bh * N + q0) * twoK;
+  const int n = (q1 - q0) * twoK;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int leaf = c[t];
+    if (leaf >= 0) atomicAdd(&hist[leaf], 1);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n1; t += 256) {
+    const int h = hist[t];
+    if (h) hist[t] = off[bh * n1 + t] + atomicAdd(&cursor[bh * n1 + t], h);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int leaf = c[t];
+    if (leaf < 0) continue;
+    const int pos = hist[leaf] + atomicAdd(&lcur[leaf], 1);
+    entries[pos] = ((q0 + t / twoK) << 6) | (t % twoK);
+  }
+}
+
 }  // namespace
 
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st) {
@@ -75,6 +113,12 @@ int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t
 
 int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                    hipStream_t st) {
+  if (g.n1 <= kHistMaxBins) {
+    const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+    scatter_hist_kernel<<<grid, 256, 2 * sizeof(int) * (size_t)g.n1, st>>>(cand, g.N, g.B * g.Hkv, 2 * g.K, g.n1,
+                                                                            off, cursor, entries);
+    return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+  }
   const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
   scatter_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(cand, slots, g.N, 2 * g.K, g.n1, off, cursor,
                                                                    entries);

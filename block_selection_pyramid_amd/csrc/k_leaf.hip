@@ -17,20 +17,14 @@
 //
 // MFMA operand layout (v_mfma_f32_32x32x16_bf16, wave64): lane l supplies row (l & 31)
 // of A and column (l & 31) of B, each with the 8 consecutive k of group (l >> 5); the
-// 16 results of lane l are column (l & 31), rows 8*(v/4) + 4*(l >> 5) + (v & 3).  The
-// head dimension is walked as k-step s, group hh -> d = hh*(d/2) + 8s .. 8s+7, the same
-// map for A and B, so each lane reads one contiguous half row of its query.
+// 16 results of lane l are column (l & 31), rows 8(v/4) + 4(l >> 5) + (v & 3).  The head
+// dimension is walked as k-step s, group hh -> dims 16s + 8hh .. +8, the same map for A
+// and B, so the two lanes of a column read 32 contiguous bytes of its query row per load.
 #include "final_dev.h"
 
 namespace pisa {
 
 namespace {
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int acc_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
 
 // Stages rows [row0, row0 + 64) of one (b,h)'s keys into LDS (zero past N).
 template <int D>
@@ -45,12 +39,35 @@ __device__ __forceinline__ void stage_tile(const bf16* __restrict__ kb, int row0
   }
 }
 
-// 64 keys (LDS tile) x 32 columns (B fragments) -> two 32x32 accumulators.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// B fragments of one query row for v_mfma_f32_32x32x16_bf16: k-step s, lane half
+// hh = lane >> 5 <-> dims 16s + 8hh .. +8 (the two lanes of a column read 32 contiguous
+// bytes of its query row per load).
 template <int D>
-__device__ __forceinline__ void tile_mfma(const bf16* kt, const bf16x8* bq, int col, int hh, f32x16& acc0,
-                                          f32x16& acc1) {
+__device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool valid, int hh, bf16x8* bq) {
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (valid) {
+      bq[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
+    }
+  }
+}
+
+// 64 keys (LDS tile, two M-tiles of 32) x 32 columns: acc0/acc1[v] of lane l hold keys
+// key_row(v, l >> 5) and 32 + key_row(v, l >> 5) against column l & 31.
+template <int D>
+__device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, int lane, f32x16& acc0,
+                                            f32x16& acc1) {
   constexpr int LDSR = D + 8;
   constexpr int KS = D / 16;
+  const int col = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
     acc0[v] = 0.f;
@@ -58,16 +75,18 @@ __device__ __forceinline__ void tile_mfma(const bf16* kt, const bf16x8* bq, int 
   }
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + hh * (D / 2) + s * 8);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + hh * (D / 2) + s * 8);
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + 16 * s + 8 * hh);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + 16 * s + 8 * hh);
     acc0 = mfma32(a0, bq[s], acc0);
     acc1 = mfma32(a1, bq[s], acc1);
   }
 }
 
-// Per-column LSE over the 64 rows held by this lane and its partner lane (l ^ 32),
-// in units of the scaled dot product.  Masked rows hold -inf; at least one row is live.
-__device__ __forceinline__ float column_lse(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
+__device__ __forceinline__ int key_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
+
+// LSE over the 64 keys of this lane's column (32 here, 32 in lane l ^ 32), in units of
+// the scaled dot product.  Masked keys hold -inf; at least one key is live.
+__device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
   float m = -INFINITY;
 #pragma unroll
   for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(a0[v], a1[v]));
@@ -80,20 +99,8 @@ __device__ __forceinline__ float column_lse(const f32x16& a0, const f32x16& a1, 
   return s * m + logf(sum);
 }
 
-template <int D>
-__device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool valid, bf16x8* bq) {
-  constexpr int KS = D / 16;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (valid) {
-      bq[s] = *reinterpret_cast<const bf16x8*>(qrow + s * 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
-    }
-  }
-}
-
+// Workgroup = one chunk of a leaf block's list (QC = 128/G entries); each wavefront
+// scores 32/G entries (32 columns = (entry, head) pairs per MFMA tile).
 template <int D, int G>
 __global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                         Geo geo, const int32_t* __restrict__ off,
@@ -101,7 +108,7 @@ __global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__
                                                         const int32_t* __restrict__ entries, int32_t M,
                                                         float* __restrict__ lscore) {
   constexpr int EW = 32 / G;   // entries per wavefront
-  constexpr int QC = 4 * EW;   // entries per chunk (workgroup)
+  constexpr int QC = 128 / G;  // entries per chunk (workgroup)
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
 
@@ -117,9 +124,6 @@ __global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__
   const int e0 = off[list] + (c - choff[list]) * QC;
   const int e1 = min(e0 + QC, off[list + 1]);
 
-  stage_tile<D>(k + (int64_t)bh * geo.N * D, j * kLeaf, geo.N, kt);
-  __syncthreads();
-
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
   const int e = e0 + wave * EW + col / G;
@@ -128,23 +132,26 @@ __global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__
   const int ent = valid ? entries[e] : 0;
   const int i = ent >> 6, slot = ent & 63;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-
+  // query fragments first: their latency overlaps the key-tile staging
   bf16x8 bq[KS];
-  load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D + hh * (D / 2), valid, bq);
-  f32x16 acc0, acc1;
-  tile_mfma<D>(kt, bq, col, hh, acc0, acc1);
+  load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D, valid, hh, bq);
 
+  stage_tile<D>(k + (int64_t)bh * geo.N * D, j * kLeaf, geo.N, kt);
+  __syncthreads();
+
+  f32x16 acc0, acc1;
+  tile_mfma32<D>(kt, bq, lane, acc0, acc1);
   // Routed blocks lie before the query's previous block, so all 64 keys exist and are
   // causal; a short tail block is still masked for safety.
   const int live = min(kLeaf, geo.N - j * kLeaf);
   if (live < kLeaf) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      if (acc_row(v, hh) >= live) acc0[v] = -INFINITY;
-      if (32 + acc_row(v, hh) >= live) acc1[v] = -INFINITY;
+      if (key_row(v, hh) >= live) acc0[v] = -INFINITY;
+      if (32 + key_row(v, hh) >= live) acc1[v] = -INFINITY;
     }
   }
-  float lse = column_lse(acc0, acc1, geo.s, geo.s_log2e);
+  float lse = column_lse32(acc0, acc1, geo.s, geo.s_log2e);
 #pragma unroll
   for (int o = 1; o < G; o <<= 1) lse += __shfl_xor(lse, o);
   if (hh == 0 && r == 0 && valid) lscore[((int64_t)bh * geo.N + i) * (2 * geo.K) + slot] = lse;
@@ -165,12 +172,26 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
   int F[3];
   const int nf = forced_blocks(bq, F);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const int twoK = 2 * geo.K;
+
+  // Candidates and their leaf scores of this wavefront's 16 queries, loaded up front so
+  // the final Top-K does not wait on memory query by query.
+  int cl[kLeaf / 4];
+  float cv[kLeaf / 4];
+#pragma unroll
+  for (int t = 0; t < kLeaf / 4; ++t) {
+    const int i = bq * kLeaf + wave + 4 * t;
+    const int64_t row = (int64_t)bh * geo.N + i;
+    cl[t] = (i < geo.N && lane < twoK) ? cand[row * twoK + lane] : -1;
+    cv[t] = cl[t] >= 0 ? lscore[row * twoK + lane] : -INFINITY;
+  }
+
   const bf16* kb = k + (int64_t)bh * geo.N * D;
   for (int f = 0; f < nf; ++f) stage_tile<D>(kb, F[f] * kLeaf, geo.N, kt[f]);
   __syncthreads();
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col = lane & 31, hh = lane >> 5;
   // 64 queries x G heads = 2G groups of 32 columns
   for (int cg = wave; cg < 2 * G; cg += 4) {
     const int gc = cg * 32 + col;
@@ -178,19 +199,22 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
     const int i = bq * kLeaf + ql;
     const bool valid = i < geo.N;
     bf16x8 bfr[KS];
-    load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D + hh * (D / 2), valid, bfr);
+    load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D, valid, hh, bfr);
     for (int f = 0; f < nf; ++f) {
       f32x16 acc0, acc1;
-      tile_mfma<D>(kt[f], bfr, col, hh, acc0, acc1);
+      tile_mfma32<D>(kt[f], bfr, lane, acc0, acc1);
       const int t0 = F[f] * kLeaf;
+      // only the current block (and a short tail block) needs a mask
+      if (F[f] == bq || t0 + kLeaf > geo.N) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int ta = t0 + acc_row(v, hh), tb = ta + 32;
-        if (ta > i || ta >= geo.N) acc0[v] = -INFINITY;
-        if (tb > i || tb >= geo.N) acc1[v] = -INFINITY;
+        for (int v = 0; v < 16; ++v) {
+          const int ta = t0 + key_row(v, hh), tb = ta + 32;
+          if (ta > i || ta >= geo.N) acc0[v] = -INFINITY;
+          if (tb > i || tb >= geo.N) acc1[v] = -INFINITY;
+        }
       }
       // columns past N (last query block only) still see live keys, so no NaN arises
-      float lse = column_lse(acc0, acc1, geo.s, geo.s_log2e);
+      float lse = column_lse32(acc0, acc1, geo.s, geo.s_log2e);
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) lse += __shfl_xor(lse, o);
       if (hh == 0 && r == 0 && valid) fs[ql][f] = lse;
@@ -198,14 +222,13 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
   }
   __syncthreads();
 
-  const int twoK = 2 * geo.K;
-  for (int ql = wave; ql < kLeaf; ql += 4) {
+#pragma unroll
+  for (int t = 0; t < kLeaf / 4; ++t) {
+    const int ql = wave + 4 * t;
     const int i = bq * kLeaf + ql;
     if (i >= geo.N) break;
     const int64_t row = (int64_t)bh * geo.N + i;
-    const int leaf = lane < twoK ? cand[row * twoK + lane] : -1;
-    const float sc = leaf >= 0 ? lscore[row * twoK + lane] : -INFINITY;
-    finalize_row(leaf, sc, F, nf, fs[ql], geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
+    finalize_row(cl[t], cv[t], F, nf, fs[ql], geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
   }
 }
 

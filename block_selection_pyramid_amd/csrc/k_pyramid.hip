@@ -7,7 +7,8 @@
 // `fan` rows of the level below: C raw keys for l0 = 1, g nodes above that) and then the
 // up-to-4 levels above them from LDS.  For l0 = 1 the workgroup streams 16*C contiguous
 // key rows with 16-byte loads (16 rows per pass for d = 128 bf16), so k is read from HBM
-// exactly once.  A further launch with l0 = 6, 11, ... covers taller pyramids.
+// exactly once.  A further launch with l0 = 6, 11, ... covers taller pyramids.  Every
+// mean is also written to the routing copy as a bf16 hi/lo pair.
 #include "dev_common.h"
 
 namespace pisa {
@@ -33,6 +34,7 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
   const int nodes = min(kSub, geo.n[l0] - j0);
   const Tin* s = src + (int64_t)bh * src_bh_stride;
   float* P = pyr + (int64_t)bh * geo.T * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
   const int cseg = tid % TPR, rp = tid / TPR;
 
   for (int jb = 0; jb < nodes; ++jb) {
@@ -57,6 +59,7 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
       for (int p = 0; p < RPP; ++p) t += red[p][tid];
       const float m = t / (float)(r1 - r0);
       P[(int64_t)(geo.off[l0] + j) * D + tid] = m;
+      store_rcopy<D>(R, geo.off[l0] + j, tid, m);
       lvl[0][jb][tid] = m;
     }
     __syncthreads();
@@ -76,6 +79,7 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
         for (int c = c0; c < c1; ++c) a += lvl[cur][c - jbase][tid];
         const float m = a / (float)(c1 - c0);
         P[(int64_t)(geo.off[l] + p) * D + tid] = m;
+        store_rcopy<D>(R, geo.off[l] + p, tid, m);
         lvl[cur ^ 1][t][tid] = m;
       }
     }

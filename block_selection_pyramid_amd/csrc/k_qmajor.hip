@@ -11,6 +11,8 @@
 // (sequence, KV head) walks the pyramid for the new query at position N-1 (wavefront 0),
 // then all four wavefronts score the candidate and forced tiles, and wavefront 0 writes
 // the selection.  Everything stays in LDS and registers; one launch per step.
+#include <type_traits>
+
 #include "final_dev.h"
 #include "route_dev.h"
 
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
                                                      int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   __shared__ float qs[G * (D + kQPad)];
   __shared__ WalkLds wl;
+  __shared__ WalkLdsM<1> wlm;
   __shared__ int32_t tj[kMaxCand + 4];
   __shared__ float tsc[kMaxCand + 4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -72,15 +75,27 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   const int nf = forced_blocks(bq, F);
   const int twoK = 2 * geo.K;
   int leaf = -1;
-  if (wave == 0) {
-    const T* rows[G];
+  const T* rows[G];
 #pragma unroll
-    for (int r = 0; r < G; ++r) rows[r] = q + ((int64_t)b * geo.Hq + h * G + r) * D;
-    load_qrows<T, D, G>(rows, qs, lane);
+  for (int r = 0; r < G; ++r) rows[r] = q + ((int64_t)b * geo.Hq + h * G + r) * D;
+  if (wave == 0) {
+    load_qrows<T, D, G>(rows, qs, lane);  // the tile scoring below reads q from LDS
     wave_sync();
-    const int nx = route_walk<D, G>(geo, pyr + (int64_t)bh * geo.T * D, qs, bq, &wl, lane);
+    int nx;
+    const int32_t* X;
+    if constexpr (std::is_same<T, bf16>::value) {
+      MfmaWalk<D, G, 1> mw;
+      mw.R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+      mw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
+      nx = mw.walk(geo, bq, &wlm, lane);
+      X = wlm.X;
+    } else {
+      ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.T * D, qs};
+      nx = route_walk(geo, sc, bq, &wl, lane);
+      X = wl.X;
+    }
     if (lane < twoK) {
-      leaf = lane < nx ? wl.X[lane] : -1;
+      leaf = lane < nx ? X[lane] : -1;
       if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
       tj[lane] = leaf;
     }

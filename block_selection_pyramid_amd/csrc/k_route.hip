@@ -1,39 +1,44 @@
 // Prefill routing (stage one of the two-stage prefill: walk levels L..2 per query group)
 // plus the histogram of leaf candidates per (batch, KV head, leaf block) that the leaf
-// grouping needs.  One wavefront per query group, four consecutive queries (same leaf
-// block, hence the same visible pyramid) per workgroup.
+// grouping needs.  bf16 inputs: each wavefront walks up to four consecutive queries (one
+// leaf block, hence one visible pyramid) on the matrix cores from the pyramid's hi/lo
+// routing copy; fp32 inputs: one wavefront per query group on the VALU.
 //
 // Output per query group: 2K slots of leaf candidates that are not forced blocks (the
 // forced blocks are scored separately), -1 elsewhere.
+#include <type_traits>
+
 #include "route_dev.h"
 
 namespace pisa {
 
 namespace {
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ q, const float* __restrict__ pyr, Geo geo,
-                                                    int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
+constexpr int kRouteQueries = 256;              // queries per upper-level routing workgroup
+constexpr int64_t kRouteStageBytes = 64 * 1024;  // LDS for the staged top levels
+
+// fp32 inputs: one wavefront per query group, VALU scorer.
+template <int D, int G>
+__global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict__ q, const float* __restrict__ pyr,
+                                                         Geo geo, int32_t* __restrict__ cand,
+                                                         int32_t* __restrict__ cnt) {
   __shared__ float qs_all[4][G * (D + kQPad)];
   __shared__ WalkLds wl_all[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int i = blockIdx.x * 4 + wave;
   const int bh = blockIdx.y;
   if (i >= geo.N) return;  // whole wavefront; no workgroup barrier follows
-  float* qs = qs_all[wave];
   WalkLds* w = &wl_all[wave];
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-
-  const T* rows[G];
+  const float* rows[G];
 #pragma unroll
   for (int r = 0; r < G; ++r) rows[r] = q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D;
-  load_qrows<T, D, G>(rows, qs, lane);
-  wave_sync();
-
   const int bq = i / geo.C;
-  const float* P = pyr + (int64_t)bh * geo.T * D;
-  const int nx = route_walk<D, G>(geo, P, qs, bq, w, lane);
-
+  float* qs = qs_all[wave];
+  load_qrows<float, D, G>(rows, qs, lane);
+  wave_sync();
+  ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.T * D, qs};
+  const int nx = route_walk(geo, sc, bq, w, lane);
   const int twoK = 2 * geo.K;
   if (lane < twoK) {
     int leaf = lane < nx ? w->X[lane] : -1;
@@ -43,16 +48,172 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ q, con
   }
 }
 
-template <typename T, int D>
-int route_g(const Geo& g, const void* q, const float* pyr, int32_t* cand, int32_t* cnt, hipStream_t st) {
+// bf16 inputs: the walk runs in two launches so that each one gathers from at most about
+// 2 MB of routing copy per (b, h) -- small enough to stay in one XCD's 4 MB L2 -- and
+// workgroup w serves (b, h) = w mod (B*Hkv), so the workgroups one XCD runs (w mod 8)
+// share few heads.  Launch 1 walks levels L..3 (children in levels >= 2; the top levels
+// it reads are staged in LDS) and writes each query group's 2K level-2 candidates;
+// launch 2 scores level 2 against the leaf-block means, keeps Top-K and writes the leaf
+// candidates.  A workgroup owns kRouteQueries consecutive queries; its four wavefronts
+// walk GPW of them at a time.
+template <int D, int G, int GPW, bool kUpper>
+__global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
+                                                         Geo geo, int32_t stage_lo, int32_t* __restrict__ x2,
+                                                         int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
+  using Walk = MfmaWalk<D, G, GPW>;
+  constexpr int kQueries = kUpper ? kRouteQueries : kLeafQueries;
+  // upper launch: staged pyramid levels; lower launch: per-leaf-block histogram (when the
+  // blocks fit), flushed with one global add per non-empty bin
+  extern __shared__ __attribute__((aligned(16))) char stage[];
+  __shared__ WalkLdsM<GPW> wl_all[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int BH = geo.B * geo.Hkv;
+  const int bh = blockIdx.x % BH;
+  const int qr0 = (blockIdx.x / BH) * kQueries;
+  int* hist = reinterpret_cast<int*>(stage);
+  const bool lhist = !kUpper && geo.n1 <= kHistMaxBins;
+  if (lhist) {
+    for (int t = threadIdx.x; t < geo.n1; t += 256) hist[t] = 0;
+    __syncthreads();
+  }
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  const bf16* R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+
+  Walk mw;
+  mw.R = R;
+  if constexpr (kUpper) {
+    // stage levels [stage_lo, L-1]: a contiguous node range of the routing copy
+    const int sbase = stage_lo < geo.L ? geo.off[stage_lo] : 0;
+    const int snodes = stage_lo < geo.L ? geo.off[geo.L] - sbase : 0;
+    constexpr int kChunks = Walk::kRec / 16;  // 16-byte pieces per node
+    for (int t = threadIdx.x; t < snodes * kChunks; t += 256) {
+      const int nd = t / kChunks, c = t % kChunks;
+      const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(R) +
+                                                      (int64_t)(sbase + nd) * Walk::kRec + 16 * c);
+      *reinterpret_cast<uint4*>(stage + nd * Walk::kRecLds + 16 * c) = v;
+    }
+    __syncthreads();
+    mw.lds = stage;
+    mw.stage_lo = stage_lo < geo.L ? stage_lo : 1 << 30;
+    mw.stage_base = sbase;
+  }
+
+  WalkLdsM<GPW>* w = &wl_all[wave];
+  const int64_t qbase = ((int64_t)b * geo.Hq + h * G) * geo.N;
+  const int twoK = 2 * geo.K;
+  const int gl = lane / Walk::CW, xl = lane % Walk::CW;
+  for (int quad = wave; quad < kQueries / GPW; quad += 4) {
+    const int i0 = qr0 + quad * GPW;
+    if (i0 >= geo.N) break;  // uniform across the wavefront
+    const int i = i0 + gl;   // this lane's query (for its group's slots)
+    const int64_t row = (int64_t)bh * geo.N + i;
+    const int bq = i0 / geo.C;  // GPW divides C: the wave's queries share one leaf block
+    if constexpr (kUpper) {
+      // levels L..3 -> level-2 candidates
+      mw.load_q([&](int g, int r) -> const bf16* {
+        const int ii = i0 + g;
+        return ii < geo.N ? q + ((qbase + (int64_t)r * geo.N) + ii) * D : nullptr;
+      }, lane);
+      int nx = mw.init_level(geo, bq, geo.L, w, lane);
+      nx = mw.walk_levels(geo, bq, geo.L, 3, nx, w, lane);
+      if (xl < twoK && i < geo.N)
+        __builtin_nontemporal_store(xl < nx ? w->X[gl * Walk::CW + xl] : -1, &x2[row * twoK + xl]);
+    } else {
+      int nx;
+      if (geo.L >= 2) {
+        mw.load_q([&](int g, int r) -> const bf16* {
+          const int ii = i0 + g;
+          return ii < geo.N ? q + ((qbase + (int64_t)r * geo.N) + ii) * D : nullptr;
+        }, lane);
+        if (geo.L >= 3) {
+          if (xl < twoK) w->X[gl * Walk::CW + xl] = i < geo.N ? __builtin_nontemporal_load(&x2[row * twoK + xl]) : -1;
+          wave_sync();
+          nx = twoK;
+        } else {
+          nx = mw.init_level(geo, bq, 2, w, lane);
+        }
+        nx = mw.walk_levels(geo, bq, 2, 2, nx, w, lane);
+      } else {
+        nx = mw.init_level(geo, bq, 1, w, lane);
+      }
+      if (xl < twoK && i < geo.N) {
+        int leaf = xl < nx ? w->X[gl * Walk::CW + xl] : -1;
+        if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
+        __builtin_nontemporal_store(leaf, &cand[row * twoK + xl]);
+        if (leaf >= 0) {
+          if (lhist) atomicAdd(&hist[leaf], 1);
+          else atomicAdd(&cnt[bh * geo.n1 + leaf], 1);
+        }
+      }
+    }
+    wave_sync();
+  }
+  if (lhist) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < geo.n1; t += 256)
+      if (hist[t]) atomicAdd(&cnt[bh * geo.n1 + t], hist[t]);
+  }
+}
+
+template <int D, int G, int GPW>
+int route_mfma_launch(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
+                      hipStream_t st) {
+  using Walk = MfmaWalk<D, G, GPW>;
+  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kRouteQueries - 1) / kRouteQueries));
+  if (g.L >= 3) {
+    // stage the top levels (>= 2) whose nodes fit the LDS budget
+    int stage_lo = g.L;
+    int64_t bytes = 0;
+    while (stage_lo - 1 >= 2) {
+      const int64_t add = (int64_t)g.n[stage_lo - 1] * Walk::kRecLds;
+      if (bytes + add > kRouteStageBytes) break;
+      bytes += add;
+      --stage_lo;
+    }
+    route_mfma_kernel<D, G, GPW, true><<<grid, 256, (size_t)bytes, st>>>((const bf16*)q, pyr, g, stage_lo, x2,
+                                                                         cand, cnt);
+    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  }
+  const unsigned grid2 = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+  const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
+  route_mfma_kernel<D, G, GPW, false><<<grid2, 256, hbytes, st>>>((const bf16*)q, pyr, g, g.L, x2, cand, cnt);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <int D, int G>
+int route_mfma_g(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
+                 hipStream_t st) {
+  const int gpw = route_groups_per_wave(g.G, g.K);
+  if constexpr (G <= 4) {
+    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, pyr, x2, cand, cnt, st);
+  }
+  if constexpr (G <= 8) {
+    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, pyr, x2, cand, cnt, st);
+  }
+  return route_mfma_launch<D, G, 1>(g, q, pyr, x2, cand, cnt, st);
+}
+
+template <int D>
+int route_d(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
+            hipStream_t st) {
+  if (dtype == PISA_BF16) {
+    switch (g.G) {
+      case 1: return route_mfma_g<D, 1>(g, q, pyr, x2, cand, cnt, st);
+      case 2: return route_mfma_g<D, 2>(g, q, pyr, x2, cand, cnt, st);
+      case 4: return route_mfma_g<D, 4>(g, q, pyr, x2, cand, cnt, st);
+      case 8: return route_mfma_g<D, 8>(g, q, pyr, x2, cand, cnt, st);
+      case 16: return route_mfma_g<D, 16>(g, q, pyr, x2, cand, cnt, st);
+      default: return PISA_ERR_UNSUPPORTED;
+    }
+  }
   dim3 grid((g.N + 3) / 4, g.B * g.Hkv);
-  const T* qq = (const T*)q;
+  const float* qq = (const float*)q;
   switch (g.G) {
-    case 1: route_kernel<T, D, 1><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 2: route_kernel<T, D, 2><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 4: route_kernel<T, D, 4><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 8: route_kernel<T, D, 8><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 16: route_kernel<T, D, 16><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
+    case 1: route_valu_kernel<D, 1><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
+    case 2: route_valu_kernel<D, 2><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
+    case 4: route_valu_kernel<D, 4><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
+    case 8: route_valu_kernel<D, 8><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
+    case 16: route_valu_kernel<D, 16><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
@@ -65,15 +226,10 @@ __global__ void zero_kernel(int32_t* __restrict__ a, int64_t n) {
 
 }  // namespace
 
-int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* cand, int32_t* cnt,
-                 hipStream_t st) {
-  if (dtype == PISA_BF16) {
-    if (g.d == 128) return route_g<bf16, 128>(g, q, pyr, cand, cnt, st);
-    if (g.d == 64) return route_g<bf16, 64>(g, q, pyr, cand, cnt, st);
-  } else {
-    if (g.d == 128) return route_g<float, 128>(g, q, pyr, cand, cnt, st);
-    if (g.d == 64) return route_g<float, 64>(g, q, pyr, cand, cnt, st);
-  }
+int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand,
+                 int32_t* cnt, hipStream_t st) {
+  if (g.d == 128) return route_d<128>(g, dtype, q, pyr, x2, cand, cnt, st);
+  if (g.d == 64) return route_d<64>(g, dtype, q, pyr, x2, cand, cnt, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -113,7 +113,7 @@ int pisa_supported(const pisa_problem* p, int mode) {
 size_t pisa_pyramid_bytes(const pisa_problem* p) {
   Geo g;
   if (make_geo(p, &g) != PISA_OK) return 0;
-  return sizeof(float) * (size_t)g.B * g.Hkv * g.T * g.d;
+  return 2 * sizeof(float) * (size_t)g.B * g.Hkv * g.T * g.d;  // fp32 means + bf16 hi/lo copy
 }
 
 size_t pisa_workspace_bytes(const pisa_problem* p, int mode) {
@@ -160,7 +160,8 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   if ((rc = mark(0)) != PISA_OK) return rc;
   // counters are contiguous: cnt then cursor (each 256-aligned)
   if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
-  if ((rc = launch_route(g, p->dtype, q, pyramid, cand, cnt, st)) != PISA_OK) return rc;
+  // the entries region is free until the scatter: it carries the level-2 candidates
+  if ((rc = launch_route(g, p->dtype, q, pyramid, entries, cand, cnt, st)) != PISA_OK) return rc;
   if ((rc = mark(1)) != PISA_OK) return rc;
   if (p->dtype == PISA_F32) {
     if ((rc = mark(2)) != PISA_OK) return rc;

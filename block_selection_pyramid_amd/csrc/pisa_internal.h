@@ -20,6 +20,9 @@ struct Geo {
   float s_log2e;  // s * log2(e), for exp2-based LSE
   int32_t n[kMaxLevels + 2];    // n[0] = N, n[l] nodes at level l (1..L)
   int32_t off[kMaxLevels + 2];  // node offset of level l in one (b, h) pyramid
+
+  // floats of fp32 means before the routing copy in the pyramid buffer
+  __host__ __device__ int64_t means_floats() const { return (int64_t)B * Hkv * T * d; }
 };
 
 // Prefill workspace carve-up (byte offsets, 256-aligned).
@@ -33,12 +36,24 @@ int make_geo(const pisa_problem* p, Geo* g);  // PISA_OK or PISA_ERR_INVALID_ARG
 int supported(const Geo& g, int dtype, int mode);
 PrefillWs prefill_ws(const Geo& g);
 inline int chunk_entries(int G) { return 128 / G; }  // leaf entries (query groups) per chunk
+// Queries per workgroup of the level-2 routing launch and of the scatter; both keep a
+// per-leaf-block histogram in LDS when there are at most kHistMaxBins leaf blocks.
+constexpr int kLeafQueries = 2048;
+constexpr int kHistMaxBins = 8192;
+// Query groups one routing wavefront walks together: 2K candidate slots each within 64
+// lanes, one MFMA column per (group, head) within 16.
+inline int route_groups_per_wave(int G, int K) {
+  int gpw = 4;
+  while (gpw > 1 && (64 / gpw < 2 * K || G * gpw > 16)) gpw >>= 1;
+  return gpw;
+}
 
 // ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);
-int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* cand, int32_t* cnt,
-                 hipStream_t st);
+// x2: scratch of B*Hkv*N*2K int32 (level-2 candidates between the two routing launches)
+int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand,
+                 int32_t* cnt, hipStream_t st);
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
 int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                    hipStream_t st);

@@ -6,21 +6,26 @@
 // LogSumExp over its child summaries of q.child); agihunt.info summary, kernels paragraph
 // (the G query heads of a GQA group share the selection: their per-head LSEs are summed).
 //
-// Layout per level: candidate x owns child slots 2x and 2x+1 (g = 2).  A pass covers 32
-// child slots; lane l scores slot (l & 31) over half (l >> 5) of the head dimension for
-// all G heads, the halves are combined with one cross-lane exchange, the pair of lanes of
-// a candidate combines its two children into per-head LSEs, and the group score is the
-// sum over heads.  Top-K is a rank count over at most 64 candidates (score descending,
-// block index ascending); the kept node of rank r expands into slots 2r, 2r+1.  Candidate
-// ids live in LDS; a -1 marks an empty slot (a child that does not exist or is not yet
-// visible to the query).
+// Candidate x of a level owns child slots 2x and 2x+1 (g = 2).  Candidate ids live in LDS;
+// -1 marks an empty slot (a child that does not exist or is not yet visible to the query).
+// Top-K is a rank count over at most 64 candidates (score descending, block index
+// ascending); the kept node of rank r expands into slots 2r, 2r+1 of the next level.
+//
+// bf16 inputs use MfmaWalk (matrix cores, several query groups per wavefront; the child
+// summaries come from the pyramid's bf16 hi/lo routing copy, whose hi and lo accumulate
+// into the same fp32 result, so a dot product carries the fp32 mean to 2^-18 relative).
+// fp32 inputs use route_walk with ValuScorer: lane l scores child slot (l & 31) over half
+// (l >> 5) of the head dimension for all G heads from the fp32 means and fp32 query rows
+// in LDS.
 #pragma once
 
 #include "dev_common.h"
 
 namespace pisa {
 
-constexpr int kQPad = 4;  // floats of padding per query row in LDS
+constexpr int kQPad = 4;  // floats of padding per query row in LDS (VALU scorer)
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 // Per-wave LDS scratch of the walk.
 struct WalkLds {
@@ -28,56 +33,292 @@ struct WalkLds {
   float cs[kMaxCand];
 };
 
-// Scores the nx candidates X[0..nx) of level l (>= 2) for one query group whose rows
-// (fp32) sit in qs[r * (D + kQPad) + e]; writes cs[x] (-inf for empty slots).
-template <int D, int G>
-__device__ __forceinline__ void score_level(const Geo& geo, const float* __restrict__ P, const float* qs, int bq,
-                                            int l, int nx, WalkLds* w, int lane) {
-  const float* Pc = P + (int64_t)geo.off[l - 1] * D;
-  const int nchild = geo.n[l - 1];
-  const int cshift = l - 2;  // child c (level l-1) covers leaf blocks from c << cshift
-  const int half = lane >> 5;
-  for (int base = 0; base < 2 * nx; base += 32) {
-    const int slot = base + (lane & 31);
-    const int x = slot >> 1;
-    const int node = x < nx ? w->X[x] : -1;
-    const int c = node >= 0 ? 2 * node + (slot & 1) : -1;
-    const bool valid = c >= 0 && c < nchild && ((int64_t)c << cshift) <= bq;
-    float dot[G];
+__device__ __forceinline__ bool child_visible(int c, int nchild, int cshift, int bq) {
+  return c >= 0 && c < nchild && ((int64_t)c << cshift) <= bq;
+}
+
+// ---------------------------------------------------------------- MFMA walk
+// Order-preserving 64-bit key of (score, node): larger key = better candidate (higher
+// score, then lower index).  0 marks an empty slot (every real key is larger).
+__device__ __forceinline__ uint64_t cand_key(float score, int node) {
+  const uint32_t u = __float_as_uint(score);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(~(uint32_t)node);
+}
+
+template <int GPW>
+struct WalkLdsM {
+  int32_t X[kMaxCand];   // GPW groups x (64 / GPW) candidate slots
+  uint64_t key[kMaxCand];
+};
+
+// One wavefront walks GPW query groups (consecutive queries of one (b, h), hence one
+// leaf block and one visible pyramid) at once.  Scoring: v_mfma_f32_16x16x32_bf16 with
+// A = 16 child summaries x 32 dims (bf16 hi, then lo, of the routing copy) and B = 32
+// dims x 16 columns where column n carries head n % G of group n / G (k-step s, lane
+// group kg = lane >> 4 <-> dims 32s + 8kg .. +8, for A and B alike).  Group g's MFMAs
+// use a B that is zero outside its own columns, so all groups accumulate into one tile
+// and every column of the result belongs to exactly one (group, head).  Lane l then holds
+// (group, head) of column (l & 15) for child rows 4(l >> 4) + v; the pair LSE and the
+// head sum run in the log2 domain with the native exp2/log2 (ranking is unchanged by the
+// positive factor ln 2).  Ranking: lane l handles slot (l % (64/GPW)) of group
+// l / (64/GPW) and counts the better keys of its group.
+template <int D, int G, int GPW>
+struct MfmaWalk {
+  static constexpr int KS = D / 32;    // k-steps of 32 dims
+  static constexpr int CW = 64 / GPW;  // candidate slots (lanes) per group
+  static_assert(G * GPW <= 16, "one column per (group, head)");
+  static constexpr int kRec = 4 * D;         // bytes of one node in the routing copy
+  static constexpr int kRecLds = 4 * D + 16; // padded LDS record (spreads lanes over banks)
+  const bf16* R;                       // routing copy of this (b, h)'s pyramid (global)
+  const char* lds = nullptr;           // staged copy of levels [stage_lo, L-1], or null
+  int stage_lo = 1 << 30;              // lowest level held in LDS
+  int stage_base = 0;                  // node offset of stage_lo in the pyramid
+  bf16x8 qb[GPW][KS];
+
+  // row(g, r): pointer to query head r of group g, or nullptr if the group is padding
+  // (its columns stay zero; its results are never written).
+  template <class RowFn>
+  __device__ void load_q(RowFn row, int lane) {
+    const int n = lane & 15, kg = lane >> 4;
+    const int gown = n / G, r = n % G;
 #pragma unroll
-    for (int r = 0; r < G; ++r) dot[r] = 0.f;
-    if (valid) {
-      const float* pv = Pc + (int64_t)c * D + half * (D / 2);
-#pragma unroll 4
-      for (int e = 0; e < D / 2; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(pv + e);
+    for (int g = 0; g < GPW; ++g) {
+      const bf16* p = (g == gown) ? row(g, r) : nullptr;
 #pragma unroll
-        for (int r = 0; r < G; ++r) {
-          const float4 qv = *reinterpret_cast<const float4*>(qs + r * (D + kQPad) + half * (D / 2) + e);
-          dot[r] += v.x * qv.x + v.y * qv.y + v.z * qv.z + v.w * qv.w;
+      for (int s = 0; s < KS; ++s) {
+        if (p) {
+          // streamed once: keep query rows from displacing the pyramid in L2
+          qb[g][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 32 * s + 8 * kg));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qb[g][s][e] = (__bf16)0.f;
         }
       }
     }
-    float sc = 0.f;
-#pragma unroll
-    for (int r = 0; r < G; ++r) {
-      const float full = dot[r] + __shfl_xor(dot[r], 32);
-      const float y = valid ? geo.s * full : -INFINITY;
-      const float y2 = __shfl_xor(y, 1);
-      const float m = fmaxf(y, y2);
-      // m is finite whenever the candidate exists: its first child is always visible.
-      sc += m + logf(expf(y - m) + expf(y2 - m));
-    }
-    if (lane < 32 && (slot & 1) == 0 && x < nx) w->cs[x] = node >= 0 ? sc : -INFINITY;
   }
-  wave_sync();
-}
+
+  // Loads of one batch: TB tiles x GPW groups, all issued before the first MFMA.  An
+  // invisible or missing child reads node 0 of the level instead (always present); its
+  // rows are masked to -inf in the epilogue, so the loads need no branches.
+  static constexpr int TB = GPW == 1 ? 2 : 1;  // tiles per batch
+
+  template <bool kLds>
+  __device__ __forceinline__ void load_batch(const Geo& geo, const bf16* Rc, const char* Lc, int bq, int l,
+                                             int nx, int t0, const WalkLdsM<GPW>* w, int lane,
+                                             bf16x8 (&hi)[GPW][TB][KS], bf16x8 (&lo)[GPW][TB][KS]) const {
+    const int nchild = geo.n[l - 1];
+    const int cshift = l - 2;
+    const int m = lane & 15, kg = lane >> 4;
+    int ca[GPW][TB];
+#pragma unroll
+    for (int g = 0; g < GPW; ++g)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int cs = 16 * (t0 + tb) + m;
+        const int xa = cs >> 1;
+        const int na = xa < nx ? w->X[g * CW + xa] : -1;
+        const int c = na >= 0 ? 2 * na + (cs & 1) : -1;
+        ca[g][tb] = child_visible(c, nchild, cshift, bq) ? c : 0;
+      }
+#pragma unroll
+    for (int g = 0; g < GPW; ++g)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        // k-step s, lane group kg <-> dims 32s + 8kg .. +8: the four lanes of a row read 64
+        // contiguous bytes of one 128-byte chunk per instruction
+        if constexpr (kLds) {
+          const char* rp = Lc + (int64_t)ca[g][tb] * kRecLds + 16 * kg;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s);
+            lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
+          }
+        } else {
+          const bf16* rp = Rc + (int64_t)ca[g][tb] * 2 * D + 8 * kg;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s);
+            lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s + 32);
+          }
+        }
+      }
+  }
+
+  // Scores candidates X[g*CW + 0..nx) of level l (>= 2) into key[].
+  template <bool kLds>
+  __device__ void score_t(const Geo& geo, int bq, int l, int nx, WalkLdsM<GPW>* w, int lane) const {
+    const bf16* Rc = R + (int64_t)geo.off[l - 1] * 2 * D;
+    const char* Lc = kLds ? lds + (int64_t)(geo.off[l - 1] - stage_base) * kRecLds : nullptr;
+    const int nchild = geo.n[l - 1];
+    const int cshift = l - 2;
+    const int m = lane & 15, kg = lane >> 4;
+    const int gown = m / G, r = m % G;  // epilogue: this lane's column = (group, head)
+    const float sl = geo.s_log2e;
+    const int ntiles = (2 * nx + 15) >> 4;
+    for (int t0 = 0; t0 < ntiles; t0 += TB) {
+      bf16x8 hi[GPW][TB][KS], lo[GPW][TB][KS];
+      load_batch<kLds>(geo, Rc, Lc, bq, l, nx, t0, w, lane, hi, lo);
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const int t = t0 + tb;
+        if (t >= ntiles) break;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < GPW; ++g)
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[g][tb][s], qb[g][s], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[g][tb][s], qb[g][s], acc, 0, 0, 0);
+          }
+        float lse[2];
+        int node[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int x = 8 * t + 2 * kg + p;  // candidate owning child rows 4kg + 2p, +1
+          node[p] = (gown < GPW && x < nx) ? w->X[gown * CW + x] : -1;
+          float y[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int ch = node[p] >= 0 ? 2 * node[p] + c : -1;
+            y[c] = child_visible(ch, nchild, cshift, bq) ? sl * acc[2 * p + c] : -INFINITY;
+          }
+          const float a = fmaxf(y[0], y[1]), b = fminf(y[0], y[1]);
+          lse[p] = node[p] >= 0 ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a)) : 0.f;
+        }
+#pragma unroll
+        for (int o = 1; o < G; o <<= 1) {
+          lse[0] += __shfl_xor(lse[0], o);
+          lse[1] += __shfl_xor(lse[1], o);
+        }
+        if (r == 0 && gown < GPW) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int x = 8 * t + 2 * kg + p;
+            if (x < nx) w->key[gown * CW + x] = node[p] >= 0 ? cand_key(lse[p], node[p]) : 0ull;
+          }
+        }
+      }
+    }
+    wave_sync();
+  }
+
+  __device__ void score(const Geo& geo, int bq, int l, int nx, WalkLdsM<GPW>* w, int lane) const {
+    if (l - 1 >= stage_lo)
+      score_t<true>(geo, bq, l, nx, w, lane);
+    else
+      score_t<false>(geo, bq, l, nx, w, lane);
+  }
+
+  // Fills X with the visible nodes of level `l` (a prefix of the level) and returns nx.
+  __device__ int init_level(const Geo& geo, int bq, int l, WalkLdsM<GPW>* w, int lane) const {
+    const int xl = lane % CW, gl = lane / CW;
+    const int nx = l == 1 ? bq + 1 : min(geo.n[l], (bq >> (l - 1)) + 1);
+    if (xl < nx) w->X[gl * CW + xl] = xl;
+    wave_sync();
+    return nx;
+  }
+
+  // Walks levels l_top down to l_bot (>= 2): score, keep Top-K, expand.  X must hold the
+  // candidates of level l_top (nx slots per group).  On return X[g*CW + 0..nx) holds the
+  // candidates of level l_bot - 1 and the function returns their slot count (<= 2K).
+  __device__ int walk_levels(const Geo& geo, int bq, int l_top, int l_bot, int nx, WalkLdsM<GPW>* w,
+                             int lane) const {
+    const int K = geo.K;
+    const int gl = lane / CW, xl = lane % CW;
+    int* Xg = w->X + gl * CW;
+    for (int l = l_top; l >= l_bot; --l) {
+      score(geo, bq, l, nx, w, lane);
+      const uint64_t* kg = w->key + gl * CW;
+      const uint64_t my = xl < nx ? kg[xl] : 0ull;
+      const int myid = xl < nx ? Xg[xl] : -1;
+      int rank = 0;
+      for (int y = 0; y < nx; ++y) rank += kg[y] > my;
+      const unsigned long long live = __ballot(my != 0ull);
+      int nkg = 0, nmax = 0;
+#pragma unroll
+      for (int g = 0; g < GPW; ++g) {
+        const unsigned long long gm = (GPW == 1) ? ~0ull : (((1ull << CW) - 1ull) << (g * CW));
+        const int kept = min(K, (int)__popcll(live & gm));
+        if (g == gl) nkg = kept;
+        nmax = max(nmax, kept);
+      }
+      wave_sync();
+      const int nchild = geo.n[l - 1];
+      const int cshift = l - 2;
+      if (my != 0ull && rank < K) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int ch = 2 * myid + c;
+          Xg[2 * rank + c] = child_visible(ch, nchild, cshift, bq) ? ch : -1;
+        }
+      }
+      if (xl >= 2 * nkg && xl < 2 * nmax) Xg[xl] = -1;
+      nx = 2 * nmax;
+      wave_sync();
+    }
+    return nx;
+  }
+
+  // The whole walk, levels L..2; returns the leaf-candidate slot count.
+  __device__ int walk(const Geo& geo, int bq, WalkLdsM<GPW>* w, int lane) const {
+    const int nx = init_level(geo, bq, geo.L, w, lane);
+    return geo.L == 1 ? nx : walk_levels(geo, bq, geo.L, 2, nx, w, lane);
+  }
+};
+
+// ---------------------------------------------------------------- VALU scorer
+template <int D, int G>
+struct ValuScorer {
+  const float* P;   // fp32 means of this (b, h)'s pyramid
+  const float* qs;  // LDS: G rows of D (+kQPad) floats
+
+  __device__ void score(const Geo& geo, int bq, int l, int nx, WalkLds* w, int lane) const {
+    const float* Pc = P + (int64_t)geo.off[l - 1] * D;
+    const int nchild = geo.n[l - 1];
+    const int cshift = l - 2;
+    const int half = lane >> 5;
+    for (int base = 0; base < 2 * nx; base += 32) {
+      const int slot = base + (lane & 31);
+      const int x = slot >> 1;
+      const int node = x < nx ? w->X[x] : -1;
+      const int c = node >= 0 ? 2 * node + (slot & 1) : -1;
+      const bool valid = child_visible(c, nchild, cshift, bq);
+      float dot[G];
+#pragma unroll
+      for (int r = 0; r < G; ++r) dot[r] = 0.f;
+      if (valid) {
+        const float* pv = Pc + (int64_t)c * D + half * (D / 2);
+#pragma unroll 4
+        for (int e = 0; e < D / 2; e += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(pv + e);
+#pragma unroll
+          for (int r = 0; r < G; ++r) {
+            const float4 qv = *reinterpret_cast<const float4*>(qs + r * (D + kQPad) + half * (D / 2) + e);
+            dot[r] += v.x * qv.x + v.y * qv.y + v.z * qv.z + v.w * qv.w;
+          }
+        }
+      }
+      float sc = 0.f;
+#pragma unroll
+      for (int r = 0; r < G; ++r) {
+        const float full = dot[r] + __shfl_xor(dot[r], 32);
+        const float y = valid ? geo.s * full : -INFINITY;
+        const float y2 = __shfl_xor(y, 1);
+        const float m = fmaxf(y, y2);
+        // m is finite whenever the candidate exists: its first child is always visible.
+        sc += m + logf(expf(y - m) + expf(y2 - m));
+      }
+      if (lane < 32 && (slot & 1) == 0 && x < nx) w->cs[x] = node >= 0 ? sc : -INFINITY;
+    }
+    wave_sync();
+  }
+};
 
 // Runs the walk; on return w->X[0..nx) holds the leaf candidates (ids or -1) and the
-// function returns nx (<= 2K).  qs must be filled and visible to the wave.
-template <int D, int G>
-__device__ int route_walk(const Geo& geo, const float* __restrict__ P, const float* qs, int bq, WalkLds* w,
-                          int lane) {
+// function returns nx (<= 2K).
+template <class Scorer>
+__device__ int route_walk(const Geo& geo, const Scorer& sc, int bq, WalkLds* w, int lane) {
   const int L = geo.L, K = geo.K;
   if (L == 1) {
     const int nx = bq + 1;  // every visible leaf block (n_1 <= g*K)
@@ -89,8 +330,7 @@ __device__ int route_walk(const Geo& geo, const float* __restrict__ P, const flo
   if (lane < nx) w->X[lane] = lane;
   wave_sync();
   for (int l = L; l >= 2; --l) {
-    score_level<D, G>(geo, P, qs, bq, l, nx, w, lane);
-    // rank of each existing candidate
+    sc.score(geo, bq, l, nx, w, lane);
     int rank = K;
     int myid = -1;
     if (lane < nx) {
@@ -108,15 +348,13 @@ __device__ int route_walk(const Geo& geo, const float* __restrict__ P, const flo
     const unsigned long long exist = __ballot(lane < nx && myid >= 0);
     const int nkept = min(K, (int)__popcll(exist));
     wave_sync();
-    // expand kept nodes into the next level's slots
     const int nchild = geo.n[l - 1];
     const int cshift = l - 2;
     if (myid >= 0 && rank < K) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int ch = 2 * myid + c;
-        const bool ok = ch < nchild && ((int64_t)ch << cshift) <= bq;
-        w->X[2 * rank + c] = ok ? ch : -1;
+        w->X[2 * rank + c] = child_visible(ch, nchild, cshift, bq) ? ch : -1;
       }
     }
     nx = 2 * nkept;
@@ -125,7 +363,7 @@ __device__ int route_walk(const Geo& geo, const float* __restrict__ P, const flo
   return nx;
 }
 
-// Loads the G query rows of one group into LDS as fp32.  qrow(r) points at head r's row.
+// Loads the G query rows of one group into LDS as fp32 (VALU scorer).
 template <typename T, int D, int G>
 __device__ __forceinline__ void load_qrows(const T* const* rows, float* qs, int lane) {
   constexpr int VEC = Vec<T>::N;

@@ -36,8 +36,11 @@
  *   q (prefill)   [B, Hq, N, d]     dtype of the problem (fp32 or bf16)
  *   q (decode)    [B, Hq, d]        the new token's query, at position N-1
  *   k / k_cache   [B, Hkv, N, d]    dtype of the problem
- *   pyramid       [B, Hkv, T, d]    fp32, T = sum of level sizes, level 1 (leaves) first;
- *                                   see pisa_levels for the level offsets
+ *   pyramid       pisa_pyramid_bytes() bytes: first the fp32 means [B, Hkv, T, d]
+ *                 (T = sum of level sizes, level 1 (leaves) first, see pisa_levels),
+ *                 then an equally sized routing copy of the same means, each value split
+ *                 into bf16 hi + bf16 lo (hi + lo equals the fp32 mean to 2^-18
+ *                 relative), laid out per node as d/32 chunks of [hi(32) | lo(32)]
  *   out_idx       [B, Hkv, N, K] (prefill) or [B, Hkv, K] (decode), int32: selected leaf
  *                 block ids in ascending order, padded with -1
  *   out_score     same shape, fp32: each selected block's group-summed causal leaf LSE,
@@ -105,7 +108,8 @@ int pisa_levels(const pisa_problem* p, int32_t* n_levels, int64_t* level_nodes, 
 /* PISA_OK if the kernels support this problem in this mode, else the error code. */
 int pisa_supported(const pisa_problem* p, int mode);
 
-/* Bytes of the fp32 pyramid [B, Hkv, T, d]; 0 for an invalid problem. */
+/* Bytes of the pyramid buffer (fp32 means + routing copy, 2 * 4*B*Hkv*T*d); 0 for an
+ * invalid problem. */
 size_t pisa_pyramid_bytes(const pisa_problem* p);
 
 /* Bytes of device workspace a call in `mode` needs (may be 0); 0 for an invalid problem. */
@@ -115,7 +119,8 @@ size_t pisa_workspace_bytes(const pisa_problem* p, int mode);
  * Builds the pyramid of k [B, Hkv, N, d] into `pyramid` (agihunt.info, pyramid paragraph:
  * level 1 = mean of each leaf block's keys, a short last block averaging the keys it has;
  * level l = unweighted mean of the g (or fewer, at the end) level l-1 nodes below it).
- * One pass over k in HBM; the result is reused by every prefill or decode call on k.
+ * One pass over k in HBM; writes the fp32 means and their routing copy.  The result is
+ * reused by every prefill or decode call on k.
  */
 int pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyramid, pisa_stream_t stream);
 

@@ -58,12 +58,12 @@ def test_level_table_matches_oracle(pisa, N, K):
     L, nodes, offs = pisa.levels(p)
     assert nodes == oracle.levels(N, 64, K, 2)
     assert offs[0] == 0 and offs[-1] == sum(nodes[1:])
-    assert pisa.pyramid_bytes(p) == 4 * offs[-1] * 128
+    assert pisa.pyramid_bytes(p) == 2 * 4 * offs[-1] * 128
 
 
 def test_sizes(pisa):
     p = pisa.Problem(1, 262144, 16, 4, 128, 64, 8, 2)
-    assert pisa.pyramid_bytes(p) == 4 * 4 * 8176 * 128
+    assert pisa.pyramid_bytes(p) == 2 * 4 * 4 * 8176 * 128
     ws = pisa.workspace_bytes(p, pisa.PREFILL)
     slots = 4 * 262144 * 16
     assert ws >= slots * 12 and ws < slots * 12 + 4 * 4 * 4096 * 4 + 4096

@@ -65,7 +65,7 @@ def gpu_prefill(env, w, reps=1):
         torch.cuda.synchronize()
         outs.append((idx.cpu().numpy(), sc.cpu().numpy()))
     log(w.name, "done on GPU")
-    return p, op, q, k, needles, pyr.cpu().numpy(), outs
+    return p, op, q, k, needles, pyr.cpu().numpy()[0], outs
 
 
 def verify(op, q, k, opyr, rows, idx, sc, decode=False, what=""):
@@ -95,6 +95,27 @@ def check_pyramid(op, k, pyr, what):
     log(what, "pyramid max abs err %.3g" % err.max())
     assert np.all(err <= tol), "pyramid mismatch: max err %.3g" % err.max()
     return opyr
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_routing_copy_is_hi_lo_of_means(env, d):
+    # the second half of the pyramid buffer: per node d/32 chunks of [hi(32) | lo(32)]
+    torch, pisa = env
+    w = synth.custom(name="rcopy", batch=2, seq_len=64 * 37 + 5, n_q_heads=4, n_kv_heads=2, head_dim=d, top_k=4,
+                     seed=9, needles=2)
+    p, op = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    pyr = pisa.build_pyramid(p, dev(torch, k))
+    torch.cuda.synchronize()
+    a = pyr.cpu().numpy()
+    means = a[0]
+    bits = a[1].view(np.uint16).reshape(means.shape[:-1] + (d // 32, 2, 32))
+    hi = synth.bf16_bits_to_f32(bits[..., 0, :]).reshape(means.shape)
+    lo = synth.bf16_bits_to_f32(bits[..., 1, :]).reshape(means.shape)
+    assert np.array_equal(hi, synth.bf16_bits_to_f32(synth.to_bf16_bits(means)))
+    err = np.abs(hi.astype(np.float64) + lo - means)
+    assert np.all(err <= np.abs(means) * 2.0 ** -17 + 1e-30)
+    check_pyramid(op, k, means, "rcopy")
 
 
 EDGE = [
@@ -181,7 +202,7 @@ def test_decode_parity_and_matches_prefill(env, N, B, K, G):
     w = synth.custom(name="decode-%d" % N, batch=B, seq_len=N, n_q_heads=2 * G, n_kv_heads=2, head_dim=128, top_k=K,
                      seed=300 + N, needles=4, decode=True)
     p, op, q, k, qd, kd, pyr, idx, sc = gpu_decode(env, w)
-    opyr = check_pyramid(op, k, pyr.cpu().numpy(), w.name)
+    opyr = check_pyramid(op, k, pyr.cpu().numpy()[0], w.name)
     verify(op, q, k, opyr, np.arange(B * 2), idx, sc, decode=True, what=w.name)
     # the same query placed at row N-1 of a prefill problem
     qp = torch.zeros(B, 2 * G, N, 128, dtype=torch.bfloat16, device="cuda")
@@ -201,6 +222,6 @@ def test_decode_workload_full_size(env):
     w = synth.WORKLOADS["decode"]
     p, op, q, k, qd, kd, pyr, idx, sc = gpu_decode(env, w)
     opyr = oracle.build_pyramid(op, k)
-    gp = pyr.cpu().numpy()
+    gp = pyr.cpu().numpy()[0]
     assert np.max(np.abs(gp - opyr)) <= 1e-5
     verify(op, q, k, opyr, np.arange(w.batch * w.n_kv_heads), idx, sc, decode=True, what="decode-full")
