@@ -78,6 +78,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Sum over each aligned group of G consecutive lanes (G = 1, 2, 4, 8, 16), result in every
+// lane of the group.  DPP lane moves within rows of 16 (quad permutes, then the half-row
+// and row mirrors, which pair each lane with one of the other half once the halves hold
+// equal sums), so no LDS crossbar traffic.
+template <int DPP>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group of 1..16 lanes");
+  if constexpr (G >= 2) v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (G >= 4) v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (G >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
+  if constexpr (G >= 16) v += dpp_move<0x140>(v); // row_mirror
+  return v;
+}
+
 // Forced leaf blocks of a query in leaf block bq: {0, bq-1, bq} that exist, ascending.
 __device__ __forceinline__ int forced_blocks(int bq, int* f) {
   int m = 0;

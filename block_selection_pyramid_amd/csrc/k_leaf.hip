@@ -152,8 +152,7 @@ __global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__
     }
   }
   float lse = column_lse32(acc0, acc1, geo.s, geo.s_log2e);
-#pragma unroll
-  for (int o = 1; o < G; o <<= 1) lse += __shfl_xor(lse, o);
+  lse = group_sum<G>(lse);
   if (hh == 0 && r == 0 && valid) lscore[((int64_t)bh * geo.N + i) * (2 * geo.K) + slot] = lse;
 }
 
@@ -215,8 +214,7 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
       }
       // columns past N (last query block only) still see live keys, so no NaN arises
       float lse = column_lse32(acc0, acc1, geo.s, geo.s_log2e);
-#pragma unroll
-      for (int o = 1; o < G; o <<= 1) lse += __shfl_xor(lse, o);
+      lse = group_sum<G>(lse);
       if (hh == 0 && r == 0 && valid) fs[ql][f] = lse;
     }
   }

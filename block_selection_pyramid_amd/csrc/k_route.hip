@@ -1,8 +1,9 @@
 // Prefill routing (stage one of the two-stage prefill: walk levels L..2 per query group)
 // plus the histogram of leaf candidates per (batch, KV head, leaf block) that the leaf
-// grouping needs.  bf16 inputs: each wavefront walks up to four consecutive queries (one
-// leaf block, hence one visible pyramid) on the matrix cores from the pyramid's hi/lo
-// routing copy; fp32 inputs: one wavefront per query group on the VALU.
+// grouping needs.  bf16 inputs: levels L..3 are scored densely per leaf block (separate
+// launch), level 2 here on the matrix cores from the pyramid's hi/lo routing copy, up to
+// four consecutive queries per wavefront; fp32 inputs: one wavefront per query group on
+// the VALU for the whole walk.
 //
 // Output per query group: 2K slots of leaf candidates that are not forced blocks (the
 // forced blocks are scored separately), -1 elsewhere.
@@ -14,8 +15,7 @@ namespace pisa {
 
 namespace {
 
-constexpr int kRouteQueries = 256;              // queries per upper-level routing workgroup
-constexpr int64_t kRouteStageBytes = 64 * 1024;  // LDS for the staged top levels
+constexpr int kLowerQueries = 512;  // queries per level-2 routing workgroup
 
 // fp32 inputs: one wavefront per query group, VALU scorer.
 template <int D, int G>
@@ -48,102 +48,68 @@ __global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict
   }
 }
 
-// bf16 inputs: the walk runs in two launches so that each one gathers from at most about
-// 2 MB of routing copy per (b, h) -- small enough to stay in one XCD's 4 MB L2 -- and
-// workgroup w serves (b, h) = w mod (B*Hkv), so the workgroups one XCD runs (w mod 8)
-// share few heads.  Launch 1 walks levels L..3 (children in levels >= 2; the top levels
-// it reads are staged in LDS) and writes each query group's 2K level-2 candidates;
-// launch 2 scores level 2 against the leaf-block means, keeps Top-K and writes the leaf
-// candidates.  A workgroup owns kRouteQueries consecutive queries; its four wavefronts
-// walk GPW of them at a time.
-template <int D, int G, int GPW, bool kUpper>
+// bf16 inputs, level 2: each wavefront takes GPW query groups (consecutive queries of one
+// leaf block) with their 2K level-2 candidates -- written by the dense upper-level launch,
+// or the visible prefix of level 2 when L == 2 -- scores them against the leaf-block means
+// of the routing copy (a per-query gather: level 1 is too wide to score densely), keeps
+// the Top-K and writes the leaf candidates that are not forced blocks.  Workgroup w
+// serves (b, h) = w mod (B*Hkv), so the workgroups of one XCD (w mod 8) share few heads
+// and gather from an L2-sized part of the routing copy.
+template <int D, int G, int GPW>
 __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
-                                                         Geo geo, int32_t stage_lo, int32_t* __restrict__ x2,
+                                                         Geo geo, const int32_t* __restrict__ x2,
                                                          int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
   using Walk = MfmaWalk<D, G, GPW>;
-  constexpr int kQueries = kUpper ? kRouteQueries : kLeafQueries;
-  // upper launch: staged pyramid levels; lower launch: per-leaf-block histogram (when the
-  // blocks fit), flushed with one global add per non-empty bin
-  extern __shared__ __attribute__((aligned(16))) char stage[];
+  // per-leaf-block histogram (when the blocks fit), flushed with one global add per bin
+  extern __shared__ __attribute__((aligned(16))) int hist[];
   __shared__ WalkLdsM<GPW> wl_all[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int BH = geo.B * geo.Hkv;
   const int bh = blockIdx.x % BH;
-  const int qr0 = (blockIdx.x / BH) * kQueries;
-  int* hist = reinterpret_cast<int*>(stage);
-  const bool lhist = !kUpper && geo.n1 <= kHistMaxBins;
+  const int qr0 = (blockIdx.x / BH) * kLowerQueries;
+  const bool lhist = geo.n1 <= kHistMaxBins;
   if (lhist) {
     for (int t = threadIdx.x; t < geo.n1; t += 256) hist[t] = 0;
     __syncthreads();
   }
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-  const bf16* R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
-
   Walk mw;
-  mw.R = R;
-  if constexpr (kUpper) {
-    // stage levels [stage_lo, L-1]: a contiguous node range of the routing copy
-    const int sbase = stage_lo < geo.L ? geo.off[stage_lo] : 0;
-    const int snodes = stage_lo < geo.L ? geo.off[geo.L] - sbase : 0;
-    constexpr int kChunks = Walk::kRec / 16;  // 16-byte pieces per node
-    for (int t = threadIdx.x; t < snodes * kChunks; t += 256) {
-      const int nd = t / kChunks, c = t % kChunks;
-      const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(R) +
-                                                      (int64_t)(sbase + nd) * Walk::kRec + 16 * c);
-      *reinterpret_cast<uint4*>(stage + nd * Walk::kRecLds + 16 * c) = v;
-    }
-    __syncthreads();
-    mw.lds = stage;
-    mw.stage_lo = stage_lo < geo.L ? stage_lo : 1 << 30;
-    mw.stage_base = sbase;
-  }
+  mw.R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
 
   WalkLdsM<GPW>* w = &wl_all[wave];
   const int64_t qbase = ((int64_t)b * geo.Hq + h * G) * geo.N;
   const int twoK = 2 * geo.K;
   const int gl = lane / Walk::CW, xl = lane % Walk::CW;
-  for (int quad = wave; quad < kQueries / GPW; quad += 4) {
+  for (int quad = wave; quad < kLowerQueries / GPW; quad += 4) {
     const int i0 = qr0 + quad * GPW;
     if (i0 >= geo.N) break;  // uniform across the wavefront
     const int i = i0 + gl;   // this lane's query (for its group's slots)
     const int64_t row = (int64_t)bh * geo.N + i;
     const int bq = i0 / geo.C;  // GPW divides C: the wave's queries share one leaf block
-    if constexpr (kUpper) {
-      // levels L..3 -> level-2 candidates
+    int nx;
+    if (geo.L >= 2) {
       mw.load_q([&](int g, int r) -> const bf16* {
         const int ii = i0 + g;
         return ii < geo.N ? q + ((qbase + (int64_t)r * geo.N) + ii) * D : nullptr;
       }, lane);
-      int nx = mw.init_level(geo, bq, geo.L, w, lane);
-      nx = mw.walk_levels(geo, bq, geo.L, 3, nx, w, lane);
-      if (xl < twoK && i < geo.N)
-        __builtin_nontemporal_store(xl < nx ? w->X[gl * Walk::CW + xl] : -1, &x2[row * twoK + xl]);
-    } else {
-      int nx;
-      if (geo.L >= 2) {
-        mw.load_q([&](int g, int r) -> const bf16* {
-          const int ii = i0 + g;
-          return ii < geo.N ? q + ((qbase + (int64_t)r * geo.N) + ii) * D : nullptr;
-        }, lane);
-        if (geo.L >= 3) {
-          if (xl < twoK) w->X[gl * Walk::CW + xl] = i < geo.N ? __builtin_nontemporal_load(&x2[row * twoK + xl]) : -1;
-          wave_sync();
-          nx = twoK;
-        } else {
-          nx = mw.init_level(geo, bq, 2, w, lane);
-        }
-        nx = mw.walk_levels(geo, bq, 2, 2, nx, w, lane);
+      if (geo.L >= 3) {
+        if (xl < twoK) w->X[gl * Walk::CW + xl] = i < geo.N ? __builtin_nontemporal_load(&x2[row * twoK + xl]) : -1;
+        wave_sync();
+        nx = twoK;
       } else {
-        nx = mw.init_level(geo, bq, 1, w, lane);
+        nx = mw.init_level(geo, bq, 2, w, lane);
       }
-      if (xl < twoK && i < geo.N) {
-        int leaf = xl < nx ? w->X[gl * Walk::CW + xl] : -1;
-        if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
-        __builtin_nontemporal_store(leaf, &cand[row * twoK + xl]);
-        if (leaf >= 0) {
-          if (lhist) atomicAdd(&hist[leaf], 1);
-          else atomicAdd(&cnt[bh * geo.n1 + leaf], 1);
-        }
+      nx = mw.walk_levels(geo, bq, 2, 2, nx, w, lane);
+    } else {
+      nx = mw.init_level(geo, bq, 1, w, lane);
+    }
+    if (xl < twoK && i < geo.N) {
+      int leaf = xl < nx ? w->X[gl * Walk::CW + xl] : -1;
+      if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
+      __builtin_nontemporal_store(leaf, &cand[row * twoK + xl]);
+      if (leaf >= 0) {
+        if (lhist) atomicAdd(&hist[leaf], 1);
+        else atomicAdd(&cnt[bh * geo.n1 + leaf], 1);
       }
     }
     wave_sync();
@@ -158,25 +124,13 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
 template <int D, int G, int GPW>
 int route_mfma_launch(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
                       hipStream_t st) {
-  using Walk = MfmaWalk<D, G, GPW>;
-  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kRouteQueries - 1) / kRouteQueries));
   if (g.L >= 3) {
-    // stage the top levels (>= 2) whose nodes fit the LDS budget
-    int stage_lo = g.L;
-    int64_t bytes = 0;
-    while (stage_lo - 1 >= 2) {
-      const int64_t add = (int64_t)g.n[stage_lo - 1] * Walk::kRecLds;
-      if (bytes + add > kRouteStageBytes) break;
-      bytes += add;
-      --stage_lo;
-    }
-    route_mfma_kernel<D, G, GPW, true><<<grid, 256, (size_t)bytes, st>>>((const bf16*)q, pyr, g, stage_lo, x2,
-                                                                         cand, cnt);
-    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+    const int rc = launch_route_upper_dense(g, q, pyr, x2, st);
+    if (rc != PISA_OK) return rc;
   }
-  const unsigned grid2 = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));
   const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
-  route_mfma_kernel<D, G, GPW, false><<<grid2, 256, hbytes, st>>>((const bf16*)q, pyr, g, g.L, x2, cand, cnt);
+  route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 

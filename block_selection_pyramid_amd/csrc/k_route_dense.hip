@@ -1,0 +1,319 @@
+// Prefill routing, upper pyramid levels (L down to 3), scored densely.
+//
+// What is computed is the top-down walk of "Block Sparse Attention with Log-Linear
+// Complexity" (rcap.io explainer, top-down walk and scoring paragraphs; agihunt.info
+// summary, kernels paragraph for the GQA head sum): at each level a candidate's score is
+// the sum over the G heads of the LogSumExp of s*q.child over its visible children, the
+// Top-K candidates (score descending, lower index first) are kept, and their children are
+// the next level's candidates.
+//
+// How it is computed differs from a per-query gather.  The queries of one leaf block see
+// the same prefix of every level, and at the upper levels that prefix is small, so a
+// workgroup scores every visible child of a level against all of its queries: a dense
+// contraction on the matrix cores (v_mfma_f32_32x32x16_bf16, A = 32 child summaries from
+// the hi/lo routing copy staged in LDS once per workgroup, B = 32 (query, head) columns
+// held in registers).  The epilogue forms the pair LSE of each node's two children and the
+// head sum, and each wavefront keeps only the scores of its own queries' candidates.  The
+// staged child tiles do not depend on the walk, so the next tile is fetched from L2 while
+// the current one is scored, across level boundaries too.
+//
+// Output: per query group, the 2K level-2 candidate slots (children of the Top-K nodes of
+// level 3, -1 where a child does not exist or is not visible), the input of the level-2
+// routing launch.
+#include "route_dev.h"
+
+namespace pisa {
+
+namespace {
+
+constexpr int kDenseWaves = 4;
+
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Columns of the B operand: 32 (query, head) pairs per column group, head fastest.
+template <int G>
+struct DenseShape {
+  static constexpr int NCG = (G <= 2) ? 1 : 2;  // column groups per wavefront
+  static constexpr int QPW = 32 * NCG / G;      // queries per wavefront
+};
+
+template <int D, int G, int KC>
+constexpr size_t dense_lds_bytes() {
+  return 2 * (size_t)(2 * (D / 16) * 1024) + (size_t)kDenseWaves * DenseShape<G>::QPW * (64 + 20 * KC);
+}
+
+// Staging of child tile t of level l - 1 (children 32t .. 32t+31) into fragment-major LDS:
+// fragment f = 2 ks + hi/lo, lane slot = child (lane & 31) and dims 8 (lane >> 5) .. of
+// k-step ks, so every MFMA A-operand read is one conflict-free 16-byte row per lane.  The
+// wavefronts of the workgroup take fragments wave, wave + 4, ...
+template <int D, int NU>
+__device__ __forceinline__ void dense_load_tile(const char* Rb, const Geo& geo, int l, int t, int wave, int lane,
+                                                u32x4 (&stg)[NU]) {
+  const int child = min(32 * t + (lane & 31), geo.n[l - 1] - 1);  // a missing child reads a real node
+  const char* base = Rb + (int64_t)(geo.off[l - 1] + child) * (4 * D) + 16 * (lane >> 5);
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int f = wave + kDenseWaves * u, ks = f >> 1, hl = f & 1;
+    stg[u] = *reinterpret_cast<const u32x4*>(base + (ks >> 1) * 128 + hl * 64 + (ks & 1) * 32);
+  }
+}
+template <int D, int NU>
+__device__ __forceinline__ void dense_store_tile(char* lds, int buf, int wave, int lane, const u32x4 (&stg)[NU]) {
+  constexpr int TILE = 2 * (D / 16) * 1024;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int f = wave + kDenseWaves * u;
+    *reinterpret_cast<u32x4*>(lds + buf * TILE + (f * 64 + lane) * 16) = stg[u];
+  }
+}
+
+// KC >= K: capacity of kept nodes per query (the 2*KC candidate slots hold 2K in use).
+template <int D, int G, int KC>
+__global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
+                                                          Geo geo, int32_t l_bot, int32_t* __restrict__ x2) {
+  constexpr int NCG = DenseShape<G>::NCG, QPW = DenseShape<G>::QPW;
+  constexpr int KS = D / 16;         // k-steps of 16 dims
+  constexpr int F = 2 * KS;          // 1 KB fragments of a staged child tile (hi, lo per k-step)
+  constexpr int TILE = F * 1024;     // bytes of one staged tile of 32 children
+  constexpr int ITEMS = QPW * KC;    // (query, kept-node rank) items of a wavefront
+  constexpr int M = (ITEMS + 63) / 64;
+  constexpr int SLOTS = 2 * KC;
+  static_assert(F % kDenseWaves == 0, "fragments split evenly over the wavefronts");
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  char* wl = lds + 2 * TILE + wave * (QPW * (64 + 20 * KC));
+  float* Sx = reinterpret_cast<float*>(wl);                                     // [QPW][16] node scores
+  uint64_t* key = reinterpret_cast<uint64_t*>(wl + QPW * 64);                   // [QPW][SLOTS]
+  int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (64 + 16 * KC));          // [QPW][KC]
+
+  const int N = geo.N, C = geo.C, K = geo.K, L = geo.L;
+  const int BH = geo.B * geo.Hkv;
+  const int bh = blockIdx.x % BH;  // workgroups of one XCD (w mod 8) share few heads
+  const int iwg = (blockIdx.x / BH) * (kDenseWaves * QPW);
+  const int iw = iwg + wave * QPW;
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  const int bqmax = (min(N, iwg + kDenseWaves * QPW) - 1) / C;
+  const char* Rb = reinterpret_cast<const char*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * (4 * D);
+
+  // B operand: lane column j <-> (query j / G, head j % G) of column group cg, dims
+  // 16 ks + 8 hh .. +8 of k-step ks.
+  const int j = lane & 31, hh = lane >> 5;
+  bf16x8 qf[NCG][KS];
+  int bqc[NCG];
+#pragma unroll
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int i = iw + cg * (32 / G) + j / G;
+    bqc[cg] = min(i, N - 1) / C;
+    if (i < N) {
+      const bf16* p = q + (((int64_t)b * geo.Hq + h * G + j % G) * N + i) * D + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[cg][ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 16 * ks));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[cg][ks][e] = (__bf16)0.f;
+    }
+  }
+
+  // Walk state.  Item (query iq, rank r) = lane + 64 m holds the node ip kept at rank r one
+  // level up; its candidates are ip's two children, with scores sc.  At the top level the
+  // candidates are the visible prefix of level L, i.e. "children" of a virtual node r.
+  int ip[M], ibq[M];
+  float sc[M][2];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int it = lane + 64 * m;
+    const int iq = it / KC, ir = it % KC;
+    ibq[m] = min(iw + iq, N - 1) / C;
+    const int nvis = min(geo.n[L], (ibq[m] >> (L - 1)) + 1);
+    ip[m] = (it < ITEMS && 2 * ir < nvis) ? ir : -1;
+    sc[m][0] = sc[m][1] = 0.f;
+  }
+
+  u32x4 stg[F / kDenseWaves];
+  auto ntiles = [&](int l) {
+    const int nv = min(geo.n[l - 1], (bqmax >> (l - 2)) + 1);
+    return (nv + 31) >> 5;
+  };
+
+  const float sl = geo.s_log2e;
+  int l = L, t = 0, nt = ntiles(L), buf = 0;
+  dense_load_tile<D>(Rb, geo, l, 0, wave, lane, stg);
+  dense_store_tile<D>(lds, 0, wave, lane, stg);
+  __syncthreads();
+  for (;;) {
+    int ln = l, tn = t + 1;
+    if (tn == nt) {
+      ln = l - 1;
+      tn = 0;
+    }
+    const bool more = ln >= l_bot;
+    // unconditional (the last step reloads its own tile): a branch here would make the
+    // compiler wait for each load in turn
+    dense_load_tile<D>(Rb, geo, more ? ln : l, more ? tn : t, wave, lane, stg);
+
+    // ---- scores of the 16 nodes of tile t for this wavefront's queries
+    const char* Tt = lds + buf * TILE;
+    f32x16 acc[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[cg][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks) * 64 + lane) * 16);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks + 1) * 64 + lane) * 16);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[cg][ks], acc[cg], 0, 0, 0);
+        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[cg][ks], acc[cg], 0, 0, 0);
+      }
+    }
+    const int nchild = geo.n[l - 1], cshift = l - 2;
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      // result row (child) 8a + 4hh + (v & 3) for v = 4a + (v & 3); visible rows: <= lim
+      const int lim = min(nchild - 1, bqc[cg] >> cshift) - 32 * t;
+      float ls[8];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int v = 4 * a + 2 * p, row = 8 * a + 4 * hh + 2 * p;
+          const float y0 = row <= lim ? sl * acc[cg][v] : -INFINITY;
+          const float y1 = row + 1 <= lim ? sl * acc[cg][v + 1] : -INFINITY;
+          const float mx = fmaxf(y0, y1), mn = fminf(y0, y1);
+          const float e = mx + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(mn - mx));
+          ls[2 * a + p] = row <= lim ? e : -INFINITY;  // node visible <=> its first child is
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ls[e] = group_sum<G>(ls[e]);
+      if (j % G == 0) {
+        const int qi = cg * (32 / G) + j / G;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          *reinterpret_cast<float2*>(Sx + qi * 16 + 4 * a + 2 * hh) = make_float2(ls[2 * a], ls[2 * a + 1]);
+      }
+    }
+    wave_sync();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      if (ip[m] >= 8 * t && ip[m] < 8 * t + 8) {
+        const int iq = (lane + 64 * m) / KC;
+        const float2 v = *reinterpret_cast<const float2*>(Sx + iq * 16 + 2 * (ip[m] - 8 * t));
+        sc[m][0] = v.x;
+        sc[m][1] = v.y;
+      }
+    }
+    wave_sync();
+
+    if (t == nt - 1) {
+      // ---- Top-K of level l per query; the kept node of rank r becomes item r's parent
+      const int nl = geo.n[l];
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int it = lane + 64 * m;
+        if (it < ITEMS) {
+          const int iq = it / KC, ir = it % KC;
+          const int n0 = 2 * ip[m], n1 = n0 + 1;
+          const bool v0 = ip[m] >= 0;
+          const bool v1 = v0 && n1 < nl && ((int64_t)n1 << (l - 1)) <= ibq[m];
+          key[iq * SLOTS + 2 * ir] = v0 ? cand_key(sc[m][0], n0) : 0ull;
+          key[iq * SLOTS + 2 * ir + 1] = v1 ? cand_key(sc[m][1], n1) : 0ull;
+          np[iq * KC + ir] = -1;
+        }
+      }
+      wave_sync();
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int it = lane + 64 * m;
+        if (it < ITEMS) {
+          const int iq = it / KC, ir = it % KC;
+          const uint64_t* kq = key + iq * SLOTS;
+          const uint64_t k0 = kq[2 * ir], k1 = kq[2 * ir + 1];
+          int r0 = 0, r1 = 0;
+#pragma unroll 4
+          for (int s = 0; s < SLOTS; s += 2) {
+            const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(kq + s);
+            r0 += (kk.x > k0) + (kk.y > k0);
+            r1 += (kk.x > k1) + (kk.y > k1);
+          }
+          if (k0 != 0ull && r0 < K) np[iq * KC + r0] = 2 * ip[m];
+          if (k1 != 0ull && r1 < K) np[iq * KC + r1] = 2 * ip[m] + 1;
+        }
+      }
+      wave_sync();
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int it = lane + 64 * m;
+        if (it < ITEMS) ip[m] = np[(it / KC) * KC + it % KC];
+      }
+      wave_sync();
+    }
+
+    if (more) dense_store_tile<D>(lds, buf ^ 1, wave, lane, stg);
+    __syncthreads();
+    if (!more) break;
+    if (ln != l) nt = ntiles(ln);
+    l = ln;
+    t = tn;
+    buf ^= 1;
+  }
+
+  // ---- level l_bot - 1 candidates: the children of each kept node, 2K slots per query
+  const int lc = l_bot - 1, twoK = 2 * K;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int it = lane + 64 * m;
+    const int iq = it / KC, ir = it % KC, i = iw + iq;
+    if (it < ITEMS && ir < K && i < N) {
+      const int p = ip[m];
+      const int c0 = p >= 0 ? 2 * p : -1;
+      const int c1 = (p >= 0 && 2 * p + 1 < geo.n[lc] && ((int64_t)(2 * p + 1) << (lc - 1)) <= ibq[m]) ? 2 * p + 1 : -1;
+      int32_t* dst = x2 + ((int64_t)bh * N + i) * twoK + 2 * ir;
+      __builtin_nontemporal_store(c0, dst);
+      __builtin_nontemporal_store(c1, dst + 1);
+    }
+  }
+}
+
+template <int D, int G, int KC>
+int dense_launch(const Geo& g, const bf16* q, const float* pyr, int32_t* x2, hipStream_t st) {
+  constexpr int QW = kDenseWaves * DenseShape<G>::QPW;  // queries per workgroup
+  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + QW - 1) / QW));
+  route_dense_kernel<D, G, KC><<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, g, 3, x2);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <int D, int G>
+int dense_k(const Geo& g, const bf16* q, const float* pyr, int32_t* x2, hipStream_t st) {
+  if (g.K <= 8) return dense_launch<D, G, 8>(g, q, pyr, x2, st);
+  if (g.K <= 16) return dense_launch<D, G, 16>(g, q, pyr, x2, st);
+  return dense_launch<D, G, 32>(g, q, pyr, x2, st);
+}
+
+template <int D>
+int dense_g(const Geo& g, const bf16* q, const float* pyr, int32_t* x2, hipStream_t st) {
+  switch (g.G) {
+    case 1: return dense_k<D, 1>(g, q, pyr, x2, st);
+    case 2: return dense_k<D, 2>(g, q, pyr, x2, st);
+    case 4: return dense_k<D, 4>(g, q, pyr, x2, st);
+    case 8: return dense_k<D, 8>(g, q, pyr, x2, st);
+    case 16: return dense_k<D, 16>(g, q, pyr, x2, st);
+    default: return PISA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, int32_t* x2, hipStream_t st) {
+  if (g.L < 3 || g.K > 32) return PISA_ERR_UNSUPPORTED;
+  if (g.d == 128) return dense_g<128>(g, (const bf16*)q, pyr, x2, st);
+  if (g.d == 64) return dense_g<64>(g, (const bf16*)q, pyr, x2, st);
+  return PISA_ERR_UNSUPPORTED;
+}
+
+}  // namespace pisa

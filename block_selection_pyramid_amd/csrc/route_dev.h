@@ -186,11 +186,8 @@ struct MfmaWalk {
           const float a = fmaxf(y[0], y[1]), b = fminf(y[0], y[1]);
           lse[p] = node[p] >= 0 ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a)) : 0.f;
         }
-#pragma unroll
-        for (int o = 1; o < G; o <<= 1) {
-          lse[0] += __shfl_xor(lse[0], o);
-          lse[1] += __shfl_xor(lse[1], o);
-        }
+        lse[0] = group_sum<G>(lse[0]);
+        lse[1] = group_sum<G>(lse[1]);
         if (r == 0 && gown < GPW) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
