@@ -3,7 +3,9 @@
 Each ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in parallel), then
 linked into ``block_selection_pyramid_amd/libpisa.so``.  Packed-fp32 instructions are
 disabled for the device code (``-packed-fp32-ops``); hipcc's host pass warns that it does
-not know that feature, which is harmless.
+not know that feature, which is harmless.  Matrix-core results are kept in ordinary
+VGPRs (``-amdgpu-mfma-vgpr-form``) so that the epilogues read them without accvgpr
+moves.
 
 Usage: ``python -m block_selection_pyramid_amd.build [--force] [-j N]``.
 """
@@ -28,6 +30,7 @@ ARCH = os.environ.get("PISA_OFFLOAD_ARCH", "gfx950")
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", CSRC, "-I", INCLUDE,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 

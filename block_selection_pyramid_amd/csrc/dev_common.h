@@ -84,7 +84,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 // equal sums), so no LDS crossbar traffic.
 template <int DPP>
 __device__ __forceinline__ float dpp_move(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP, 0xF, 0xF, false));
+  // every lane reads a lane of its own row, so bound_ctrl never applies; setting it lets
+  // the compiler fold the move into the consuming add or multiply
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), DPP, 0xF, 0xF, true));
 }
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
@@ -93,6 +95,16 @@ __device__ __forceinline__ float group_sum(float v) {
   if constexpr (G >= 4) v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]
   if constexpr (G >= 8) v += dpp_move<0x141>(v);  // row_half_mirror
   if constexpr (G >= 16) v += dpp_move<0x140>(v); // row_mirror
+  return v;
+}
+
+template <int G>
+__device__ __forceinline__ float group_prod(float v) {
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group of 1..16 lanes");
+  if constexpr (G >= 2) v *= dpp_move<0xB1>(v);
+  if constexpr (G >= 4) v *= dpp_move<0x4E>(v);
+  if constexpr (G >= 8) v *= dpp_move<0x141>(v);
+  if constexpr (G >= 16) v *= dpp_move<0x140>(v);
   return v;
 }
 

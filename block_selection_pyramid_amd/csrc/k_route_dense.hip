@@ -83,9 +83,9 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   char* wl = lds + 2 * TILE + wave * (QPW * (64 + 20 * KC));
-  float* Sx = reinterpret_cast<float*>(wl);                                     // [QPW][16] node scores
-  uint64_t* key = reinterpret_cast<uint64_t*>(wl + QPW * 64);                   // [QPW][SLOTS]
-  int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (64 + 16 * KC));          // [QPW][KC]
+  float* Sx = reinterpret_cast<float*>(wl);                             // [QPW][16] node scores
+  uint64_t* key = reinterpret_cast<uint64_t*>(wl + QPW * 64);           // [QPW][SLOTS]
+  int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (64 + 16 * KC));  // [QPW][KC]
 
   const int N = geo.N, C = geo.C, K = geo.K, L = geo.L;
   const int BH = geo.B * geo.Hkv;
@@ -101,6 +101,7 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
   const int j = lane & 31, hh = lane >> 5;
   bf16x8 qf[NCG][KS];
   int bqc[NCG];
+  const int bqw = min(iw, N - 1) / C;  // bq of this wavefront's first (smallest) query
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int i = iw + cg * (32 / G) + j / G;
@@ -173,29 +174,66 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
       }
     }
     const int nchild = geo.n[l - 1], cshift = l - 2;
+    // Epilogue.  Result row (child) 8a + 4hh + 2p (+1) sits in acc[4a + 2p] (+1); node
+    // 4a + 2hh + p of the tile owns that pair.  Per head: mx = max of the pair, f = 1 +
+    // 2^(s log2e (min - mx)) in [1, 2]; the head reduction is sum(mx) and prod(f), so the
+    // node score sum_h LSE_h (log2 units) = s log2e sum(mx) + log2 prod(f), and the G lanes
+    // of a query split the logarithms among themselves.  A node whose first child is
+    // visible has a finite mx; other nodes are never read, so only the second child of
+    // the pair needs a mask, and only in the tile holding the visibility boundary.
+    const bool full = 32 * t + 32 <= min(nchild, (bqw >> cshift) + 1);  // bqw: smallest bq
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
-      // result row (child) 8a + 4hh + (v & 3) for v = 4a + (v & 3); visible rows: <= lim
-      const int lim = min(nchild - 1, bqc[cg] >> cshift) - 32 * t;
-      float ls[8];
+      if (!full) {
+        const int lim = min(nchild - 1, bqc[cg] >> cshift) - 32 * t;  // visible rows: <= lim
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+            if (8 * a + 4 * hh + 2 * p + 1 > lim) acc[cg][4 * a + 2 * p + 1] = -INFINITY;
+      }
+      float mxs[8], prd[8];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int v = 4 * a + 2 * p, row = 8 * a + 4 * hh + 2 * p;
-          const float y0 = row <= lim ? sl * acc[cg][v] : -INFINITY;
-          const float y1 = row + 1 <= lim ? sl * acc[cg][v + 1] : -INFINITY;
-          const float mx = fmaxf(y0, y1), mn = fminf(y0, y1);
-          const float e = mx + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(mn - mx));
-          ls[2 * a + p] = row <= lim ? e : -INFINITY;  // node visible <=> its first child is
+          const float a0 = acc[cg][4 * a + 2 * p], a1 = acc[cg][4 * a + 2 * p + 1];
+          const bool first = a0 >= a1;
+          const float mx = first ? a0 : a1, mn = first ? a1 : a0;
+          mxs[2 * a + p] = mx;
+          prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(sl * (mn - mx));
         }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ls[e] = group_sum<G>(ls[e]);
-      if (j % G == 0) {
-        const int qi = cg * (32 / G) + j / G;
+      for (int e = 0; e < 8; ++e) {
+        mxs[e] = group_sum<G>(mxs[e]);
+        prd[e] = group_prod<G>(prd[e]);
+      }
+      // lane r < GE of a query's group finishes values r*VPL .. r*VPL + VPL - 1
+      constexpr int GE = G < 8 ? G : 8, VPL = 8 / GE;
+      const int r = j % G;
+      const int qi = cg * (32 / G) + j / G;
+      float out[VPL];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          *reinterpret_cast<float2*>(Sx + qi * 16 + 4 * a + 2 * hh) = make_float2(ls[2 * a], ls[2 * a + 1]);
+      for (int u = 0; u < VPL; ++u) {
+        float m = mxs[u], f = prd[u];
+#pragma unroll
+        for (int k = 1; k < GE; ++k) {
+          m = r == k ? mxs[k * VPL + u] : m;
+          f = r == k ? prd[k * VPL + u] : f;
+        }
+        out[u] = sl * m + __builtin_amdgcn_logf(f);
+      }
+      if (r < GE) {
+        float* dst = Sx + qi * 16 + 2 * hh;
+        if constexpr (VPL == 1) {
+          dst[4 * (r >> 1) + (r & 1)] = out[0];
+        } else {
+#pragma unroll
+          for (int u = 0; u < VPL; u += 2) {
+            const int a = (r * VPL + u) >> 1;  // value index r*VPL + u = 2a (+1)
+            *reinterpret_cast<float2*>(dst + 4 * a) = make_float2(out[u], out[u + 1]);
+          }
+        }
       }
     }
     wave_sync();
