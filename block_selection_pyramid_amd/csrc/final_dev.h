@@ -92,4 +92,60 @@ __device__ __forceinline__ void finalize_row(int leaf, float sc, const int* F, i
   }
 }
 
+// The same selection for 64 / SL query groups at once (SL >= 2K slots per group, a power of
+// two): lane = (group lane / SL, slot lane % SL) holds candidate `leaf` (-1 if none) with
+// score `sc`; fsc is this lane's group's forced-block scores.  kx and lx are 64-entry
+// per-wavefront LDS scratch; `live` is false for lanes of a group past the last query
+// (they take part in the exchange but write nothing).
+template <int SL>
+__device__ __forceinline__ void finalize_rows(int leaf, float sc, const int* F, int nf, const float* fsc, int K,
+                                              int lane, bool live, uint64_t* kx, int32_t* lx,
+                                              int32_t* __restrict__ oi, float* __restrict__ os) {
+  const int base = lane & ~(SL - 1), slot = lane & (SL - 1);
+  const uint32_t u = __float_as_uint(sc);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint64_t my = leaf >= 0 ? (((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)leaf)) : 0ull;
+  kx[lane] = my;
+  wave_sync();
+  int rank = 0;
+#pragma unroll
+  for (int y = 0; y < SL; y += 2) {
+    const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(kx + base + y);
+    rank += (kk.x > my) + (kk.y > my);
+  }
+  const bool kept = leaf >= 0 && rank < K - nf;
+  lx[lane] = kept ? leaf : 0x7fffffff;
+  wave_sync();
+  // ascending output position: selected entries (kept or forced) with a smaller index
+  const int fj = slot < nf ? (slot == 0 ? F[0] : (slot == 1 ? F[1] : F[2])) : 0x7fffffff;
+  int pos = 0, pf = 0;
+#pragma unroll
+  for (int y = 0; y < SL; y += 4) {
+    const int4 o = *reinterpret_cast<const int4*>(lx + base + y);
+    pos += (o.x < leaf) + (o.y < leaf) + (o.z < leaf) + (o.w < leaf);
+    pf += (o.x < fj) + (o.y < fj) + (o.z < fj) + (o.w < fj);
+  }
+  for (int f = 0; f < nf; ++f) {
+    pos += F[f] < leaf;
+    pf += F[f] < fj;
+  }
+  const uint64_t gmask = (SL == 64) ? ~0ull : (((1ull << SL) - 1ull) << base);
+  const int nsel = (int)__popcll(__ballot(kept) & gmask) + nf;
+  if (live) {
+    if (kept && pos < K) {
+      oi[pos] = leaf;
+      os[pos] = sc;
+    }
+    if (slot < nf && pf < K) {
+      oi[pf] = fj;
+      os[pf] = fsc[slot];
+    }
+    if (slot >= nsel && slot < K) {
+      oi[slot] = -1;
+      os[slot] = -INFINITY;
+    }
+  }
+  wave_sync();  // kx, lx are rewritten by the next call
+}
+
 }  // namespace pisa

@@ -156,7 +156,11 @@ __global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__
   if (hh == 0 && r == 0 && valid) lscore[((int64_t)bh * geo.N + i) * (2 * geo.K) + slot] = lse;
 }
 
-template <int D, int G>
+// Workgroup = one leaf block of queries (64) of one (b, h): stages the forced blocks'
+// key tiles (0, bq - 1, bq) in LDS, scores them for the block's 64 x G (query, head)
+// columns (32 per MFMA tile; the query fragments of the next column group are loaded
+// while the current one is scored), then each wavefront finalizes 16 of the queries.
+template <int D, int G, int SL>
 __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                            Geo geo, const int32_t* __restrict__ cand,
                                                            const float* __restrict__ lscore,
@@ -164,8 +168,12 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
                                                            float* __restrict__ out_score) {
   constexpr int KS = D / 16;
   constexpr int LDSR = D + 8;
+  constexpr int NQ = 64 / SL;          // query groups finalized per pass
+  constexpr int PASSES = 16 / NQ;      // passes for a wavefront's 16 queries
   __shared__ __attribute__((aligned(16))) bf16 kt[3][kLeaf * LDSR];
   __shared__ float fs[kLeaf][4];
+  __shared__ __attribute__((aligned(16))) uint64_t kx_all[4][64];
+  __shared__ __attribute__((aligned(16))) int32_t lx_all[4][64];
 
   const int bq = blockIdx.x, bh = blockIdx.y;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
@@ -174,31 +182,40 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
   const int twoK = 2 * geo.K;
+  const int slot = lane % SL, qq = lane / SL;
 
-  // Candidates and their leaf scores of this wavefront's 16 queries, loaded up front so
-  // the final Top-K does not wait on memory query by query.
-  int cl[kLeaf / 4];
-  float cv[kLeaf / 4];
+  // Routed candidates and their leaf scores for this wavefront's queries
+  // ql = wave + 4 (p NQ + qq), loaded up front.
+  int cl[PASSES];
+  float cv[PASSES];
 #pragma unroll
-  for (int t = 0; t < kLeaf / 4; ++t) {
-    const int i = bq * kLeaf + wave + 4 * t;
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
     const int64_t row = (int64_t)bh * geo.N + i;
-    cl[t] = (i < geo.N && lane < twoK) ? cand[row * twoK + lane] : -1;
-    cv[t] = cl[t] >= 0 ? lscore[row * twoK + lane] : -INFINITY;
+    cl[p] = (i < geo.N && slot < twoK) ? cand[row * twoK + slot] : -1;
+    cv[p] = cl[p] >= 0 ? lscore[row * twoK + slot] : -INFINITY;
   }
+
+  // 64 queries x G heads = 2G groups of 32 columns; this wavefront takes cg = wave + 4m
+  auto qrow = [&](int cg) {
+    const int gc = cg * 32 + col;
+    return q + (((int64_t)b * geo.Hq + h * G + gc % G) * geo.N + bq * kLeaf + gc / G) * D;
+  };
+  auto qvalid = [&](int cg) { return cg < 2 * G && bq * kLeaf + (cg * 32 + col) / G < geo.N; };
+  bf16x8 bfr[KS];
+  load_bfrag<D>(qrow(wave), qvalid(wave), hh, bfr);
 
   const bf16* kb = k + (int64_t)bh * geo.N * D;
   for (int f = 0; f < nf; ++f) stage_tile<D>(kb, F[f] * kLeaf, geo.N, kt[f]);
   __syncthreads();
 
-  // 64 queries x G heads = 2G groups of 32 columns
   for (int cg = wave; cg < 2 * G; cg += 4) {
+    bf16x8 bfn[KS];
+    load_bfrag<D>(qrow(cg + 4), qvalid(cg + 4), hh, bfn);
     const int gc = cg * 32 + col;
     const int ql = gc / G, r = gc % G;
     const int i = bq * kLeaf + ql;
     const bool valid = i < geo.N;
-    bf16x8 bfr[KS];
-    load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D, valid, hh, bfr);
     for (int f = 0; f < nf; ++f) {
       f32x16 acc0, acc1;
       tile_mfma32<D>(kt[f], bfr, lane, acc0, acc1);
@@ -217,16 +234,19 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
       lse = group_sum<G>(lse);
       if (hh == 0 && r == 0 && valid) fs[ql][f] = lse;
     }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) bfr[s] = bfn[s];
   }
   __syncthreads();
 
 #pragma unroll
-  for (int t = 0; t < kLeaf / 4; ++t) {
-    const int ql = wave + 4 * t;
+  for (int p = 0; p < PASSES; ++p) {
+    const int ql = wave + 4 * (p * NQ + qq);
     const int i = bq * kLeaf + ql;
-    if (i >= geo.N) break;
-    const int64_t row = (int64_t)bh * geo.N + i;
-    finalize_row(cl[t], cv[t], F, nf, fs[ql], geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
+    const bool live = i < geo.N;
+    const int64_t row = (int64_t)bh * geo.N + (live ? i : 0);
+    finalize_rows<SL>(cl[p], cv[p], F, nf, fs[ql], geo.K, lane, live, kx_all[wave], lx_all[wave],
+                      out_idx + row * geo.K, out_score + row * geo.K);
   }
 }
 
@@ -249,21 +269,30 @@ int leaf_d(const Geo& g, const void* q, const void* k, const int32_t* off, const
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
-template <int D>
-int forced_d(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore, int32_t* oi,
-             float* os, hipStream_t st) {
+template <int D, int SL>
+int forced_sl(const Geo& g, const bf16* q, const bf16* k, const int32_t* cand, const float* lscore, int32_t* oi,
+              float* os, hipStream_t st) {
   dim3 grid(g.n1, g.B * g.Hkv);
-  const bf16* qq = (const bf16*)q;
-  const bf16* kk = (const bf16*)k;
   switch (g.G) {
-    case 1: forced_final_kernel<D, 1><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
-    case 2: forced_final_kernel<D, 2><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
-    case 4: forced_final_kernel<D, 4><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
-    case 8: forced_final_kernel<D, 8><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
-    case 16: forced_final_kernel<D, 16><<<grid, 256, 0, st>>>(qq, kk, g, cand, lscore, oi, os); break;
+    case 1: forced_final_kernel<D, 1, SL><<<grid, 256, 0, st>>>(q, k, g, cand, lscore, oi, os); break;
+    case 2: forced_final_kernel<D, 2, SL><<<grid, 256, 0, st>>>(q, k, g, cand, lscore, oi, os); break;
+    case 4: forced_final_kernel<D, 4, SL><<<grid, 256, 0, st>>>(q, k, g, cand, lscore, oi, os); break;
+    case 8: forced_final_kernel<D, 8, SL><<<grid, 256, 0, st>>>(q, k, g, cand, lscore, oi, os); break;
+    case 16: forced_final_kernel<D, 16, SL><<<grid, 256, 0, st>>>(q, k, g, cand, lscore, oi, os); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <int D>
+int forced_d(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore, int32_t* oi,
+             float* os, hipStream_t st) {
+  const bf16* qq = (const bf16*)q;
+  const bf16* kk = (const bf16*)k;
+  // slots per query group: 2K rounded up to a power of two (at least 16)
+  if (2 * g.K <= 16) return forced_sl<D, 16>(g, qq, kk, cand, lscore, oi, os, st);
+  if (2 * g.K <= 32) return forced_sl<D, 32>(g, qq, kk, cand, lscore, oi, os, st);
+  return forced_sl<D, 64>(g, qq, kk, cand, lscore, oi, os, st);
 }
 
 }  // namespace

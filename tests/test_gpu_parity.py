@@ -129,6 +129,7 @@ EDGE = [
     ("G1-d64", 3000, 2, 2, 64, 8, synth.BF16, 1),
     ("G8", 2500, 16, 2, 128, 6, synth.BF16, 1),
     ("G16", 2048 + 1, 16, 1, 128, 7, synth.BF16, 1),
+    ("G16-deep", 16384 + 100, 16, 1, 128, 8, synth.BF16, 1),
     ("K32-L1", 2048, 4, 1, 128, 32, synth.BF16, 1),
     ("K16-odd-levels", 64 * 101 + 9, 4, 2, 128, 16, synth.BF16, 1),
     ("f32-G4", 1500, 8, 2, 128, 8, synth.F32, 1),
