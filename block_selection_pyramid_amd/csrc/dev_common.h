@@ -22,8 +22,9 @@ __device__ __forceinline__ uint32_t f2bf_rne(float f) {
 }
 
 // Routing copy of the pyramid: node n of one (b, h) occupies 2*D bf16 as D/32 chunks of
-// [hi(32 dims) | lo(32 dims)] (128 bytes, one cache line each) with hi = bf16(P) and
-// lo = bf16(P - hi).  It follows the fp32 means in the pyramid buffer.
+// [hi(32 dims) | lo(32 dims)] (128 bytes, one cache line each) with hi = bf16(v) and
+// lo = bf16(v - hi) for v = fp32(s log2(e) P): a dot product with a query row is then the
+// scaled score in log2 units.  It follows the fp32 means in the pyramid buffer.
 __device__ __forceinline__ int64_t rcopy_index(int64_t node, int e, int D) {
   return node * 2 * D + (e >> 5) * 64 + (e & 31);
 }

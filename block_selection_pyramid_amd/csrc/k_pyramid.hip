@@ -1,14 +1,14 @@
 // Pyramid construction ("Block Sparse Attention with Log-Linear Complexity", agihunt.info
 // summary, pyramid paragraph; rcap.io explainer, "think of the keys as leaves of a tree"):
 // level 1 node j = mean of the keys of leaf block j, level l node j = mean of level l-1
-// nodes 2j, 2j+1 (g = 2), unweighted over the children that exist.
+// nodes 2j, 2j+1 (g = 2), unweighted over the children that exist.  Every mean also goes
+// to the routing copy, scaled by s log2(e) and split into bf16 hi + lo.
 //
 // One workgroup reduces a subtree: 16 consecutive nodes of level l0 (each the mean of
 // `fan` rows of the level below: C raw keys for l0 = 1, g nodes above that) and then the
 // up-to-4 levels above them from LDS.  For l0 = 1 the workgroup streams 16*C contiguous
 // key rows with 16-byte loads (16 rows per pass for d = 128 bf16), so k is read from HBM
-// exactly once.  A further launch with l0 = 6, 11, ... covers taller pyramids.  Every
-// mean is also written to the routing copy as a bf16 hi/lo pair.
+// exactly once.  A further launch with l0 = 6, 11, ... covers taller pyramids.
 #include "dev_common.h"
 
 namespace pisa {
@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
       for (int p = 0; p < RPP; ++p) t += red[p][tid];
       const float m = t / (float)(r1 - r0);
       P[(int64_t)(geo.off[l0] + j) * D + tid] = m;
-      store_rcopy<D>(R, geo.off[l0] + j, tid, m);
+      store_rcopy<D>(R, geo.off[l0] + j, tid, m * geo.s_log2e);
       lvl[0][jb][tid] = m;
     }
     __syncthreads();
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
         for (int c = c0; c < c1; ++c) a += lvl[cur][c - jbase][tid];
         const float m = a / (float)(c1 - c0);
         P[(int64_t)(geo.off[l] + p) * D + tid] = m;
-        store_rcopy<D>(R, geo.off[l] + p, tid, m);
+        store_rcopy<D>(R, geo.off[l] + p, tid, m * geo.s_log2e);
         lvl[cur ^ 1][t][tid] = m;
       }
     }

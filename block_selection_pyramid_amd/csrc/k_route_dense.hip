@@ -12,8 +12,9 @@
 // workgroup scores every visible child of a level against all of its queries: a dense
 // contraction on the matrix cores (v_mfma_f32_32x32x16_bf16, A = 32 child summaries from
 // the hi/lo routing copy staged in LDS once per workgroup, B = 32 (query, head) columns
-// held in registers).  The epilogue forms the pair LSE of each node's two children and the
-// head sum, and each wavefront keeps only the scores of its own queries' candidates.  The
+// held in registers; the routing copy is pre-scaled by s log2(e), so the products are the
+// scores in log2 units).  The epilogue forms the pair LSE of each node's two children and
+// the head sum, and each wavefront keeps only the scores of its own queries' candidates.  The
 // staged child tiles do not depend on the walk, so the next tile is fetched from L2 while
 // the current one is scored, across level boundaries too.
 //
@@ -140,7 +141,6 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
     return (nv + 31) >> 5;
   };
 
-  const float sl = geo.s_log2e;
   int l = L, t = 0, nt = ntiles(L), buf = 0;
   dense_load_tile<D>(Rb, geo, l, 0, wave, lane, stg);
   dense_store_tile<D>(lds, 0, wave, lane, stg);
@@ -175,12 +175,14 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
     }
     const int nchild = geo.n[l - 1], cshift = l - 2;
     // Epilogue.  Result row (child) 8a + 4hh + 2p (+1) sits in acc[4a + 2p] (+1); node
-    // 4a + 2hh + p of the tile owns that pair.  Per head: mx = max of the pair, f = 1 +
-    // 2^(s log2e (min - mx)) in [1, 2]; the head reduction is sum(mx) and prod(f), so the
-    // node score sum_h LSE_h (log2 units) = s log2e sum(mx) + log2 prod(f), and the G lanes
-    // of a query split the logarithms among themselves.  A node whose first child is
-    // visible has a finite mx; other nodes are never read, so only the second child of
-    // the pair needs a mask, and only in the tile holding the visibility boundary.
+    // 4a + 2hh + p of the tile owns that pair.  Per head, with d = a0 - a1: mx = a0 -
+    // min(d, 0) is the max of the pair and f = 1 + 2^-|d| lies in [1, 2]; the head
+    // reduction is sum(mx) and prod(f), so the node score sum_h LSE_h (log2 units) =
+    // sum(mx) + log2 prod(f), and the G lanes of a query split the logarithms among
+    // themselves.  A node whose first child is visible has a finite mx; other nodes are
+    // never read, so only the second child of a pair needs a mask (-inf, giving mx = a0
+    // and f = 1), and only in the tile holding the visibility boundary.  (Forming the max
+    // from the difference keeps the compiler from canonicalising the raw MFMA results.)
     const bool full = 32 * t + 32 <= min(nchild, (bqw >> cshift) + 1);  // bqw: smallest bq
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
@@ -198,10 +200,9 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const float a0 = acc[cg][4 * a + 2 * p], a1 = acc[cg][4 * a + 2 * p + 1];
-          const bool first = a0 >= a1;
-          const float mx = first ? a0 : a1, mn = first ? a1 : a0;
-          mxs[2 * a + p] = mx;
-          prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(sl * (mn - mx));
+          const float dd = a0 - a1;
+          mxs[2 * a + p] = a0 - fminf(dd, 0.f);
+          prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(-fabsf(dd));
         }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
           m = r == k ? mxs[k * VPL + u] : m;
           f = r == k ? prd[k * VPL + u] : f;
         }
-        out[u] = sl * m + __builtin_amdgcn_logf(f);
+        out[u] = m + __builtin_amdgcn_logf(f);
       }
       if (r < GE) {
         float* dst = Sx + qi * 16 + 2 * hh;

@@ -12,8 +12,9 @@
 // ascending); the kept node of rank r expands into slots 2r, 2r+1 of the next level.
 //
 // bf16 inputs use MfmaWalk (matrix cores, several query groups per wavefront; the child
-// summaries come from the pyramid's bf16 hi/lo routing copy, whose hi and lo accumulate
-// into the same fp32 result, so a dot product carries the fp32 mean to 2^-18 relative).
+// summaries come from the pyramid's bf16 hi/lo routing copy of s log2(e) times the means,
+// whose hi and lo accumulate into the same fp32 result, so a dot product is the scaled
+// score in log2 units to 2^-18 relative).
 // fp32 inputs use route_walk with ValuScorer: lane l scores child slot (l & 31) over half
 // (l >> 5) of the head dimension for all G heads from the fp32 means and fp32 query rows
 // in LDS.
@@ -154,7 +155,6 @@ struct MfmaWalk {
     const int cshift = l - 2;
     const int m = lane & 15, kg = lane >> 4;
     const int gown = m / G, r = m % G;  // epilogue: this lane's column = (group, head)
-    const float sl = geo.s_log2e;
     const int ntiles = (2 * nx + 15) >> 4;
     for (int t0 = 0; t0 < ntiles; t0 += TB) {
       bf16x8 hi[GPW][TB][KS], lo[GPW][TB][KS];
@@ -181,7 +181,7 @@ struct MfmaWalk {
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int ch = node[p] >= 0 ? 2 * node[p] + c : -1;
-            y[c] = child_visible(ch, nchild, cshift, bq) ? sl * acc[2 * p + c] : -INFINITY;
+            y[c] = child_visible(ch, nchild, cshift, bq) ? acc[2 * p + c] : -INFINITY;
           }
           const float a = fmaxf(y[0], y[1]), b = fminf(y[0], y[1]);
           lse[p] = node[p] >= 0 ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a)) : 0.f;

@@ -38,9 +38,11 @@
  *   k / k_cache   [B, Hkv, N, d]    dtype of the problem
  *   pyramid       pisa_pyramid_bytes() bytes: first the fp32 means [B, Hkv, T, d]
  *                 (T = sum of level sizes, level 1 (leaves) first, see pisa_levels),
- *                 then an equally sized routing copy of the same means, each value split
- *                 into bf16 hi + bf16 lo (hi + lo equals the fp32 mean to 2^-18
- *                 relative), laid out per node as d/32 chunks of [hi(32) | lo(32)]
+ *                 then an equally sized routing copy: each mean times s * log2(e)
+ *                 (fp32 product, s as resolved from the problem) split into bf16 hi +
+ *                 bf16 lo (hi + lo equals that product to 2^-18 relative), laid out per
+ *                 node as d/32 chunks of [hi(32) | lo(32)]; the copy is therefore tied
+ *                 to the problem's scale
  *   out_idx       [B, Hkv, N, K] (prefill) or [B, Hkv, K] (decode), int32: selected leaf
  *                 block ids in ascending order, padded with -1
  *   out_score     same shape, fp32: each selected block's group-summed causal leaf LSE,

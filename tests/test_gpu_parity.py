@@ -112,9 +112,13 @@ def test_routing_copy_is_hi_lo_of_means(env, d):
     bits = a[1].view(np.uint16).reshape(means.shape[:-1] + (d // 32, 2, 32))
     hi = synth.bf16_bits_to_f32(bits[..., 0, :]).reshape(means.shape)
     lo = synth.bf16_bits_to_f32(bits[..., 1, :]).reshape(means.shape)
-    assert np.array_equal(hi, synth.bf16_bits_to_f32(synth.to_bf16_bits(means)))
-    err = np.abs(hi.astype(np.float64) + lo - means)
-    assert np.all(err <= np.abs(means) * 2.0 ** -17 + 1e-30)
+    # the copy holds fp32(s * log2(e)) * mean, s = 1/sqrt(d) in fp32 (the default scale)
+    s = np.float32(1.0) / np.sqrt(np.float32(d))
+    c = np.float32(s * np.float32(1.4426950408889634))
+    v = (means * c).astype(np.float32)
+    assert np.array_equal(hi, synth.bf16_bits_to_f32(synth.to_bf16_bits(v)))
+    err = np.abs(hi.astype(np.float64) + lo - v)
+    assert np.all(err <= np.abs(v) * 2.0 ** -17 + 1e-30)
     check_pyramid(op, k, means, "rcopy")
 
 
