@@ -9,10 +9,12 @@ follows a 1 GiB write that evicts L2 and MALL; warm: back to back).
 
 Prints one JSON line.  Per-stage times come from HIP events recorded by the library on
 the stream its kernels run on (pisa_select_prefill_staged) and around pisa_build_pyramid.
-The roofline entry is for the stage with the largest average time; its algorithmic work
-per launch is stated in the design notes.  ``cpu_baseline`` times the fp64 CPU oracle
-(test infrastructure) on a bounded sample of the 256K workload and scales it to the
-whole workload.
+The roofline entry is for the stage with the largest average time (the dense upper-level
+routing launch); its algorithmic work per launch is stated in the design notes, and its
+HBM traffic comes from the committed counter summary under profiles/ while the kernel's
+sources still match it (else null).  ``cpu_baseline`` times the fp64 CPU oracle (test
+infrastructure) on a bounded sample of the 256K workload and scales it to the whole
+workload.
 """
 from __future__ import annotations
 
@@ -44,7 +46,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-64k", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=262144)
+    ap.add_argument("--cpu-sample-rows", type=int, default=393216)
     ap.add_argument("--only", choices=["256k", "64k", "decode"], default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -63,24 +65,59 @@ def visible(n_l, bq, shift):
     return np.minimum(n_l, (bq >> shift) + 1)
 
 
-def routing_dots_per_query(levels, K, bq):
-    """Child dot products one query (one head) scores over the routing levels L..2.
+def routing_dots_by_level(levels, K, bq):
+    """Child dot products one query (one head) scores at each routing level l = L..2
+    (returned as {l: array over queries}).
 
     Candidates at the top level are its visible nodes; below, the visible children of at
     most K kept nodes (2K slots).  Exact except that a kept frontier node may have one
     visible child instead of two (at most one dot per level less)."""
     L = len(levels) - 1
+    out = {}
     if L == 1:
-        return np.zeros_like(bq)
-    dots = np.zeros_like(bq)
+        return out
     cand = visible(levels[L], bq, L - 1)
     for l in range(L, 1, -1):
         vis_child = visible(levels[l - 1], bq, l - 2)
         all_vis = cand == visible(levels[l], bq, l - 1)
         d = np.where(all_vis, vis_child, np.minimum(2 * cand, vis_child))
-        dots += d
+        out[l] = d
         cand = np.where(cand <= K, d, np.minimum(2 * K, vis_child))
-    return dots
+    return out
+
+
+# Counter summary of the dominant kernel (HBM traffic per launch), valid while the
+# kernel's sources are unchanged.
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "route_dense_kernel_256k_hbm_traffic.md")
+TRAFFIC_SOURCES = ["k_route_dense.hip", "route_dev.h", "dev_common.h", "pisa_internal.h"]
+
+
+def kernel_sources_sha1():
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_selection_pyramid_amd", "csrc")
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dense routing kernel from the committed counter summary,
+    or None if there is none or the kernel changed since the counters were taken."""
+    try:
+        fields = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if "=" in line and line.lstrip().startswith("- "):
+                    k, v = line.lstrip()[2:].split("=", 1)
+                    fields[k.strip()] = v.strip().strip("`")
+        if fields.get("sources_sha1") != kernel_sources_sha1():
+            return None
+        return int(fields["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def forced_keys_per_query(N, C):
@@ -116,14 +153,14 @@ class Prefill:
             return
         ev[0].record()
         pisa.build_pyramid(self.p, self.k, self.pyr)
-        pisa.select_prefill_staged(self.p, self.q, self.k, self.pyr, self.ws, self.oi, self.os, ev[1:6])
+        pisa.select_prefill_staged(self.p, self.q, self.k, self.pyr, self.ws, self.oi, self.os, ev[1:7])
 
     def run(self, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         for e in evs:  # torch creates the HIP event on first record; the library records them later
             for x in e:
                 x.record()
@@ -133,12 +170,12 @@ class Prefill:
             self.step(evs[s])
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-        names = ["build", "route", "group", "leaf", "final"]
+        names = ["build", "route_upper", "route_l2", "group", "leaf", "final"]
         stage = {n: [] for n in names}
         for e in evs:
             for j, n in enumerate(names):
                 stage[n].append(e[j].elapsed_time(e[j + 1]))
-        total = [e[0].elapsed_time(e[5]) for e in evs]
+        total = [e[0].elapsed_time(e[6]) for e in evs]
         return wall_ms, {n: statistics.mean(v) for n, v in stage.items()}, statistics.median(total)
 
     def work(self):
@@ -149,17 +186,20 @@ class Prefill:
         T = offs[-1]
         BH = p.batch * p.n_kv_heads
         bq = np.arange(p.seq_len) // C
-        rdots = int(routing_dots_per_query(levels, K, bq).sum())
+        by_level = routing_dots_by_level(levels, K, bq)
+        upper = int(sum(v.sum() for l, v in by_level.items() if l >= 3))
+        l2 = int(by_level[2].sum()) if 2 in by_level else 0
         pairs = self.pisa.routed_pairs(p, self.ws)
         fkeys = int(forced_keys_per_query(p.seq_len, C).sum())
         return {
             "build": ("hbm", BH * (p.seq_len * d * 2 + T * d * 8), "GB/s"),
-            "route": ("alu", BH * rdots * G * 2 * d, "TFLOP/s"),
+            "route_upper": ("mfma", BH * upper * G * 2 * d, "TFLOP/s"),
+            "route_l2": ("mfma", BH * l2 * G * 2 * d, "TFLOP/s"),
             "leaf": ("mfma", pairs * G * C * 2 * d, "TFLOP/s"),
             "final": ("mfma", BH * fkeys * G * 2 * d, "TFLOP/s"),
             "group": ("hbm", BH * p.seq_len * 2 * K * 4 * 4, "GB/s"),
             "_pairs": pairs,
-            "_route_dots": BH * rdots,
+            "_route_dots": BH * (upper + l2),
         }
 
 
@@ -172,8 +212,9 @@ def roofline(stage_ms, work):
     else:
         achieved = amount / t / 1e12
         peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else VALU_FP32_PEAK_TFLOPS
+    traffic = recorded_traffic() if dom == "route_upper" else None
     return dom, {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                 "frac": round(achieved / peak, 4), "traffic": None}
+                 "frac": round(achieved / peak, 4), "traffic": traffic}
 
 
 def time_decode(torch, pisa, synth, steps):

@@ -123,11 +123,12 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
 
 template <int D, int G, int GPW>
 int route_mfma_launch(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
-                      hipStream_t st) {
+                      hipEvent_t mid, hipStream_t st) {
   if (g.L >= 3) {
     const int rc = launch_route_upper_dense(g, q, pyr, x2, st);
     if (rc != PISA_OK) return rc;
   }
+  if (mid && hipEventRecord(mid, st) != hipSuccess) return PISA_ERR_HIP;
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));
   const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
   route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt);
@@ -136,27 +137,27 @@ int route_mfma_launch(const Geo& g, const void* q, const float* pyr, int32_t* x2
 
 template <int D, int G>
 int route_mfma_g(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
-                 hipStream_t st) {
+                 hipEvent_t mid, hipStream_t st) {
   const int gpw = route_groups_per_wave(g.G, g.K);
   if constexpr (G <= 4) {
-    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, pyr, x2, cand, cnt, st);
+    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, pyr, x2, cand, cnt, mid, st);
   }
   if constexpr (G <= 8) {
-    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, pyr, x2, cand, cnt, st);
+    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, pyr, x2, cand, cnt, mid, st);
   }
-  return route_mfma_launch<D, G, 1>(g, q, pyr, x2, cand, cnt, st);
+  return route_mfma_launch<D, G, 1>(g, q, pyr, x2, cand, cnt, mid, st);
 }
 
 template <int D>
 int route_d(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
-            hipStream_t st) {
+            hipEvent_t mid, hipStream_t st) {
   if (dtype == PISA_BF16) {
     switch (g.G) {
-      case 1: return route_mfma_g<D, 1>(g, q, pyr, x2, cand, cnt, st);
-      case 2: return route_mfma_g<D, 2>(g, q, pyr, x2, cand, cnt, st);
-      case 4: return route_mfma_g<D, 4>(g, q, pyr, x2, cand, cnt, st);
-      case 8: return route_mfma_g<D, 8>(g, q, pyr, x2, cand, cnt, st);
-      case 16: return route_mfma_g<D, 16>(g, q, pyr, x2, cand, cnt, st);
+      case 1: return route_mfma_g<D, 1>(g, q, pyr, x2, cand, cnt, mid, st);
+      case 2: return route_mfma_g<D, 2>(g, q, pyr, x2, cand, cnt, mid, st);
+      case 4: return route_mfma_g<D, 4>(g, q, pyr, x2, cand, cnt, mid, st);
+      case 8: return route_mfma_g<D, 8>(g, q, pyr, x2, cand, cnt, mid, st);
+      case 16: return route_mfma_g<D, 16>(g, q, pyr, x2, cand, cnt, mid, st);
       default: return PISA_ERR_UNSUPPORTED;
     }
   }
@@ -170,7 +171,8 @@ int route_d(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x
     case 16: route_valu_kernel<D, 16><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
-  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  return (mid && hipEventRecord(mid, st) != hipSuccess) ? PISA_ERR_HIP : PISA_OK;
 }
 
 __global__ void zero_kernel(int32_t* __restrict__ a, int64_t n) {
@@ -181,9 +183,9 @@ __global__ void zero_kernel(int32_t* __restrict__ a, int64_t n) {
 }  // namespace
 
 int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand,
-                 int32_t* cnt, hipStream_t st) {
-  if (g.d == 128) return route_d<128>(g, dtype, q, pyr, x2, cand, cnt, st);
-  if (g.d == 64) return route_d<64>(g, dtype, q, pyr, x2, cand, cnt, st);
+                 int32_t* cnt, hipEvent_t mid, hipStream_t st) {
+  if (g.d == 128) return route_d<128>(g, dtype, q, pyr, x2, cand, cnt, mid, st);
+  if (g.d == 64) return route_d<64>(g, dtype, q, pyr, x2, cand, cnt, mid, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -161,21 +161,23 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   // counters are contiguous: cnt then cursor (each 256-aligned)
   if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
   // the entries region is free until the scatter: it carries the level-2 candidates
-  if ((rc = launch_route(g, p->dtype, q, pyramid, entries, cand, cnt, st)) != PISA_OK) return rc;
-  if ((rc = mark(1)) != PISA_OK) return rc;
+  if ((rc = launch_route(g, p->dtype, q, pyramid, entries, cand, cnt, ev ? (hipEvent_t)ev[1] : nullptr, st)) !=
+      PISA_OK)
+    return rc;
+  if ((rc = mark(2)) != PISA_OK) return rc;
   if (p->dtype == PISA_F32) {
-    if ((rc = mark(2)) != PISA_OK) return rc;
-    if ((rc = launch_qmajor(g, p->dtype, q, k, cand, out_idx, out_score, st)) != PISA_OK) return rc;
     if ((rc = mark(3)) != PISA_OK) return rc;
-    return mark(4);
+    if ((rc = launch_qmajor(g, p->dtype, q, k, cand, out_idx, out_score, st)) != PISA_OK) return rc;
+    if ((rc = mark(4)) != PISA_OK) return rc;
+    return mark(5);
   }
   if ((rc = launch_scan(cnt, w.M, chunk_entries(g.G), off, choff, st)) != PISA_OK) return rc;
   if ((rc = launch_scatter(g, cand, off, cursor, entries, st)) != PISA_OK) return rc;
-  if ((rc = mark(2)) != PISA_OK) return rc;
-  if ((rc = launch_leaf_mfma(g, q, k, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
   if ((rc = mark(3)) != PISA_OK) return rc;
+  if ((rc = launch_leaf_mfma(g, q, k, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
+  if ((rc = mark(4)) != PISA_OK) return rc;
   if ((rc = launch_forced_final(g, q, k, cand, lscore, out_idx, out_score, st)) != PISA_OK) return rc;
-  return mark(4);
+  return mark(5);
 }
 
 int pisa_select_prefill(const pisa_problem* p, const void* q, const void* k, const float* pyramid, void* workspace,
@@ -187,8 +189,8 @@ int pisa_select_prefill(const pisa_problem* p, const void* q, const void* k, con
 int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void* k, const float* pyramid,
                                void* workspace, size_t workspace_bytes, int32_t* out_idx, float* out_score,
                                void* const* events, int32_t n_events, pisa_stream_t stream) {
-  if (!events || n_events != 5) return PISA_ERR_INVALID_ARG;
-  for (int i = 0; i < 5; ++i)
+  if (!events || n_events != 6) return PISA_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
     if (!events[i]) return PISA_ERR_INVALID_ARG;
   return select_prefill_impl(p, q, k, pyramid, workspace, workspace_bytes, out_idx, out_score, events,
                              (hipStream_t)stream);

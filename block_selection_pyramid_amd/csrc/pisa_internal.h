@@ -51,9 +51,10 @@ inline int route_groups_per_wave(int G, int K) {
 // ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);
-// x2: scratch of B*Hkv*N*2K int32 (level-2 candidates between the two routing launches)
+// x2: scratch of B*Hkv*N*2K int32 (level-2 candidates between the two routing launches);
+// mid (may be null) is recorded between the upper-level and the level-2 launch
 int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand,
-                 int32_t* cnt, hipStream_t st);
+                 int32_t* cnt, hipEvent_t mid, hipStream_t st);
 // Levels L..3 of the bf16 walk (L >= 3), scored densely per leaf block; writes x2.
 int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, int32_t* x2, hipStream_t st);
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);

@@ -207,8 +207,8 @@ def select_prefill(p: Problem, q: torch.Tensor, k: torch.Tensor, pyramid: torch.
 
 
 def select_prefill_staged(p: Problem, q, k, pyramid, ws, out_idx, out_score, events, stream=None):
-    """pisa_select_prefill recording 5 torch.cuda.Event (enable_timing=True) at its stage
-    boundaries (route | group | leaf | forced+final)."""
+    """pisa_select_prefill recording 6 torch.cuda.Event (enable_timing=True) at its stage
+    boundaries (upper-level routing | level-2 routing | group | leaf | forced+final)."""
     oshape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
     qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.seq_len, p.head_dim))
     kp = _dev(k, "k", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
@@ -216,10 +216,10 @@ def select_prefill_staged(p: Problem, q, k, pyramid, ws, out_idx, out_score, eve
     wp = _dev(ws, "workspace", torch.uint8)
     ip = _dev(out_idx, "out_idx", torch.int32, oshape)
     sp = _dev(out_score, "out_score", torch.float32, oshape)
-    if len(events) != 5:
-        raise ValueError("need 5 events")
-    arr = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
-    _check(load().pisa_select_prefill_staged(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, arr, 5,
+    if len(events) != 6:
+        raise ValueError("need 6 events")
+    arr = (ctypes.c_void_p * 6)(*[e.cuda_event for e in events])
+    _check(load().pisa_select_prefill_staged(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, arr, 6,
                                              _stream(stream)), "pisa_select_prefill_staged")
     return out_idx, out_score
 

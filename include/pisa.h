@@ -149,11 +149,13 @@ int pisa_select_decode(const pisa_problem* p, const void* q, const void* k_cache
 /*
  * Same as pisa_select_prefill, and additionally records caller-created HIP events
  * (hipEvent_t handles, e.g. from hipEventCreate) on `stream` at the stage boundaries:
- * events[0] before the first kernel, events[1] after routing (counter clearing + the
- * routing walk), events[2] after leaf grouping (scan + scatter), events[3] after leaf
- * scoring, events[4] after forced blocks + final Top-K.  n_events must be 5.  Stages a
- * problem does not use (fp32 inputs score leaves query-major in stage 3) record their
- * boundary events back to back.  For per-kernel timing of the prefill path.
+ * events[0] before the first kernel, events[1] after counter clearing and the routing of
+ * levels L..3 (bf16: the dense upper-level launch), events[2] after the routing of level
+ * 2, events[3] after leaf grouping (scan + scatter), events[4] after leaf scoring,
+ * events[5] after forced blocks + final Top-K.  n_events must be 6.  Stages a problem does
+ * not use (L < 3; fp32 inputs walk all levels in one launch and score leaves query-major
+ * in stage 4) record their boundary events back to back.  For per-kernel timing of the
+ * prefill path.
  */
 int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void* k, const float* pyramid,
                                void* workspace, size_t workspace_bytes, int32_t* out_idx, float* out_score,

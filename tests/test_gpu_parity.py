@@ -152,6 +152,52 @@ def test_prefill_edge_cases(env, case):
     verify(op, q, k, opyr, np.arange(B * Hkv * N), idx, sc, what=name)
 
 
+@pytest.mark.parametrize("dt,d,decode", [(synth.BF16, 64, False), (synth.BF16, 128, True), (synth.F32, 64, False)])
+def test_non_default_scale(env, dt, d, decode):
+    # the routing copy carries the scale, so build and selection must both honour it
+    torch, pisa = env
+    N = 4096 + 37 if not decode else 9000
+    w = synth.custom(name="scale-%d-%d" % (d, decode), batch=2 if decode else 1, seq_len=N, n_q_heads=4,
+                     n_kv_heads=1, head_dim=d, top_k=5, dtype=dt, seed=500 + d, needles=6, decode=decode)
+    p, op = problems(pisa, w, scale=0.037)
+    q, k, _ = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log(w.name, "scale 0.037: launching")
+    pyr = pisa.build_pyramid(p, kd)
+    if decode:
+        idx, sc = pisa.select_decode(p, qd, kd, pyr)
+    else:
+        idx, sc = pisa.select_prefill(p, qd, kd, pyr, pisa.workspace(p))
+    torch.cuda.synchronize()
+    opyr = check_pyramid(op, k, pyr.cpu().numpy()[0], w.name)
+    rows = np.arange(w.batch * w.n_kv_heads * (1 if decode else N))
+    verify(op, q, k, opyr, rows, idx.cpu().numpy(), sc.cpu().numpy(), decode=decode, what=w.name)
+
+
+def test_staged_call_matches_plain_call(env):
+    torch, pisa = env
+    w = synth.WORKLOADS["4k"]
+    p, _ = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    pyr = pisa.build_pyramid(p, kd)
+    ws = pisa.workspace(p)
+    i1, s1 = pisa.select_prefill(p, qd, kd, pyr, ws)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    for e in ev:  # torch creates the HIP event on its first record
+        e.record()
+    torch.cuda.synchronize()
+    i2, s2 = torch.empty_like(i1), torch.empty_like(s1)
+    pisa.select_prefill_staged(p, qd, kd, pyr, ws, i2, s2, ev)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    gaps = [ev[j].elapsed_time(ev[j + 1]) for j in range(5)]
+    log("staged", "stage ms %s" % [round(x, 4) for x in gaps])
+    assert all(x >= 0 for x in gaps)
+    with pytest.raises(ValueError):
+        pisa.select_prefill_staged(p, qd, kd, pyr, ws, i2, s2, ev[:5])
+
+
 @pytest.mark.parametrize("name", ["tiny", "4k"])
 def test_prefill_workload_all_rows(env, name):
     w = synth.WORKLOADS[name]
