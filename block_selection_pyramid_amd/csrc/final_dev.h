@@ -11,6 +11,25 @@
 
 namespace pisa {
 
+// Key row of result register v in lane half hh of a v_mfma_f32_32x32x16_bf16 tile (A rows
+// = keys): 8 (v / 4) + 4 hh + (v mod 4).
+__device__ __forceinline__ int key_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
+
+// LSE over the 64 keys of this lane's column (32 here, 32 in lane l ^ 32), in units of
+// the scaled dot product.  Masked keys hold -inf; at least one key is live.
+__device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
+  float m = -INFINITY;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(a0[v], a1[v]));
+  m = fmaxf(m, __shfl_xor(m, 32));
+  float sum = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v)
+    sum += __builtin_amdgcn_exp2f((a0[v] - m) * s_log2e) + __builtin_amdgcn_exp2f((a1[v] - m) * s_log2e);
+  sum += __shfl_xor(sum, 32);
+  return s * m + logf(sum);
+}
+
 // VALU score of one leaf tile for one query group: lane = key of the tile.
 template <typename T, int D, int G>
 __device__ float score_tile_valu(const T* __restrict__ keys /* this (b,h) */, int j, int i, int N, int C,

@@ -82,23 +82,6 @@ __device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, in
   }
 }
 
-__device__ __forceinline__ int key_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
-
-// LSE over the 64 keys of this lane's column (32 here, 32 in lane l ^ 32), in units of
-// the scaled dot product.  Masked keys hold -inf; at least one key is live.
-__device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
-  float m = -INFINITY;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(a0[v], a1[v]));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  float sum = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v)
-    sum += __builtin_amdgcn_exp2f((a0[v] - m) * s_log2e) + __builtin_amdgcn_exp2f((a1[v] - m) * s_log2e);
-  sum += __shfl_xor(sum, 32);
-  return s * m + logf(sum);
-}
-
 // Workgroup = one chunk of a leaf block's list (QC = 128/G entries); each wavefront
 // scores 32/G entries (32 columns = (entry, head) pairs per MFMA tile).
 template <int D, int G>
@@ -250,6 +233,42 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
   }
 }
 
+// Final selection for problems whose forced blocks the dense routing launch scored (fsc:
+// the forced blocks' scores of each query group, ascending): workgroup = the 64 queries of
+// one leaf block of one (b, h); each wavefront finalizes 16 of them, 64/SL per pass.
+template <int SL>
+__global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __restrict__ cand,
+                                                    const float* __restrict__ lscore, const float* __restrict__ fsc,
+                                                    int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+  constexpr int NQ = 64 / SL;      // query groups finalized per pass
+  constexpr int PASSES = 16 / NQ;  // passes for a wavefront's 16 queries
+  __shared__ __attribute__((aligned(16))) uint64_t kx_all[4][64];
+  __shared__ __attribute__((aligned(16))) int32_t lx_all[4][64];
+  const int bq = blockIdx.x, bh = blockIdx.y;
+  int F[3];
+  const int nf = forced_blocks(bq, F);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int twoK = 2 * geo.K;
+  const int slot = lane % SL, qq = lane / SL;
+  int cl[PASSES];
+  float cv[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
+    const int64_t row = (int64_t)bh * geo.N + i;
+    cl[p] = (i < geo.N && slot < twoK) ? cand[row * twoK + slot] : -1;
+    cv[p] = cl[p] >= 0 ? lscore[row * twoK + slot] : -INFINITY;
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
+    const bool live = i < geo.N;
+    const int64_t row = (int64_t)bh * geo.N + (live ? i : 0);
+    finalize_rows<SL>(cl[p], cv[p], F, nf, fsc + row * 3, geo.K, lane, live, kx_all[wave], lx_all[wave],
+                      out_idx + row * geo.K, out_score + row * geo.K);
+  }
+}
+
 template <int D>
 int leaf_d(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
            const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
@@ -302,6 +321,15 @@ int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* 
   if (g.d == 128) return leaf_d<128>(g, q, k, off, choff, entries, M, lscore, st);
   if (g.d == 64) return leaf_d<64>(g, q, k, off, choff, entries, M, lscore, st);
   return PISA_ERR_UNSUPPORTED;
+}
+
+int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const float* fsc, int32_t* out_idx,
+                 float* out_score, hipStream_t st) {
+  dim3 grid(g.n1, g.B * g.Hkv);
+  if (2 * g.K <= 16) final_kernel<16><<<grid, 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+  else if (2 * g.K <= 32) final_kernel<32><<<grid, 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+  else final_kernel<64><<<grid, 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 int launch_forced_final(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore,

@@ -122,10 +122,10 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
 }
 
 template <int D, int G, int GPW>
-int route_mfma_launch(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
-                      hipEvent_t mid, hipStream_t st) {
+int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
+                      int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st) {
   if (g.L >= 3) {
-    const int rc = launch_route_upper_dense(g, q, pyr, x2, st);
+    const int rc = launch_route_upper_dense(g, q, pyr, k, x2, fsc, st);
     if (rc != PISA_OK) return rc;
   }
   if (mid && hipEventRecord(mid, st) != hipSuccess) return PISA_ERR_HIP;
@@ -136,28 +136,28 @@ int route_mfma_launch(const Geo& g, const void* q, const float* pyr, int32_t* x2
 }
 
 template <int D, int G>
-int route_mfma_g(const Geo& g, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
-                 hipEvent_t mid, hipStream_t st) {
+int route_mfma_g(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
+                 int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st) {
   const int gpw = route_groups_per_wave(g.G, g.K);
   if constexpr (G <= 4) {
-    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, pyr, x2, cand, cnt, mid, st);
+    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
   }
   if constexpr (G <= 8) {
-    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, pyr, x2, cand, cnt, mid, st);
+    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
   }
-  return route_mfma_launch<D, G, 1>(g, q, pyr, x2, cand, cnt, mid, st);
+  return route_mfma_launch<D, G, 1>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
 }
 
 template <int D>
-int route_d(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand, int32_t* cnt,
-            hipEvent_t mid, hipStream_t st) {
+int route_d(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
+            int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st) {
   if (dtype == PISA_BF16) {
     switch (g.G) {
-      case 1: return route_mfma_g<D, 1>(g, q, pyr, x2, cand, cnt, mid, st);
-      case 2: return route_mfma_g<D, 2>(g, q, pyr, x2, cand, cnt, mid, st);
-      case 4: return route_mfma_g<D, 4>(g, q, pyr, x2, cand, cnt, mid, st);
-      case 8: return route_mfma_g<D, 8>(g, q, pyr, x2, cand, cnt, mid, st);
-      case 16: return route_mfma_g<D, 16>(g, q, pyr, x2, cand, cnt, mid, st);
+      case 1: return route_mfma_g<D, 1>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
+      case 2: return route_mfma_g<D, 2>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
+      case 4: return route_mfma_g<D, 4>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
+      case 8: return route_mfma_g<D, 8>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
+      case 16: return route_mfma_g<D, 16>(g, q, k, pyr, x2, fsc, cand, cnt, mid, st);
       default: return PISA_ERR_UNSUPPORTED;
     }
   }
@@ -182,10 +182,10 @@ __global__ void zero_kernel(int32_t* __restrict__ a, int64_t n) {
 
 }  // namespace
 
-int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand,
-                 int32_t* cnt, hipEvent_t mid, hipStream_t st) {
-  if (g.d == 128) return route_d<128>(g, dtype, q, pyr, x2, cand, cnt, mid, st);
-  if (g.d == 64) return route_d<64>(g, dtype, q, pyr, x2, cand, cnt, mid, st);
+int launch_route(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2,
+                 float* fsc, int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st) {
+  if (g.d == 128) return route_d<128>(g, dtype, q, k, pyr, x2, fsc, cand, cnt, mid, st);
+  if (g.d == 64) return route_d<64>(g, dtype, q, k, pyr, x2, fsc, cand, cnt, mid, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -20,7 +20,12 @@
 //
 // Output: per query group, the 2K level-2 candidate slots (children of the Top-K nodes of
 // level 3, -1 where a child does not exist or is not visible), the input of the level-2
-// routing launch.
+// routing launch.  The same workgroup then scores its queries' forced leaf blocks
+// ("Block Sparse Attention with Log-Linear Complexity", agihunt.info summary, LSE and
+// forced-block paragraph: first, previous and current block; leaf score = causal LSE over
+// the block's raw keys, summed over the G heads) with the query rows it already holds:
+// each forced key tile is staged in LDS once and contracted on the matrix cores.
+#include "final_dev.h"
 #include "route_dev.h"
 
 namespace pisa {
@@ -68,10 +73,28 @@ __device__ __forceinline__ void dense_store_tile(char* lds, int buf, int wave, i
   }
 }
 
+// Forced key tile f (64 raw keys) into fragment-major LDS: fragment fi = rb KS + ks holds
+// keys 64 f + 32 rb + (lane & 31), dims 16 ks + 8 (lane >> 5) .. +8; keys past N read
+// zeros (the row index is clamped and the value replaced, so no load sits behind a branch).
+template <int D, int NU>
+__device__ __forceinline__ void dense_load_keys(const bf16* kb, int N, int f, int wave, int lane, u32x4 (&stg)[NU]) {
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int fi = wave + kDenseWaves * u, rb = fi / KS, ks = fi % KS;
+    const int key = 64 * f + 32 * rb + (lane & 31);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(kb + (int64_t)min(key, N - 1) * D + 16 * ks + 8 * (lane >> 5));
+    stg[u] = key < N ? v : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 // KC >= K: capacity of kept nodes per query (the 2*KC candidate slots hold 2K in use).
+// K <= 8 asks for three wavefronts per SIMD: the few registers this costs spill only in
+// the phases after the routing loop.
 template <int D, int G, int KC>
-__global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
-                                                          Geo geo, int32_t l_bot, int32_t* __restrict__ x2) {
+__global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
+                                                          const bf16* __restrict__ k, Geo geo, int32_t l_bot,
+                                                          int32_t* __restrict__ x2, float* __restrict__ fsc) {
   constexpr int NCG = DenseShape<G>::NCG, QPW = DenseShape<G>::QPW;
   constexpr int KS = D / 16;         // k-steps of 16 dims
   constexpr int F = 2 * KS;          // 1 KB fragments of a staged child tile (hi, lo per k-step)
@@ -317,41 +340,106 @@ __global__ __launch_bounds__(256) void route_dense_kernel(const bf16* __restrict
       __builtin_nontemporal_store(c1, dst + 1);
     }
   }
+
+  // ---- forced leaf blocks {0, bw - 1, bw} of this wavefront's queries (one leaf block bw:
+  // QPW divides C).  The workgroup's tiles are 0 and bfirst - 1 .. bqmax (at most 4).
+  static_assert(kLeaf % QPW == 0, "a wavefront's queries share one leaf block");
+  const int bfirst = iwg / C;
+  int ft[4];
+  int nft = 0;
+  ft[nft++] = 0;
+  for (int f = max(1, bfirst - 1); f <= bqmax && nft < 4; ++f) ft[nft++] = f;
+  const bf16* kb = k + (int64_t)bh * N * D;
+  __syncthreads();  // the staging buffers are free again
+  dense_load_keys<D>(kb, N, ft[0], wave, lane, stg);
+  dense_store_tile<D>(lds, 0, wave, lane, stg);
+  __syncthreads();
+  int nfw = 0;  // |F| of this wavefront's leaf block
+  {
+    int Fw[3];
+    nfw = forced_blocks(bqw, Fw);
+  }
+  for (int x = 0; x < nft; ++x) {
+    const int f = ft[x];
+    dense_load_keys<D>(kb, N, ft[min(x + 1, nft - 1)], wave, lane, stg);  // next tile (or this one again)
+    const bool mine = iw < N && (f == 0 || f == bqw - 1 || f == bqw);
+    if (mine) {
+      const int fidx = f == 0 ? 0 : (f == bqw - 1 ? 1 : nfw - 1);  // position in F (ascending)
+      const char* Tt = lds + (x & 1) * TILE;
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        f32x16 a0, a1;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) a0[v] = a1[v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          // fragments read per k-step (and per column group): this phase runs once, and
+          // holding all of them would cost the routing loop a wavefront per SIMD
+          const bf16x8 f0 = *reinterpret_cast<const bf16x8*>(Tt + (ks * 64 + lane) * 16);
+          const bf16x8 f1 = *reinterpret_cast<const bf16x8*>(Tt + ((KS + ks) * 64 + lane) * 16);
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[cg][ks], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[cg][ks], a1, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const int i = iw + cg * (32 / G) + j / G;  // this lane's column's query
+        if (f == bqw || 64 * f + 64 > N) {          // causal mask: only the current (or a short) block
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int ta = 64 * f + key_row(v, hh), tb = ta + 32;
+            if (ta > i || ta >= N) a0[v] = -INFINITY;
+            if (tb > i || tb >= N) a1[v] = -INFINITY;
+          }
+        }
+        // columns past N still see live keys (ta <= N - 1 < i), so no NaN arises
+        float lse = column_lse32(a0, a1, geo.s, geo.s_log2e);
+        lse = group_sum<G>(lse);
+        if (hh == 0 && j % G == 0 && i < N) fsc[((int64_t)bh * N + i) * 3 + fidx] = lse;
+        // one column group at a time: overlapping them would raise the kernel's register
+        // count above what three wavefronts per SIMD allow
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (x + 1 < nft) dense_store_tile<D>(lds, (x + 1) & 1, wave, lane, stg);
+    __syncthreads();
+  }
 }
 
 template <int D, int G, int KC>
-int dense_launch(const Geo& g, const bf16* q, const float* pyr, int32_t* x2, hipStream_t st) {
+int dense_launch(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc,
+                 hipStream_t st) {
   constexpr int QW = kDenseWaves * DenseShape<G>::QPW;  // queries per workgroup
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + QW - 1) / QW));
-  route_dense_kernel<D, G, KC><<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, g, 3, x2);
+  route_dense_kernel<D, G, KC><<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, 3, x2,
+                                                                                           fsc);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 template <int D, int G>
-int dense_k(const Geo& g, const bf16* q, const float* pyr, int32_t* x2, hipStream_t st) {
-  if (g.K <= 8) return dense_launch<D, G, 8>(g, q, pyr, x2, st);
-  if (g.K <= 16) return dense_launch<D, G, 16>(g, q, pyr, x2, st);
-  return dense_launch<D, G, 32>(g, q, pyr, x2, st);
+int dense_k(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc, hipStream_t st) {
+  if (g.K <= 8) return dense_launch<D, G, 8>(g, q, pyr, k, x2, fsc, st);
+  if (g.K <= 16) return dense_launch<D, G, 16>(g, q, pyr, k, x2, fsc, st);
+  return dense_launch<D, G, 32>(g, q, pyr, k, x2, fsc, st);
 }
 
 template <int D>
-int dense_g(const Geo& g, const bf16* q, const float* pyr, int32_t* x2, hipStream_t st) {
+int dense_g(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc, hipStream_t st) {
   switch (g.G) {
-    case 1: return dense_k<D, 1>(g, q, pyr, x2, st);
-    case 2: return dense_k<D, 2>(g, q, pyr, x2, st);
-    case 4: return dense_k<D, 4>(g, q, pyr, x2, st);
-    case 8: return dense_k<D, 8>(g, q, pyr, x2, st);
-    case 16: return dense_k<D, 16>(g, q, pyr, x2, st);
+    case 1: return dense_k<D, 1>(g, q, pyr, k, x2, fsc, st);
+    case 2: return dense_k<D, 2>(g, q, pyr, k, x2, fsc, st);
+    case 4: return dense_k<D, 4>(g, q, pyr, k, x2, fsc, st);
+    case 8: return dense_k<D, 8>(g, q, pyr, k, x2, fsc, st);
+    case 16: return dense_k<D, 16>(g, q, pyr, k, x2, fsc, st);
     default: return PISA_ERR_UNSUPPORTED;
   }
 }
 
 }  // namespace
 
-int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, int32_t* x2, hipStream_t st) {
+int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, const void* k, int32_t* x2, float* fsc,
+                              hipStream_t st) {
   if (g.L < 3 || g.K > 32) return PISA_ERR_UNSUPPORTED;
-  if (g.d == 128) return dense_g<128>(g, (const bf16*)q, pyr, x2, st);
-  if (g.d == 64) return dense_g<64>(g, (const bf16*)q, pyr, x2, st);
+  if (g.d == 128) return dense_g<128>(g, (const bf16*)q, pyr, (const bf16*)k, x2, fsc, st);
+  if (g.d == 64) return dense_g<64>(g, (const bf16*)q, pyr, (const bf16*)k, x2, fsc, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -77,6 +77,7 @@ PrefillWs prefill_ws(const Geo& g) {
   w.off = o;     o = align256(o + sizeof(int32_t) * (w.M + 1));
   w.choff = o;   o = align256(o + sizeof(int32_t) * (w.M + 1));
   w.entries = o; o = align256(o + sizeof(int32_t) * w.slots);
+  w.fsc = o;     o = align256(o + sizeof(float) * 3 * (size_t)g.B * g.Hkv * g.N);
   w.total = o;
   return w;
 }
@@ -154,6 +155,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   int32_t* off = (int32_t*)(ws + w.off);
   int32_t* choff = (int32_t*)(ws + w.choff);
   int32_t* entries = (int32_t*)(ws + w.entries);
+  float* fsc = (float*)(ws + w.fsc);
   auto mark = [&](int i) { return ev ? (hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess ? PISA_OK : PISA_ERR_HIP)
                                      : PISA_OK; };
 
@@ -161,8 +163,8 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   // counters are contiguous: cnt then cursor (each 256-aligned)
   if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
   // the entries region is free until the scatter: it carries the level-2 candidates
-  if ((rc = launch_route(g, p->dtype, q, pyramid, entries, cand, cnt, ev ? (hipEvent_t)ev[1] : nullptr, st)) !=
-      PISA_OK)
+  if ((rc = launch_route(g, p->dtype, q, k, pyramid, entries, fsc, cand, cnt, ev ? (hipEvent_t)ev[1] : nullptr,
+                        st)) != PISA_OK)
     return rc;
   if ((rc = mark(2)) != PISA_OK) return rc;
   if (p->dtype == PISA_F32) {
@@ -176,7 +178,9 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   if ((rc = mark(3)) != PISA_OK) return rc;
   if ((rc = launch_leaf_mfma(g, q, k, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
   if ((rc = mark(4)) != PISA_OK) return rc;
-  if ((rc = launch_forced_final(g, q, k, cand, lscore, out_idx, out_score, st)) != PISA_OK) return rc;
+  rc = route_scores_forced(g, p->dtype) ? launch_final(g, cand, lscore, fsc, out_idx, out_score, st)
+                                        : launch_forced_final(g, q, k, cand, lscore, out_idx, out_score, st);
+  if (rc != PISA_OK) return rc;
   return mark(5);
 }
 

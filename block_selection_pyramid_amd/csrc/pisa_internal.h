@@ -27,7 +27,7 @@ struct Geo {
 
 // Prefill workspace carve-up (byte offsets, 256-aligned).
 struct PrefillWs {
-  size_t cand, lscore, cnt, cursor, off, choff, entries, total;
+  size_t cand, lscore, cnt, cursor, off, choff, entries, fsc, total;
   int64_t slots;  // B*Hkv*N*2K
   int32_t M;      // B*Hkv*n1 leaf lists
 };
@@ -52,16 +52,23 @@ inline int route_groups_per_wave(int G, int K) {
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);
 // x2: scratch of B*Hkv*N*2K int32 (level-2 candidates between the two routing launches);
-// mid (may be null) is recorded between the upper-level and the level-2 launch
-int launch_route(const Geo& g, int dtype, const void* q, const float* pyr, int32_t* x2, int32_t* cand,
-                 int32_t* cnt, hipEvent_t mid, hipStream_t st);
-// Levels L..3 of the bf16 walk (L >= 3), scored densely per leaf block; writes x2.
-int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, int32_t* x2, hipStream_t st);
+// fsc: forced-block scores, written when route_scores_forced(); mid (may be null) is
+// recorded between the upper-level and the level-2 launch
+int launch_route(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2,
+                 float* fsc, int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st);
+// Levels L..3 of the bf16 walk (L >= 3), scored densely per leaf block; writes x2 and the
+// forced blocks' scores fsc [B*Hkv*N*3] (ascending forced-block order).
+int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, const void* k, int32_t* x2, float* fsc,
+                              hipStream_t st);
+// true when launch_route scores the forced blocks (into fsc) for this problem
+inline bool route_scores_forced(const Geo& g, int dtype) { return dtype == PISA_BF16 && g.L >= 3; }
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
 int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                    hipStream_t st);
 int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
                      const int32_t* entries, int32_t M, float* lscore, hipStream_t st);
+int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const float* fsc, int32_t* out_idx,
+                 float* out_score, hipStream_t st);
 int launch_forced_final(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore,
                         int32_t* out_idx, float* out_score, hipStream_t st);
 int launch_qmajor(const Geo& g, int dtype, const void* q, const void* k, const int32_t* cand, int32_t* out_idx,
