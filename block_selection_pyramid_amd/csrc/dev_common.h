@@ -12,6 +12,8 @@ using bf16 = uint16_t;  // raw bfloat16 bits
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+// 16 raw bytes as a native vector (HIP's uint4 struct can keep arrays of it in scratch)
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -110,12 +112,12 @@ __device__ __forceinline__ float group_prod(float v) {
 }
 
 // Forced leaf blocks of a query in leaf block bq: {0, bq-1, bq} that exist, ascending.
+// (Constant indices only, so the array stays in registers.)
 __device__ __forceinline__ int forced_blocks(int bq, int* f) {
-  int m = 0;
-  f[m++] = 0;
-  if (bq - 1 > 0) f[m++] = bq - 1;
-  if (bq > 0) f[m++] = bq;
-  return m;
+  f[0] = 0;
+  f[1] = bq >= 2 ? bq - 1 : bq;  // bq = 1: {0, 1}
+  f[2] = bq;                      // bq >= 2: {0, bq - 1, bq}
+  return bq == 0 ? 1 : (bq == 1 ? 2 : 3);
 }
 __device__ __forceinline__ bool is_forced(int j, int bq) { return j == 0 || j == bq || j == bq - 1; }
 

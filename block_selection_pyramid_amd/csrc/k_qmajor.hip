@@ -7,10 +7,12 @@
 //
 // Decode ("Block Sparse Attention with Log-Linear Complexity", agihunt.info summary,
 // kernels paragraph: a single-stage kernel for decode avoids launch overhead; rcap.io
-// explainer: one query at a time leaves no cross-query tile reuse): one workgroup per
-// (sequence, KV head) walks the pyramid for the new query at position N-1 (wavefront 0),
-// then all four wavefronts score the candidate and forced tiles, and wavefront 0 writes
-// the selection.  Everything stays in LDS and registers; one launch per step.
+// explainer: one query at a time leaves no cross-query tile reuse): one workgroup of 16
+// wavefronts per (sequence, KV head).  All of them first load the query rows and stage
+// the top pyramid levels' routing copy in LDS (one parallel burst); wavefront 0 then walks
+// the pyramid for the new query at position N-1, its top levels from LDS; then every
+// wavefront scores one of the <= 2K + 3 candidate and forced tiles (so their loads are in
+// flight together), and wavefront 0 writes the selection.  One launch per step.
 #include <type_traits>
 
 #include "final_dev.h"
@@ -57,10 +59,15 @@ __global__ __launch_bounds__(256) void qmajor_kernel(const T* __restrict__ q, co
   finalize_row(leaf, sc, F, nf, scs + twoK, geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
 }
 
+constexpr int kDecodeWaves = 16;
+constexpr int64_t kDecodeStageBytes = 64 * 1024;  // LDS for the staged top levels
+
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                     const float* __restrict__ pyr, Geo geo,
-                                                     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                                   const float* __restrict__ pyr, Geo geo,
+                                                                   int32_t stage_lo, int32_t* __restrict__ out_idx,
+                                                                   float* __restrict__ out_score) {
+  extern __shared__ __attribute__((aligned(16))) char stage[];  // bf16: levels [stage_lo, L-1]
   __shared__ float qs[G * (D + kQPad)];
   __shared__ WalkLds wl;
   __shared__ WalkLdsM<1> wlm;
@@ -78,14 +85,44 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   const T* rows[G];
 #pragma unroll
   for (int r = 0; r < G; ++r) rows[r] = q + ((int64_t)b * geo.Hq + h * G + r) * D;
+
+  // query rows (fp32, for the tile scoring) and the staged top levels, by all wavefronts
+  {
+    constexpr int VEC = Vec<T>::N;
+    constexpr int PER_ROW = D / VEC;
+    for (int t = threadIdx.x; t < G * PER_ROW; t += 64 * kDecodeWaves) {
+      const int r = t / PER_ROW, e = (t % PER_ROW) * VEC;
+      float x[VEC];
+      Vec<T>::load(q + ((int64_t)b * geo.Hq + h * G + r) * D + e, x);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) qs[r * (D + kQPad) + e + v] = x[v];
+    }
+  }
+  const bf16* R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+  int sbase = 0;
+  if constexpr (std::is_same<T, bf16>::value) {
+    using Walk = MfmaWalk<D, G, 1>;
+    sbase = stage_lo < geo.L ? geo.off[stage_lo] : 0;
+    const int snodes = stage_lo < geo.L ? geo.off[geo.L] - sbase : 0;
+    constexpr int kChunks = Walk::kRec / 16;  // 16-byte pieces per node
+    for (int t = threadIdx.x; t < snodes * kChunks; t += 64 * kDecodeWaves) {
+      const int nd = t / kChunks, c = t % kChunks;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(R) +
+                                                      (int64_t)(sbase + nd) * Walk::kRec + 16 * c);
+      *reinterpret_cast<u32x4*>(stage + nd * Walk::kRecLds + 16 * c) = v;
+    }
+  }
+  __syncthreads();
+
   if (wave == 0) {
-    load_qrows<T, D, G>(rows, qs, lane);  // the tile scoring below reads q from LDS
-    wave_sync();
     int nx;
     const int32_t* X;
     if constexpr (std::is_same<T, bf16>::value) {
       MfmaWalk<D, G, 1> mw;
-      mw.R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+      mw.R = R;
+      mw.lds = stage;
+      mw.stage_lo = stage_lo < geo.L ? stage_lo : 1 << 30;
+      mw.stage_base = sbase;
       mw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
       nx = mw.walk(geo, bq, &wlm, lane);
       X = wlm.X;
@@ -103,7 +140,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const T* __restrict__ q, co
   }
   __syncthreads();
   const T* keys = k + (int64_t)bh * geo.N * D;
-  for (int t = wave; t < twoK + nf; t += 4) {
+  for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
     const int j = tj[t];
     if (j < 0) continue;
     const float s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
@@ -140,12 +177,25 @@ int decode_g(const Geo& g, const void* q, const void* k, const float* pyr, int32
   const unsigned grid = g.B * g.Hkv;
   const T* qq = (const T*)q;
   const T* kk = (const T*)k;
+  // bf16: stage the levels >= 2 nearest the top whose routing-copy records fit the budget
+  int stage_lo = g.L;
+  int64_t bytes = 0;
+  if (std::is_same<T, bf16>::value) {
+    constexpr int64_t kRecLds = 4 * D + 16;
+    while (stage_lo - 1 >= 2) {
+      const int64_t add = (int64_t)g.n[stage_lo - 1] * kRecLds;
+      if (bytes + add > kDecodeStageBytes) break;
+      bytes += add;
+      --stage_lo;
+    }
+  }
+  const unsigned block = 64 * kDecodeWaves;
   switch (g.G) {
-    case 1: decode_kernel<T, D, 1><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
-    case 2: decode_kernel<T, D, 2><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
-    case 4: decode_kernel<T, D, 4><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
-    case 8: decode_kernel<T, D, 8><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
-    case 16: decode_kernel<T, D, 16><<<grid, 256, 0, st>>>(qq, kk, pyr, g, oi, os); break;
+    case 1: decode_kernel<T, D, 1><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
+    case 2: decode_kernel<T, D, 2><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
+    case 4: decode_kernel<T, D, 4><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
+    case 8: decode_kernel<T, D, 8><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
+    case 16: decode_kernel<T, D, 16><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;

@@ -34,8 +34,6 @@ namespace {
 
 constexpr int kDenseWaves = 4;
 
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-
 // Columns of the B operand: 32 (query, head) pairs per column group, head fastest.
 template <int G>
 struct DenseShape {
