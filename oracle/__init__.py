@@ -29,6 +29,9 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 MAXL = 48
 
 F32, BF16 = 0, 1
+# routing-level scorers: the LSE over child summaries and its first- / second-order
+# Taylor truncations (PISA-1 / PISA-2)
+LSE, PISA1, PISA2 = 0, 1, 2
 
 
 def build(force: bool = False) -> str:
@@ -60,6 +63,7 @@ class _Problem(ctypes.Structure):
         ("branch", ctypes.c_int32),
         ("scale", ctypes.c_double),
         ("dtype", ctypes.c_int32),
+        ("scorer", ctypes.c_int32),
     ]
 
 
@@ -117,6 +121,7 @@ class Problem:
     branch: int = 2
     scale: float = 0.0  # <= 0 selects 1/sqrt(head_dim)
     dtype: int = BF16
+    scorer: int = LSE  # routing-level score: LSE, PISA1 or PISA2
 
     @property
     def group(self) -> int:
@@ -128,7 +133,7 @@ class Problem:
 
     def c(self) -> _Problem:
         return _Problem(self.batch, self.seq_len, self.n_q_heads, self.n_kv_heads, self.head_dim,
-                        self.block, self.top_k, self.branch, self.s, self.dtype)
+                        self.block, self.top_k, self.branch, self.s, self.dtype, self.scorer)
 
 
 def _ptr(a: np.ndarray | None):

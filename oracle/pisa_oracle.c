@@ -35,7 +35,15 @@
  *    LSE; Top-K orders by (score descending, block index ascending);
  *  - forced blocks F = {0, b-1, b} within [0, b] count inside K:
  *    Sel = F u TopK_{K-|F|}(X_1 \ F), reported ascending with their leaf
- *    scores, padded with (-1, -inf); K >= 3 is required.
+ *    scores, padded with (-1, -inf); K >= 3 is required;
+ *  - the PISA-1 / PISA-2 ablations ([A] LSE paragraph: the first keeps only
+ *    the mean, the second adds the variance term of the LSE's Taylor
+ *    expansion; [B] scoring-rule paragraph: truncations at first and second
+ *    order) replace the routing levels' per-head LSE over the m visible
+ *    children's scaled dots x_c by log m + mean(x) (PISA-1) or
+ *    log m + mean(x) + Var(x)/2 (PISA-2, population variance), the Taylor
+ *    expansion of log sum exp(x_c) = log m + log mean exp(x_c) about the mean;
+ *    leaf and forced scores stay the exact raw-key LSE.
  */
 #include <math.h>
 #include <stdint.h>
@@ -48,6 +56,7 @@ typedef struct {
   int32_t batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k, branch;
   double scale; /* > 0; the caller resolves the 1/sqrt(d) default */
   int32_t dtype; /* 0 = float32 values, 1 = bfloat16 bit patterns */
+  int32_t scorer; /* routing-level score: 0 = LSE, 1 = PISA-1, 2 = PISA-2 */
 } orc_problem;
 
 typedef struct {
@@ -77,7 +86,7 @@ typedef struct {
   int64_t n[ORC_MAXL + 2];
   int64_t off[ORC_MAXL + 2]; /* node offset of level l inside one head's pyramid */
   int64_t span[ORC_MAXL + 2]; /* g^(l-1): leaf blocks per level-l node */
-  int L, G, d, C, K, g;
+  int L, G, d, C, K, g, scorer;
   int64_t N, T;
   double s;
 } geo_t;
@@ -92,6 +101,7 @@ static void geo_init(geo_t* q, const orc_problem* P) {
   q->g = P->branch;
   q->G = P->n_q_heads / P->n_kv_heads;
   q->s = P->scale;
+  q->scorer = P->scorer;
   q->L = orc_levels(q->N, q->C, q->K, q->g, q->n);
   q->off[1] = 0;
   q->span[1] = 1;
@@ -188,8 +198,25 @@ typedef struct {
 
 static int visible(const row_t* r, int l, int64_t j) { return j * r->q->span[l] <= r->bq; }
 
-/* Score of node x at level l >= 2: sum over heads of LSE over its visible
- * children c (level l-1) of s * <q_h, P_{l-1}[c]>.  per_head may be NULL. */
+/* Routing score of m values: their LSE, or its first- / second-order Taylor
+ * truncation about the mean (PISA-1 / PISA-2). */
+static double routing_score(const double* x, int64_t m, int scorer) {
+  if (scorer == 0) return orc_lse(x, m);
+  double mean = 0.0;
+  for (int64_t c = 0; c < m; ++c) mean += x[c];
+  mean /= (double)m;
+  double out = log((double)m) + mean;
+  if (scorer == 2) {
+    double var = 0.0;
+    for (int64_t c = 0; c < m; ++c) var += (x[c] - mean) * (x[c] - mean);
+    out += 0.5 * var / (double)m;
+  }
+  return out;
+}
+
+/* Score of node x at level l >= 2: sum over heads of the routing score (LSE,
+ * or a truncation of it) over its visible children c (level l-1) of
+ * s * <q_h, P_{l-1}[c]>.  per_head may be NULL. */
 static double node_score(const row_t* r, int l, int64_t x, double* per_head) {
   const geo_t* q = r->q;
   int64_t c0 = x * q->g, c1 = c0 + q->g < q->n[l - 1] ? c0 + q->g : q->n[l - 1];
@@ -201,7 +228,7 @@ static double node_score(const row_t* r, int l, int64_t x, double* per_head) {
       if (!visible(r, l - 1, c)) continue;
       vals[m++] = q->s * dot(r->qrows + (int64_t)h * q->d, r->pyr + (q->off[l - 1] + c) * q->d, q->d);
     }
-    double v = orc_lse(vals, m);
+    double v = routing_score(vals, m, q->scorer);
     if (per_head) per_head[h] = v;
     total += v;
   }
@@ -392,6 +419,7 @@ int orc_valid_problem(const orc_problem* P) {
   if (P->head_dim < 1 || P->block < 1 || P->branch < 2 || P->branch > 64 || P->top_k < 3) return 0;
   if ((int64_t)P->branch * P->top_k > 4096) return 0;
   if (!(P->scale > 0.0) || (P->dtype != 0 && P->dtype != 1)) return 0;
+  if (P->scorer < 0 || P->scorer > 2) return 0;
   return 1;
 }
 

@@ -39,6 +39,12 @@ MUTANTS = {
     "leaf-takes-one-less": ("  int Kp = K - nf;\n  int take", "  int Kp = K - nf - 1;\n  int take"),
     "level-stop-early": ("while (n[L] > (int64_t)g * K && L < ORC_MAXL)", "while (n[L] > (int64_t)K && L < ORC_MAXL)"),
     "transposed-child-level": ("r->pyr + (q->off[l - 1] + c) * q->d, q->d);", "r->pyr + (q->off[l] + c % q->n[l]) * q->d, q->d);"),
+    "pisa-scorer-ignored": ("  if (scorer == 0) return orc_lse(x, m);", "  return orc_lse(x, m);"),
+    "pisa-drops-log-m": ("  double out = log((double)m) + mean;", "  double out = mean;"),
+    "pisa1-keeps-variance": ("  if (scorer == 2) {\n    double var", "  if (scorer >= 1) {\n    double var"),
+    "pisa2-variance-sign": ("    out += 0.5 * var / (double)m;", "    out -= 0.5 * var / (double)m;"),
+    "pisa2-sample-variance": ("    out += 0.5 * var / (double)m;", "    out += 0.5 * var / (double)(m > 1 ? m - 1 : 1);"),
+    "pisa2-no-half": ("    out += 0.5 * var / (double)m;", "    out += var / (double)m;"),
 }
 
 

@@ -11,6 +11,7 @@ paragraph with the Jensen remark; the paragraph on Appendix A's sandwich).
 import json
 import math
 import os
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -398,3 +399,192 @@ def test_dominant_needle_is_found():
         kk[0, 0, pos] = 4000.0 * q[0, 0, i] / np.linalg.norm(q[0, 0, i])
         idx, _ = oracle.select(p, q, kk, rows=[i])
         assert pos // 64 in idx[0].tolist()
+
+
+# ------------------------------------------ PISA-1 / PISA-2 routing scorers
+# The ablations replace a routing node's per-head LSE over its visible children by the
+# first- or second-order truncation of its expansion about the children's mean
+# (agihunt.info LSE paragraph; rcap.io scoring-rule paragraph).  The pins below tie the two
+# truncations to the oracle's pinned LSE and pyramid, never to a retyped formula.
+
+PISA1, PISA2 = oracle.PISA1, oracle.PISA2
+
+
+def _visible_children(sizes, l, j, bq, g):
+    return [c for c in range(j * g, min(j * g + g, sizes[l - 1])) if c * g ** (l - 2) <= bq]
+
+
+def _three_scores(p, q, pyr, row, l, j):
+    return [oracle.node_score(replace(p, scorer=s), q, pyr, row, l, j)[1] for s in (oracle.LSE, PISA1, PISA2)]
+
+
+def test_pisa_two_children_log_cosh():
+    # two children with dots a, b: LSE - PISA-1 = log cosh((a-b)/2) and
+    # PISA-2 - PISA-1 = ((a-b)/2)^2 / 2, so PISA-2 - PISA-1 = acosh(exp(LSE - PISA-1))^2 / 2;
+    # one child: all three equal its dot
+    N, K, g = 64 * 200 + 9, 4, 2
+    p, q, k = _prefill(80, N, 2, 1, 16, K)
+    pyr = oracle.build_pyramid(p, k)
+    sizes = oracle.levels(N, 64, K, g)
+    seen = {1: 0, 2: 0}
+    for i in (N - 1, 64 * 131 + 5, 64 * 64):
+        bq = i // 64
+        for l in range(2, len(sizes)):
+            for j in range(sizes[l]):
+                m = len(_visible_children(sizes, l, j, bq, g))
+                if m == 0:
+                    continue
+                e, a, b = _three_scores(p, q, pyr, i, l, j)
+                seen[m] += 1
+                if m == 1:
+                    np.testing.assert_allclose(a, e, rtol=0, atol=1e-12)
+                    np.testing.assert_allclose(b, e, rtol=0, atol=1e-12)
+                    continue
+                assert np.all(a <= e + 1e-12) and np.all(e <= b + 1e-12)  # log cosh t <= t^2/2
+                half_gap = np.arccosh(np.exp(e - a))
+                np.testing.assert_allclose(b - a, half_gap ** 2 / 2, rtol=1e-6, atol=1e-10)
+    assert seen[1] > 0 and seen[2] > 20
+
+
+def test_pisa1_of_fully_visible_node_is_parent_mean():
+    # when every existing child is visible, the mean of the children's dots is the dot with
+    # their mean, which is the parent node itself: PISA-1 = log m + s <q, P_l[j]>
+    N, K, g = 64 * 90 + 40, 3, 3  # ragged: the last node of a level may have fewer children
+    p, q, k = _prefill(81, N, 2, 1, 16, K, g=g)
+    pyr = oracle.build_pyramid(p, k)
+    sizes = oracle.levels(N, 64, K, g)
+    offs = np.cumsum([0] + sizes[1:])
+    i = N - 1
+    bq = i // 64
+    n = 0
+    for l in range(2, len(sizes)):
+        for j in range(sizes[l]):
+            kids = _visible_children(sizes, l, j, bq, g)
+            m = min(j * g + g, sizes[l - 1]) - j * g
+            if len(kids) != m:
+                continue
+            _, a = oracle.node_score(replace(p, scorer=PISA1), q, pyr, i, l, j)
+            for r in range(2):
+                expect = math.log(m) + p.s * float(q[0, r, i].astype(np.float64) @ pyr[0, 0, offs[l - 1] + j])
+                assert abs(a[r] - expect) < 1e-10
+            n += 1
+    assert n > 10
+
+
+def test_pisa_truncation_orders_in_the_small_scale_limit():
+    # with the dots scaled by t -> 0: LSE - PISA-1 = t^2 Var/2 + O(t^3) (halving t quarters
+    # it) while LSE - PISA-2 = O(t^3) (halving t divides it by 8, or 16 for two children
+    # whose third cumulant vanishes); partially visible nodes (m < g) pin log m, not log g
+    N, K, g = 64 * 60 + 17, 3, 3
+    p, q, k = _prefill(82, N, 2, 1, 16, K, g=g)
+    pyr = oracle.build_pyramid(p, k)
+    sizes = oracle.levels(N, 64, K, g)
+    checked = {2: 0, 3: 0}
+    for i in (N - 1, N - 1 - 64 * 4, 64 * 19 + 3):
+        bq = i // 64
+        for l in range(2, len(sizes)):
+            for j in range(sizes[l]):
+                m = len(_visible_children(sizes, l, j, bq, g))
+                if m < 2:
+                    continue
+                d1, d2 = [], []
+                for t in (2.0 ** -5, 2.0 ** -6):
+                    e, a, b = _three_scores(replace(p, scale=p.s * t), q, pyr, i, l, j)
+                    d1.append(e - a)
+                    d2.append(e - b)
+                r1 = d1[0] / d1[1]
+                r2 = np.abs(d2[0]) / np.maximum(np.abs(d2[1]), 1e-300)
+                assert np.all(np.abs(r1 - 4) < 0.3), (l, j, m, r1)
+                assert np.all(r2 > 7) and np.all(np.abs(d2[1]) < 1e-2 * d1[1]), (l, j, m, r2)
+                if m == 2:
+                    assert np.all(np.abs(r2 - 16) < 2), (l, j, r2)
+                checked[m] += 1
+    assert checked[2] > 0 and checked[3] > 5
+
+
+def test_pisa1_below_lse_for_any_branching():
+    # Jensen: the mean of the dots never exceeds log mean exp of them
+    N, K, g = 64 * 100, 3, 4
+    p, q, k = _prefill(83, N, 4, 2, 16, K, g=g)
+    pyr = oracle.build_pyramid(p, k)
+    sizes = oracle.levels(N, 64, K, g)
+    for row in (N - 1, 2 * N - 1, N + 3000):
+        bq = (row % N) // 64
+        for l in range(2, len(sizes)):
+            for j in range(sizes[l]):
+                if not _visible_children(sizes, l, j, bq, g):
+                    continue
+                e, a, b = _three_scores(p, q, pyr, row, l, j)
+                assert np.all(a <= e + 1e-12)
+                assert np.all(b >= a - 1e-12)  # the variance term is non-negative
+
+
+def test_pisa_selection_invariants_and_exact_leaf_scores():
+    # the scorers only change which leaf candidates survive the routing levels: the result
+    # keeps the forced blocks and the K-slot layout, and every reported score is the exact
+    # causal leaf LSE of its block
+    N, K = 4096 + 37, 6
+    p, q, k = _prefill(84, N, 4, 2, 16, K, B=2)
+    pyr = oracle.build_pyramid(p, k)
+    rows = list(range(0, N, 37)) + [N - 1, 3 * N + 2000, 4 * N - 1]
+    base, _ = oracle.select(p, q, k, pyr, rows=rows)
+    differs = 0
+    for scorer in (PISA1, PISA2):
+        ps = replace(p, scorer=scorer)
+        idx, sc = oracle.select(ps, q, k, pyr, rows=rows)
+        differs += int((idx != base).any(axis=1).sum())
+        for t, row in enumerate(rows):
+            b = (row % N) // 64
+            n = int((idx[t] >= 0).sum())
+            assert n == min(K, b + 1)
+            sel = idx[t, :n]
+            assert np.all(np.diff(sel) > 0) and sel.min() >= 0 and sel.max() <= b
+            assert {f for f in (0, b - 1, b) if f >= 0} <= set(sel.tolist())
+            for u, j in enumerate(sel):
+                assert abs(sc[t, u] - oracle.leaf_score(p, q, k, row, int(j))[0]) < 1e-12
+        st, _ = oracle.check(ps, q, k, pyr, rows, idx, sc.astype(np.float32), tau=1e-9, rtol=1e-6)
+        assert np.all(st == 0)
+    assert differs > 0  # the truncations do change some selections at this size
+
+
+def test_pisa_scorers_do_not_matter_without_routing_levels():
+    # L == 1 (every leaf block fits in g*K): selection is leaf scoring alone
+    N, K = 64 * 16, 8
+    p, q, k = _prefill(85, N, 2, 1, 16, K)
+    assert len(oracle.levels(N, 64, K, 2)) == 2
+    i0, s0 = oracle.select(p, q, k)
+    for scorer in (PISA1, PISA2):
+        i1, s1 = oracle.select(replace(p, scorer=scorer), q, k)
+        assert np.array_equal(i0, i1)
+        np.testing.assert_array_equal(s0, s1)
+
+
+@pytest.mark.parametrize("scorer", [PISA1, PISA2])
+def test_pisa_decode_equals_last_prefill_row(scorer):
+    N, K = 4096 + 11, 8
+    p, q, k = _prefill(86, N, 4, 2, 16, K, B=2)
+    p = replace(p, scorer=scorer)
+    pyr = oracle.build_pyramid(p, k)
+    qdec = np.ascontiguousarray(q[:, :, N - 1, :])
+    idd, sd = oracle.select(p, qdec, k, pyr, decode=True)
+    rows = [(b * 2 + h) * N + N - 1 for b in range(2) for h in range(2)]
+    ip, sp = oracle.select(p, q, k, pyr, rows=rows)
+    assert np.array_equal(idd, ip)
+    np.testing.assert_array_equal(sd, sp)
+
+
+@pytest.mark.parametrize("scorer,g", [(PISA1, 2), (PISA2, 2), (PISA2, 3)])
+def test_pisa_matches_independent_numpy_walk(scorer, g):
+    N, K = 2048 + 50, 4
+    p, q, k = _prefill(87 + g, N, 2, 1, 16, K, g=g)
+    p = replace(p, scorer=scorer)
+    pyr = oracle.build_pyramid(p, k)
+    rows = list(range(0, N, 41)) + [N - 1]
+    idx, _ = oracle.select(p, q, k, pyr, rows=rows)
+    kd = k[0, 0].astype(np.float64)
+    for t, i in enumerate(rows):
+        wi, ws = select_one(q[0, :, i].astype(np.float64), kd, i, 64, K, g, p.s, scorer=scorer)
+        if idx[t].tolist() != wi:
+            st, _ = oracle.check(p, q, k, pyr, [i], np.array([wi]), np.array([ws], dtype=np.float32),
+                                 tau=1e-9, rtol=1e-9)
+            assert st[0] == 0, (i, idx[t], wi)

@@ -33,8 +33,12 @@ def pyramid(keys: np.ndarray, C: int, K: int, g: int):
     return levels
 
 
-def select_one(qrows: np.ndarray, keys: np.ndarray, i: int, C: int, K: int, g: int, s: float):
-    """qrows [G, d], keys [N, d] (float64).  Returns (idx list, score list) of length K."""
+def select_one(qrows: np.ndarray, keys: np.ndarray, i: int, C: int, K: int, g: int, s: float, scorer: int = 0):
+    """qrows [G, d], keys [N, d] (float64).  Returns (idx list, score list) of length K.
+
+    scorer 0 routes by the LSE over a node's visible children, 1 by log m + their mean
+    (PISA-1), 2 by that plus half their population variance (PISA-2).
+    """
     N = keys.shape[0]
     levels = pyramid(keys, C, K, g)
     L = len(levels) - 1
@@ -49,7 +53,12 @@ def select_one(qrows: np.ndarray, keys: np.ndarray, i: int, C: int, K: int, g: i
     def route_score(l, j):
         kids = children(l, j)
         dots = s * (qrows @ levels[l - 1][kids].T)  # [G, |kids|]
-        return float(logsumexp(dots, axis=1).sum())
+        if scorer == 0:
+            return float(logsumexp(dots, axis=1).sum())
+        per_head = math.log(len(kids)) + dots.mean(axis=1)
+        if scorer == 2:
+            per_head = per_head + dots.var(axis=1) / 2
+        return float(per_head.sum())
 
     def leaf_score(j):
         hi = min(j * C + C, N, i + 1)
