@@ -5,7 +5,8 @@ Headline (one "step"): pyramid build + prefill selection at 256K tokens, C=64, K
 16 query / 4 KV heads, d=128, bf16 (the pages' selection-latency workload, synthetic
 inputs resident in HBM).  Also timed in the same run: the same step at 64K, and one
 decode step (32 sequences x 262144-token cache, precomputed pyramid; cold: each step
-follows a 1 GiB write that evicts L2 and MALL; warm: back to back).
+follows a 1 GiB write that evicts L2 and MALL; warm: back to back), and the 256K step
+with the PISA-1 / PISA-2 routing scorers (ablations; extra fields).
 
 Prints one JSON line.  Per-stage times come from HIP events recorded by the library on
 the stream its kernels run on (pisa_select_prefill_staged) and around pisa_build_pyramid.
@@ -46,6 +47,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-64k", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scorers", action="store_true",
+                    help="skip the PISA-1 / PISA-2 ablation timings at 256K")
     ap.add_argument("--cpu-sample-rows", type=int, default=393216)
     ap.add_argument("--only", choices=["256k", "64k", "decode"], default=None,
                     help="time one workload only (profiling runs)")
@@ -301,6 +304,17 @@ def main():
         head = (b.w, wall_ms, stage_ms, ev_ms, dom, roof, work)
         log("256k: wall %.3f ms/step, events %.3f ms; stages %s" % (
             wall_ms, ev_ms, {k: round(v, 3) for k, v in stage_ms.items()}))
+        if not a.no_scorers:
+            # the PISA-1 / PISA-2 routing scorers on the same inputs (ablations, not the headline)
+            from dataclasses import replace
+            lse_p = b.p
+            for name, scorer in (("pisa1", pisa.PISA1), ("pisa2", pisa.PISA2)):
+                b.p = replace(lse_p, scorer=scorer)
+                ws, sms, _ = b.run(a.steps, a.warmup)
+                extra["prefill_256k_%s_ms" % name] = round(ws, 4)
+                extra["prefill_256k_%s_stages_ms" % name] = {k: round(v, 4) for k, v in sms.items()}
+                log("256k %s: wall %.3f ms/step; stages %s" % (name, ws, extra["prefill_256k_%s_stages_ms" % name]))
+            b.p = lse_p
         del b
         torch.cuda.empty_cache()
     if a.only in (None, "64k") and not a.no_64k:

@@ -119,6 +119,24 @@ __device__ __forceinline__ int forced_blocks(int bq, int* f) {
   f[2] = bq;                      // bq >= 2: {0, bq - 1, bq}
   return bq == 0 ? 1 : (bq == 1 ? 2 : 3);
 }
+// Routing score of one head for a node with the scaled dots y0 (first child, visible) and
+// y1 (second child, -inf when missing or not visible) under the PISA-1 / PISA-2 truncations
+// of the pair LSE about the children's mean ("Block Sparse Attention with Log-Linear
+// Complexity": agihunt.info summary, LSE paragraph; rcap.io explainer, scoring-rule
+// paragraph): log m + mean, plus half the population variance for PISA-2.  With two
+// children the variance is (y0 - y1)^2 / 4.  `one` is log(2) in the dots' units and c2 the
+// coefficient of (y0 - y1)^2: 0 for PISA-1, 1/8 in natural units, ln(2)/8 in log2 units
+// (where a natural-units quantity v reads v / ln 2, so the variance term scales by ln 2).
+__device__ __forceinline__ float pair_trunc(float y0, float y1, float one, float c2) {
+  const float d = y0 - y1;
+  const float v = fmaf(c2 * d, d, one + 0.5f * (y0 + y1));
+  return y1 == -INFINITY ? y0 : v;
+}
+// c2 of pair_trunc for the scorer, in log2 (log2 = true) or natural units.
+__host__ __device__ __forceinline__ float trunc_c2(int scorer, bool log2) {
+  return scorer == PISA_PISA2 ? (log2 ? 0.6931471805599453f / 8.f : 0.125f) : 0.f;
+}
+
 __device__ __forceinline__ bool is_forced(int j, int bq) { return j == 0 || j == bq || j == bq - 1; }
 
 }  // namespace pisa

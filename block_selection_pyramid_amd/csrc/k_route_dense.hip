@@ -13,8 +13,9 @@
 // contraction on the matrix cores (v_mfma_f32_32x32x16_bf16, A = 32 child summaries from
 // the hi/lo routing copy staged in LDS once per workgroup, B = 32 (query, head) columns
 // held in registers; the routing copy is pre-scaled by s log2(e), so the products are the
-// scores in log2 units).  The epilogue forms the pair LSE of each node's two children and
-// the head sum, and each wavefront keeps only the scores of its own queries' candidates.  The
+// scores in log2 units).  The epilogue forms the pair LSE of each node's two children (or,
+// for the PISA-1 / PISA-2 ablations, its truncation about their mean) and the head sum,
+// and each wavefront keeps only the scores of its own queries' candidates.  The
 // staged child tiles do not depend on the walk, so the next tile is fetched from L2 while
 // the current one is scored, across level boundaries too.
 //
@@ -88,8 +89,9 @@ __device__ __forceinline__ void dense_load_keys(const bf16* kb, int N, int f, in
 
 // KC >= K: capacity of kept nodes per query (the 2*KC candidate slots hold 2K in use).
 // K <= 8 asks for three wavefronts per SIMD: the few registers this costs spill only in
-// the phases after the routing loop.
-template <int D, int G, int KC>
+// the phases after the routing loop.  TRUNC selects the PISA-1 / PISA-2 node scores (a
+// separate instantiation keeps the LSE kernel's register allocation as it is).
+template <int D, int G, int KC, bool TRUNC>
 __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
                                                           const bf16* __restrict__ k, Geo geo, int32_t l_bot,
                                                           int32_t* __restrict__ x2, float* __restrict__ fsc) {
@@ -110,6 +112,8 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (64 + 16 * KC));  // [QPW][KC]
 
   const int N = geo.N, C = geo.C, K = geo.K, L = geo.L;
+  constexpr bool trunc = TRUNC;
+  const float c2 = trunc_c2(geo.scorer, true);
   const int BH = geo.B * geo.Hkv;
   const int bh = blockIdx.x % BH;  // workgroups of one XCD (w mod 8) share few heads
   const int iwg = (blockIdx.x / BH) * (kDenseWaves * QPW);
@@ -216,19 +220,31 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
             if (8 * a + 4 * hh + 2 * p + 1 > lim) acc[cg][4 * a + 2 * p + 1] = -INFINITY;
       }
       float mxs[8], prd[8];
+      if constexpr (!trunc) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const float a0 = acc[cg][4 * a + 2 * p], a1 = acc[cg][4 * a + 2 * p + 1];
-          const float dd = a0 - a1;
-          mxs[2 * a + p] = a0 - fminf(dd, 0.f);
-          prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(-fabsf(dd));
+          for (int p = 0; p < 2; ++p) {
+            const float a0 = acc[cg][4 * a + 2 * p], a1 = acc[cg][4 * a + 2 * p + 1];
+            const float dd = a0 - a1;
+            mxs[2 * a + p] = a0 - fminf(dd, 0.f);
+            prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(-fabsf(dd));
+          }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          mxs[e] = group_sum<G>(mxs[e]);
+          prd[e] = group_prod<G>(prd[e]);
         }
+      } else {  // PISA-1 / PISA-2: per-head truncated scores, summed over the heads
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        mxs[e] = group_sum<G>(mxs[e]);
-        prd[e] = group_prod<G>(prd[e]);
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            mxs[2 * a + p] = pair_trunc(acc[cg][4 * a + 2 * p], acc[cg][4 * a + 2 * p + 1], 1.f, c2);
+            prd[2 * a + p] = 1.f;
+          }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mxs[e] = group_sum<G>(mxs[e]);
       }
       // lane r < GE of a query's group finishes values r*VPL .. r*VPL + VPL - 1
       constexpr int GE = G < 8 ? G : 8, VPL = 8 / GE;
@@ -243,7 +259,10 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
           m = r == k ? mxs[k * VPL + u] : m;
           f = r == k ? prd[k * VPL + u] : f;
         }
-        out[u] = m + __builtin_amdgcn_logf(f);
+        if constexpr (trunc)
+          out[u] = m;
+        else
+          out[u] = m + __builtin_amdgcn_logf(f);
       }
       if (r < GE) {
         float* dst = Sx + qi * 16 + 2 * hh;
@@ -407,8 +426,12 @@ int dense_launch(const Geo& g, const bf16* q, const float* pyr, const bf16* k, i
                  hipStream_t st) {
   constexpr int QW = kDenseWaves * DenseShape<G>::QPW;  // queries per workgroup
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + QW - 1) / QW));
-  route_dense_kernel<D, G, KC><<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, 3, x2,
-                                                                                           fsc);
+  if (g.scorer == PISA_LSE)
+    route_dense_kernel<D, G, KC, false>
+        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, 3, x2, fsc);
+  else
+    route_dense_kernel<D, G, KC, true>
+        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, 3, x2, fsc);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 

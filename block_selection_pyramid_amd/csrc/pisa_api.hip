@@ -16,6 +16,7 @@ int make_geo(const pisa_problem* p, Geo* g) {
   if (p->n_q_heads % p->n_kv_heads) return PISA_ERR_INVALID_ARG;
   if (p->head_dim < 1 || p->block < 1 || p->top_k < 3 || p->branch < 2) return PISA_ERR_INVALID_ARG;
   if (p->dtype != PISA_F32 && p->dtype != PISA_BF16) return PISA_ERR_INVALID_ARG;
+  if (p->scorer != PISA_LSE && p->scorer != PISA_PISA1 && p->scorer != PISA_PISA2) return PISA_ERR_INVALID_ARG;
   if (!isfinite(p->scale)) return PISA_ERR_INVALID_ARG;
   if ((int64_t)p->top_k * p->branch > (1 << 20)) return PISA_ERR_INVALID_ARG;
   memset(g, 0, sizeof(*g));
@@ -28,6 +29,7 @@ int make_geo(const pisa_problem* p, Geo* g) {
   g->C = p->block;
   g->K = p->top_k;
   g->g = p->branch;
+  g->scorer = p->scorer;
   g->s = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)p->head_dim);
   g->s_log2e = g->s * 1.4426950408889634f;
   int64_t n = ((int64_t)g->N + g->C - 1) / g->C;

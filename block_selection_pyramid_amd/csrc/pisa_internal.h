@@ -16,6 +16,7 @@ constexpr int kMaxCand = 64;  // g*K <= 64 candidates per level (one per lane)
 // Geometry of one problem, passed by value to every kernel.
 struct Geo {
   int32_t B, Hq, Hkv, G, N, d, C, K, g, L, n1, T;
+  int32_t scorer;  // enum pisa_scorer of the routing levels
   float s;        // scale applied to every dot product
   float s_log2e;  // s * log2(e), for exp2-based LSE
   int32_t n[kMaxLevels + 2];    // n[0] = N, n[l] nodes at level l (1..L)

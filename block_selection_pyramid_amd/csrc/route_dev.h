@@ -5,6 +5,8 @@
 // at most g*K candidates per level) and scoring paragraph (a candidate's score is the
 // LogSumExp over its child summaries of q.child); agihunt.info summary, kernels paragraph
 // (the G query heads of a GQA group share the selection: their per-head LSEs are summed).
+// Under the PISA-1 / PISA-2 ablations the per-head LSE is replaced by its first- or
+// second-order truncation about the children's mean (pair_trunc).
 //
 // Candidate x of a level owns child slots 2x and 2x+1 (g = 2).  Candidate ids live in LDS;
 // -1 marks an empty slot (a child that does not exist or is not yet visible to the query).
@@ -184,7 +186,9 @@ struct MfmaWalk {
             y[c] = child_visible(ch, nchild, cshift, bq) ? acc[2 * p + c] : -INFINITY;
           }
           const float a = fmaxf(y[0], y[1]), b = fminf(y[0], y[1]);
-          lse[p] = node[p] >= 0 ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a)) : 0.f;
+          const float v = geo.scorer == PISA_LSE ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a))
+                                                 : pair_trunc(a, b, 1.f, trunc_c2(geo.scorer, true));
+          lse[p] = node[p] >= 0 ? v : 0.f;
         }
         lse[0] = group_sum<G>(lse[0]);
         lse[1] = group_sum<G>(lse[1]);
@@ -304,7 +308,9 @@ struct ValuScorer {
         const float y2 = __shfl_xor(y, 1);
         const float m = fmaxf(y, y2);
         // m is finite whenever the candidate exists: its first child is always visible.
-        sc += m + logf(expf(y - m) + expf(y2 - m));
+        // (Odd slots' sums are never written.)
+        sc += geo.scorer == PISA_LSE ? m + logf(expf(y - m) + expf(y2 - m))
+                                     : pair_trunc(m, fminf(y, y2), 0.6931471805599453f, trunc_c2(geo.scorer, false));
       }
       if (lane < 32 && (slot & 1) == 0 && x < nx) w->cs[x] = node >= 0 ? sc : -INFINITY;
     }

@@ -22,6 +22,7 @@ from . import build as _build
 
 F32, BF16 = 0, 1
 PREFILL, DECODE = 0, 1
+LSE, PISA1, PISA2 = 0, 1, 2  # enum pisa_scorer
 MAX_LEVELS = 32
 LIB_PATH = _build.OUT
 
@@ -47,6 +48,7 @@ class _CProblem(ctypes.Structure):
         ("branch", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("scorer", ctypes.c_int32),
     ]
 
 
@@ -62,10 +64,11 @@ class Problem:
     branch: int = 2
     scale: float = 0.0
     dtype: int = BF16
+    scorer: int = LSE  # routing-level score: LSE, PISA1 or PISA2 (enum pisa_scorer)
 
     def c(self) -> _CProblem:
         return _CProblem(self.batch, self.seq_len, self.n_q_heads, self.n_kv_heads, self.head_dim, self.block,
-                         self.top_k, self.branch, self.scale, self.dtype)
+                         self.top_k, self.branch, self.scale, self.dtype, self.scorer)
 
     @property
     def torch_dtype(self):

@@ -76,6 +76,17 @@ enum pisa_dtype { PISA_F32 = 0, PISA_BF16 = 1 };
 
 enum pisa_mode { PISA_PREFILL = 0, PISA_DECODE = 1 };
 
+/*
+ * Score of a routing node (levels L..2) for one head, over the scaled dots x_c of its m
+ * visible children (m = 1 or 2 here).  PISA_LSE: log sum exp(x_c), the method itself.
+ * PISA_PISA1 / PISA_PISA2: the ablations that truncate that LSE about the children's mean
+ * at first / second order ("Block Sparse Attention with Log-Linear Complexity":
+ * agihunt.info summary, LSE paragraph; rcap.io explainer, scoring-rule paragraph):
+ * log m + mean(x), and that plus half the population variance of x (for two children
+ * (x_0 - x_1)^2 / 8).  Leaf and forced-block scores are the exact LSE under every scorer.
+ */
+enum pisa_scorer { PISA_LSE = 0, PISA_PISA1 = 1, PISA_PISA2 = 2 };
+
 enum pisa_status {
   PISA_OK = 0,
   PISA_ERR_INVALID_ARG = 1, /* bad shape, null pointer, misalignment */
@@ -96,6 +107,7 @@ typedef struct {
   int32_t branch;     /* g >= 2, children per pyramid node */
   float scale;        /* s; <= 0 selects 1/sqrt(d) */
   int32_t dtype;      /* enum pisa_dtype, of q and k */
+  int32_t scorer;     /* enum pisa_scorer; 0 (PISA_LSE) is the method */
 } pisa_problem;
 
 /*

@@ -80,7 +80,7 @@ def _call_prefill(pisa, p, ws_bytes=1 << 40, q=0x1000, k=0x1000, pyr=0x1000, ws=
 
 @pytest.mark.parametrize("field,value", [("batch", 0), ("seq_len", 0), ("n_q_heads", 6), ("n_kv_heads", 0),
                                          ("top_k", 2), ("branch", 1), ("head_dim", 0), ("block", 0),
-                                         ("dtype", 7)])
+                                         ("dtype", 7), ("scorer", 3), ("scorer", -1)])
 def test_invalid_arguments(pisa, field, value):
     base = dict(batch=1, seq_len=4096, n_q_heads=16, n_kv_heads=4, head_dim=128)
     base[field] = value

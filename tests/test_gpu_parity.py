@@ -276,3 +276,58 @@ def test_decode_workload_full_size(env):
     gp = pyr.cpu().numpy()[0]
     assert np.max(np.abs(gp - opyr)) <= 1e-5
     verify(op, q, k, opyr, np.arange(w.batch * w.n_kv_heads), idx, sc, decode=True, what="decode-full")
+
+
+# PISA-1 / PISA-2: the routing levels score a node by the first- / second-order truncation
+# of its LSE about the children's mean; leaf and forced scores stay exact.  Every path that
+# scores routing nodes is covered: the dense upper-level launch and the level-2 gather
+# (bf16 prefill), the VALU walk (fp32 prefill and decode) and the fused decode walk.
+SCORER_CASES = [
+    # name, N, Hq, Hkv, d, K, dtype, B, decode
+    ("4k-G4", 4096, 16, 4, 128, 8, synth.BF16, 1, False),
+    ("ragged-G16-K16", 64 * 101 + 9, 16, 1, 128, 16, synth.BF16, 1, False),
+    ("d64-G1-K5", 4096 + 37, 2, 2, 64, 5, synth.BF16, 2, False),
+    ("L2-only", 64 * 20 + 3, 4, 1, 128, 8, synth.BF16, 1, False),
+    ("f32-G2", 3000, 4, 2, 64, 6, synth.F32, 1, False),
+    ("decode-bf16", 16384 + 5, 8, 2, 128, 8, synth.BF16, 4, True),
+    ("decode-f32", 5000, 4, 1, 64, 4, synth.F32, 2, True),
+]
+
+
+@pytest.mark.parametrize("scorer", [oracle.PISA1, oracle.PISA2], ids=["pisa1", "pisa2"])
+@pytest.mark.parametrize("case", SCORER_CASES, ids=[c[0] for c in SCORER_CASES])
+def test_pisa_scorers(env, case, scorer):
+    torch, pisa = env
+    name, N, Hq, Hkv, d, K, dt, B, decode = case
+    w = synth.custom(name=name, batch=B, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K, dtype=dt,
+                     seed=700 + N, needles=6, decode=decode)
+    p, op = problems(pisa, w, scorer=scorer)
+    q, k, _ = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log(name, "scorer %d: launching" % scorer)
+    pyr = pisa.build_pyramid(p, kd)
+    if decode:
+        idx, sc = pisa.select_decode(p, qd, kd, pyr)
+    else:
+        idx, sc = pisa.select_prefill(p, qd, kd, pyr, pisa.workspace(p))
+    torch.cuda.synchronize()
+    opyr = oracle.build_pyramid(op, k)
+    rows = np.arange(B * Hkv * (1 if decode else N))
+    verify(op, q, k, opyr, rows, idx.cpu().numpy(), sc.cpu().numpy(), decode=decode,
+           what="%s-pisa%d" % (name, scorer))
+
+
+def test_pisa2_64k_sampled(env):
+    # many routing levels (L = 8) in the dense launch, in bench.py's launch configuration
+    torch, pisa = env
+    w = synth.WORKLOADS["64k"]
+    p, op = problems(pisa, w, scorer=oracle.PISA2)
+    q, k, needles = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log("64k-pisa2", "launching")
+    pyr = pisa.build_pyramid(p, kd)
+    idx, sc = pisa.select_prefill(p, qd, kd, pyr, pisa.workspace(p))
+    torch.cuda.synchronize()
+    opyr = oracle.build_pyramid(op, k)
+    verify(op, q, k, opyr, sample_rows(w, needles, 1000, 11), idx.cpu().numpy(), sc.cpu().numpy(),
+           what="64k-pisa2")
