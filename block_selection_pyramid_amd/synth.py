@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "csrc", "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
 F32, BF16 = 0, 1
-TENSOR_Q, TENSOR_K, TENSOR_NEEDLE = 0, 1, 2
+TENSOR_Q, TENSOR_K, TENSOR_NEEDLE, TENSOR_BLOCK = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
@@ -152,3 +152,17 @@ def custom(name: str = "custom", batch=1, seq_len=1024, n_q_heads=4, n_kv_heads=
            block=64, top_k=8, branch=2, dtype=BF16, seed=11, needles=4, decode=False) -> Workload:
     return Workload(name, batch, seq_len, n_q_heads, n_kv_heads, head_dim, block, top_k, branch, dtype,
                     seed, needles, decode)
+
+
+def add_block_offsets(w: Workload, k: np.ndarray, sigma: float) -> np.ndarray:
+    """Keys with a shared offset per leaf block: key t of block b (C = w.block keys) gets
+    sigma * v_b added, v_b i.i.d. N(0, 1) per (batch, KV head, block) and dimension, then
+    bf16 workloads are rounded again.  The pyramid's means then keep a norm of about
+    sigma * sqrt(d) at every level, so sibling nodes' scores lie far apart: the inputs on
+    which truncated routing scores visibly depart from the LSE."""
+    B, H, N, d = k.shape
+    nb = (N + w.block - 1) // w.block
+    off = normal(w.seed, TENSOR_BLOCK, (B, H, nb, d), F32) * np.float32(sigma)
+    kf = bf16_bits_to_f32(k) if w.dtype == BF16 else k
+    kf = kf + np.repeat(off, w.block, axis=2)[:, :, :N, :]
+    return to_bf16_bits(kf) if w.dtype == BF16 else np.ascontiguousarray(kf, dtype=np.float32)

@@ -11,6 +11,7 @@ the rows that planted needles target, run in the same launch configuration as be
 """
 import sys
 import time
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -290,11 +291,21 @@ SCORER_CASES = [
     ("L2-only", 64 * 20 + 3, 4, 1, 128, 8, synth.BF16, 1, False),
     ("f32-G2", 3000, 4, 2, 64, 6, synth.F32, 1, False),
     ("decode-bf16", 16384 + 5, 8, 2, 128, 8, synth.BF16, 4, True),
-    ("decode-f32", 5000, 4, 1, 64, 4, synth.F32, 2, True),
+    ("decode-f32", 5000, 4, 2, 64, 4, synth.F32, 6, True),
 ]
 
 
-@pytest.mark.parametrize("scorer", [oracle.PISA1, oracle.PISA2], ids=["pisa1", "pisa2"])
+def scorer_sensitive(op, q, k, opyr, rows, decode):
+    """Rows where the LSE selection fails the truncated scorer's check: the inputs must tell
+    the scorers apart, or a path that ignored the scorer would pass."""
+    li, ls = oracle.select(replace(op, scorer=oracle.LSE), q, k, opyr, rows=rows, decode=decode)
+    st, _ = oracle.check(op, q, k, opyr, rows, li, ls.astype(np.float32), tau=TAU, rtol=RTOL, decode=decode)
+    return int((st != 0).sum())
+
+
+# Keys carry a shared offset per leaf block (sigma = 2), so sibling nodes' scores lie far
+# apart and the three scorers select differently on many rows.
+@pytest.mark.parametrize("scorer", [oracle.LSE, oracle.PISA1, oracle.PISA2], ids=["lse", "pisa1", "pisa2"])
 @pytest.mark.parametrize("case", SCORER_CASES, ids=[c[0] for c in SCORER_CASES])
 def test_pisa_scorers(env, case, scorer):
     torch, pisa = env
@@ -303,6 +314,7 @@ def test_pisa_scorers(env, case, scorer):
                      seed=700 + N, needles=6, decode=decode)
     p, op = problems(pisa, w, scorer=scorer)
     q, k, _ = synth.make_inputs(w)
+    k = synth.add_block_offsets(w, k, 2.0)
     qd, kd = dev(torch, q), dev(torch, k)
     log(name, "scorer %d: launching" % scorer)
     pyr = pisa.build_pyramid(p, kd)
@@ -314,7 +326,9 @@ def test_pisa_scorers(env, case, scorer):
     opyr = oracle.build_pyramid(op, k)
     rows = np.arange(B * Hkv * (1 if decode else N))
     verify(op, q, k, opyr, rows, idx.cpu().numpy(), sc.cpu().numpy(), decode=decode,
-           what="%s-pisa%d" % (name, scorer))
+           what="%s-scorer%d" % (name, scorer))
+    if scorer != oracle.LSE:
+        assert scorer_sensitive(op, q, k, opyr, rows, decode) > 0
 
 
 def test_pisa2_64k_sampled(env):
@@ -323,11 +337,13 @@ def test_pisa2_64k_sampled(env):
     w = synth.WORKLOADS["64k"]
     p, op = problems(pisa, w, scorer=oracle.PISA2)
     q, k, needles = synth.make_inputs(w)
+    k = synth.add_block_offsets(w, k, 2.0)
     qd, kd = dev(torch, q), dev(torch, k)
     log("64k-pisa2", "launching")
     pyr = pisa.build_pyramid(p, kd)
     idx, sc = pisa.select_prefill(p, qd, kd, pyr, pisa.workspace(p))
     torch.cuda.synchronize()
     opyr = oracle.build_pyramid(op, k)
-    verify(op, q, k, opyr, sample_rows(w, needles, 1000, 11), idx.cpu().numpy(), sc.cpu().numpy(),
-           what="64k-pisa2")
+    rows = sample_rows(w, needles, 1000, 11)
+    verify(op, q, k, opyr, rows, idx.cpu().numpy(), sc.cpu().numpy(), what="64k-pisa2")
+    assert scorer_sensitive(op, q, k, opyr, rows, False) > 0
