@@ -103,6 +103,11 @@ def _load():
             ctypes.c_double, ctypes.c_double, ctypes.c_int32, vp, vp,
         ]
         lib.orc_valid_problem.argtypes = [P]
+        lib.orc_bsa_select_rows.argtypes = [P, vp, vp, ctypes.c_int32, i64, vp, vp, vp]
+        lib.orc_bsa_scores.argtypes = [P, vp, vp, ctypes.c_int32, i64, vp]
+        lib.orc_bsa_scores.restype = i64
+        lib.orc_bsa_check_rows.argtypes = [P, vp, vp, ctypes.c_int32, i64, vp, vp, vp, ctypes.c_double,
+                                           ctypes.c_double, vp]
         _lib = lib
     return _lib
 
@@ -253,3 +258,47 @@ def check(p: Problem, q: np.ndarray, k: np.ndarray, pyr: np.ndarray, rows, idx: 
     if rc != 0:
         raise ValueError("invalid problem for the oracle: %r" % (p,))
     return status, br
+
+
+# ------------------------------------------------------------------ BSA baseline
+# The full-scan selector the pages compare against: every causal leaf block scored by the
+# dot product of the queries with its mean-pooled keys (pyramid level 1), heads summed,
+# forced blocks as in the pyramid selector (reported with score +inf), Top-(K-|F|) of the
+# rest by (score descending, index ascending).
+
+def bsa_select(p: Problem, q: np.ndarray, pyr: np.ndarray, rows=None, decode: bool = False):
+    """BSA selection for query groups (rows as for ``select``); idx int32 / score float64 [n, K]."""
+    _check_input(p, q)
+    r, n = _rows_arg(rows)
+    if r is None:
+        n = p.batch * p.n_kv_heads * (1 if decode else p.seq_len)
+    idx = np.zeros((n, p.top_k), dtype=np.int32)
+    sc = np.zeros((n, p.top_k), dtype=np.float64)
+    rc = _load().orc_bsa_select_rows(ctypes.byref(p.c()), _ptr(q), _ptr(pyr), int(decode), n, _ptr(r), _ptr(idx),
+                                     _ptr(sc))
+    if rc != 0:
+        raise ValueError("invalid problem for the oracle: %r" % (p,))
+    return idx, sc
+
+
+def bsa_scores(p: Problem, q: np.ndarray, pyr: np.ndarray, row: int, decode: bool = False) -> np.ndarray:
+    """Scores of blocks 0..b (every causal block, forced ones included) for one row."""
+    out = np.zeros(levels(p.seq_len, p.block, p.top_k, p.branch)[1], dtype=np.float64)
+    n = _load().orc_bsa_scores(ctypes.byref(p.c()), _ptr(q), _ptr(pyr), int(decode), row, _ptr(out))
+    return out[:n]
+
+
+def bsa_check(p: Problem, q: np.ndarray, pyr: np.ndarray, rows, idx: np.ndarray, score: np.ndarray,
+              tau: float = 1e-3, rtol: float = 1e-3, decode: bool = False) -> np.ndarray:
+    """Tie-tolerant verification of another BSA selection; status int32 [n] (codes of ``check``)."""
+    r, n = _rows_arg(rows)
+    if r is None:
+        n = p.batch * p.n_kv_heads * (1 if decode else p.seq_len)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(n, p.top_k)
+    score = np.ascontiguousarray(score, dtype=np.float32).reshape(n, p.top_k)
+    status = np.zeros(n, dtype=np.int32)
+    rc = _load().orc_bsa_check_rows(ctypes.byref(p.c()), _ptr(q), _ptr(pyr), int(decode), n, _ptr(r), _ptr(idx),
+                                    _ptr(score), tau, rtol, _ptr(status))
+    if rc != 0:
+        raise ValueError("invalid problem for the oracle: %r" % (p,))
+    return status

@@ -43,7 +43,9 @@
  *    children's scaled dots x_c by log m + mean(x) (PISA-1) or
  *    log m + mean(x) + Var(x)/2 (PISA-2, population variance), the Taylor
  *    expansion of log sum exp(x_c) = log m + log mean exp(x_c) about the mean;
- *    leaf and forced scores stay the exact raw-key LSE.
+ *    leaf and forced scores stay the exact raw-key LSE;
+ *  - the full-scan BSA selector the pages compare against has its own
+ *    section and readings at the end of this file.
  */
 #include <math.h>
 #include <stdint.h>
@@ -691,6 +693,155 @@ int orc_check_rows(const orc_problem* P, const void* qp, const void* k, const do
       if (!ok) st = v.capped ? 5 : 4;
       free(X);
       free(R);
+    }
+    status[t] = st;
+    free(qbuf);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------- BSA baseline */
+
+/*
+ * The full-scan selector the pages compare the pyramid against ([A] first
+ * paragraphs and baselines paragraph; [B] "the catch is the picking step"
+ * paragraph and the comparison-point paragraph: standard block-sparse
+ * attention scores every query against every block summary, O(N^2/C); the
+ * baseline is NSA's selected branch with mean-pooled block summaries).
+ * Readings (also in the design notes):
+ *  - the summary of leaf block j is its mean-pooled keys, i.e. pyramid
+ *    level 1 (a short last block averages the keys it has);
+ *  - block j's score for a query group is the sum over its G heads of the
+ *    plain dot product s * <q_h, mean_j> (no LSE);
+ *  - candidates are the blocks 0..b of the query's leaf block b, the forced
+ *    blocks F = {0, b-1, b} are kept as in the pyramid selector, and
+ *    Sel = F u TopK_{K-|F|}(candidates \ F) by (score descending, block
+ *    index ascending);
+ *  - output ascending by block index; the forced blocks are not ranked and
+ *    report the score +inf (the current block's summary would average keys
+ *    after the query); padding (-1, -inf).
+ */
+static double bsa_score(const row_t* r, int64_t j) {
+  const geo_t* q = r->q;
+  double total = 0.0;
+  for (int h = 0; h < q->G; ++h)
+    total += q->s * dot(r->qrows + (int64_t)h * q->d, r->pyr + (q->off[1] + j) * q->d, q->d);
+  return total;
+}
+
+static void bsa_row(const row_t* r, int32_t* out_idx, double* out_score) {
+  const geo_t* q = r->q;
+  const int K = q->K;
+  int64_t F[3];
+  int nf = n_forced(r->bq, F);
+  cand_t* S = (cand_t*)malloc(sizeof(cand_t) * (size_t)(r->bq + 1 + 3));
+  int nr = 0;
+  for (int64_t j = 0; j <= r->bq; ++j) {
+    if (is_in(F, nf, j)) continue;
+    S[nr].j = j;
+    S[nr].s = bsa_score(r, j);
+    ++nr;
+  }
+  qsort(S, (size_t)nr, sizeof(cand_t), by_score);
+  int Kp = K - nf;
+  int take = Kp < nr ? Kp : nr;
+  for (int t = 0; t < nf; ++t) {
+    S[take + t].j = F[t];
+    S[take + t].s = INFINITY;
+  }
+  int ns = take + nf;
+  qsort(S, (size_t)ns, sizeof(cand_t), by_index);
+  for (int t = 0; t < K; ++t) {
+    out_idx[t] = t < ns ? (int32_t)S[t].j : -1;
+    out_score[t] = t < ns ? S[t].s : -INFINITY;
+  }
+  free(S);
+}
+
+/* Selection for a list of query groups (rows as for orc_select_rows). */
+int orc_bsa_select_rows(const orc_problem* P, const void* qp, const double* pyr, int32_t decode, int64_t n_rows,
+                        const int64_t* rows, int32_t* idx, double* score) {
+  if (!orc_valid_problem(P)) return 1;
+  geo_t q;
+  geo_init(&q, P);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    double* qbuf = (double*)malloc(sizeof(double) * (size_t)q.G * (size_t)q.d);
+    row_t r;
+    row_setup(&q, qp, NULL, pyr, decode, rows ? rows[t] : t, qbuf, &r);
+    bsa_row(&r, idx + t * q.K, score + t * q.K);
+    free(qbuf);
+  }
+  return 0;
+}
+
+/* Scores of blocks 0..b for one row; returns b + 1 (out must hold n_1). */
+int64_t orc_bsa_scores(const orc_problem* P, const void* qp, const double* pyr, int32_t decode, int64_t rid,
+                       double* out) {
+  geo_t q;
+  geo_init(&q, P);
+  double* qbuf = (double*)malloc(sizeof(double) * (size_t)q.G * (size_t)q.d);
+  row_t r;
+  row_setup(&q, qp, NULL, pyr, decode, rid, qbuf, &r);
+  for (int64_t j = 0; j <= r.bq; ++j) out[j] = bsa_score(&r, j);
+  free(qbuf);
+  return r.bq + 1;
+}
+
+/*
+ * Tie-tolerant check of a BSA selection from another implementation: the
+ * shape and padding as for orc_check_rows, every forced block present with
+ * score +inf, every other reported score within rtol (floor 1) of the fp64
+ * score, and the non-forced blocks a Top-(K-|F|) of the candidates up to
+ * tau: min(K-|F|, |candidates|) of them, none scoring more than tau below
+ * a candidate left out.  Status codes as for orc_check_rows.
+ */
+int orc_bsa_check_rows(const orc_problem* P, const void* qp, const double* pyr, int32_t decode, int64_t n_rows,
+                       const int64_t* rows, const int32_t* gidx, const float* gscore, double tau, double rtol,
+                       int32_t* status) {
+  if (!orc_valid_problem(P)) return 1;
+  geo_t q;
+  geo_init(&q, P);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    double* qbuf = (double*)malloc(sizeof(double) * (size_t)q.G * (size_t)q.d);
+    row_t r;
+    row_setup(&q, qp, NULL, pyr, decode, rows ? rows[t] : t, qbuf, &r);
+    const int32_t* gi = gidx + t * q.K;
+    const float* gs = gscore + t * q.K;
+    int st = 0;
+    int64_t want = q.K < r.bq + 1 ? q.K : r.bq + 1;
+    int ns = 0;
+    while (ns < q.K && gi[ns] >= 0) ++ns;
+    if (ns != want) st = 1;
+    for (int u = 0; u < ns && !st; ++u)
+      if (gi[u] > r.bq || (u > 0 && gi[u] <= gi[u - 1])) st = 1;
+    for (int u = ns; u < q.K && !st; ++u)
+      if (gi[u] != -1 || !(isinf(gs[u]) && gs[u] < 0)) st = 1;
+    int64_t F[3];
+    int nf = n_forced(r.bq, F);
+    for (int u = 0; u < nf && !st; ++u) {
+      int found = 0;
+      for (int w = 0; w < ns; ++w)
+        if (gi[w] == F[u]) found = isinf(gs[w]) && gs[w] > 0 ? 1 : -1;
+      if (found == 0) st = 2;
+      if (found < 0) st = 3;
+    }
+    double kept_min = INFINITY;
+    for (int u = 0; u < ns && !st; ++u) {
+      if (is_in(F, nf, gi[u])) continue;
+      double ref = bsa_score(&r, gi[u]);
+      double tol = rtol * (fabs(ref) > 1.0 ? fabs(ref) : 1.0);
+      if (!(fabs((double)gs[u] - ref) <= tol)) st = 3;
+      if (ref < kept_min) kept_min = ref;
+    }
+    if (!st) {
+      for (int64_t j = 0; j <= r.bq && !st; ++j) {
+        if (is_in(F, nf, j)) continue;
+        int chosen = 0;
+        for (int u = 0; u < ns; ++u) chosen |= gi[u] == j;
+        if (!chosen && bsa_score(&r, j) > kept_min + tau) st = 4;
+      }
     }
     status[t] = st;
     free(qbuf);

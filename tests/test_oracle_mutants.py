@@ -36,7 +36,8 @@ MUTANTS = {
     "node-mean-weighted-wrong": ("        o[e] = acc / (double)(c1 - c0);", "        o[e] = acc / (double)q->g;"),
     "lse-missing-log": ("  return m + log(acc);", "  return m + acc;"),
     "route-keeps-K-minus-1": ("      int nk = nx < K ? nx : K;", "      int nk = nx < K - 1 ? nx : K - 1;"),
-    "leaf-takes-one-less": ("  int Kp = K - nf;\n  int take", "  int Kp = K - nf - 1;\n  int take"),
+    "leaf-takes-one-less": ("  int Kp = K - nf;\n  int take = Kp < nr ? Kp : nr;\n  if (nr > Kp",
+                            "  int Kp = K - nf - 1;\n  int take = Kp < nr ? Kp : nr;\n  if (nr > Kp"),
     "level-stop-early": ("while (n[L] > (int64_t)g * K && L < ORC_MAXL)", "while (n[L] > (int64_t)K && L < ORC_MAXL)"),
     "transposed-child-level": ("r->pyr + (q->off[l - 1] + c) * q->d, q->d);", "r->pyr + (q->off[l] + c % q->n[l]) * q->d, q->d);"),
     "pisa-scorer-ignored": ("  if (scorer == 0) return orc_lse(x, m);", "  return orc_lse(x, m);"),
@@ -45,6 +46,15 @@ MUTANTS = {
     "pisa2-variance-sign": ("    out += 0.5 * var / (double)m;", "    out -= 0.5 * var / (double)m;"),
     "pisa2-sample-variance": ("    out += 0.5 * var / (double)m;", "    out += 0.5 * var / (double)(m > 1 ? m - 1 : 1);"),
     "pisa2-no-half": ("    out += 0.5 * var / (double)m;", "    out += var / (double)m;"),
+    "bsa-uses-level-2": ("r->pyr + (q->off[1] + j) * q->d, q->d);", "r->pyr + (q->off[2] + j) * q->d, q->d);"),
+    "bsa-scale-dropped": ("    total += q->s * dot(r->qrows + (int64_t)h * q->d, r->pyr + (q->off[1] + j)",
+                          "    total += dot(r->qrows + (int64_t)h * q->d, r->pyr + (q->off[1] + j)"),
+    "bsa-first-head-only": ("  for (int h = 0; h < q->G; ++h)\n    total += q->s", "  for (int h = 0; h < 1; ++h)\n    total += q->s"),
+    "bsa-sees-next-block": ("  for (int64_t j = 0; j <= r->bq; ++j) {\n    if (is_in(F, nf, j)) continue;\n    S[nr].j = j;",
+                            "  for (int64_t j = 0; j <= r->bq + 1 && j < q->n[1]; ++j) {\n    if (is_in(F, nf, j)) continue;\n    S[nr].j = j;"),
+    "bsa-keeps-one-more": ("  int Kp = K - nf;\n  int take = Kp < nr ? Kp : nr;\n  for (int t = 0; t < nf; ++t) {",
+                           "  int Kp = K - nf + 1;\n  int take = Kp < nr ? Kp : nr;\n  for (int t = 0; t < nf; ++t) {"),
+    "bsa-forced-scored": ("    S[take + t].s = INFINITY;", "    S[take + t].s = bsa_score(r, F[t]);"),
 }
 
 

@@ -588,3 +588,160 @@ def test_pisa_matches_independent_numpy_walk(scorer, g):
             st, _ = oracle.check(p, q, k, pyr, [i], np.array([wi]), np.array([ws], dtype=np.float32),
                                  tau=1e-9, rtol=1e-9)
             assert st[0] == 0, (i, idx[t], wi)
+
+
+# ------------------------------------------------------- BSA full-scan baseline
+# The selector the pages compare against scores every causal block by the dot product with
+# its mean-pooled keys ("Block Sparse Attention with Log-Linear Complexity": agihunt.info
+# opening and baselines paragraphs; rcap.io picking-step and comparison-point paragraphs).
+
+def test_bsa_score_is_mean_of_raw_key_dots():
+    # linearity: the dot with a block's mean is the mean of the dots with its keys (the
+    # short last block included), summed over the group's heads
+    N, K = 64 * 30 + 21, 8
+    p, q, k = _prefill(90, N, 4, 2, 16, K, B=2)
+    pyr = oracle.build_pyramid(p, k)
+    for row in (N - 1, 2 * N + 700, 4 * N - 1, 3 * N + 64 * 12):
+        bh, i = divmod(row, N)
+        b, h = divmod(bh, 2)
+        sc = oracle.bsa_scores(p, q, pyr, row)
+        assert len(sc) == i // 64 + 1
+        kd = k[b, h].astype(np.float64)
+        qd = q[b, 2 * h:2 * h + 2, i].astype(np.float64)
+        for j in range(len(sc)):
+            keys = kd[64 * j:min(64 * j + 64, N)]
+            expect = p.s * (keys @ qd.T).mean(axis=0).sum()
+            assert abs(sc[j] - expect) < 1e-12 * max(1.0, abs(expect))
+
+
+def test_bsa_score_below_block_lse():
+    # Jensen: per head, s<q, mean_j> <= LSE over block j's keys - log C (complete past blocks)
+    N, K = 64 * 24, 8
+    p, q, k = _prefill(91, N, 2, 1, 16, K)
+    pyr = oracle.build_pyramid(p, k)
+    i = N - 1
+    p1 = oracle.Problem(1, N, 1, 1, 16, 64, K, 2, dtype=F32)
+    for r in range(2):
+        qr = np.ascontiguousarray(q[:, r:r + 1])
+        sc = oracle.bsa_scores(p1, qr, pyr, i)
+        for j in range(i // 64):
+            lse, _ = oracle.leaf_score(p1, qr, k, i, j)
+            assert sc[j] <= lse - math.log(64) + 1e-12
+
+
+def test_bsa_selection_is_forced_plus_top_scores():
+    N, K = 64 * 40 + 5, 7
+    p, q, k = _prefill(92, N, 2, 1, 16, K, B=2)
+    pyr = oracle.build_pyramid(p, k)
+    rows = list(range(0, 2 * N, 23)) + [N - 1, 2 * N - 1]
+    idx, sc = oracle.bsa_select(p, q, pyr, rows=rows)
+    for t, row in enumerate(rows):
+        b = (row % N) // 64
+        forced = {f for f in (0, b - 1, b) if f >= 0}
+        n = int((idx[t] >= 0).sum())
+        assert n == min(K, b + 1)
+        sel = idx[t, :n].tolist()
+        assert sel == sorted(sel) and forced <= set(sel)
+        assert np.all(idx[t, n:] == -1) and np.all(np.isneginf(sc[t, n:]))
+        allsc = oracle.bsa_scores(p, q, pyr, row)
+        rest = [j for j in range(b + 1) if j not in forced]
+        # brute force: rank the non-forced blocks by (score desc, index asc) with python's sort
+        want = sorted(sorted(rest, key=lambda j: (-allsc[j], j))[:K - len(forced)])
+        assert sorted(set(sel) - forced) == want
+        for u, j in enumerate(sel):
+            assert (sc[t, u] == math.inf) if j in forced else (sc[t, u] == allsc[j])
+
+
+def test_bsa_shift_of_all_keys_shifts_every_score():
+    # adding one vector c to every key adds sum_h s<q_h, c> to every block score: the
+    # selection is unchanged
+    N, K = 64 * 33, 6
+    p, q, k = _prefill(93, N, 2, 1, 16, K)
+    c = np.random.default_rng(5).standard_normal(16).astype(np.float32)
+    k2 = (k + c).astype(np.float32)
+    pyr, pyr2 = oracle.build_pyramid(p, k), oracle.build_pyramid(p, k2)
+    rows = list(range(64 * 5, N, 97)) + [N - 1]
+    i1, s1 = oracle.bsa_select(p, q, pyr, rows=rows)
+    i2, s2 = oracle.bsa_select(p, q, pyr2, rows=rows)
+    assert np.array_equal(i1, i2)
+    for t, row in enumerate(rows):
+        shift = p.s * float(q[0, :, row].astype(np.float64).sum(axis=0) @ c.astype(np.float64))
+        fin = np.isfinite(s1[t])
+        np.testing.assert_allclose(s2[t, fin] - s1[t, fin], shift, atol=1e-6)  # k + c rounds in fp32
+
+
+def test_bsa_ties_go_to_the_lower_block():
+    # blocks with identical keys tie exactly; the lower index wins
+    N, K, d = 64 * 20, 5, 8
+    r = np.random.default_rng(6)
+    k = r.standard_normal((1, 1, N, d)).astype(np.float32)
+    for j in (3, 7, 11, 15):
+        k[0, 0, 64 * j:64 * j + 64] = k[0, 0, 64 * 5:64 * 5 + 64] + 0.0
+    k[0, 0, 64 * 5:64 * 5 + 64] += 3.0  # make the tied blocks' common mean large
+    for j in (3, 7, 11, 15):
+        k[0, 0, 64 * j:64 * j + 64] = k[0, 0, 64 * 5:64 * 5 + 64]
+    q = np.ones((1, 1, N, d), dtype=np.float32)
+    p = oracle.Problem(1, N, 1, 1, d, 64, K, 2, dtype=F32)
+    pyr = oracle.build_pyramid(p, k)
+    idx, _ = oracle.bsa_select(p, q, pyr, rows=[N - 1])
+    # forced {0, 18, 19}; two slots among the five tied blocks 3, 5, 7, 11, 15
+    assert idx[0].tolist() == [0, 3, 5, 18, 19]
+
+
+def test_bsa_small_K_and_short_prefixes():
+    N, K = 64 * 12, 3
+    p, q, k = _prefill(94, N, 1, 1, 16, K)
+    pyr = oracle.build_pyramid(p, k)
+    idx, sc = oracle.bsa_select(p, q, pyr)
+    for i in range(N):
+        b = i // 64
+        want = sorted({0, b - 1, b} - {-1})
+        assert idx[i, :len(want)].tolist() == want and np.all(idx[i, len(want):] == -1)
+    K = 16  # K >= every causal block: all of them
+    p = oracle.Problem(1, N, 1, 1, 16, 64, K, 2, dtype=F32)
+    idx, sc = oracle.bsa_select(p, q, pyr)
+    for i in range(0, N, 7):
+        b = i // 64
+        assert idx[i, :b + 1].tolist() == list(range(b + 1)) and np.all(idx[i, b + 1:] == -1)
+
+
+def test_bsa_gqa_and_decode():
+    N, K = 4096 + 11, 8
+    p1, q1, k = _prefill(95, N, 1, 1, 16, K)
+    pyr = oracle.build_pyramid(p1, k)
+    G = 4
+    pG = oracle.Problem(1, N, G, 1, 16, 64, K, 2, dtype=F32)
+    qG = np.ascontiguousarray(np.repeat(q1, G, axis=1))
+    rows = list(range(0, N, 31))
+    i1, s1 = oracle.bsa_select(p1, q1, pyr, rows=rows)
+    iG, sG = oracle.bsa_select(pG, qG, pyr, rows=rows)
+    assert np.array_equal(i1, iG)
+    fin = np.isfinite(s1)
+    np.testing.assert_allclose(sG[fin], G * s1[fin], rtol=1e-12)
+    # decode = the last prefill row
+    p, q, k = _prefill(96, N, 4, 2, 16, K, B=2)
+    pyr = oracle.build_pyramid(p, k)
+    idd, sd = oracle.bsa_select(p, np.ascontiguousarray(q[:, :, N - 1, :]), pyr, decode=True)
+    ip, sp = oracle.bsa_select(p, q, pyr, rows=[(b * 2 + h) * N + N - 1 for b in range(2) for h in range(2)])
+    assert np.array_equal(idd, ip)
+    np.testing.assert_array_equal(sd, sp)
+
+
+def test_bsa_checker_accepts_oracle_and_rejects_swaps():
+    N, K = 64 * 50, 8
+    p, q, k = _prefill(97, N, 2, 1, 16, K)
+    pyr = oracle.build_pyramid(p, k)
+    rows = list(range(64 * 10, N, 53))
+    idx, sc = oracle.bsa_select(p, q, pyr, rows=rows)
+    assert np.all(oracle.bsa_check(p, q, pyr, rows, idx, sc, tau=0.0, rtol=1e-6) == 0)
+    bad = idx.copy()
+    for t, row in enumerate(rows):
+        b = row // 64
+        allsc = oracle.bsa_scores(p, q, pyr, row)
+        out = [j for j in range(1, b - 1) if j not in bad[t]]
+        worst = min(out, key=lambda j: allsc[j])
+        u = next(u for u in range(K) if bad[t, u] not in (0, b - 1, b))
+        bad[t, u] = worst
+        bad[t] = np.sort(bad[t])
+    st = oracle.bsa_check(p, q, pyr, rows, bad, np.where(np.isinf(sc), sc, 0.0), tau=1e-3, rtol=1e3)
+    assert np.all(st == 4)
