@@ -6,7 +6,9 @@ Headline (one "step"): pyramid build + prefill selection at 256K tokens, C=64, K
 inputs resident in HBM).  Also timed in the same run: the same step at 64K, and one
 decode step (32 sequences x 262144-token cache, precomputed pyramid; cold: each step
 follows a 1 GiB write that evicts L2 and MALL; warm: back to back), and the 256K step
-with the PISA-1 / PISA-2 routing scorers (ablations; extra fields).
+with the PISA-1 / PISA-2 routing scorers (ablations; extra fields), and the pyramid
+selector against the full-scan BSA selector from 4K to 256K tokens (the pages'
+selection-kernel comparison at C=64, K=8).
 
 Prints one JSON line.  Per-stage times come from HIP events recorded by the library on
 the stream its kernels run on (pisa_select_prefill_staged) and around pisa_build_pyramid.
@@ -47,10 +49,11 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-64k", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bsa", action="store_true", help="skip the BSA full-scan crossover timings")
     ap.add_argument("--no-scorers", action="store_true",
                     help="skip the PISA-1 / PISA-2 ablation timings at 256K")
     ap.add_argument("--cpu-sample-rows", type=int, default=393216)
-    ap.add_argument("--only", choices=["256k", "64k", "decode"], default=None,
+    ap.add_argument("--only", choices=["256k", "64k", "decode", "bsa"], default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 1 GiB device-to-device copy (reference kernel for HBM counters)")
@@ -254,6 +257,57 @@ def time_decode(torch, pisa, synth, steps):
     return statistics.median(cold), warm
 
 
+CROSSOVER_SIZES = [4096, 16384, 65536, 131072, 262144]
+
+
+def crossover(torch, pisa, synth, steps, warmup):
+    """Pyramid selector vs the full-scan BSA selector at C=64, K=8, 16/4 heads, d=128 (the
+    pages' selection-kernel comparison), both including the pyramid build (BSA reads its
+    level-1 summaries).  Returns {N: {pisa_ms, bsa_ms, bsa_over_pisa}}."""
+    out = {}
+    for N in CROSSOVER_SIZES:
+        name = {65536: "64k", 131072: "128k", 262144: "256k"}.get(N)
+        w = synth.WORKLOADS[name] if name else synth.custom(
+            name="crossover-%d" % N, batch=1, seq_len=N, n_q_heads=16, n_kv_heads=4, head_dim=128, top_k=8,
+            seed=20 + N // 4096, needles=max(N // 256, 1))
+        q, k, _ = synth.make_inputs(w)
+        qd, kd = dev(torch, q), dev(torch, k)
+        del q, k
+        p = pisa.Problem(**w.shape())
+        pyr = torch.empty(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+        ws = pisa.workspace(p)
+        shape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+        oi = torch.empty(shape, dtype=torch.int32, device="cuda")
+        os_ = torch.empty(shape, dtype=torch.float32, device="cuda")
+
+        def run_pisa():
+            pisa.build_pyramid(p, kd, pyr)
+            pisa.select_prefill(p, qd, kd, pyr, ws, oi, os_)
+
+        def run_bsa():
+            pisa.build_pyramid(p, kd, pyr)
+            pisa.bsa_select_prefill(p, qd, pyr, oi, os_)
+
+        res = {}
+        for tag, fn in (("pisa", run_pisa), ("bsa", run_bsa)):
+            for _ in range(warmup):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(steps):
+                fn()
+            b.record()
+            b.synchronize()
+            res[tag + "_ms"] = round(a.elapsed_time(b) / steps, 4)
+        res["bsa_over_pisa"] = round(res["bsa_ms"] / res["pisa_ms"], 3)
+        out[str(N)] = res
+        log("crossover N=%d: %s" % (N, res))
+        del qd, kd, pyr, ws, oi, os_
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(synth, sample_rows):
     import oracle
     w = synth.WORKLOADS["256k"]
@@ -331,6 +385,8 @@ def main():
         extra["decode_us_per_step_warm"] = round(warm, 2)
         log("decode: cold %.2f us, warm %.2f us" % (cold, warm))
         torch.cuda.empty_cache()
+    if a.only in (None, "bsa") and not a.no_bsa:
+        extra["crossover_c64_k8"] = crossover(torch, pisa, synth, a.steps, a.warmup)
     if head is None:
         print(json.dumps(extra))
         return

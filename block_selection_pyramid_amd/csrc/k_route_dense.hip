@@ -28,48 +28,15 @@
 // each forced key tile is staged in LDS once and contracted on the matrix cores.
 #include "final_dev.h"
 #include "route_dev.h"
+#include "tile_dev.h"
 
 namespace pisa {
 
 namespace {
 
-constexpr int kDenseWaves = 4;
-
-// Columns of the B operand: 32 (query, head) pairs per column group, head fastest.
-template <int G>
-struct DenseShape {
-  static constexpr int NCG = (G <= 2) ? 1 : 2;  // column groups per wavefront
-  static constexpr int QPW = 32 * NCG / G;      // queries per wavefront
-};
-
 template <int D, int G, int KC>
 constexpr size_t dense_lds_bytes() {
   return 2 * (size_t)(2 * (D / 16) * 1024) + (size_t)kDenseWaves * DenseShape<G>::QPW * (64 + 20 * KC);
-}
-
-// Staging of child tile t of level l - 1 (children 32t .. 32t+31) into fragment-major LDS:
-// fragment f = 2 ks + hi/lo, lane slot = child (lane & 31) and dims 8 (lane >> 5) .. of
-// k-step ks, so every MFMA A-operand read is one conflict-free 16-byte row per lane.  The
-// wavefronts of the workgroup take fragments wave, wave + 4, ...
-template <int D, int NU>
-__device__ __forceinline__ void dense_load_tile(const char* Rb, const Geo& geo, int l, int t, int wave, int lane,
-                                                u32x4 (&stg)[NU]) {
-  const int child = min(32 * t + (lane & 31), geo.n[l - 1] - 1);  // a missing child reads a real node
-  const char* base = Rb + (int64_t)(geo.off[l - 1] + child) * (4 * D) + 16 * (lane >> 5);
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int f = wave + kDenseWaves * u, ks = f >> 1, hl = f & 1;
-    stg[u] = *reinterpret_cast<const u32x4*>(base + (ks >> 1) * 128 + hl * 64 + (ks & 1) * 32);
-  }
-}
-template <int D, int NU>
-__device__ __forceinline__ void dense_store_tile(char* lds, int buf, int wave, int lane, const u32x4 (&stg)[NU]) {
-  constexpr int TILE = 2 * (D / 16) * 1024;
-#pragma unroll
-  for (int u = 0; u < NU; ++u) {
-    const int f = wave + kDenseWaves * u;
-    *reinterpret_cast<u32x4*>(lds + buf * TILE + (f * 64 + lane) * 16) = stg[u];
-  }
 }
 
 // Forced key tile f (64 raw keys) into fragment-major LDS: fragment fi = rb KS + ks holds
@@ -128,22 +95,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   bf16x8 qf[NCG][KS];
   int bqc[NCG];
   const int bqw = min(iw, N - 1) / C;  // bq of this wavefront's first (smallest) query
-#pragma unroll
-  for (int cg = 0; cg < NCG; ++cg) {
-    const int i = iw + cg * (32 / G) + j / G;
-    bqc[cg] = min(i, N - 1) / C;
-    if (i < N) {
-      const bf16* p = q + (((int64_t)b * geo.Hq + h * G + j % G) * N + i) * D + 8 * hh;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[cg][ks] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 16 * ks));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[cg][ks][e] = (__bf16)0.f;
-    }
-  }
+  load_query_cols<D, G, NCG>(q, geo, b, h, iw, lane, qf, bqc);
 
   // Walk state.  Item (query iq, rank r) = lane + 64 m holds the node ip kept at rank r one
   // level up; its candidates are ip's two children, with scores sc.  At the top level the

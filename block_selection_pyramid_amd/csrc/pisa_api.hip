@@ -245,6 +245,19 @@ int pisa_select_decode(const pisa_problem* p, const void* q, const void* k_cache
   return launch_decode(g, p->dtype, q, k_cache, pyramid, out_idx, out_score, (hipStream_t)stream);
 }
 
+int pisa_bsa_select_prefill(const pisa_problem* p, const void* q, const float* pyramid, int32_t* out_idx,
+                            float* out_score, pisa_stream_t stream) {
+  Geo g;
+  int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (!q || !pyramid || !out_idx || !out_score) return PISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(pyramid)) return PISA_ERR_INVALID_ARG;
+  rc = supported(g, p->dtype, PISA_PREFILL);
+  if (rc != PISA_OK) return rc;
+  if (p->dtype != PISA_BF16) return PISA_ERR_UNSUPPORTED;
+  return launch_bsa(g, q, pyramid, out_idx, out_score, (hipStream_t)stream);
+}
+
 const char* pisa_status_string(int status) {
   switch (status) {
     case PISA_OK: return "ok";

@@ -51,6 +51,8 @@ inline int route_groups_per_wave(int G, int K) {
 
 // ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
+// full-scan BSA selection (bf16): out_idx / out_score [B, Hkv, N, K]
+int launch_bsa(const Geo& g, const void* q, const float* pyr, int32_t* out_idx, float* out_score, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);
 // x2: scratch of B*Hkv*N*2K int32 (level-2 candidates between the two routing launches);
 // fsc: forced-block scores, written when route_scores_forced(); mid (may be null) is

@@ -83,6 +83,7 @@ _lib = None
 
 EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs", "pisa_select_decode",
+           "pisa_bsa_select_prefill",
            "pisa_status_string", "pisa_version")
 
 
@@ -108,6 +109,7 @@ def load(path: str | None = None):
     lib.pisa_select_prefill_staged.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp, ctypes.c_int32, vp]
     lib.pisa_prefill_routed_pairs.argtypes = [P, vp, sz, vp, vp]
     lib.pisa_select_decode.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.pisa_bsa_select_prefill.argtypes = [P, vp, vp, vp, vp, vp]
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_version.restype = ctypes.c_char_p
@@ -206,6 +208,24 @@ def select_prefill(p: Problem, q: torch.Tensor, k: torch.Tensor, pyramid: torch.
     sp = _dev(out_score, "out_score", torch.float32, oshape)
     _check(load().pisa_select_prefill(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, _stream(stream)),
            "pisa_select_prefill")
+    return out_idx, out_score
+
+
+def bsa_select_prefill(p: Problem, q: torch.Tensor, pyramid: torch.Tensor, out_idx: torch.Tensor | None = None,
+                       out_score: torch.Tensor | None = None, stream=None):
+    """Full-scan BSA selection (pisa_bsa_select_prefill); returns (idx int32 [B, Hkv, N, K],
+    score fp32 [B, Hkv, N, K]), forced blocks with score +inf."""
+    oshape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+    qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.seq_len, p.head_dim))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    if out_idx is None:
+        out_idx = torch.empty(oshape, dtype=torch.int32, device=q.device)
+    if out_score is None:
+        out_score = torch.empty(oshape, dtype=torch.float32, device=q.device)
+    ip = _dev(out_idx, "out_idx", torch.int32, oshape)
+    sp = _dev(out_score, "out_score", torch.float32, oshape)
+    _check(load().pisa_bsa_select_prefill(ctypes.byref(p.c()), qp, pp, ip, sp, _stream(stream)),
+           "pisa_bsa_select_prefill")
     return out_idx, out_score
 
 

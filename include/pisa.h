@@ -183,6 +183,24 @@ int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size
                               int64_t* routed_pairs, pisa_stream_t stream);
 
 /* Static description of a status code. */
+/*
+ * Full-scan BSA selection for every query position, the baseline the pyramid selector is
+ * timed against ("Block Sparse Attention with Log-Linear Complexity": agihunt.info
+ * summary, opening and baselines paragraphs; rcap.io explainer, picking-step and
+ * comparison-point paragraphs: standard block-sparse attention scores every query against
+ * every block's mean-pooled summary, O(N^2/C)).  Block j's score for query group
+ * (b, h, i) is sum over the G heads of s * <q, mean of block j's keys> (pyramid level 1;
+ * no LSE); the candidates are the blocks 0..b of the query's leaf block b; the forced
+ * blocks {0, b-1, b} are kept as in pisa_select_prefill and the K - |F| best remaining
+ * blocks (score descending, lower index first) join them.  Writes out_idx / out_score
+ * [B, Hkv, N, K] ascending by block index; forced blocks report +inf, padding (-1, -inf).
+ * `pyramid` must hold pisa_build_pyramid's result for k (only its routing copy of level 1
+ * is read).  bf16 q only (PISA_ERR_UNSUPPORTED otherwise); the scorer field has no
+ * effect.  No workspace; q [B, Hq, N, d] and pyramid 16-byte aligned.
+ */
+int pisa_bsa_select_prefill(const pisa_problem* p, const void* q, const float* pyramid, int32_t* out_idx,
+                            float* out_score, pisa_stream_t stream);
+
 const char* pisa_status_string(int status);
 
 /* Library version, e.g. "0.1.0". */

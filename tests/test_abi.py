@@ -91,6 +91,19 @@ def test_invalid_arguments(pisa, field, value):
     lib = pisa.load()
     assert lib.pisa_build_pyramid(ctypes.byref(p.c()), 0x1000, 0x1000, None) == 1
     assert lib.pisa_select_decode(ctypes.byref(p.c()), 0x1000, 0x1000, 0x1000, None, 0, 0x1000, 0x1000, None) == 1
+    assert lib.pisa_bsa_select_prefill(ctypes.byref(p.c()), 0x1000, 0x1000, 0x1000, 0x1000, None) == 1
+
+
+def test_bsa_host_checks(pisa):
+    lib = pisa.load()
+    p = pisa.Problem(1, 4096, 16, 4, 128)
+    assert lib.pisa_bsa_select_prefill(ctypes.byref(p.c()), 0, 0x1000, 0x1000, 0x1000, None) == 1
+    assert lib.pisa_bsa_select_prefill(ctypes.byref(p.c()), 0x1008, 0x1000, 0x1000, 0x1000, None) == 1
+    # fp32 inputs and problems outside the kernels' support matrix
+    f32 = pisa.Problem(1, 4096, 16, 4, 128, dtype=pisa.F32)
+    assert lib.pisa_bsa_select_prefill(ctypes.byref(f32.c()), 0x1000, 0x1000, 0x1000, 0x1000, None) == 2
+    big = pisa.Problem(1, 4096, 16, 4, 128, top_k=33)
+    assert lib.pisa_bsa_select_prefill(ctypes.byref(big.c()), 0x1000, 0x1000, 0x1000, 0x1000, None) == 2
 
 
 def test_null_and_misaligned_pointers(pisa):

@@ -347,3 +347,89 @@ def test_pisa2_64k_sampled(env):
     rows = sample_rows(w, needles, 1000, 11)
     verify(op, q, k, opyr, rows, idx.cpu().numpy(), sc.cpu().numpy(), what="64k-pisa2")
     assert scorer_sensitive(op, q, k, opyr, rows, False) > 0
+
+
+# ------------------------------------------------------------ BSA full-scan selector
+
+def bsa_verify(op, q, opyr, rows, idx, sc, what):
+    K = op.top_k
+    gi = idx.reshape(-1, K)[rows]
+    gs = sc.reshape(-1, K)[rows]
+    st = oracle.bsa_check(op, q, opyr, rows, gi, gs, tau=TAU, rtol=RTOL)
+    st5 = oracle.bsa_check(op, q, opyr, rows, gi, gs, tau=1e-5, rtol=RTOL)
+    counts = {oracle.CHECK_STATUS[s]: int(c) for s, c in enumerate(np.bincount(st, minlength=6)) if c}
+    log(what, "bsa rows=%d status=%s pass@tau1e-5=%.4f" % (len(rows), counts, float(np.mean(st5 == 0))))
+    bad = np.nonzero(st != 0)[0]
+    if len(bad):
+        r = bad[0]
+        oi, os_ = oracle.bsa_select(op, q, opyr, rows=[rows[r]])
+        pytest.fail("%s: %d/%d rows fail; first row %d status %s\n gpu idx %s\n gpu sc %s\n orc idx %s\n orc sc %s"
+                    % (what, len(bad), len(rows), rows[r], oracle.CHECK_STATUS[st[r]], gi[r], gs[r], oi[0], os_[0]))
+
+
+BSA_CASES = [
+    # name, N, Hq, Hkv, d, K, B
+    ("one-token", 1, 4, 1, 128, 8, 1),
+    ("one-block-short", 63, 4, 2, 128, 4, 2),
+    ("two-blocks", 65, 8, 1, 128, 8, 1),
+    ("first-candidate", 64 * 3 + 1, 2, 1, 64, 5, 1),
+    ("K3-forced-only", 1000, 4, 1, 128, 3, 1),
+    ("ragged-4133-G1-d64", 4096 + 37, 2, 2, 64, 5, 2),
+    ("G2", 3000, 4, 2, 128, 8, 1),
+    ("G8", 2500, 16, 2, 128, 6, 1),
+    ("G16", 4096 + 1, 16, 1, 128, 7, 1),
+    ("K16", 64 * 101 + 9, 4, 2, 128, 16, 1),
+    ("K32", 8192 + 5, 8, 2, 64, 32, 1),
+]
+
+
+@pytest.mark.parametrize("case", BSA_CASES, ids=[c[0] for c in BSA_CASES])
+def test_bsa_edge_cases(env, case):
+    torch, pisa = env
+    name, N, Hq, Hkv, d, K, B = case
+    w = synth.custom(name=name, batch=B, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     seed=900 + N, needles=min(8, max(N // 200, 1)))
+    p, op = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log(name, "bsa N=%d B=%d Hq=%d Hkv=%d d=%d K=%d: launching" % (N, B, Hq, Hkv, d, K))
+    pyr = pisa.build_pyramid(p, kd)
+    idx, sc = pisa.bsa_select_prefill(p, qd, pyr)
+    torch.cuda.synchronize()
+    opyr = oracle.build_pyramid(op, k)
+    bsa_verify(op, q, opyr, np.arange(B * Hkv * N), idx.cpu().numpy(), sc.cpu().numpy(), "bsa-" + name)
+
+
+def test_bsa_4k_all_rows_deterministic(env):
+    torch, pisa = env
+    w = synth.WORKLOADS["4k"]
+    p, op = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    pyr = pisa.build_pyramid(p, kd)
+    i1, s1 = pisa.bsa_select_prefill(p, qd, pyr)
+    i2, s2 = pisa.bsa_select_prefill(p, qd, pyr)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+    opyr = oracle.build_pyramid(op, k)
+    bsa_verify(op, q, opyr, np.arange(w.n_kv_heads * w.seq_len), i1.cpu().numpy(), s1.cpu().numpy(), "bsa-4k")
+
+
+@pytest.mark.parametrize("name,n_random", [("64k", 1500), ("256k", 1500)])
+def test_bsa_workload_sampled(env, name, n_random):
+    torch, pisa = env
+    w = synth.WORKLOADS[name]
+    p, op = problems(pisa, w)
+    q, k, needles = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log(name, "bsa: launching")
+    pyr = pisa.build_pyramid(p, kd)
+    idx, sc = pisa.bsa_select_prefill(p, qd, pyr)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    K = w.top_k
+    nsel = (idx.reshape(-1, K) >= 0).sum(1)
+    bq = np.tile(np.arange(w.seq_len) // 64, w.batch * w.n_kv_heads)
+    assert np.array_equal(nsel, np.minimum(K, bq + 1))
+    opyr = oracle.build_pyramid(op, k)
+    bsa_verify(op, q, opyr, sample_rows(w, needles, n_random, 13), idx, sc, "bsa-" + name)
