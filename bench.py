@@ -7,8 +7,8 @@ inputs resident in HBM).  Also timed in the same run: the same step at 64K, and 
 decode step (32 sequences x 262144-token cache, precomputed pyramid; cold: each step
 follows a 1 GiB write that evicts L2 and MALL; warm: back to back), and the 256K step
 with the PISA-1 / PISA-2 routing scorers (ablations; extra fields), and the pyramid
-selector against the full-scan BSA selector from 4K to 256K tokens (the pages'
-selection-kernel comparison at C=64, K=8).
+selector against the full-scan BSA selector from 4K to 1M tokens (the pages'
+selection-kernel comparison at C=64, K=8, extended past 256K).
 
 Prints one JSON line.  Per-stage times come from HIP events recorded by the library on
 the stream its kernels run on (pisa_select_prefill_staged) and around pisa_build_pyramid.
@@ -257,7 +257,7 @@ def time_decode(torch, pisa, synth, steps):
     return statistics.median(cold), warm
 
 
-CROSSOVER_SIZES = [4096, 16384, 65536, 131072, 262144]
+CROSSOVER_SIZES = [4096, 16384, 65536, 131072, 262144, 524288, 1048576]
 
 
 def crossover(torch, pisa, synth, steps, warmup):
@@ -289,17 +289,18 @@ def crossover(torch, pisa, synth, steps, warmup):
             pisa.bsa_select_prefill(p, qd, pyr, oi, os_)
 
         res = {}
+        n_steps = steps if N <= 262144 else max(2, steps // 4)  # the full scan grows as N^2
         for tag, fn in (("pisa", run_pisa), ("bsa", run_bsa)):
-            for _ in range(warmup):
+            for _ in range(min(warmup, n_steps)):
                 fn()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             a.record()
-            for _ in range(steps):
+            for _ in range(n_steps):
                 fn()
             b.record()
             b.synchronize()
-            res[tag + "_ms"] = round(a.elapsed_time(b) / steps, 4)
+            res[tag + "_ms"] = round(a.elapsed_time(b) / n_steps, 4)
         res["bsa_over_pisa"] = round(res["bsa_ms"] / res["pisa_ms"], 3)
         out[str(N)] = res
         log("crossover N=%d: %s" % (N, res))

@@ -48,16 +48,18 @@ __global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict
   }
 }
 
-// bf16 inputs, level 2: each wavefront takes GPW query groups (consecutive queries of one
-// leaf block) with their 2K level-2 candidates -- written by the dense upper-level launch,
-// or the visible prefix of level 2 when L == 2 -- scores them against the leaf-block means
-// of the routing copy (a per-query gather: level 1 is too wide to score densely), keeps
-// the Top-K and writes the leaf candidates that are not forced blocks.  Workgroup w
+// bf16 inputs, the levels below the dense launch: each wavefront takes GPW query groups
+// (consecutive queries of one leaf block) with their 2K candidates of level l_x -- written
+// by the dense upper-level launch, or the visible prefix of level 2 when L == 2 -- and
+// walks levels l_x .. 2 by per-query gathers of the child summaries from the routing copy
+// (these levels are too wide to score densely: level 2's children are the leaf-block
+// means), keeping the Top-K per level, then writes the leaf candidates that are not forced
+// blocks.  Workgroup w
 // serves (b, h) = w mod (B*Hkv), so the workgroups of one XCD (w mod 8) share few heads
 // and gather from an L2-sized part of the routing copy.
 template <int D, int G, int GPW>
 __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
-                                                         Geo geo, const int32_t* __restrict__ x2,
+                                                         Geo geo, int32_t l_x, const int32_t* __restrict__ x2,
                                                          int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
   using Walk = MfmaWalk<D, G, GPW>;
   // per-leaf-block histogram (when the blocks fit), flushed with one global add per bin
@@ -99,7 +101,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
       } else {
         nx = mw.init_level(geo, bq, 2, w, lane);
       }
-      nx = mw.walk_levels(geo, bq, 2, 2, nx, w, lane);
+      nx = mw.walk_levels(geo, bq, geo.L >= 3 ? l_x : 2, 2, nx, w, lane);
     } else {
       nx = mw.init_level(geo, bq, 1, w, lane);
     }
@@ -131,7 +133,8 @@ int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* p
   if (mid && hipEventRecord(mid, st) != hipSuccess) return PISA_ERR_HIP;
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));
   const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
-  route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt);
+  const int l_x = g.L >= 3 ? dense_bottom(g) - 1 : 2;  // level of the candidates in x2
+  route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, l_x, x2, cand, cnt);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 

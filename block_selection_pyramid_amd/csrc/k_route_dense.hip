@@ -1,4 +1,5 @@
-// Prefill routing, upper pyramid levels (L down to 3), scored densely.
+// Prefill routing, upper pyramid levels (L down to l_bot >= 3, while the levels are small),
+// scored densely.
 //
 // What is computed is the top-down walk of "Block Sparse Attention with Log-Linear
 // Complexity" (rcap.io explainer, top-down walk and scoring paragraphs; agihunt.info
@@ -19,9 +20,9 @@
 // staged child tiles do not depend on the walk, so the next tile is fetched from L2 while
 // the current one is scored, across level boundaries too.
 //
-// Output: per query group, the 2K level-2 candidate slots (children of the Top-K nodes of
-// level 3, -1 where a child does not exist or is not visible), the input of the level-2
-// routing launch.  The same workgroup then scores its queries' forced leaf blocks
+// Output: per query group, the 2K candidate slots of level l_bot - 1 (children of the Top-K
+// nodes of level l_bot, -1 where a child does not exist or is not visible), the input of
+// the gather routing launch.  The same workgroup then scores its queries' forced leaf blocks
 // ("Block Sparse Attention with Log-Linear Complexity", agihunt.info summary, LSE and
 // forced-block paragraph: first, previous and current block; leaf score = causal LSE over
 // the block's raw keys, summed over the G heads) with the query rows it already holds:
@@ -380,10 +381,10 @@ int dense_launch(const Geo& g, const bf16* q, const float* pyr, const bf16* k, i
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + QW - 1) / QW));
   if (g.scorer == PISA_LSE)
     route_dense_kernel<D, G, KC, false>
-        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, 3, x2, fsc);
+        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, dense_bottom(g), x2, fsc);
   else
     route_dense_kernel<D, G, KC, true>
-        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, 3, x2, fsc);
+        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, dense_bottom(g), x2, fsc);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 

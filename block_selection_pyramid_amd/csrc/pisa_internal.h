@@ -59,12 +59,23 @@ int launch_zero(int32_t* a, int64_t n, hipStream_t st);
 // recorded between the upper-level and the level-2 launch
 int launch_route(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2,
                  float* fsc, int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st);
-// Levels L..3 of the bf16 walk (L >= 3), scored densely per leaf block; writes x2 and the
+// Levels L..dense_bottom(g) of the bf16 walk (L >= 3), scored densely per leaf block; writes x2 and the
 // forced blocks' scores fsc [B*Hkv*N*3] (ascending forced-block order).
 int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, const void* k, int32_t* x2, float* fsc,
                               hipStream_t st);
 // true when launch_route scores the forced blocks (into fsc) for this problem
 inline bool route_scores_forced(const Geo& g, int dtype) { return dtype == PISA_BF16 && g.L >= 3; }
+// Dense scoring pays while a level is small: its cost per query grows with the visible
+// prefix of the child level, a gather's does not.  The dense launch covers levels L down
+// to dense_bottom(g), the highest routing levels whose child level has at most
+// kDenseMaxChildren nodes (n[L-1] <= 2gK always qualifies, so L >= 3 implies a dense
+// launch); the gather launch walks the levels below, down to 2.
+constexpr int kDenseMaxChildren = 2048;
+inline int dense_bottom(const Geo& g) {
+  int l = 3;
+  while (l < g.L && g.n[l - 1] > kDenseMaxChildren) ++l;
+  return l;
+}
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
 int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                    hipStream_t st);
