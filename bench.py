@@ -5,7 +5,9 @@ Headline (one "step"): pyramid build + prefill selection at 256K tokens, C=64, K
 16 query / 4 KV heads, d=128, bf16 (the pages' selection-latency workload, synthetic
 inputs resident in HBM).  Also timed in the same run: the same step at 64K, and one
 decode step (32 sequences x 262144-token cache, precomputed pyramid; cold: each step
-follows a 1 GiB write that evicts L2 and MALL; warm: back to back), and the 256K step
+follows a 1 GiB write that evicts L2 and MALL; warm: back to back) with, beside it, the
+serving-loop step on growing caches (append one key per sequence, then the varlen decode
+selection), and the 256K step
 with the PISA-1 / PISA-2 routing scorers (ablations; extra fields), and the pyramid
 selector against the full-scan BSA selector from 4K to 1M tokens (the pages'
 selection-kernel comparison at C=64, K=8, extended past 256K).
@@ -254,7 +256,41 @@ def time_decode(torch, pisa, synth, steps):
     b.record()
     b.synchronize()
     warm = a.elapsed_time(b) * 1e3 / steps
-    return statistics.median(cold), warm
+
+    # serving-loop step on growing caches: sequence b holds N - 1 - (997 b mod 4096) keys
+    # of the same 262144-key cache; a step appends one key per sequence (pisa_append_keys)
+    # and selects for the new query at the new length (pisa_select_decode_varlen)
+    lens = [p.seq_len - 1 - (997 * x) % 4096 for x in range(p.batch)]
+    old = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    new = old + 1
+    vpyr = torch.zeros_like(pyr)
+    pisa.append_keys(p, kd, torch.zeros_like(old), old, max(lens), vpyr)
+    torch.cuda.synchronize()
+
+    def step():
+        pisa.append_keys(p, kd, old, new, 1, vpyr)
+        pisa.select_decode_varlen(p, qd, kd, vpyr, new, oi, os_)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    vcold = []
+    for _ in range(steps):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        vcold.append(a.elapsed_time(b) * 1e3)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        step()
+    b.record()
+    b.synchronize()
+    vwarm = a.elapsed_time(b) * 1e3 / steps
+    return statistics.median(cold), warm, statistics.median(vcold), vwarm
 
 
 CROSSOVER_SIZES = [4096, 16384, 65536, 131072, 262144, 524288, 1048576]
@@ -381,10 +417,13 @@ def main():
         del b
         torch.cuda.empty_cache()
     if a.only in (None, "decode") and not a.no_decode:
-        cold, warm = time_decode(torch, pisa, synth, a.decode_steps)
+        cold, warm, vcold, vwarm = time_decode(torch, pisa, synth, a.decode_steps)
         extra["decode_us_per_step"] = round(cold, 2)
         extra["decode_us_per_step_warm"] = round(warm, 2)
-        log("decode: cold %.2f us, warm %.2f us" % (cold, warm))
+        extra["decode_append_varlen_us_per_step"] = round(vcold, 2)
+        extra["decode_append_varlen_us_per_step_warm"] = round(vwarm, 2)
+        log("decode: cold %.2f us, warm %.2f us; append + varlen decode: cold %.2f us, warm %.2f us" % (
+            cold, warm, vcold, vwarm))
         torch.cuda.empty_cache()
     if a.only in (None, "bsa") and not a.no_bsa:
         extra["crossover_c64_k8"] = crossover(torch, pisa, synth, a.steps, a.warmup)

@@ -19,13 +19,50 @@ constexpr int kSub = 16;       // level-l0 nodes per workgroup
 constexpr int kSubLevels = 4;  // levels built from LDS above l0 (log2 kSub)
 
 template <typename Tin, int D>
+struct RowsShape {
+  static constexpr int VEC = Vec<Tin>::N;
+  static constexpr int TPR = D / VEC;    // threads per row
+  static constexpr int RPP = 256 / TPR;  // rows per pass
+};
+
+// Mean of rows [r0, r1) of s (D wide) by a 256-thread workgroup: thread (column segment,
+// rp) sums rows r0 + rp, r0 + rp + RPP, ... of its VEC columns in order, then thread e < D
+// adds the RPP partial sums in order and divides.  Returns the mean in threads e < D.  One
+// fixed order, so the pyramid build and the incremental append produce the same bits.
+// Every thread of the workgroup must call it (it synchronises twice).
+template <typename Tin, int D>
+__device__ __forceinline__ float rows_mean(const Tin* s, int r0, int r1,
+                                           float (&red)[RowsShape<Tin, D>::RPP][D], int tid) {
+  constexpr int VEC = RowsShape<Tin, D>::VEC, TPR = RowsShape<Tin, D>::TPR, RPP = RowsShape<Tin, D>::RPP;
+  const int cseg = tid % TPR, rp = tid / TPR;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  for (int r = r0 + rp; r < r1; r += RPP) {
+    float x[VEC];
+    Vec<Tin>::load(s + (int64_t)r * D + cseg * VEC, x);
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] += x[v];
+  }
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) red[rp][cseg * VEC + v] = acc[v];
+  __syncthreads();
+  float m = 0.f;
+  if (tid < D) {
+    float t = 0.f;
+#pragma unroll 8
+    for (int p = 0; p < RPP; ++p) t += red[p][tid];
+    m = t / (float)(r1 - r0);
+  }
+  __syncthreads();
+  return m;
+}
+
+template <typename Tin, int D>
 __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ src, int64_t src_bh_stride,
                                                       int32_t src_rows, int32_t fan, float* __restrict__ pyr,
                                                       Geo geo, int32_t l0) {
-  constexpr int VEC = Vec<Tin>::N;
-  constexpr int TPR = D / VEC;    // threads per row
-  constexpr int RPP = 256 / TPR;  // rows per pass
-  __shared__ float red[RPP][D];
+  __shared__ float red[RowsShape<Tin, D>::RPP][D];
   __shared__ float lvl[2][kSub][D];
 
   const int tid = threadIdx.x;
@@ -35,35 +72,18 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
   const Tin* s = src + (int64_t)bh * src_bh_stride;
   float* P = pyr + (int64_t)bh * geo.T * D;
   bf16* R = reinterpret_cast<bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
-  const int cseg = tid % TPR, rp = tid / TPR;
-
   for (int jb = 0; jb < nodes; ++jb) {
     const int j = j0 + jb;
     const int r0 = j * fan;
     const int r1 = min(r0 + fan, src_rows);
-    float acc[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-    for (int r = r0 + rp; r < r1; r += RPP) {
-      float x[VEC];
-      Vec<Tin>::load(s + (int64_t)r * D + cseg * VEC, x);
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) acc[v] += x[v];
-    }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) red[rp][cseg * VEC + v] = acc[v];
-    __syncthreads();
+    const float m = rows_mean<Tin, D>(s, r0, r1, red, tid);
     if (tid < D) {
-      float t = 0.f;
-#pragma unroll 8
-      for (int p = 0; p < RPP; ++p) t += red[p][tid];
-      const float m = t / (float)(r1 - r0);
       P[(int64_t)(geo.off[l0] + j) * D + tid] = m;
       store_rcopy<D>(R, geo.off[l0] + j, tid, m * geo.s_log2e);
-      lvl[0][jb][tid] = m;
+      lvl[0][jb][tid] = m;  // read back only by this thread
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // Levels above l0 inside this subtree (g = 2): parents of [jbase, jbase + cnt).
   int cur = 0, cnt = nodes, jbase = j0;
@@ -106,7 +126,105 @@ int build_t(const Geo& g, const Tin* k, float* pyr, hipStream_t st) {
   return PISA_OK;
 }
 
+// ---- incremental append (a growing key cache; pyramid laid out for the capacity) ----
+//
+// "Block Sparse Attention with Log-Linear Complexity", agihunt.info summary, pyramid
+// paragraph: a new key changes only its leaf block's mean and that block's ancestors, one
+// node per level.  Sequence b grows from old_len[b] to new_len[b] keys; the leaf blocks
+// holding positions old_len .. new_len - 1 are recomputed from their raw keys (rows_mean:
+// the same bits as a fresh build), then every level above recomputes the ancestors of that
+// block range from their children present at new_len, up to the capacity's top level (so
+// levels that only a longer cache will walk are kept current too).
+
+// Clamped dirty leaf-block range [*lo, *hi] of sequence b; false when nothing changed.
+__device__ __forceinline__ bool dirty_blocks(const Geo& cap, const int32_t* old_len, const int32_t* new_len, int b,
+                                             int max_blocks, int* len, int* lo, int* hi) {
+  const int nl = min(max(new_len[b], 0), cap.N);
+  const int ol = min(max(old_len[b], 0), nl);
+  *len = nl;
+  if (nl <= ol) return false;
+  *lo = ol / cap.C;
+  *hi = min((nl - 1) / cap.C, *lo + max_blocks - 1);
+  return true;
+}
+
+template <typename Tin, int D>
+__global__ __launch_bounds__(256) void append_leaf_kernel(const Tin* __restrict__ k, Geo cap,
+                                                          const int32_t* __restrict__ old_len,
+                                                          const int32_t* __restrict__ new_len, int32_t max_blocks,
+                                                          float* __restrict__ pyr) {
+  __shared__ float red[RowsShape<Tin, D>::RPP][D];
+  const int tid = threadIdx.x, bh = blockIdx.y;
+  int len, lo, hi;
+  if (!dirty_blocks(cap, old_len, new_len, bh / cap.Hkv, max_blocks, &len, &lo, &hi)) return;  // whole workgroup
+  const int j0 = lo + blockIdx.x * kSub;
+  const Tin* s = k + (int64_t)bh * cap.N * D;
+  float* P = pyr + (int64_t)bh * cap.T * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.T * 2 * D;
+  for (int j = j0; j < j0 + kSub && j <= hi; ++j) {
+    const float m = rows_mean<Tin, D>(s, j * cap.C, min(j * cap.C + cap.C, len), red, tid);
+    if (tid < D) {
+      P[(int64_t)(cap.off[1] + j) * D + tid] = m;
+      store_rcopy<D>(R, cap.off[1] + j, tid, m * cap.s_log2e);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void append_up_kernel(Geo cap, const int32_t* __restrict__ old_len,
+                                                        const int32_t* __restrict__ new_len, int32_t max_blocks,
+                                                        float* __restrict__ pyr) {
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  int len, lo, hi;
+  if (!dirty_blocks(cap, old_len, new_len, bh / cap.Hkv, max_blocks, &len, &lo, &hi)) return;  // whole workgroup
+  float* P = pyr + (int64_t)bh * cap.T * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.T * 2 * D;
+  int nprev = (len + cap.C - 1) / cap.C;  // nodes of level l - 1 at this length
+  for (int l = 2; l <= cap.L; ++l) {
+    const int ncur = (nprev + 1) >> 1;
+    const int plo = lo >> (l - 1), phi = hi >> (l - 1);
+    for (int t = tid; t < (phi - plo + 1) * D; t += 256) {
+      const int node = plo + t / D, e = t % D;
+      if (node >= ncur) continue;
+      const int c0 = 2 * node, c1 = min(2 * node + 2, nprev);
+      float a = 0.f;
+      for (int c = c0; c < c1; ++c) a += P[(int64_t)(cap.off[l - 1] + c) * D + e];
+      const float m = a / (float)(c1 - c0);
+      P[(int64_t)(cap.off[l] + node) * D + e] = m;
+      store_rcopy<D>(R, cap.off[l] + node, e, m * cap.s_log2e);
+    }
+    __syncthreads();  // level l is complete before level l + 1 reads it (one CU, one L1)
+    nprev = ncur;
+  }
+}
+
+template <typename Tin, int D>
+int append_t(const Geo& cap, const Tin* k, const int32_t* old_len, const int32_t* new_len, int max_new,
+             float* pyr, hipStream_t st) {
+  const int max_blocks = (max_new + cap.C - 1) / cap.C + 1;  // a range of max_new positions spans this many
+  dim3 grid((max_blocks + kSub - 1) / kSub, cap.B * cap.Hkv);
+  append_leaf_kernel<Tin, D><<<grid, 256, 0, st>>>(k, cap, old_len, new_len, max_blocks, pyr);
+  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  if (cap.L >= 2) {
+    append_up_kernel<D><<<cap.B * cap.Hkv, 256, 0, st>>>(cap, old_len, new_len, max_blocks, pyr);
+    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  }
+  return PISA_OK;
+}
+
 }  // namespace
+
+int launch_append(const Geo& cap, int dtype, const void* k, const int32_t* old_len, const int32_t* new_len,
+                  int max_new, float* pyr, hipStream_t st) {
+  if (dtype == PISA_BF16) {
+    if (cap.d == 128) return append_t<bf16, 128>(cap, (const bf16*)k, old_len, new_len, max_new, pyr, st);
+    if (cap.d == 64) return append_t<bf16, 64>(cap, (const bf16*)k, old_len, new_len, max_new, pyr, st);
+  } else {
+    if (cap.d == 128) return append_t<float, 128>(cap, (const float*)k, old_len, new_len, max_new, pyr, st);
+    if (cap.d == 64) return append_t<float, 64>(cap, (const float*)k, old_len, new_len, max_new, pyr, st);
+  }
+  return PISA_ERR_UNSUPPORTED;
+}
 
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st) {
   if (dtype == PISA_BF16) {

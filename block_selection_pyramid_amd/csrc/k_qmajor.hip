@@ -12,7 +12,9 @@
 // the top pyramid levels' routing copy in LDS (one parallel burst); wavefront 0 then walks
 // the pyramid for the new query at position N-1, its top levels from LDS; then every
 // wavefront scores one of the <= 2K + 3 candidate and forced tiles (so their loads are in
-// flight together), and wavefront 0 writes the selection.  One launch per step.
+// flight together), and wavefront 0 writes the selection.  One launch per step.  With
+// per-sequence lengths each workgroup first re-derives its sequence's level table in LDS
+// (node offsets stay those of the capacity layout that pisa_append_keys maintains).
 #include <type_traits>
 
 #include "final_dev.h"
@@ -62,17 +64,28 @@ __global__ __launch_bounds__(256) void qmajor_kernel(const T* __restrict__ q, co
 constexpr int kDecodeWaves = 16;
 constexpr int64_t kDecodeStageBytes = 64 * 1024;  // LDS for the staged top levels
 
+template <int D, int G>
+struct DecodeLds {
+  float qs[G * (D + kQPad)];
+  WalkLds wl;
+  WalkLdsM<1> wlm;
+  int32_t tj[kMaxCand + 4];
+  float tsc[kMaxCand + 4];
+};
+
+// The decode step for one (sequence, KV head) = blockIdx.x.  geo: the sequence's geometry
+// (its length N and level table; node offsets, T and the batch shape of the buffers);
+// kstride: key rows per (b, h) in k (the cache capacity).
 template <typename T, int D, int G>
-__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
-                                                                   const float* __restrict__ pyr, Geo geo,
-                                                                   int32_t stage_lo, int32_t* __restrict__ out_idx,
-                                                                   float* __restrict__ out_score) {
-  extern __shared__ __attribute__((aligned(16))) char stage[];  // bf16: levels [stage_lo, L-1]
-  __shared__ float qs[G * (D + kQPad)];
-  __shared__ WalkLds wl;
-  __shared__ WalkLdsM<1> wlm;
-  __shared__ int32_t tj[kMaxCand + 4];
-  __shared__ float tsc[kMaxCand + 4];
+__device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __restrict__ k,
+                                            const float* __restrict__ pyr, const Geo& geo, int64_t kstride,
+                                            int stage_lo, char* stage, DecodeLds<D, G>& sh, int32_t* __restrict__ out_idx,
+                                            float* __restrict__ out_score) {
+  float* qs = sh.qs;
+  WalkLds& wl = sh.wl;
+  WalkLdsM<1>& wlm = sh.wlm;
+  int32_t* tj = sh.tj;
+  float* tsc = sh.tsc;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int bh = blockIdx.x;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
@@ -139,7 +152,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const T* __re
     if (lane < nf) tj[twoK + lane] = lane == 0 ? F[0] : (lane == 1 ? F[1] : F[2]);
   }
   __syncthreads();
-  const T* keys = k + (int64_t)bh * geo.N * D;
+  const T* keys = k + (int64_t)bh * kstride * D;
   for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
     const int j = tj[t];
     if (j < 0) continue;
@@ -151,6 +164,45 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const T* __re
     const float sc = leaf >= 0 ? tsc[lane] : -INFINITY;
     finalize_row(leaf, sc, F, nf, tsc + twoK, geo.K, twoK, lane, out_idx + (int64_t)bh * geo.K,
                  out_score + (int64_t)bh * geo.K);
+  }
+}
+
+// Level table of a sequence of n keys inside geometry g (whose node offsets, T and batch
+// shape stay those of the buffers): n_0 = n, n_l = ceil halving, L = first level <= gK.
+__device__ __forceinline__ void relevel(Geo& g, int n) {
+  g.N = n;
+  g.n[0] = n;
+  int m = (n + g.C - 1) / g.C, L = 1;
+  g.n[1] = m;
+  while (m > g.g * g.K && L + 1 < kMaxLevels) {
+    m = (m + 1) >> 1;
+    g.n[++L] = m;
+  }
+  g.L = L;
+  g.n1 = g.n[1];
+}
+
+// lengths == nullptr: every sequence holds geo.N keys.  Otherwise sequence b holds
+// lengths[b] keys (clamped to [1, geo.N]) of a cache of capacity geo.N, and the pyramid is
+// laid out for the capacity (pisa_append_keys).
+template <typename T, int D, int G, bool VARLEN>
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                                   const float* __restrict__ pyr, Geo geo,
+                                                                   const int32_t* __restrict__ lengths,
+                                                                   int32_t stage_lo, int32_t* __restrict__ out_idx,
+                                                                   float* __restrict__ out_score) {
+  extern __shared__ __attribute__((aligned(16))) char stage[];  // bf16: levels [stage_lo, L-1]
+  __shared__ DecodeLds<D, G> sh;
+  if constexpr (VARLEN) {
+    __shared__ Geo gs;
+    if (threadIdx.x == 0) {
+      gs = geo;
+      relevel(gs, min(max(lengths[blockIdx.x / geo.Hkv], 1), geo.N));
+    }
+    __syncthreads();
+    decode_body<T, D, G>(q, k, pyr, gs, geo.N, stage_lo, stage, sh, out_idx, out_score);
+  } else {
+    decode_body<T, D, G>(q, k, pyr, geo, geo.N, stage_lo, stage, sh, out_idx, out_score);
   }
 }
 
@@ -171,9 +223,9 @@ int qmajor_g(const Geo& g, const void* q, const void* k, const int32_t* cand, in
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
-template <typename T, int D>
-int decode_g(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* oi, float* os,
-             hipStream_t st) {
+template <typename T, int D, bool VARLEN>
+int decode_g(const Geo& g, const void* q, const void* k, const float* pyr, const int32_t* lengths, int32_t* oi,
+             float* os, hipStream_t st) {
   const unsigned grid = g.B * g.Hkv;
   const T* qq = (const T*)q;
   const T* kk = (const T*)k;
@@ -191,11 +243,11 @@ int decode_g(const Geo& g, const void* q, const void* k, const float* pyr, int32
   }
   const unsigned block = 64 * kDecodeWaves;
   switch (g.G) {
-    case 1: decode_kernel<T, D, 1><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
-    case 2: decode_kernel<T, D, 2><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
-    case 4: decode_kernel<T, D, 4><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
-    case 8: decode_kernel<T, D, 8><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
-    case 16: decode_kernel<T, D, 16><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, stage_lo, oi, os); break;
+    case 1: decode_kernel<T, D, 1, VARLEN><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, lengths, stage_lo, oi, os); break;
+    case 2: decode_kernel<T, D, 2, VARLEN><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, lengths, stage_lo, oi, os); break;
+    case 4: decode_kernel<T, D, 4, VARLEN><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, lengths, stage_lo, oi, os); break;
+    case 8: decode_kernel<T, D, 8, VARLEN><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, lengths, stage_lo, oi, os); break;
+    case 16: decode_kernel<T, D, 16, VARLEN><<<grid, block, (size_t)bytes, st>>>(qq, kk, pyr, g, lengths, stage_lo, oi, os); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
@@ -215,16 +267,23 @@ int launch_qmajor(const Geo& g, int dtype, const void* q, const void* k, const i
   return PISA_ERR_UNSUPPORTED;
 }
 
-int launch_decode(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* out_idx,
-                  float* out_score, hipStream_t st) {
+template <bool VARLEN>
+int decode_d(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, const int32_t* lengths,
+             int32_t* out_idx, float* out_score, hipStream_t st) {
   if (dtype == PISA_BF16) {
-    if (g.d == 128) return decode_g<bf16, 128>(g, q, k, pyr, out_idx, out_score, st);
-    if (g.d == 64) return decode_g<bf16, 64>(g, q, k, pyr, out_idx, out_score, st);
+    if (g.d == 128) return decode_g<bf16, 128, VARLEN>(g, q, k, pyr, lengths, out_idx, out_score, st);
+    if (g.d == 64) return decode_g<bf16, 64, VARLEN>(g, q, k, pyr, lengths, out_idx, out_score, st);
   } else {
-    if (g.d == 128) return decode_g<float, 128>(g, q, k, pyr, out_idx, out_score, st);
-    if (g.d == 64) return decode_g<float, 64>(g, q, k, pyr, out_idx, out_score, st);
+    if (g.d == 128) return decode_g<float, 128, VARLEN>(g, q, k, pyr, lengths, out_idx, out_score, st);
+    if (g.d == 64) return decode_g<float, 64, VARLEN>(g, q, k, pyr, lengths, out_idx, out_score, st);
   }
   return PISA_ERR_UNSUPPORTED;
+}
+
+int launch_decode(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, const int32_t* lengths,
+                  int32_t* out_idx, float* out_score, hipStream_t st) {
+  return lengths ? decode_d<true>(g, dtype, q, k, pyr, lengths, out_idx, out_score, st)
+                 : decode_d<false>(g, dtype, q, k, pyr, nullptr, out_idx, out_score, st);
 }
 
 }  // namespace pisa

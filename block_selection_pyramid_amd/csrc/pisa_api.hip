@@ -85,6 +85,7 @@ PrefillWs prefill_ws(const Geo& g) {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 }  // namespace pisa
 
@@ -242,7 +243,34 @@ int pisa_select_decode(const pisa_problem* p, const void* q, const void* k_cache
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(pyramid)) return PISA_ERR_INVALID_ARG;
   rc = supported(g, p->dtype, PISA_DECODE);
   if (rc != PISA_OK) return rc;
-  return launch_decode(g, p->dtype, q, k_cache, pyramid, out_idx, out_score, (hipStream_t)stream);
+  return launch_decode(g, p->dtype, q, k_cache, pyramid, nullptr, out_idx, out_score, (hipStream_t)stream);
+}
+
+int pisa_append_keys(const pisa_problem* p, const void* k_cache, const int32_t* old_lengths,
+                     const int32_t* new_lengths, int32_t max_new_keys, float* pyramid, pisa_stream_t stream) {
+  Geo g;
+  int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (!k_cache || !old_lengths || !new_lengths || !pyramid) return PISA_ERR_INVALID_ARG;
+  if (!aligned16(k_cache) || !aligned16(pyramid) || !aligned4(old_lengths) || !aligned4(new_lengths))
+    return PISA_ERR_INVALID_ARG;
+  if (max_new_keys < 0 || max_new_keys > p->seq_len) return PISA_ERR_INVALID_ARG;
+  rc = supported(g, p->dtype, PISA_DECODE);
+  if (rc != PISA_OK) return rc;
+  if (max_new_keys == 0) return PISA_OK;
+  return launch_append(g, p->dtype, k_cache, old_lengths, new_lengths, max_new_keys, pyramid, (hipStream_t)stream);
+}
+
+int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* k_cache, const float* pyramid,
+                              const int32_t* lengths, int32_t* out_idx, float* out_score, pisa_stream_t stream) {
+  Geo g;
+  int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (!q || !k_cache || !pyramid || !lengths || !out_idx || !out_score) return PISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(pyramid) || !aligned4(lengths)) return PISA_ERR_INVALID_ARG;
+  rc = supported(g, p->dtype, PISA_DECODE);
+  if (rc != PISA_OK) return rc;
+  return launch_decode(g, p->dtype, q, k_cache, pyramid, lengths, out_idx, out_score, (hipStream_t)stream);
 }
 
 int pisa_bsa_select_prefill(const pisa_problem* p, const void* q, const float* pyramid, int32_t* out_idx,

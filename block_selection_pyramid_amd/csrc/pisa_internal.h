@@ -87,7 +87,13 @@ int launch_forced_final(const Geo& g, const void* q, const void* k, const int32_
                         int32_t* out_idx, float* out_score, hipStream_t st);
 int launch_qmajor(const Geo& g, int dtype, const void* q, const void* k, const int32_t* cand, int32_t* out_idx,
                   float* out_score, hipStream_t st);
-int launch_decode(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* out_idx,
-                  float* out_score, hipStream_t st);
+// lengths: nullptr (every sequence holds g.N keys) or device int32 [B] per-sequence lengths
+// in a cache of capacity g.N (pyramid in the capacity layout)
+int launch_decode(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, const int32_t* lengths,
+                  int32_t* out_idx, float* out_score, hipStream_t st);
+// incremental pyramid update of sequences growing from old_len[b] to new_len[b] keys
+// (capacity geometry g; at most max_new keys per sequence)
+int launch_append(const Geo& g, int dtype, const void* k, const int32_t* old_len, const int32_t* new_len,
+                  int max_new, float* pyr, hipStream_t st);
 
 }  // namespace pisa

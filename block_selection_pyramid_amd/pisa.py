@@ -83,7 +83,7 @@ _lib = None
 
 EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs", "pisa_select_decode",
-           "pisa_bsa_select_prefill",
+           "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen",
            "pisa_status_string", "pisa_version")
 
 
@@ -110,6 +110,8 @@ def load(path: str | None = None):
     lib.pisa_prefill_routed_pairs.argtypes = [P, vp, sz, vp, vp]
     lib.pisa_select_decode.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.pisa_bsa_select_prefill.argtypes = [P, vp, vp, vp, vp, vp]
+    lib.pisa_append_keys.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, vp]
+    lib.pisa_select_decode_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_version.restype = ctypes.c_char_p
@@ -208,6 +210,39 @@ def select_prefill(p: Problem, q: torch.Tensor, k: torch.Tensor, pyramid: torch.
     sp = _dev(out_score, "out_score", torch.float32, oshape)
     _check(load().pisa_select_prefill(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, _stream(stream)),
            "pisa_select_prefill")
+    return out_idx, out_score
+
+
+def append_keys(p: Problem, k_cache: torch.Tensor, old_lengths: torch.Tensor, new_lengths: torch.Tensor,
+                max_new_keys: int, pyramid: torch.Tensor, stream=None):
+    """pisa_append_keys: p.seq_len is the cache capacity; lengths are int32 [B] on the device."""
+    kp = _dev(k_cache, "k_cache", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    op = _dev(old_lengths, "old_lengths", torch.int32, (p.batch,))
+    np_ = _dev(new_lengths, "new_lengths", torch.int32, (p.batch,))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    _check(load().pisa_append_keys(ctypes.byref(p.c()), kp, op, np_, int(max_new_keys), pp, _stream(stream)),
+           "pisa_append_keys")
+    return pyramid
+
+
+def select_decode_varlen(p: Problem, q: torch.Tensor, k_cache: torch.Tensor, pyramid: torch.Tensor,
+                         lengths: torch.Tensor, out_idx: torch.Tensor | None = None,
+                         out_score: torch.Tensor | None = None, stream=None):
+    """pisa_select_decode_varlen: the query of sequence b sits at position lengths[b] - 1 of a
+    cache of capacity p.seq_len.  Returns (idx int32 [B, Hkv, K], score fp32 [B, Hkv, K])."""
+    oshape = (p.batch, p.n_kv_heads, p.top_k)
+    qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.head_dim))
+    kp = _dev(k_cache, "k_cache", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    lp = _dev(lengths, "lengths", torch.int32, (p.batch,))
+    if out_idx is None:
+        out_idx = torch.empty(oshape, dtype=torch.int32, device=q.device)
+    if out_score is None:
+        out_score = torch.empty(oshape, dtype=torch.float32, device=q.device)
+    ip = _dev(out_idx, "out_idx", torch.int32, oshape)
+    sp = _dev(out_score, "out_score", torch.float32, oshape)
+    _check(load().pisa_select_decode_varlen(ctypes.byref(p.c()), qp, kp, pp, lp, ip, sp, _stream(stream)),
+           "pisa_select_decode_varlen")
     return out_idx, out_score
 
 

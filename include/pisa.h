@@ -184,6 +184,37 @@ int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size
 
 /* Static description of a status code. */
 /*
+ * Growing key caches (decode with per-sequence lengths).  Here p->seq_len is the cache
+ * capacity: k_cache is [B, Hkv, capacity, d] and the pyramid buffer is laid out for the
+ * capacity (pisa_pyramid_bytes(p), level offsets of pisa_levels(p)); sequence b holds
+ * lengths[b] keys and uses, inside that layout, the level table of its own length (n_l
+ * and L of a problem with seq_len = lengths[b]).
+ *
+ * pisa_append_keys updates the pyramid after sequence b grew from old_lengths[b] to
+ * new_lengths[b] keys (the caller has written the new keys into k_cache): the leaf blocks
+ * holding positions old..new-1 are recomputed from their raw keys and every ancestor of
+ * those blocks from its children present at the new length, one node per level for a
+ * single new key ("Block Sparse Attention with Log-Linear Complexity", agihunt.info
+ * summary, pyramid paragraph: each level mean-pools the one below, so a key changes one
+ * node per level).  The updated nodes hold the same bits as pisa_build_pyramid of a
+ * problem with seq_len = new_lengths[b] on the same keys; levels above the sequence's own
+ * top level are maintained too, for when it grows.  old_lengths = 0 builds a sequence from
+ * scratch.  old_lengths / new_lengths: device int32 [B] with 0 <= old <= new <= capacity
+ * and new - old <= max_new_keys (host int, 0 <= max_new_keys <= capacity); values outside
+ * that contract are clamped on the device and leave the pyramid unspecified, never an
+ * out-of-bounds access.  Two launches on `stream`; no workspace.
+ *
+ * pisa_select_decode_varlen is pisa_select_decode for the query of sequence b at position
+ * lengths[b] - 1 (device int32 [B], 1 <= lengths[b] <= capacity, clamped on the device),
+ * on the pyramid that pisa_append_keys maintains.  Equal to pisa_select_decode on a
+ * problem with seq_len = lengths[b] for each sequence.  q [B, Hq, d].
+ */
+int pisa_append_keys(const pisa_problem* p, const void* k_cache, const int32_t* old_lengths,
+                     const int32_t* new_lengths, int32_t max_new_keys, float* pyramid, pisa_stream_t stream);
+int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* k_cache, const float* pyramid,
+                              const int32_t* lengths, int32_t* out_idx, float* out_score, pisa_stream_t stream);
+
+/*
  * Full-scan BSA selection for every query position, the baseline the pyramid selector is
  * timed against ("Block Sparse Attention with Log-Linear Complexity": agihunt.info
  * summary, opening and baselines paragraphs; rcap.io explainer, picking-step and

@@ -94,6 +94,22 @@ def test_invalid_arguments(pisa, field, value):
     assert lib.pisa_bsa_select_prefill(ctypes.byref(p.c()), 0x1000, 0x1000, 0x1000, 0x1000, None) == 1
 
 
+def test_append_and_varlen_host_checks(pisa):
+    lib = pisa.load()
+    p = pisa.Problem(2, 4096, 16, 4, 128)
+    P = ctypes.byref(p.c())
+    assert lib.pisa_append_keys(P, 0, 0x1000, 0x1000, 1, 0x1000, None) == 1          # null cache
+    assert lib.pisa_append_keys(P, 0x1000, 0x1002, 0x1000, 1, 0x1000, None) == 1     # misaligned lengths
+    assert lib.pisa_append_keys(P, 0x1000, 0x1000, 0x1000, -1, 0x1000, None) == 1    # negative count
+    assert lib.pisa_append_keys(P, 0x1000, 0x1000, 0x1000, 4097, 0x1000, None) == 1  # beyond capacity
+    assert lib.pisa_append_keys(P, 0x1000, 0x1000, 0x1000, 0, 0x1000, None) == 0     # nothing to do
+    assert lib.pisa_select_decode_varlen(P, 0x1000, 0x1000, 0x1000, 0, 0x1000, 0x1000, None) == 1
+    assert lib.pisa_select_decode_varlen(P, 0x1000, 0x1000, 0x1008, 0x1000, 0x1000, 0x1000, None) == 1
+    bad = pisa.Problem(2, 4096, 16, 4, 96)
+    assert lib.pisa_select_decode_varlen(ctypes.byref(bad.c()), 0x1000, 0x1000, 0x1000, 0x1000, 0x1000, 0x1000,
+                                         None) == 2
+
+
 def test_bsa_host_checks(pisa):
     lib = pisa.load()
     p = pisa.Problem(1, 4096, 16, 4, 128)

@@ -446,3 +446,115 @@ def test_bsa_workload_sampled(env, name, n_random):
     assert np.array_equal(nsel, np.minimum(K, bq + 1))
     opyr = oracle.build_pyramid(op, k)
     bsa_verify(op, q, opyr, sample_rows(w, needles, n_random, 13), idx, sc, "bsa-" + name)
+
+
+# --------------------------------------- growing caches: incremental pyramid, varlen decode
+
+def _levels_offsets(pisa, N, B, Hq, Hkv, d, K, dtype):
+    L, nodes, offs = pisa.levels(pisa.Problem(B, N, Hq, Hkv, d, 64, K, 2, dtype=dtype))
+    return L, nodes, offs
+
+
+@pytest.mark.parametrize("dt,d", [(synth.BF16, 128), (synth.F32, 64)])
+def test_append_keys_matches_fresh_build(env, dt, d):
+    # appends of assorted sizes (single keys, block boundaries, long runs, none) leave every
+    # node a sequence's own level table uses bit-identical to a fresh build at its length
+    torch, pisa = env
+    B, Hq, Hkv, K, cap = 3, 8, 2, 8, 5000
+    w = synth.custom(name="append", batch=B, seq_len=cap, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     dtype=dt, seed=1234 + d, needles=8, decode=True)
+    _, k, _ = synth.make_inputs(w)
+    p = pisa.Problem(B, cap, Hq, Hkv, d, 64, K, 2, dtype=dt)
+    kd = dev(torch, k)
+    pyr = torch.zeros(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+    _, _, coff = _levels_offsets(pisa, cap, B, Hq, Hkv, d, K, dt)
+    old = [0, 0, 0]
+    for new in ([1, 700, 64], [65, 1500, 64], [66, 1501, 128], [1000, 4000, 129], [4999, 4001, 2500],
+                [5000, 5000, 5000]):
+        log("append", "d=%d %s -> %s" % (d, old, new))
+        ot = torch.tensor(old, dtype=torch.int32, device="cuda")
+        nt = torch.tensor(new, dtype=torch.int32, device="cuda")
+        pisa.append_keys(p, kd, ot, nt, max(n - o for n, o in zip(new, old)), pyr)
+        torch.cuda.synchronize()
+        app = pyr.cpu().numpy().view(np.uint32)
+        for b in range(B):
+            n = new[b]
+            pb = pisa.Problem(1, n, Hq, Hkv, d, 64, K, 2, dtype=dt)
+            fresh = pisa.build_pyramid(pb, kd[b:b + 1, :, :n].contiguous())
+            torch.cuda.synchronize()
+            fr = fresh.cpu().numpy().view(np.uint32)
+            L, nodes, foff = _levels_offsets(pisa, n, 1, Hq, Hkv, d, K, dt)
+            for l in range(1, L + 1):
+                a = app[:, b, :, coff[l - 1]:coff[l - 1] + nodes[l]]
+                f = fr[:, 0, :, foff[l - 1]:foff[l - 1] + nodes[l]]
+                assert np.array_equal(a, f), "sequence %d length %d level %d differs" % (b, n, l)
+        old = new
+
+
+def _oracle_decode_rows(op_kw, q, k, lengths, b):
+    n = int(lengths[b])
+    kw = dict(op_kw, batch=1, seq_len=n)
+    op = oracle.Problem(**kw)
+    kb = np.ascontiguousarray(k[b:b + 1, :, :n])
+    qb = np.ascontiguousarray(q[b:b + 1])
+    return op, qb, kb, oracle.build_pyramid(op, kb)
+
+
+@pytest.mark.parametrize("dt,d,G", [(synth.BF16, 128, 4), (synth.F32, 64, 2), (synth.BF16, 64, 16)])
+def test_decode_varlen_parity(env, dt, d, G):
+    torch, pisa = env
+    lengths = [1, 64, 65, 7777, 20000, 129]
+    B, Hkv, K, cap = len(lengths), 2, 8, 20000
+    w = synth.custom(name="varlen", batch=B, seq_len=cap, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     dtype=dt, seed=4321 + d, needles=6, decode=True)
+    q, k, _ = synth.make_inputs(w)
+    p = pisa.Problem(B, cap, G * Hkv, Hkv, d, 64, K, 2, dtype=dt)
+    qd, kd = dev(torch, q), dev(torch, k)
+    pyr = torch.zeros(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+    lt = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    log("varlen", "d=%d G=%d lengths %s: launching" % (d, G, lengths))
+    pisa.append_keys(p, kd, torch.zeros_like(lt), lt, max(lengths), pyr)
+    idx, sc = pisa.select_decode_varlen(p, qd, kd, pyr, lt)
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    kw = dict(w.shape())
+    for b, n in enumerate(lengths):
+        op, qb, kb, opyr = _oracle_decode_rows(kw, q, k, lengths, b)
+        verify(op, qb, kb, opyr, np.arange(Hkv), idx[b], sc[b], decode=True, what="varlen-len%d" % n)
+        # the fixed-length decode on the sequence alone gives the same bits
+        pb = pisa.Problem(1, n, G * Hkv, Hkv, d, 64, K, 2, dtype=dt)
+        kbd = kd[b:b + 1, :, :n].contiguous()
+        fi, fs = pisa.select_decode(pb, qd[b:b + 1].contiguous(), kbd, pisa.build_pyramid(pb, kbd))
+        torch.cuda.synchronize()
+        assert np.array_equal(fi.cpu().numpy()[0], idx[b]) and np.array_equal(fs.cpu().numpy()[0], sc[b])
+
+
+def test_decode_steps_with_appends(env):
+    # a serving loop: each step appends one key per sequence, then selects for its query
+    torch, pisa = env
+    start = [3000, 100, 8000, 64]
+    B, G, Hkv, d, K, cap, steps = len(start), 4, 2, 128, 8, 9000, 12
+    w = synth.custom(name="steps", batch=B, seq_len=cap, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     seed=99, needles=8, decode=True)
+    _, k, _ = synth.make_inputs(w)
+    p = pisa.Problem(B, cap, G * Hkv, Hkv, d, 64, K, 2)
+    kd = dev(torch, k)
+    pyr = torch.zeros(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+    lt = torch.tensor(start, dtype=torch.int32, device="cuda")
+    pisa.append_keys(p, kd, torch.zeros_like(lt), lt, max(start), pyr)
+    kw = dict(w.shape())
+    lengths = list(start)
+    for s in range(steps):
+        new = [n + 1 for n in lengths]
+        q = synth.normal(500 + s, synth.TENSOR_Q, (B, G * Hkv, d), synth.BF16)
+        qd = dev(torch, q)
+        ot = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        nt = torch.tensor(new, dtype=torch.int32, device="cuda")
+        pisa.append_keys(p, kd, ot, nt, 1, pyr)
+        idx, sc = pisa.select_decode_varlen(p, qd, kd, pyr, nt)
+        torch.cuda.synchronize()
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        for b in range(B):
+            op, qb, kb, opyr = _oracle_decode_rows(kw, q, k, new, b)
+            verify(op, qb, kb, opyr, np.arange(Hkv), idx[b], sc[b], decode=True, what="step%d-seq%d" % (s, b))
+        lengths = new
