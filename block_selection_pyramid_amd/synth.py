@@ -24,7 +24,7 @@ _SRC = os.path.join(_HERE, "csrc", "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
 F32, BF16 = 0, 1
-TENSOR_Q, TENSOR_K, TENSOR_NEEDLE, TENSOR_BLOCK = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_NEEDLE, TENSOR_BLOCK, TENSOR_V = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -166,3 +166,8 @@ def add_block_offsets(w: Workload, k: np.ndarray, sigma: float) -> np.ndarray:
     kf = bf16_bits_to_f32(k) if w.dtype == BF16 else k
     kf = kf + np.repeat(off, w.block, axis=2)[:, :, :N, :]
     return to_bf16_bits(kf) if w.dtype == BF16 else np.ascontiguousarray(kf, dtype=np.float32)
+
+
+def make_values(w: Workload) -> np.ndarray:
+    """v [B, Hkv, N, d] (the values block-sparse attention reads), i.i.d. N(0, 1) like k."""
+    return normal(w.seed, TENSOR_V, (w.batch, w.n_kv_heads, w.seq_len, w.head_dim), w.dtype)

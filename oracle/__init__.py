@@ -108,6 +108,7 @@ def _load():
         lib.orc_bsa_scores.restype = i64
         lib.orc_bsa_check_rows.argtypes = [P, vp, vp, ctypes.c_int32, i64, vp, vp, vp, ctypes.c_double,
                                            ctypes.c_double, vp]
+        lib.orc_attention_rows.argtypes = [P, vp, vp, vp, ctypes.c_int32, i64, vp, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -302,3 +303,26 @@ def bsa_check(p: Problem, q: np.ndarray, pyr: np.ndarray, rows, idx: np.ndarray,
     if rc != 0:
         raise ValueError("invalid problem for the oracle: %r" % (p,))
     return status
+
+
+# ------------------------------------------------------------ block-sparse attention
+
+def attention(p: Problem, q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, rows=None,
+              decode: bool = False):
+    """Attention of each row's G query heads over the keys of its selected blocks (idx
+    [n, K], entries < 0 or past the query's block skipped, keys causal).  Returns
+    out float64 [n, G, d] and lse float64 [n, G]."""
+    _check_input(p, q)
+    _check_input(p, k)
+    _check_input(p, v)
+    r, n = _rows_arg(rows)
+    if r is None:
+        n = p.batch * p.n_kv_heads * (1 if decode else p.seq_len)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(n, p.top_k)
+    out = np.zeros((n, p.group, p.head_dim), dtype=np.float64)
+    lse = np.zeros((n, p.group), dtype=np.float64)
+    rc = _load().orc_attention_rows(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), int(decode), n, _ptr(r),
+                                    _ptr(idx), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("invalid problem for the oracle: %r" % (p,))
+    return out, lse

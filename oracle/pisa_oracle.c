@@ -848,3 +848,67 @@ int orc_bsa_check_rows(const orc_problem* P, const void* qp, const double* pyr, 
   }
   return 0;
 }
+
+/* ------------------------------------------- block-sparse attention */
+
+/*
+ * Attention of each query over the keys of its selected blocks, the
+ * consumer of the selection ([A] opening paragraph: each query reads only
+ * its Top-K tiles of C keys; [B] first paragraphs: attention then runs over
+ * the original keys of the picked blocks).  Readings: one selection per
+ * (batch, KV head, position), shared by the group's G query heads; the keys
+ * are those of blocks idx[0..K) that lie in [0, b] (entries < 0 or > b are
+ * skipped), each key t also causal (t <= i); per query head
+ *   out = sum_t softmax_t(s * <q, k_t>) v_t,   lse = log sum_t exp(s * <q, k_t>)
+ * (no key visible: out = 0, lse = -inf).  v has the shape of k.
+ * rows as for orc_select_rows; idx [n_rows, K] (the selection of each
+ * row); out [n_rows, G, d], lse [n_rows, G] (may be NULL).
+ */
+int orc_attention_rows(const orc_problem* P, const void* qp, const void* k, const void* v, int32_t decode,
+                       int64_t n_rows, const int64_t* rows, const int32_t* idx, double* out, double* lse) {
+  if (!orc_valid_problem(P)) return 1;
+  geo_t q;
+  geo_init(&q, P);
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t t = 0; t < n_rows; ++t) {
+    double* qbuf = (double*)malloc(sizeof(double) * (size_t)q.G * (size_t)q.d);
+    double* x = (double*)malloc(sizeof(double) * (size_t)q.K * (size_t)q.C);
+    int64_t* key = (int64_t*)malloc(sizeof(int64_t) * (size_t)q.K * (size_t)q.C);
+    row_t r;
+    row_setup(&q, qp, k, NULL, decode, rows ? rows[t] : t, qbuf, &r);
+    const int32_t* sel = idx + t * q.K;
+    /* the attended keys: every position of a selected block in [0, b], causal */
+    int64_t m = 0;
+    for (int u = 0; u < q.K; ++u) {
+      int64_t j = sel[u];
+      if (j < 0 || j > r.bq) continue;
+      int64_t lo = j * q.C, hi = lo + q.C < q.N ? lo + q.C : q.N;
+      if (hi > r.i + 1) hi = r.i + 1;
+      for (int64_t p = lo; p < hi; ++p) key[m++] = p;
+    }
+    for (int h = 0; h < q.G; ++h) {
+      double* o = out + (t * q.G + h) * q.d;
+      for (int e = 0; e < q.d; ++e) o[e] = 0.0;
+      if (m == 0) {
+        if (lse) lse[t * q.G + h] = -INFINITY;
+        continue;
+      }
+      const double* qh = r.qrows + (int64_t)h * q.d;
+      for (int64_t c = 0; c < m; ++c) {
+        double acc = 0.0;
+        for (int e = 0; e < q.d; ++e) acc += qh[e] * ld(k, r.kbase + key[c] * q.d + e, P->dtype);
+        x[c] = q.s * acc;
+      }
+      double z = orc_lse(x, m);
+      for (int64_t c = 0; c < m; ++c) {
+        double w = exp(x[c] - z);
+        for (int e = 0; e < q.d; ++e) o[e] += w * ld(v, r.kbase + key[c] * q.d + e, P->dtype);
+      }
+      if (lse) lse[t * q.G + h] = z;
+    }
+    free(key);
+    free(x);
+    free(qbuf);
+  }
+  return 0;
+}

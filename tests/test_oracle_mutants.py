@@ -55,6 +55,16 @@ MUTANTS = {
     "bsa-keeps-one-more": ("  int Kp = K - nf;\n  int take = Kp < nr ? Kp : nr;\n  for (int t = 0; t < nf; ++t) {",
                            "  int Kp = K - nf + 1;\n  int take = Kp < nr ? Kp : nr;\n  for (int t = 0; t < nf; ++t) {"),
     "bsa-forced-scored": ("    S[take + t].s = INFINITY;", "    S[take + t].s = bsa_score(r, F[t]);"),
+    "attn-causal-dropped": ('      if (hi > r.i + 1) hi = r.i + 1;\n      for (int64_t p = lo; p < hi; ++p) key[m++] = p;',
+                           '      for (int64_t p = lo; p < hi; ++p) key[m++] = p;'),
+    "attn-skips-block-0": ('      if (j < 0 || j > r.bq) continue;',
+                           '      if (j <= 0 || j > r.bq) continue;'),
+    "attn-scale-dropped": ('        x[c] = q.s * acc;',
+                          '        x[c] = acc;'),
+    "attn-values-are-keys": ('o[e] += w * ld(v, r.kbase',
+                            'o[e] += w * ld(k, r.kbase'),
+    "attn-unnormalised": ('        double w = exp(x[c] - z);',
+                         '        double w = exp(x[c] - x[0]);'),
 }
 
 

@@ -745,3 +745,114 @@ def test_bsa_checker_accepts_oracle_and_rejects_swaps():
         bad[t] = np.sort(bad[t])
     st = oracle.bsa_check(p, q, pyr, rows, bad, np.where(np.isinf(sc), sc, 0.0), tau=1e-3, rtol=1e3)
     assert np.all(st == 4)
+
+
+# ------------------------------------------------- block-sparse attention (consumer)
+# Each query attends the keys of its selected blocks ("Block Sparse Attention with
+# Log-Linear Complexity": agihunt.info opening paragraph; rcap.io first paragraphs).
+
+def _attn_inputs(seed, N, Hq, Hkv, d, K, B=1):
+    w = synth.custom(batch=B, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K, dtype=F32, seed=seed,
+                     needles=2)
+    q, k, _ = synth.make_inputs(w)
+    v = synth.make_values(w)
+    return oracle.Problem(B, N, Hq, Hkv, d, 64, K, 2, dtype=F32), q, k, v
+
+
+def test_attention_over_every_block_is_causal_attention():
+    # selecting every causal block reduces to dense causal attention (torch's fp64 routine)
+    import torch
+    N, d, K = 64 * 6 + 10, 16, 8
+    p, q, k, v = _attn_inputs(100, N, 2, 1, d, K)
+    idx = np.full((N, K), -1, dtype=np.int32)
+    for i in range(N):
+        b = i // 64
+        idx[i, :b + 1] = np.arange(b + 1)
+    out, lse = oracle.attention(p, q, k, v, idx)
+    qt = torch.from_numpy(q[0].astype(np.float64))
+    kt = torch.from_numpy(k[0].astype(np.float64)).expand(2, N, d)
+    vt = torch.from_numpy(v[0].astype(np.float64)).expand(2, N, d)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True, scale=p.s)
+    np.testing.assert_allclose(out.transpose(1, 0, 2), ref.numpy(), rtol=1e-10, atol=1e-12)
+    logits = p.s * torch.einsum("hid,hjd->hij", qt, kt)
+    logits = logits.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), -math.inf)
+    np.testing.assert_allclose(lse.T, torch.logsumexp(logits, dim=-1).numpy(), rtol=0, atol=1e-10)
+
+
+def test_attention_special_values():
+    N, d, K = 64 * 8, 16, 4
+    p, q, k, v = _attn_inputs(101, N, 2, 1, d, K)
+    idx = np.full((N, K), -1, dtype=np.int32)
+    for i in range(N):
+        b = i // 64
+        idx[i, :3] = sorted({0, max(b - 1, 0), b})[:3] + [-1] * (3 - len({0, max(b - 1, 0), b}))
+    # constant values: the output is that constant
+    vc = np.ascontiguousarray(np.broadcast_to(np.arange(d, dtype=np.float32), v.shape))
+    out, _ = oracle.attention(p, q, k, vc, idx)
+    np.testing.assert_allclose(out, np.broadcast_to(np.arange(d), out.shape), rtol=0, atol=1e-12)
+    # a query whose only visible key is its own: out = that value, lse = its scaled dot
+    one = np.full((1, K), -1, dtype=np.int32)
+    one[0, 0] = 3
+    out, lse = oracle.attention(p, q, k, v, one, rows=[64 * 3])
+    np.testing.assert_allclose(out[0], np.broadcast_to(v[0, 0, 64 * 3], (2, d)), rtol=0, atol=1e-12)
+    for r in range(2):
+        dot = p.s * float(q[0, r, 64 * 3].astype(np.float64) @ k[0, 0, 64 * 3].astype(np.float64))
+        assert abs(lse[0, r] - dot) < 1e-12
+
+
+def test_attention_ignores_order_padding_and_future_blocks():
+    N, d, K = 64 * 10, 16, 6
+    p, q, k, v = _attn_inputs(102, N, 4, 2, d, K, B=2)
+    rows = [64 * 7 + 5, N + 64 * 9 + 63, 3 * N + 100]
+    base = np.array([[0, 2, 5, 6, 7, -1], [0, 1, 4, 8, 9, -1], [0, 1, -1, -1, -1, -1]], dtype=np.int32)
+    o1, l1 = oracle.attention(p, q, k, v, base, rows=rows)
+    shuffled = np.array([[7, -1, 5, 0, 6, 2], [9, 8, -1, 4, 1, 0], [-1, 1, -1, 0, -1, -1]], dtype=np.int32)
+    o2, l2 = oracle.attention(p, q, k, v, shuffled, rows=rows)
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+    future = base.copy()
+    future[:, 5] = [8, 10, 3]  # blocks after the query's own are not attended (row 3: i = 100, b = 1)
+    future[2, 2] = 2
+    o3, l3 = oracle.attention(p, q, k, v, future, rows=rows)
+    np.testing.assert_allclose(o3, o1, rtol=0, atol=0)
+    np.testing.assert_allclose(l3, l1, rtol=0, atol=0)
+
+
+def test_attention_lse_and_weights_from_scipy():
+    N, d, K = 64 * 5, 16, 4
+    p, q, k, v = _attn_inputs(103, N, 2, 1, d, K)
+    i = 64 * 4 + 17
+    sel = np.array([[0, 2, 3, 4]], dtype=np.int32)
+    out, lse = oracle.attention(p, q, k, v, sel, rows=[i])
+    keys = [t for j in (0, 2, 3, 4) for t in range(64 * j, min(64 * j + 64, i + 1))]
+    for r in range(2):
+        x = p.s * (k[0, 0, keys].astype(np.float64) @ q[0, r, i].astype(np.float64))
+        z = float(logsumexp(x))
+        assert abs(lse[0, r] - z) < 1e-12
+        np.testing.assert_allclose(out[0, r], np.exp(x - z) @ v[0, 0, keys].astype(np.float64), rtol=1e-10,
+                                   atol=1e-12)
+
+
+def test_attention_on_the_selection_gqa_and_decode():
+    N, d, K = 4096 + 5, 16, 8
+    p, q, k, v = _attn_inputs(104, N, 4, 2, d, K, B=2)
+    pyr = oracle.build_pyramid(p, k)
+    rows = [(bh * N) + N - 1 for bh in range(4)]
+    idx, _ = oracle.select(p, q, k, pyr, rows=rows)
+    out, lse = oracle.attention(p, q, k, v, idx, rows=rows)
+    # each query head on its own (a one-head problem) gives that head's output
+    for t, row in enumerate(rows):
+        bh, i = divmod(row, N)
+        b, h = divmod(bh, 2)
+        for r in range(2):
+            p1 = oracle.Problem(1, N, 1, 1, d, 64, K, 2, dtype=F32)
+            q1 = np.ascontiguousarray(q[b:b + 1, 2 * h + r:2 * h + r + 1])
+            k1 = np.ascontiguousarray(k[b:b + 1, h:h + 1])
+            v1 = np.ascontiguousarray(v[b:b + 1, h:h + 1])
+            o1, l1 = oracle.attention(p1, q1, k1, v1, idx[t:t + 1], rows=[i])
+            np.testing.assert_allclose(o1[0, 0], out[t, r], rtol=0, atol=1e-12)
+    # decode = the last prefill row
+    qd = np.ascontiguousarray(q[:, :, N - 1, :])
+    od, ld = oracle.attention(p, qd, k, v, idx, decode=True)
+    np.testing.assert_array_equal(od, out)
+    np.testing.assert_array_equal(ld, lse)
