@@ -8,7 +8,8 @@ decode step (32 sequences x 262144-token cache, precomputed pyramid; cold: each 
 follows a 1 GiB write that evicts L2 and MALL; warm: back to back) with, beside it, the
 serving-loop step on growing caches (append one key per sequence, then the varlen decode
 selection), and the 256K step
-with the PISA-1 / PISA-2 routing scorers (ablations; extra fields), and the pyramid
+with the PISA-1 / PISA-2 routing scorers (ablations; extra fields), block-sparse attention
+over that step's selection (the consumer; extra field), and the pyramid
 selector against the full-scan BSA selector from 4K to 1M tokens (the pages'
 selection-kernel comparison at C=64, K=8, extended past 256K).
 
@@ -52,6 +53,7 @@ def parse():
     ap.add_argument("--no-64k", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bsa", action="store_true", help="skip the BSA full-scan crossover timings")
+    ap.add_argument("--no-attention", action="store_true", help="skip the block-sparse attention timing")
     ap.add_argument("--no-scorers", action="store_true",
                     help="skip the PISA-1 / PISA-2 ablation timings at 256K")
     ap.add_argument("--cpu-sample-rows", type=int, default=393216)
@@ -185,6 +187,30 @@ class Prefill:
                 stage[n].append(e[j].elapsed_time(e[j + 1]))
         total = [e[0].elapsed_time(e[6]) for e in evs]
         return wall_ms, {n: statistics.mean(v) for n, v in stage.items()}, statistics.median(total)
+
+    def attention(self, steps, warmup):
+        """Block-sparse attention over this step's own selection (values i.i.d. N(0, 1)):
+        time per call and the rate at which it moves key and value tiles (2 C d bf16 per
+        selected (query group, block) pair)."""
+        torch, pisa, w, p = self.torch, self.pisa, self.w, self.p
+        from block_selection_pyramid_amd import synth
+        v = dev(torch, synth.make_values(w))
+        self.step()
+        out = torch.empty_like(self.q)
+        lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device="cuda")
+        for _ in range(warmup):
+            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse)
+        b.record()
+        b.synchronize()
+        ms = a.elapsed_time(b) / steps
+        pairs = int((self.oi >= 0).sum().item())
+        tile_bytes = pairs * 2 * p.block * p.head_dim * 2
+        return {"ms": round(ms, 4), "pairs": pairs, "tile_GBps": round(tile_bytes / (ms * 1e-3) / 1e9, 1)}
 
     def work(self):
         """Algorithmic work of each stage for one step (see the design notes)."""
@@ -406,6 +432,9 @@ def main():
                 extra["prefill_256k_%s_stages_ms" % name] = {k: round(v, 4) for k, v in sms.items()}
                 log("256k %s: wall %.3f ms/step; stages %s" % (name, ws, extra["prefill_256k_%s_stages_ms" % name]))
             b.p = lse_p
+        if not a.no_attention:
+            extra["attention_256k"] = b.attention(a.steps, a.warmup)
+            log("256k attention: %s" % extra["attention_256k"])
         del b
         torch.cuda.empty_cache()
     if a.only in (None, "64k") and not a.no_64k:

@@ -273,6 +273,20 @@ int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* 
   return launch_decode(g, p->dtype, q, k_cache, pyramid, lengths, out_idx, out_score, (hipStream_t)stream);
 }
 
+int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, const void* k, const void* v,
+                          const int32_t* idx, void* out, float* lse, pisa_stream_t stream) {
+  Geo g;
+  int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (mode != PISA_PREFILL && mode != PISA_DECODE) return PISA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !idx || !out) return PISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned4(idx) || !aligned4(lse))
+    return PISA_ERR_INVALID_ARG;
+  rc = supported(g, p->dtype, mode);
+  if (rc != PISA_OK) return rc;
+  return launch_attention(g, p->dtype, q, k, v, idx, mode == PISA_DECODE, out, lse, (hipStream_t)stream);
+}
+
 int pisa_bsa_select_prefill(const pisa_problem* p, const void* q, const float* pyramid, int32_t* out_idx,
                             float* out_score, pisa_stream_t stream) {
   Geo g;

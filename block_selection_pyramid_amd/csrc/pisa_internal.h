@@ -51,6 +51,9 @@ inline int route_groups_per_wave(int G, int K) {
 
 // ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
+// block-sparse attention over selected blocks (decode != 0: one query per sequence at N-1)
+int launch_attention(const Geo& g, int dtype, const void* q, const void* k, const void* v, const int32_t* idx,
+                     int decode, void* out, float* lse, hipStream_t st);
 // full-scan BSA selection (bf16): out_idx / out_score [B, Hkv, N, K]
 int launch_bsa(const Geo& g, const void* q, const float* pyr, int32_t* out_idx, float* out_score, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);

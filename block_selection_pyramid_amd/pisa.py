@@ -83,7 +83,7 @@ _lib = None
 
 EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs", "pisa_select_decode",
-           "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen",
+           "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
            "pisa_status_string", "pisa_version")
 
 
@@ -112,6 +112,7 @@ def load(path: str | None = None):
     lib.pisa_bsa_select_prefill.argtypes = [P, vp, vp, vp, vp, vp]
     lib.pisa_append_keys.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, vp]
     lib.pisa_select_decode_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.pisa_sparse_attention.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_version.restype = ctypes.c_char_p
@@ -244,6 +245,31 @@ def select_decode_varlen(p: Problem, q: torch.Tensor, k_cache: torch.Tensor, pyr
     _check(load().pisa_select_decode_varlen(ctypes.byref(p.c()), qp, kp, pp, lp, ip, sp, _stream(stream)),
            "pisa_select_decode_varlen")
     return out_idx, out_score
+
+
+def sparse_attention(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                     decode: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                     want_lse: bool = True, stream=None):
+    """pisa_sparse_attention: returns (out [B, Hq, N, d] or [B, Hq, d] in q's dtype, lse fp32
+    [B, Hq, N] or [B, Hq], or None when want_lse is False)."""
+    qshape = (p.batch, p.n_q_heads, p.head_dim) if decode else (p.batch, p.n_q_heads, p.seq_len, p.head_dim)
+    ishape = (p.batch, p.n_kv_heads, p.top_k) if decode else (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+    kshape = (p.batch, p.n_kv_heads, p.seq_len, p.head_dim)
+    qp = _dev(q, "q", p.torch_dtype, qshape)
+    kp = _dev(k, "k", p.torch_dtype, kshape)
+    vp_ = _dev(v, "v", p.torch_dtype, kshape)
+    ip = _dev(idx, "idx", torch.int32, ishape)
+    if out is None:
+        out = torch.empty(qshape, dtype=p.torch_dtype, device=q.device)
+    op = _dev(out, "out", p.torch_dtype, qshape)
+    lp = None
+    if want_lse:
+        if lse is None:
+            lse = torch.empty(qshape[:-1], dtype=torch.float32, device=q.device)
+        lp = _dev(lse, "lse", torch.float32, qshape[:-1])
+    _check(load().pisa_sparse_attention(ctypes.byref(p.c()), DECODE if decode else PREFILL, qp, kp, vp_, ip, op, lp,
+                                        _stream(stream)), "pisa_sparse_attention")
+    return out, (lse if want_lse else None)
 
 
 def bsa_select_prefill(p: Problem, q: torch.Tensor, pyramid: torch.Tensor, out_idx: torch.Tensor | None = None,

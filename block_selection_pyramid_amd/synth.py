@@ -171,3 +171,32 @@ def add_block_offsets(w: Workload, k: np.ndarray, sigma: float) -> np.ndarray:
 def make_values(w: Workload) -> np.ndarray:
     """v [B, Hkv, N, d] (the values block-sparse attention reads), i.i.d. N(0, 1) like k."""
     return normal(w.seed, TENSOR_V, (w.batch, w.n_kv_heads, w.seq_len, w.head_dim), w.dtype)
+
+
+def random_selection(w: Workload, seed: int, pad: int = 0) -> np.ndarray:
+    """A valid selection of the kind the selectors return, drawn at random: int32
+    [B, Hkv, N, K] (decode: [B, Hkv, K], the query at N - 1) holding, per row, the existing
+    blocks of {0, b - 1, b} and min(K - |F|, b - 2) - pad distinct blocks of 1 .. b - 2,
+    ascending, then -1.  Feeds the attention tests without running a selector."""
+    rng = np.random.default_rng(seed)
+    K, C = w.top_k, w.block
+    nq = 1 if w.decode else w.seq_len
+    pos = np.full(nq, w.seq_len - 1) if w.decode else np.arange(w.seq_len)
+    b = np.tile(pos // C, w.batch * w.n_kv_heads).astype(np.int64)  # leaf block of each row
+    nf = np.where(b == 0, 1, np.where(b == 1, 2, 3))
+    m = np.clip(np.minimum(K - nf, b - 2) - pad, 0, None)
+    R, big = len(b), np.int64(1) << 40
+    # m distinct blocks of 1 .. b - 2 without rejection: sorted draws y_0 <= .. <= y_{m-1}
+    # from 0 .. b - 2 - m, then x_u = 1 + y_u + u (strictly increasing, at most b - 2)
+    room = np.maximum(b - 2 - m + 1, 1)[:, None]
+    y = (rng.random((R, K)) * room).astype(np.int64)
+    y = np.where(np.arange(K)[None, :] < m[:, None], y, big)
+    y.sort(axis=1)
+    picks = np.where(y < big, 1 + y + np.arange(K)[None, :], big)
+    forced = np.stack([np.zeros(R, np.int64), np.where(b >= 2, b - 1, big), np.where(b >= 1, b, big)], axis=1)
+    allv = np.concatenate([forced, picks], axis=1)
+    allv.sort(axis=1)
+    allv = allv[:, :K]
+    out = np.where(allv < big, allv, -1).astype(np.int32)
+    shape = (w.batch, w.n_kv_heads, K) if w.decode else (w.batch, w.n_kv_heads, nq, K)
+    return out.reshape(shape)

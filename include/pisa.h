@@ -215,6 +215,24 @@ int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* 
                               const int32_t* lengths, int32_t* out_idx, float* out_score, pisa_stream_t stream);
 
 /*
+ * Block-sparse attention over a selection, the consumer the selector feeds
+ * ("Block Sparse Attention with Log-Linear Complexity": agihunt.info summary, opening
+ * paragraph: each query reads only its Top-K tiles of C keys; rcap.io explainer, first
+ * paragraphs: attention then runs over the original keys of the picked blocks).  For every
+ * query head hq of KV head h and position i (mode PISA_PREFILL: q [B, Hq, N, d], idx
+ * [B, Hkv, N, K], out [B, Hq, N, d], lse [B, Hq, N]; mode PISA_DECODE: the query at N-1,
+ * q [B, Hq, d], idx [B, Hkv, K], out [B, Hq, d], lse [B, Hq]):
+ *   out = sum_t softmax_t(s * <q, k_t>) v_t,   lse = log sum_t exp(s * <q, k_t>),
+ * over the keys t <= i of the blocks idx[b, h, i, 0..K) (shared by the G heads of the
+ * group; entries < 0 or after the query's own block are skipped; entries must be distinct,
+ * as pisa_select_* produce them).  k and v [B, Hkv, N, d] of q's dtype; out has q's dtype
+ * (bf16 rounded to nearest even from fp32 accumulation); lse fp32, may be NULL.  A row
+ * with no attended key gets out = 0, lse = -inf.  No workspace.
+ */
+int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, const void* k, const void* v,
+                          const int32_t* idx, void* out, float* lse, pisa_stream_t stream);
+
+/*
  * Full-scan BSA selection for every query position, the baseline the pyramid selector is
  * timed against ("Block Sparse Attention with Log-Linear Complexity": agihunt.info
  * summary, opening and baselines paragraphs; rcap.io explainer, picking-step and

@@ -558,3 +558,85 @@ def test_decode_steps_with_appends(env):
             op, qb, kb, opyr = _oracle_decode_rows(kw, q, k, new, b)
             verify(op, qb, kb, opyr, np.arange(Hkv), idx[b], sc[b], decode=True, what="step%d-seq%d" % (s, b))
         lengths = new
+
+
+# ------------------------------------------------- block-sparse attention (consumer)
+# Tolerance derived from the arithmetic: fp32 accumulation over <= K*C keys (~1e-6
+# relative), then bf16 output rounding to nearest even (<= 2^-8 relative); lse stays fp32.
+ATT_TOL = {synth.BF16: (2.0 ** -8 + 1e-5, 1e-4), synth.F32: (1e-5, 1e-5)}
+
+
+def attn_verify(op, q, k, v, idx, rows, out, lse, decode, dt, what):
+    ref, rlse = oracle.attention(op, q, k, v, idx.reshape(-1, op.top_k)[rows], rows=rows, decode=decode)
+    G, d = op.group, op.head_dim
+    go = out.reshape(op.batch, op.n_kv_heads, G, -1, d)
+    gl = lse.reshape(op.batch, op.n_kv_heads, G, -1)
+    nq = 1 if decode else op.seq_len
+    got = np.empty_like(ref)
+    glse = np.empty_like(rlse)
+    for t, row in enumerate(rows):
+        bh, i = divmod(int(row), nq)
+        b, h = divmod(bh, op.n_kv_heads)
+        got[t] = go[b, h, :, i, :]
+        glse[t] = gl[b, h, :, i]
+    rtol, atol = ATT_TOL[dt]
+    err = np.abs(got - ref) - (atol + rtol * np.abs(ref))
+    lerr = np.abs(glse - rlse) - 1e-4 * np.maximum(1.0, np.abs(rlse))
+    log(what, "attention rows=%d max|out err|=%.3g max|lse err|=%.3g" % (
+        len(rows), np.abs(got - ref).max(), np.abs(glse - rlse).max()))
+    assert err.max() <= 0, "%s: out outside tolerance (worst excess %.3g)" % (what, err.max())
+    assert lerr.max() <= 0, "%s: lse outside tolerance" % what
+
+
+def to_f32(a, dt):
+    return synth.bf16_bits_to_f32(a) if dt == synth.BF16 else a
+
+
+ATT_CASES = [
+    # name, N, Hq, Hkv, d, K, dtype, B, decode, source of the selection
+    ("4k-G4-oracle-sel", 4096, 16, 4, 128, 8, synth.BF16, 1, False, "oracle"),
+    ("ragged-G2-f32", 3000 + 17, 4, 2, 64, 6, synth.F32, 2, False, "random"),
+    ("G16-d64-padded", 2048 + 9, 16, 1, 64, 7, synth.BF16, 1, False, "random-pad"),
+    ("G1-K32", 5000, 2, 2, 128, 32, synth.BF16, 1, False, "random"),
+    ("decode-G4", 9000, 8, 2, 128, 8, synth.BF16, 3, True, "oracle"),
+    ("decode-f32-G8", 777, 8, 1, 64, 4, synth.F32, 2, True, "random"),
+]
+
+
+@pytest.mark.parametrize("case", ATT_CASES, ids=[c[0] for c in ATT_CASES])
+def test_sparse_attention_parity(env, case):
+    torch, pisa = env
+    name, N, Hq, Hkv, d, K, dt, B, decode, src = case
+    w = synth.custom(name=name, batch=B, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K, dtype=dt,
+                     seed=1500 + N, needles=6, decode=decode)
+    p, op = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    v = synth.make_values(w)
+    if src == "oracle":
+        idx, _ = oracle.select(op, q, k, decode=decode)  # the oracle's own selection
+        idx = idx.reshape((B, Hkv, K) if decode else (B, Hkv, N, K))
+    else:
+        idx = synth.random_selection(w, 7, pad=2 if src == "random-pad" else 0)
+    log(name, "attention N=%d B=%d Hq=%d Hkv=%d d=%d K=%d decode=%d: launching" % (N, B, Hq, Hkv, d, K, decode))
+    out, lse = pisa.sparse_attention(p, dev(torch, q), dev(torch, k), dev(torch, v),
+                                     torch.from_numpy(np.ascontiguousarray(idx)).cuda(), decode=decode)
+    torch.cuda.synchronize()
+    o = out.float().cpu().numpy() if dt == synth.BF16 else out.cpu().numpy()
+    rows = np.arange(B * Hkv * (1 if decode else N))
+    attn_verify(op, q, k, v, idx, rows, o, lse.cpu().numpy(), decode, dt, "attn-" + name)
+
+
+def test_sparse_attention_256k_sampled(env):
+    # the full-size workload in bench.py's launch configuration, on a random valid selection
+    torch, pisa = env
+    w = synth.WORKLOADS["256k"]
+    p, op = problems(pisa, w)
+    q, k, needles = synth.make_inputs(w)
+    v = synth.make_values(w)
+    idx = synth.random_selection(w, 11)
+    log("256k", "attention: launching")
+    out, lse = pisa.sparse_attention(p, dev(torch, q), dev(torch, k), dev(torch, v), torch.from_numpy(idx).cuda())
+    torch.cuda.synchronize()
+    rows = sample_rows(w, needles, 1500, 19)
+    attn_verify(op, q, k, v, idx, rows, out.float().cpu().numpy(), lse.cpu().numpy(), False, synth.BF16,
+                "attn-256k")
