@@ -77,7 +77,8 @@ __device__ __forceinline__ void finalize_row(int leaf, float sc, const int* F, i
   const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   const uint64_t my = leaf >= 0 ? (((uint64_t)ord << 32) | (uint32_t)(~(uint32_t)leaf)) : 0ull;
   int rank = 0;
-  for (int y = 0; y < twoK; ++y) {
+#pragma unroll 8
+  for (int y = 0; y < twoK; ++y) {  // unrolled: the lane reads go out together
     const uint64_t oy = __shfl(my, y);
     rank += oy > my;
   }
@@ -85,6 +86,7 @@ __device__ __forceinline__ void finalize_row(int leaf, float sc, const int* F, i
   // ascending output position: selected entries (kept or forced) with a smaller index
   const int fj = lane < nf ? (lane == 0 ? F[0] : (lane == 1 ? F[1] : F[2])) : 0x7fffffff;
   int pos = 0, pf = 0;
+#pragma unroll 8
   for (int y = 0; y < twoK; ++y) {
     const int oy = __shfl(leaf, y);
     const int ky = __shfl(kept, y);

@@ -12,7 +12,8 @@
 // the top pyramid levels' routing copy in LDS (one parallel burst); wavefront 0 then walks
 // the pyramid for the new query at position N-1, its top levels from LDS; then every
 // wavefront scores one of the <= 2K + 3 candidate and forced tiles (so their loads are in
-// flight together), and wavefront 0 writes the selection.  One launch per step.  With
+// flight together; bf16 on the matrix cores, 16 keys x 32 dims per MFMA against the G
+// head columns), and wavefront 0 writes the selection.  One launch per step.  With
 // per-sequence lengths each workgroup first re-derives its sequence's level table in LDS
 // (node offsets stay those of the capacity layout that pisa_append_keys maintains).
 #include <type_traits>
@@ -153,11 +154,23 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
   }
   __syncthreads();
   const T* keys = k + (int64_t)bh * kstride * D;
-  for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
-    const int j = tj[t];
-    if (j < 0) continue;
-    const float s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
-    if (lane == 0) tsc[t] = s;
+  if constexpr (std::is_same<T, bf16>::value) {
+    // every wavefront scores its tiles on the matrix cores with its own query fragments
+    MfmaWalk<D, G, 1> tw;
+    tw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
+    for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
+      const int j = tj[t];
+      if (j < 0) continue;
+      const float s = score_tile_mfma<D, G>(keys, j, i, geo.N, geo.C, tw.qb[0], lane, geo.s, geo.s_log2e);
+      if (lane == 0) tsc[t] = s;
+    }
+  } else {
+    for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
+      const int j = tj[t];
+      if (j < 0) continue;
+      const float s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
+      if (lane == 0) tsc[t] = s;
+    }
   }
   __syncthreads();
   if (wave == 0) {

@@ -54,7 +54,8 @@ __global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict
 // walks levels l_x .. 2 by per-query gathers of the child summaries from the routing copy
 // (these levels are too wide to score densely: level 2's children are the leaf-block
 // means), keeping the Top-K per level, then writes the leaf candidates that are not forced
-// blocks.  Workgroup w
+// blocks.  The gathers read the hi halves only and re-score exactly just the candidates
+// whose error bounds leave their membership open (MfmaWalk::walk_levels<true>).  Workgroup w
 // serves (b, h) = w mod (B*Hkv), so the workgroups of one XCD (w mod 8) share few heads
 // and gather from an L2-sized part of the routing copy.
 template <int D, int G, int GPW>
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
       } else {
         nx = mw.init_level(geo, bq, 2, w, lane);
       }
-      nx = mw.walk_levels(geo, bq, geo.L >= 3 ? l_x : 2, 2, nx, w, lane);
+      nx = mw.template walk_levels<true>(geo, bq, geo.L >= 3 ? l_x : 2, 2, nx, w, lane);
     } else {
       nx = mw.init_level(geo, bq, 1, w, lane);
     }

@@ -53,7 +53,17 @@ template <int GPW>
 struct WalkLdsM {
   int32_t X[kMaxCand];   // GPW groups x (64 / GPW) candidate slots
   uint64_t key[kMaxCand];
+  // bounded-approximation walk (walk_levels<true>): approximate scores and their error
+  // bounds, candidate classes, and the uncertain candidates re-scored exactly
+  float sc[kMaxCand], er[kMaxCand];
+  int32_t cls[kMaxCand], U[kMaxCand];
+  uint64_t key2[kMaxCand];
 };
+
+// |lo| <= 2^-8 (1 + 2^-8) |hi| elementwise for hi = v rounded to nearest in bf16 and
+// lo = v - hi rounded again, so |q.lo| <= this factor times |q|.|hi| (with slack for the
+// fp32 accumulation of that product).
+constexpr float kLoBound = 0.00393677f;  // 2^-8 (1 + 2^-7)
 
 // One wavefront walks GPW query groups (consecutive queries of one (b, h), hence one
 // leaf block and one visible pyramid) at once.  Scoring: v_mfma_f32_16x16x32_bf16 with
@@ -106,9 +116,9 @@ struct MfmaWalk {
   // rows are masked to -inf in the epilogue, so the loads need no branches.
   static constexpr int TB = GPW == 1 ? 2 : 1;  // tiles per batch
 
-  template <bool kLds>
+  template <bool kLds, bool kLo>
   __device__ __forceinline__ void load_batch(const Geo& geo, const bf16* Rc, const char* Lc, int bq, int l,
-                                             int nx, int t0, const WalkLdsM<GPW>* w, int lane,
+                                             int nx, int t0, const int32_t* Xs, int lane,
                                              bf16x8 (&hi)[GPW][TB][KS], bf16x8 (&lo)[GPW][TB][KS]) const {
     const int nchild = geo.n[l - 1];
     const int cshift = l - 2;
@@ -120,7 +130,7 @@ struct MfmaWalk {
       for (int tb = 0; tb < TB; ++tb) {
         const int cs = 16 * (t0 + tb) + m;
         const int xa = cs >> 1;
-        const int na = xa < nx ? w->X[g * CW + xa] : -1;
+        const int na = xa < nx ? Xs[g * CW + xa] : -1;
         const int c = na >= 0 ? 2 * na + (cs & 1) : -1;
         ca[g][tb] = child_visible(c, nchild, cshift, bq) ? c : 0;
       }
@@ -135,22 +145,26 @@ struct MfmaWalk {
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s);
-            lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
+            if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
           }
         } else {
           const bf16* rp = Rc + (int64_t)ca[g][tb] * 2 * D + 8 * kg;
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s);
-            lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s + 32);
+            if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s + 32);
           }
         }
       }
   }
 
-  // Scores candidates X[g*CW + 0..nx) of level l (>= 2) into key[].
-  template <bool kLds>
-  __device__ void score_t(const Geo& geo, int bq, int l, int nx, WalkLdsM<GPW>* w, int lane) const {
+  // Scores candidates Xs[g*CW + 0..nx) of level l (>= 2) into keys[].  kApprox: from the
+  // hi halves only, also writing each candidate's approximate score to sc[] and a bound on
+  // its distance from the hi + lo score to er[] (the MFMA of |hi| against |q| takes the
+  // place of the lo one, and the lo halves are not read).
+  template <bool kLds, bool kApprox>
+  __device__ void score_t(const Geo& geo, int bq, int l, int nx, const int32_t* Xs, uint64_t* keys, float* sc,
+                          float* er, int lane) const {
     const bf16* Rc = R + (int64_t)geo.off[l - 1] * 2 * D;
     const char* Lc = kLds ? lds + (int64_t)(geo.off[l - 1] - stage_base) * kRecLds : nullptr;
     const int nchild = geo.n[l - 1];
@@ -160,43 +174,69 @@ struct MfmaWalk {
     const int ntiles = (2 * nx + 15) >> 4;
     for (int t0 = 0; t0 < ntiles; t0 += TB) {
       bf16x8 hi[GPW][TB][KS], lo[GPW][TB][KS];
-      load_batch<kLds>(geo, Rc, Lc, bq, l, nx, t0, w, lane, hi, lo);
+      load_batch<kLds, !kApprox>(geo, Rc, Lc, bq, l, nx, t0, Xs, lane, hi, lo);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int t = t0 + tb;
         if (t >= ntiles) break;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < GPW; ++g)
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[g][tb][s], qb[g][s], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[g][tb][s], qb[g][s], acc, 0, 0, 0);
+            if constexpr (kApprox) {
+              // |hi| and |q|: clear the bf16 sign bits (|q| formed at each use: keeping it
+              // for the whole walk would cost a wavefront per SIMD)
+              u32x4 qa = __builtin_bit_cast(u32x4, qb[g][s]);
+              asm volatile("" : "+v"(qa));
+              qa &= 0x7FFF7FFFu;
+              const u32x4 ha = __builtin_bit_cast(u32x4, hi[g][tb][s]) & 0x7FFF7FFFu;
+              acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ha),
+                                                             __builtin_bit_cast(bf16x8, qa), acc2, 0, 0, 0);
+            } else {
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[g][tb][s], qb[g][s], acc, 0, 0, 0);
+            }
           }
-        float lse[2];
+        float lse[2], err[2];
         int node[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           const int x = 8 * t + 2 * kg + p;  // candidate owning child rows 4kg + 2p, +1
-          node[p] = (gown < GPW && x < nx) ? w->X[gown * CW + x] : -1;
-          float y[2];
+          node[p] = (gown < GPW && x < nx) ? Xs[gown * CW + x] : -1;
+          float y[2], bnd[2];
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int ch = node[p] >= 0 ? 2 * node[p] + c : -1;
-            y[c] = child_visible(ch, nchild, cshift, bq) ? acc[2 * p + c] : -INFINITY;
+            const bool vis = child_visible(ch, nchild, cshift, bq);
+            y[c] = vis ? acc[2 * p + c] : -INFINITY;
+            bnd[c] = vis ? acc2[2 * p + c] : 0.f;
           }
           const float a = fmaxf(y[0], y[1]), b = fminf(y[0], y[1]);
           const float v = geo.scorer == PISA_LSE ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a))
                                                  : pair_trunc(a, b, 1.f, trunc_c2(geo.scorer, true));
           lse[p] = node[p] >= 0 ? v : 0.f;
+          // the pair LSE moves by at most the larger child error; 2^-20 |score| more covers
+          // the differing fp32 rounding of the two evaluations
+          err[p] = node[p] >= 0 ? kLoBound * fmaxf(bnd[0], bnd[1]) + 9.6e-7f * fabsf(v) : 0.f;
         }
         lse[0] = group_sum<G>(lse[0]);
         lse[1] = group_sum<G>(lse[1]);
+        if constexpr (kApprox) {
+          err[0] = group_sum<G>(err[0]);
+          err[1] = group_sum<G>(err[1]);
+        }
         if (r == 0 && gown < GPW) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const int x = 8 * t + 2 * kg + p;
-            if (x < nx) w->key[gown * CW + x] = node[p] >= 0 ? cand_key(lse[p], node[p]) : 0ull;
+            if (x < nx) {
+              keys[gown * CW + x] = node[p] >= 0 ? cand_key(lse[p], node[p]) : 0ull;
+              if constexpr (kApprox) {
+                sc[gown * CW + x] = lse[p];
+                er[gown * CW + x] = err[p];
+              }
+            }
           }
         }
       }
@@ -204,11 +244,13 @@ struct MfmaWalk {
     wave_sync();
   }
 
-  __device__ void score(const Geo& geo, int bq, int l, int nx, WalkLdsM<GPW>* w, int lane) const {
+  template <bool kApprox>
+  __device__ void score(const Geo& geo, int bq, int l, int nx, const int32_t* Xs, uint64_t* keys, float* sc,
+                        float* er, int lane) const {
     if (l - 1 >= stage_lo)
-      score_t<true>(geo, bq, l, nx, w, lane);
+      score_t<true, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
     else
-      score_t<false>(geo, bq, l, nx, w, lane);
+      score_t<false, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
   }
 
   // Fills X with the visible nodes of level `l` (a prefix of the level) and returns nx.
@@ -223,18 +265,68 @@ struct MfmaWalk {
   // Walks levels l_top down to l_bot (>= 2): score, keep Top-K, expand.  X must hold the
   // candidates of level l_top (nx slots per group).  On return X[g*CW + 0..nx) holds the
   // candidates of level l_bot - 1 and the function returns their slot count (<= 2K).
+  //
+  // kApprox (LSE scorer only): each level is first scored from the hi halves with error
+  // bounds (score_t<., true>).  A candidate is surely kept when fewer than K others could
+  // score above it within the bounds, surely dropped when K others surely score above it,
+  // and uncertain otherwise; only the uncertain ones are scored again exactly (hi + lo),
+  // and the K - (surely kept) best of them by exact score are kept.  The kept set is the
+  // one exact scoring gives, at about half the gathered bytes.
+  template <bool kApprox = false>
   __device__ int walk_levels(const Geo& geo, int bq, int l_top, int l_bot, int nx, WalkLdsM<GPW>* w,
                              int lane) const {
     const int K = geo.K;
     const int gl = lane / CW, xl = lane % CW;
     int* Xg = w->X + gl * CW;
+    const bool approx = kApprox && geo.scorer == PISA_LSE;
     for (int l = l_top; l >= l_bot; --l) {
-      score(geo, bq, l, nx, w, lane);
       const uint64_t* kg = w->key + gl * CW;
-      const uint64_t my = xl < nx ? kg[xl] : 0ull;
-      const int myid = xl < nx ? Xg[xl] : -1;
+      uint64_t my;
       int rank = 0;
-      for (int y = 0; y < nx; ++y) rank += kg[y] > my;
+      if (approx) {
+        score<true>(geo, bq, l, nx, w->X, w->key, w->sc, w->er, lane);
+        const float* sg = w->sc + gl * CW;
+        const float* eg = w->er + gl * CW;
+        my = xl < nx ? kg[xl] : 0ull;
+        const float lo_x = xl < nx ? sg[xl] - eg[xl] : 0.f, up_x = xl < nx ? sg[xl] + eg[xl] : 0.f;
+        int may = 0, sure = 0;  // others that may / surely score above this candidate
+        for (int y = 0; y < nx; ++y) {
+          if (y == xl || kg[y] == 0ull) continue;
+          may += sg[y] + eg[y] >= lo_x;
+          sure += sg[y] - eg[y] > up_x;
+        }
+        const int cls = my == 0ull ? -1 : (may < K ? 2 : (sure >= K ? 0 : 1));
+        const unsigned long long unc = __ballot(cls == 1);
+        if (unc) {
+          // compact each group's uncertain candidates and score them exactly
+          const unsigned long long gm = (GPW == 1) ? ~0ull : (((1ull << CW) - 1ull) << (gl * CW));
+          const int pos = (int)__popcll(unc & gm & ((1ull << lane) - 1ull));
+          int nu = 0;
+#pragma unroll
+          for (int g = 0; g < GPW; ++g) {
+            const unsigned long long gmg = (GPW == 1) ? ~0ull : (((1ull << CW) - 1ull) << (g * CW));
+            nu = max(nu, (int)__popcll(unc & gmg));
+          }
+          w->U[lane] = -1;
+          wave_sync();
+          if (cls == 1) w->U[gl * CW + pos] = Xg[xl];
+          wave_sync();
+          score<false>(geo, bq, l, nu, w->U, w->key2, nullptr, nullptr, lane);
+          if (cls == 1) my = w->key2[gl * CW + pos];
+        }
+        w->cls[lane] = cls;
+        wave_sync();
+        w->key[lane] = xl < nx ? my : 0ull;
+        wave_sync();
+        const int32_t* cg = w->cls + gl * CW;
+        for (int y = 0; y < nx; ++y) rank += cg[y] > cls || (cg[y] == cls && kg[y] > my);
+      } else {
+        score<false>(geo, bq, l, nx, w->X, w->key, nullptr, nullptr, lane);
+        my = xl < nx ? kg[xl] : 0ull;
+#pragma unroll 8
+        for (int y = 0; y < nx; ++y) rank += kg[y] > my;  // unrolled: the LDS reads go out together
+      }
+      const int myid = xl < nx ? Xg[xl] : -1;
       const unsigned long long live = __ballot(my != 0ull);
       int nkg = 0, nmax = 0;
 #pragma unroll
@@ -267,6 +359,53 @@ struct MfmaWalk {
     return geo.L == 1 ? nx : walk_levels(geo, bq, geo.L, 2, nx, w, lane);
   }
 };
+
+// Leaf score of tile j for one query group on the matrix cores (decode): A = 16 raw keys
+// x 32 dims of the tile (bf16 inputs are exact), B = the group's G head columns in the
+// MfmaWalk<D, G, 1> layout (column n = head n; k-step s, lane group kg = lane >> 4 <-> dims
+// 32s + 8kg .. +8; columns >= G are zero), four row blocks of 16 keys.  Lane l then holds
+// head l & 15 for keys 16rb + 4(l >> 4) + v.  Returns the head-summed causal LSE over the
+// keys t <= i (t < N) of the block, in natural units, in every lane.
+template <int D, int G>
+__device__ __forceinline__ float score_tile_mfma(const bf16* __restrict__ keys, int j, int i, int N, int C,
+                                                 const bf16x8 (&qb)[D / 32], int lane, float s, float s_log2e) {
+  constexpr int KS = D / 32;
+  const int m = lane & 15, kg = lane >> 4;
+  bf16x8 a[4][KS];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int t = min(j * C + 16 * rb + m, N - 1);  // rows past N read a real key; masked below
+#pragma unroll
+    for (int k = 0; k < KS; ++k) a[rb][k] = *reinterpret_cast<const bf16x8*>(keys + (int64_t)t * D + 32 * k + 8 * kg);
+  }
+  f32x4 acc[4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KS; ++k) acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb][k], qb[k], acc[rb], 0, 0, 0);
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int t = j * C + 16 * rb + 4 * kg + v;
+      if (t > i || t >= N) acc[rb][v] = -INFINITY;
+      mx = fmaxf(mx, acc[rb][v]);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));  // key jC <= i is live, so mx is finite
+  float sum = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f((acc[rb][v] - mx) * s_log2e);
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  const float lse = group_sum<G>(s * mx + logf(sum));  // lanes 0 .. G-1: the group's heads
+  return __shfl(lse, 0);
+}
 
 // ---------------------------------------------------------------- VALU scorer
 template <int D, int G>
