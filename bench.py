@@ -316,6 +316,7 @@ def time_decode(torch, pisa, synth, steps):
     b.record()
     b.synchronize()
     vwarm = a.elapsed_time(b) * 1e3 / steps
+
     return statistics.median(cold), warm, statistics.median(vcold), vwarm
 
 

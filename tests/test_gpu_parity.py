@@ -640,3 +640,49 @@ def test_sparse_attention_256k_sampled(env):
     rows = sample_rows(w, needles, 1500, 19)
     attn_verify(op, q, k, v, idx, rows, out.float().cpu().numpy(), lse.cpu().numpy(), False, synth.BF16,
                 "attn-256k")
+
+
+def test_decode_step_graph_replays_match_eager(env):
+    # a serving step (append one key per sequence, then the varlen selection) captured in a
+    # HIP graph: every replay, with eager work and synchronisations in between, must give
+    # the eager step's bits (the path records no memset nodes)
+    torch, pisa = env
+    lengths = [5000, 700, 9000, 65]
+    B, G, Hkv, d, K, cap = len(lengths), 4, 2, 128, 8, 9001
+    w = synth.custom(name="graph", batch=B, seq_len=cap, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     seed=321, needles=6, decode=True)
+    q, k, _ = synth.make_inputs(w)
+    p = pisa.Problem(B, cap, G * Hkv, Hkv, d, 64, K, 2)
+    qd, kd = dev(torch, q), dev(torch, k)
+    old = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    new = old + 1
+    pyr_e = torch.zeros(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+    pisa.append_keys(p, kd, torch.zeros_like(old), old, max(lengths), pyr_e)
+    pyr_g = pyr_e.clone()
+    oi_e = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+    os_e = torch.empty((B, Hkv, K), dtype=torch.float32, device="cuda")
+    pisa.append_keys(p, kd, old, new, 1, pyr_e)
+    pisa.select_decode_varlen(p, qd, kd, pyr_e, new, oi_e, os_e)
+    torch.cuda.synchronize()
+    oi_g, os_g = torch.empty_like(oi_e), torch.empty_like(os_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm the launch path once outside the capture
+        pisa.append_keys(p, kd, old, new, 1, pyr_g)
+        pisa.select_decode_varlen(p, qd, kd, pyr_g, new, oi_g, os_g)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pisa.append_keys(p, kd, old, new, 1, pyr_g)
+        pisa.select_decode_varlen(p, qd, kd, pyr_g, new, oi_g, os_g)
+    for rep in range(4):
+        oi_g.fill_(-7)
+        os_g.fill_(0.5)
+        graph.replay()
+        torch.cuda.synchronize()
+        log("graph", "replay %d" % rep)
+        assert torch.equal(oi_g, oi_e) and torch.equal(os_g.view(torch.int32), os_e.view(torch.int32)), rep
+        assert torch.equal(pyr_g.view(torch.int32), pyr_e.view(torch.int32)), rep
+        junk = torch.randn(1 << 20, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
