@@ -372,6 +372,38 @@ def crossover(torch, pisa, synth, steps, warmup):
     return out
 
 
+def extra_rooflines(extra):
+    """Roofline fractions of the rows timed beside the headline (algorithmic work per
+    launch in the design notes): the full scan at 256K (MFMA: every causal block's summary
+    dot, counted once although hi and lo are both contracted), block-sparse attention at
+    256K (MFMA: the selected keys' score and value products; its unique bytes are far
+    below the HBM roof), and the 32 x 256K decode step (HBM: the walk's node gathers plus
+    the scored key tiles and the query rows)."""
+    out = {}
+    N, Hkv, G, d, C, K = 262144, 4, 4, 128, 64, 8
+    cross = extra.get("crossover_c64_k8", {}).get(str(N))
+    if cross:
+        blocks = int(((np.arange(N) // C) + 1).sum())
+        flops = Hkv * blocks * G * 2 * d
+        ach = flops / (cross["bsa_ms"] * 1e-3) / 1e12
+        out["bsa_256k"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    att = extra.get("attention_256k")
+    if att:
+        flops = att["pairs"] * C * G * d * 4  # score and value products, 2 flops each
+        ach = flops / (att["ms"] * 1e-3) / 1e12
+        out["attention_256k"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    dec = extra.get("decode_us_per_step")
+    if dec:
+        units, L = 32 * Hkv, 9
+        per_unit = (L - 1) * 2 * K * 4 * d + (2 * K + 3) * C * d * 2 + G * d * 2
+        ach = units * per_unit / (dec * 1e-6) / 1e9
+        out["decode_cold"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(ach / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def cpu_baseline(synth, sample_rows):
     import oracle
     w = synth.WORKLOADS["256k"]
@@ -457,6 +489,7 @@ def main():
         torch.cuda.empty_cache()
     if a.only in (None, "bsa") and not a.no_bsa:
         extra["crossover_c64_k8"] = crossover(torch, pisa, synth, a.steps, a.warmup)
+    extra["rooflines"] = extra_rooflines(extra)
     if head is None:
         print(json.dumps(extra))
         return
