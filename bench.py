@@ -198,13 +198,14 @@ class Prefill:
         self.step()
         out = torch.empty_like(self.q)
         lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device="cuda")
+        aws = torch.empty(max(pisa.attention_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
         for _ in range(warmup):
-            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse)
+            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse, ws=aws)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
-            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse)
+            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse, ws=aws)
         b.record()
         b.synchronize()
         ms = a.elapsed_time(b) / steps

@@ -15,6 +15,67 @@ namespace pisa {
 // = keys): 8 (v / 4) + 4 hh + (v mod 4).
 __device__ __forceinline__ int key_row(int v, int hh) { return 8 * (v >> 2) + 4 * hh + (v & 3); }
 
+// ---- key tiles on the matrix cores (v_mfma_f32_32x32x16_bf16, wave64): lane l supplies
+// row (l & 31) of A and column (l & 31) of B, each with the 8 consecutive k of group
+// (l >> 5); its 16 results are column (l & 31), rows key_row(v, l >> 5).  The head
+// dimension is walked as k-step s, group hh -> dims 16s + 8hh .. +8 for A and B alike.
+
+// Stages rows [row0, row0 + 64) of one (b,h)'s keys into LDS (zero past N).
+template <int D>
+__device__ __forceinline__ void stage_tile(const bf16* __restrict__ kb, int row0, int N, bf16* kt) {
+  constexpr int LDSR = D + 8;
+  constexpr int TPR = D / 8;
+  for (int t = threadIdx.x; t < kLeaf * TPR; t += 256) {
+    const int r = t / TPR, c = (t % TPR) * 8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row0 + r < N) v = *reinterpret_cast<const uint4*>(kb + (int64_t)(row0 + r) * D + c);
+    *reinterpret_cast<uint4*>(kt + r * LDSR + c) = v;
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// B fragments of one query row for v_mfma_f32_32x32x16_bf16: k-step s, lane half
+// hh = lane >> 5 <-> dims 16s + 8hh .. +8 (the two lanes of a column read 32 contiguous
+// bytes of its query row per load).
+template <int D>
+__device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool valid, int hh, bf16x8* bq) {
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (valid) {
+      bq[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
+    }
+  }
+}
+
+// 64 keys (LDS tile, two M-tiles of 32) x 32 columns: acc0/acc1[v] of lane l hold keys
+// key_row(v, l >> 5) and 32 + key_row(v, l >> 5) against column l & 31.
+template <int D>
+__device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, int lane, f32x16& acc0,
+                                            f32x16& acc1) {
+  constexpr int LDSR = D + 8;
+  constexpr int KS = D / 16;
+  const int col = lane & 31, hh = lane >> 5;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    acc0[v] = 0.f;
+    acc1[v] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + 16 * s + 8 * hh);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + 16 * s + 8 * hh);
+    acc0 = mfma32(a0, bq[s], acc0);
+    acc1 = mfma32(a1, bq[s], acc1);
+  }
+}
+
 // LSE over the 64 keys of this lane's column (32 here, 32 in lane l ^ 32), in units of
 // the scaled dot product.  Masked keys hold -inf; at least one key is live.
 __device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {

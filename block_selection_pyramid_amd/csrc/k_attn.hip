@@ -13,6 +13,7 @@
 // the end.  Every (query group, block) pair reads its key and value tiles (2 C d elements),
 // which is the pass's traffic: there is no reuse between query groups that picked the same
 // block.
+#include "final_dev.h"
 #include "route_dev.h"
 
 namespace pisa {
@@ -170,10 +171,281 @@ int attn_g(const Geo& g, const void* q, const void* k, const void* v, const int3
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
+// ---- key-major form (bf16 prefill) ----
+//
+// The (query group, selected block) pairs are sorted by block (counting sort, as for the
+// leaf scores), so each block's key and value tiles are staged in LDS once per chunk of
+// 128/G pairs instead of being gathered for every pair.  Per chunk, on
+// v_mfma_f32_32x32x16_bf16: S = K Q^T (rows = 64 keys, columns = 32 (pair, head) per
+// wavefront), the block softmax in registers, then O = P^T V with the keys of each k-step
+// taken in the order the lane already holds its probabilities (k-step s, lane half hh,
+// element e <-> key 32 (s >> 1) + 16 (s & 1) + 8 (e >> 2) + 4 hh + (e & 3)), the value tile
+// staged transposed so that those keys are two 8-byte LDS reads.  Each pair writes its
+// block-normalised output (bf16) and log2-sum-exp; one wavefront per query group then
+// merges its K partials.
+
+// Candidate array of the pairs (per_row = K slots per query group, -1 where the slot is
+// padding or names a block after the query's own) and their count per (b, h, block).
+__global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restrict__ idx, Geo geo,
+                                                        int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
+  extern __shared__ __attribute__((aligned(16))) int hist[];
+  const int BH = geo.B * geo.Hkv, K = geo.K;
+  const int bh = blockIdx.x % BH;
+  const int q0 = (blockIdx.x / BH) * kLeafQueries, q1 = min(geo.N, q0 + kLeafQueries);
+  const bool lhist = geo.n1 <= kHistMaxBins;
+  if (lhist) {
+    for (int t = threadIdx.x; t < geo.n1; t += 256) hist[t] = 0;
+    __syncthreads();
+  }
+  const int64_t base = ((int64_t)bh * geo.N + q0) * K;
+  const int n = (q1 - q0) * K;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int i = q0 + t / K;
+    const int j = idx[base + t];
+    const bool ok = j >= 0 && j <= i / geo.C;
+    cand[base + t] = ok ? j : -1;
+    if (ok) {
+      if (lhist) atomicAdd(&hist[j], 1);
+      else atomicAdd(&cnt[bh * geo.n1 + j], 1);
+    }
+  }
+  if (lhist) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < geo.n1; t += 256)
+      if (hist[t]) atomicAdd(&cnt[bh * geo.n1 + t], hist[t]);
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                         const bf16* __restrict__ v, Geo geo,
+                                                         const int32_t* __restrict__ off,
+                                                         const int32_t* __restrict__ choff,
+                                                         const int32_t* __restrict__ entries, int32_t M,
+                                                         float* __restrict__ plse, bf16* __restrict__ po) {
+  constexpr int EW = 32 / G;   // pairs per wavefront
+  constexpr int QC = 128 / G;  // pairs per chunk (workgroup)
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int VTR = kLeaf + 8;  // padded row (keys) of the transposed value tile
+  __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
+  __shared__ __attribute__((aligned(16))) bf16 vt[D * VTR];
+  __shared__ float ls_all[4][32];
+  __shared__ int64_t px_all[4][32];
+
+  const int c = blockIdx.x;
+  if (c >= choff[M]) return;  // uniform: grid is an upper bound on the chunk count
+  int lo = 0, hi = M;         // largest list whose first chunk is <= c
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (choff[mid] <= c) lo = mid; else hi = mid;
+  }
+  const int list = lo;
+  const int bh = list / geo.n1, j = list % geo.n1;
+  const int e0 = off[list] + (c - choff[list]) * QC;
+  const int e1 = min(e0 + QC, off[list + 1]);
+  const int N = geo.N, K = geo.K;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const int e = e0 + wave * EW + col / G;
+  const int r = col % G;
+  const bool valid = e < e1;
+  const int ent = valid ? entries[e] : 0;
+  const int i = ent >> 6, slot = ent & 63;
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  bf16x8 bq[KS];
+  load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * N + i) * D, valid, hh, bq);
+
+  stage_tile<D>(k + (int64_t)bh * N * D, j * kLeaf, N, kt);
+  {  // value tile, transposed: vt[dim][key] (zeros past N)
+    const bf16* vb = v + (int64_t)bh * N * D;
+    for (int t = threadIdx.x; t < kLeaf * (D / 8); t += 256) {
+      const int key = t / (D / 8), d8 = (t % (D / 8)) * 8;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (j * kLeaf + key < N) x = *reinterpret_cast<const u32x4*>(vb + (int64_t)(j * kLeaf + key) * D + d8);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vt[(d8 + 2 * w) * VTR + key] = (bf16)(x[w] & 0xFFFFu);
+        vt[(d8 + 2 * w + 1) * VTR + key] = (bf16)(x[w] >> 16);
+      }
+    }
+  }
+  __syncthreads();
+
+  f32x16 s0, s1;
+  tile_mfma32<D>(kt, bq, lane, s0, s1);
+  // block softmax of the column in log2 units; keys after the query or past N are masked
+  const float sl = geo.s_log2e;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int t0 = j * kLeaf + key_row(w, hh), t1 = t0 + 32;
+    s0[w] = (t0 <= i && t0 < N) ? s0[w] * sl : -INFINITY;
+    s1[w] = (t1 <= i && t1 < N) ? s1[w] * sl : -INFINITY;
+    mx = fmaxf(mx, fmaxf(s0[w], s1[w]));
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 32));  // key 64 j <= i is live for a valid pair
+  if (!valid) mx = 0.f;                // padding columns: all probabilities 0, never written
+  float sum = 0.f;
+  bf16x8 pa[4];
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const float p0 = __builtin_amdgcn_exp2f(s0[w] - mx), p1 = __builtin_amdgcn_exp2f(s1[w] - mx);
+    sum += p0 + p1;
+    pa[w >> 3][w & 7] = (__bf16)p0;
+    pa[2 + (w >> 3)][w & 7] = (__bf16)p1;
+  }
+  sum += __shfl_xor(sum, 32);
+
+  f32x16 ao[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int w = 0; w < 16; ++w) ao[db][w] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16* vr = vt + (32 * db + col) * VTR + 32 * (s >> 1) + 16 * (s & 1) + 4 * hh;
+      const uint2 x0 = *reinterpret_cast<const uint2*>(vr), x1 = *reinterpret_cast<const uint2*>(vr + 8);
+      const u32x4 xv = {x0.x, x0.y, x1.x, x1.y};
+      ao[db] = mfma32(pa[s], __builtin_bit_cast(bf16x8, xv), ao[db]);
+    }
+  }
+
+  // lane (col, hh) holds O[column key_row(w, hh)][dim 32 db + col]
+  float* ls = ls_all[wave];
+  int64_t* px = px_all[wave];
+  if (hh == 0) {
+    ls[col] = sum;
+    const int64_t pi = ((((int64_t)bh * N + i) * K + slot) * G + r);
+    px[col] = valid ? pi : -1;
+    if (valid) plse[pi] = mx + __builtin_amdgcn_logf(sum);
+  }
+  wave_sync();
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int m = key_row(w, hh);
+    const int64_t pi = px[m];
+    if (pi < 0) continue;
+    const float inv = 1.f / ls[m];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) po[pi * D + 32 * db + col] = (bf16)f2bf_rne(ao[db][w] * inv);
+  }
+}
+
+// One wavefront per query group: merges the K block partials of each head.
+template <int D, int G>
+__global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restrict__ idx, Geo geo,
+                                                         const float* __restrict__ plse,
+                                                         const bf16* __restrict__ po, bf16* __restrict__ out,
+                                                         float* __restrict__ lse) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int N = geo.N, K = geo.K;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+  if (row >= (int64_t)geo.B * geo.Hkv * N) return;  // whole wavefront; no barrier follows
+  const int bh = (int)(row / N), i = (int)(row % N);
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv, bq = i / geo.C;
+  const int my_blk = lane < K ? idx[row * K + lane] : -1;
+#pragma unroll 1
+  for (int r = 0; r < G; ++r) {
+    float m = -INFINITY, l = 0.f, acc[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+    for (int u = 0; u < K; ++u) {
+      const int jb = __shfl(my_blk, u);
+      if (jb < 0 || jb > bq) continue;  // uniform
+      const int64_t pi = (row * K + u) * G + r;
+      const float x = plse[pi];
+      const float mn = fmaxf(m, x);
+      const float sc = __builtin_amdgcn_exp2f(m - mn), wgt = __builtin_amdgcn_exp2f(x - mn);
+      l = l * sc + wgt;
+      const bf16* o = po + pi * D + lane * DPL;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[e] = acc[e] * sc + wgt * bf2f(o[e]);
+      m = mn;
+    }
+    const int64_t orow = ((int64_t)b * geo.Hq + h * G + r) * N + i;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) out[orow * D + lane * DPL + e] = (bf16)f2bf_rne(acc[e] * inv);
+    if (lse && lane == 0) lse[orow] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+template <int D, int G>
+int attn_km_g(const Geo& g, const bf16* q, const bf16* k, const bf16* v, const int32_t* idx, const AttnWs& w,
+              char* ws, bf16* out, float* lse, hipStream_t st) {
+  int32_t* cand = (int32_t*)(ws + w.cand);
+  int32_t* cnt = (int32_t*)(ws + w.cnt);
+  int32_t* cursor = (int32_t*)(ws + w.cursor);
+  int32_t* off = (int32_t*)(ws + w.off);
+  int32_t* choff = (int32_t*)(ws + w.choff);
+  int32_t* entries = (int32_t*)(ws + w.entries);
+  float* plse = (float*)(ws + w.plse);
+  bf16* po = (bf16*)(ws + w.po);
+  int rc;
+  if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
+  const unsigned cgrid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+  const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
+  attn_cand_kernel<<<cgrid, 256, hbytes, st>>>(idx, g, cand, cnt);
+  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  const int qc = 128 / G;
+  if ((rc = launch_scan(cnt, w.M, qc, off, choff, st)) != PISA_OK) return rc;
+  if ((rc = launch_scatter(g, g.K, cand, off, cursor, entries, st)) != PISA_OK) return rc;
+  const int64_t grid = (w.slots + qc - 1) / qc + w.M;  // bound on the chunk count
+  attn_chunk_kernel<D, G><<<(unsigned)grid, 256, 0, st>>>(q, k, v, g, off, choff, entries, w.M, plse, po);
+  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  const int64_t rows = (int64_t)g.B * g.Hkv * g.N;
+  attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, out, lse);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
+
+template <int D>
+int attn_km_d(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx, void* ws,
+              void* out, float* lse, hipStream_t st) {
+  const AttnWs w = attention_ws(g);
+  const bf16 *qq = (const bf16*)q, *kk = (const bf16*)k, *vv = (const bf16*)v;
+  bf16* oo = (bf16*)out;
+  char* wc = (char*)ws;
+  switch (g.G) {
+    case 1: return attn_km_g<D, 1>(g, qq, kk, vv, idx, w, wc, oo, lse, st);
+    case 2: return attn_km_g<D, 2>(g, qq, kk, vv, idx, w, wc, oo, lse, st);
+    case 4: return attn_km_g<D, 4>(g, qq, kk, vv, idx, w, wc, oo, lse, st);
+    case 8: return attn_km_g<D, 8>(g, qq, kk, vv, idx, w, wc, oo, lse, st);
+    case 16: return attn_km_g<D, 16>(g, qq, kk, vv, idx, w, wc, oo, lse, st);
+    default: return PISA_ERR_UNSUPPORTED;
+  }
+}
+
 }  // namespace
 
+bool attention_key_major(const Geo& g, int dtype, int decode) { return dtype == PISA_BF16 && !decode; }
+
+AttnWs attention_ws(const Geo& g) {
+  AttnWs w;
+  auto align256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  w.slots = (int64_t)g.B * g.Hkv * g.N * g.K;
+  w.M = g.B * g.Hkv * g.n1;
+  size_t o = 0;
+  w.cand = o;    o = align256(o + sizeof(int32_t) * w.slots);
+  w.cnt = o;     o = align256(o + sizeof(int32_t) * w.M);
+  w.cursor = o;  o = align256(o + sizeof(int32_t) * w.M);
+  w.off = o;     o = align256(o + sizeof(int32_t) * (w.M + 1));
+  w.choff = o;   o = align256(o + sizeof(int32_t) * (w.M + 1));
+  w.entries = o; o = align256(o + sizeof(int32_t) * w.slots);
+  w.plse = o;    o = align256(o + sizeof(float) * w.slots * g.G);
+  w.po = o;      o = align256(o + sizeof(uint16_t) * w.slots * g.G * g.d);
+  w.total = o;
+  return w;
+}
+
 int launch_attention(const Geo& g, int dtype, const void* q, const void* k, const void* v, const int32_t* idx,
-                     int decode, void* out, float* lse, hipStream_t st) {
+                     int decode, void* ws, void* out, float* lse, hipStream_t st) {
+  if (attention_key_major(g, dtype, decode)) {
+    if (g.d == 128) return attn_km_d<128>(g, q, k, v, idx, ws, out, lse, st);
+    if (g.d == 64) return attn_km_d<64>(g, q, k, v, idx, ws, out, lse, st);
+    return PISA_ERR_UNSUPPORTED;
+  }
   if (dtype == PISA_BF16) {
     if (g.d == 128) return attn_g<bf16, 128>(g, q, k, v, idx, decode, out, lse, st);
     if (g.d == 64) return attn_g<bf16, 64>(g, q, k, v, idx, decode, out, lse, st);

@@ -111,16 +111,16 @@ int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
-int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
-                   hipStream_t st) {
+int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
+                   int32_t* entries, hipStream_t st) {
   if (g.n1 <= kHistMaxBins) {
     const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
-    scatter_hist_kernel<<<grid, 256, 2 * sizeof(int) * (size_t)g.n1, st>>>(cand, g.N, g.B * g.Hkv, 2 * g.K, g.n1,
+    scatter_hist_kernel<<<grid, 256, 2 * sizeof(int) * (size_t)g.n1, st>>>(cand, g.N, g.B * g.Hkv, per_row, g.n1,
                                                                             off, cursor, entries);
     return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
   }
-  const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
-  scatter_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(cand, slots, g.N, 2 * g.K, g.n1, off, cursor,
+  const int64_t slots = (int64_t)g.B * g.Hkv * g.N * per_row;
+  scatter_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(cand, slots, g.N, per_row, g.n1, off, cursor,
                                                                    entries);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }

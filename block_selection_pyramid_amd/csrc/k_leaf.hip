@@ -26,62 +26,6 @@ namespace pisa {
 
 namespace {
 
-// Stages rows [row0, row0 + 64) of one (b,h)'s keys into LDS (zero past N).
-template <int D>
-__device__ __forceinline__ void stage_tile(const bf16* __restrict__ kb, int row0, int N, bf16* kt) {
-  constexpr int LDSR = D + 8;
-  constexpr int TPR = D / 8;
-  for (int t = threadIdx.x; t < kLeaf * TPR; t += 256) {
-    const int r = t / TPR, c = (t % TPR) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < N) v = *reinterpret_cast<const uint4*>(kb + (int64_t)(row0 + r) * D + c);
-    *reinterpret_cast<uint4*>(kt + r * LDSR + c) = v;
-  }
-}
-
-__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// B fragments of one query row for v_mfma_f32_32x32x16_bf16: k-step s, lane half
-// hh = lane >> 5 <-> dims 16s + 8hh .. +8 (the two lanes of a column read 32 contiguous
-// bytes of its query row per load).
-template <int D>
-__device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool valid, int hh, bf16x8* bq) {
-  constexpr int KS = D / 16;
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (valid) {
-      bq[s] = *reinterpret_cast<const bf16x8*>(qrow + 16 * s + 8 * hh);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
-    }
-  }
-}
-
-// 64 keys (LDS tile, two M-tiles of 32) x 32 columns: acc0/acc1[v] of lane l hold keys
-// key_row(v, l >> 5) and 32 + key_row(v, l >> 5) against column l & 31.
-template <int D>
-__device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, int lane, f32x16& acc0,
-                                            f32x16& acc1) {
-  constexpr int LDSR = D + 8;
-  constexpr int KS = D / 16;
-  const int col = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    acc0[v] = 0.f;
-    acc1[v] = 0.f;
-  }
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + 16 * s + 8 * hh);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + 16 * s + 8 * hh);
-    acc0 = mfma32(a0, bq[s], acc0);
-    acc1 = mfma32(a1, bq[s], acc1);
-  }
-}
-
 // Workgroup = one chunk of a leaf block's list (QC = 128/G entries); each wavefront
 // scores 32/G entries (32 columns = (entry, head) pairs per MFMA tile).
 template <int D, int G>

@@ -177,7 +177,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
     return mark(5);
   }
   if ((rc = launch_scan(cnt, w.M, chunk_entries(g.G), off, choff, st)) != PISA_OK) return rc;
-  if ((rc = launch_scatter(g, cand, off, cursor, entries, st)) != PISA_OK) return rc;
+  if ((rc = launch_scatter(g, 2 * g.K, cand, off, cursor, entries, st)) != PISA_OK) return rc;
   if ((rc = mark(3)) != PISA_OK) return rc;
   if ((rc = launch_leaf_mfma(g, q, k, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
   if ((rc = mark(4)) != PISA_OK) return rc;
@@ -273,8 +273,15 @@ int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* 
   return launch_decode(g, p->dtype, q, k_cache, pyramid, lengths, out_idx, out_score, (hipStream_t)stream);
 }
 
+size_t pisa_attention_workspace_bytes(const pisa_problem* p, int32_t mode) {
+  Geo g;
+  if (make_geo(p, &g) != PISA_OK || (mode != PISA_PREFILL && mode != PISA_DECODE)) return 0;
+  return attention_key_major(g, p->dtype, mode == PISA_DECODE) ? attention_ws(g).total : 0;
+}
+
 int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, const void* k, const void* v,
-                          const int32_t* idx, void* out, float* lse, pisa_stream_t stream) {
+                          const int32_t* idx, void* workspace, size_t workspace_bytes, void* out, float* lse,
+                          pisa_stream_t stream) {
   Geo g;
   int rc = make_geo(p, &g);
   if (rc != PISA_OK) return rc;
@@ -284,7 +291,12 @@ int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, co
     return PISA_ERR_INVALID_ARG;
   rc = supported(g, p->dtype, mode);
   if (rc != PISA_OK) return rc;
-  return launch_attention(g, p->dtype, q, k, v, idx, mode == PISA_DECODE, out, lse, (hipStream_t)stream);
+  if (attention_key_major(g, p->dtype, mode == PISA_DECODE)) {
+    if (!workspace || !aligned16(workspace)) return PISA_ERR_INVALID_ARG;
+    if (workspace_bytes < attention_ws(g).total) return PISA_ERR_WORKSPACE;
+  }
+  return launch_attention(g, p->dtype, q, k, v, idx, mode == PISA_DECODE, workspace, out, lse,
+                          (hipStream_t)stream);
 }
 
 int pisa_bsa_select_prefill(const pisa_problem* p, const void* q, const float* pyramid, int32_t* out_idx,

@@ -51,9 +51,17 @@ inline int route_groups_per_wave(int G, int K) {
 
 // ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
-// block-sparse attention over selected blocks (decode != 0: one query per sequence at N-1)
+// block-sparse attention over selected blocks (decode != 0: one query per sequence at N-1);
+// bf16 prefill runs key-major and needs the workspace laid out by attention_ws
+struct AttnWs {
+  size_t cand, cnt, cursor, off, choff, entries, plse, po, total;
+  int64_t slots;  // B*Hkv*N*K
+  int32_t M;      // B*Hkv*n1 block lists
+};
+bool attention_key_major(const Geo& g, int dtype, int decode);
+AttnWs attention_ws(const Geo& g);
 int launch_attention(const Geo& g, int dtype, const void* q, const void* k, const void* v, const int32_t* idx,
-                     int decode, void* out, float* lse, hipStream_t st);
+                     int decode, void* ws, void* out, float* lse, hipStream_t st);
 // full-scan BSA selection (bf16): out_idx / out_score [B, Hkv, N, K]
 int launch_bsa(const Geo& g, const void* q, const float* pyr, int32_t* out_idx, float* out_score, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);
@@ -80,8 +88,9 @@ inline int dense_bottom(const Geo& g) {
   return l;
 }
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
-int launch_scatter(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
-                   hipStream_t st);
+// scatter of per_row candidate slots per query group (-1 = none) into per-leaf-block lists
+int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
+                   int32_t* entries, hipStream_t st);
 int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
                      const int32_t* entries, int32_t M, float* lscore, hipStream_t st);
 int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const float* fsc, int32_t* out_idx,

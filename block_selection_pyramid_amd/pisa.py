@@ -84,6 +84,7 @@ _lib = None
 EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs", "pisa_select_decode",
            "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
+           "pisa_attention_workspace_bytes",
            "pisa_status_string", "pisa_version")
 
 
@@ -112,7 +113,9 @@ def load(path: str | None = None):
     lib.pisa_bsa_select_prefill.argtypes = [P, vp, vp, vp, vp, vp]
     lib.pisa_append_keys.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, vp]
     lib.pisa_select_decode_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
-    lib.pisa_sparse_attention.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, vp]
+    lib.pisa_sparse_attention.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.pisa_attention_workspace_bytes.argtypes = [P, ctypes.c_int32]
+    lib.pisa_attention_workspace_bytes.restype = sz
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_version.restype = ctypes.c_char_p
@@ -247,9 +250,13 @@ def select_decode_varlen(p: Problem, q: torch.Tensor, k_cache: torch.Tensor, pyr
     return out_idx, out_score
 
 
+def attention_workspace_bytes(p: Problem, decode: bool = False) -> int:
+    return int(load().pisa_attention_workspace_bytes(ctypes.byref(p.c()), DECODE if decode else PREFILL))
+
+
 def sparse_attention(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                      decode: bool = False, out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                     want_lse: bool = True, stream=None):
+                     want_lse: bool = True, ws: torch.Tensor | None = None, stream=None):
     """pisa_sparse_attention: returns (out [B, Hq, N, d] or [B, Hq, d] in q's dtype, lse fp32
     [B, Hq, N] or [B, Hq], or None when want_lse is False)."""
     qshape = (p.batch, p.n_q_heads, p.head_dim) if decode else (p.batch, p.n_q_heads, p.seq_len, p.head_dim)
@@ -267,8 +274,13 @@ def sparse_attention(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tens
         if lse is None:
             lse = torch.empty(qshape[:-1], dtype=torch.float32, device=q.device)
         lp = _dev(lse, "lse", torch.float32, qshape[:-1])
-    _check(load().pisa_sparse_attention(ctypes.byref(p.c()), DECODE if decode else PREFILL, qp, kp, vp_, ip, op, lp,
-                                        _stream(stream)), "pisa_sparse_attention")
+    nws = attention_workspace_bytes(p, decode)
+    if nws and ws is None:
+        ws = torch.empty(nws, dtype=torch.uint8, device=q.device)
+    wp = _dev(ws, "workspace", torch.uint8) if nws else None
+    wn = ws.numel() if nws else 0
+    _check(load().pisa_sparse_attention(ctypes.byref(p.c()), DECODE if decode else PREFILL, qp, kp, vp_, ip, wp, wn,
+                                        op, lp, _stream(stream)), "pisa_sparse_attention")
     return out, (lse if want_lse else None)
 
 

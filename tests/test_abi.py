@@ -110,6 +110,21 @@ def test_append_and_varlen_host_checks(pisa):
                                          None) == 2
 
 
+def test_attention_host_checks(pisa):
+    lib = pisa.load()
+    p = pisa.Problem(1, 4096, 16, 4, 128)
+    P = ctypes.byref(p.c())
+    need = lib.pisa_attention_workspace_bytes(P, pisa.PREFILL)
+    assert need > 0 and lib.pisa_attention_workspace_bytes(P, pisa.DECODE) == 0
+    f32 = pisa.Problem(1, 4096, 16, 4, 128, dtype=pisa.F32)
+    assert lib.pisa_attention_workspace_bytes(ctypes.byref(f32.c()), pisa.PREFILL) == 0
+    a = (0x1000, 0x1000, 0x1000, 0x1000)
+    assert lib.pisa_sparse_attention(P, pisa.PREFILL, *a, None, need, 0x1000, None, None) == 1       # no workspace
+    assert lib.pisa_sparse_attention(P, pisa.PREFILL, *a, 0x1000, need - 1, 0x1000, None, None) == 3  # too small
+    assert lib.pisa_sparse_attention(P, 7, *a, 0x1000, need, 0x1000, None, None) == 1                 # bad mode
+    assert lib.pisa_sparse_attention(P, pisa.PREFILL, 0, *a[1:], 0x1000, need, 0x1000, None, None) == 1
+
+
 def test_bsa_host_checks(pisa):
     lib = pisa.load()
     p = pisa.Problem(1, 4096, 16, 4, 128)
