@@ -227,8 +227,10 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   constexpr int QC = 128 / G;  // pairs per chunk (workgroup)
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int VTR = kLeaf + 8;  // padded row (keys) of the transposed value tile
-  __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
-  __shared__ __attribute__((aligned(16))) bf16 vt[D * VTR];
+  // key tile, then the transposed value tile; later the staged outputs of the 4 wavefronts
+  __shared__ __attribute__((aligned(16))) bf16 tiles[kLeaf * (D + 8) + D * VTR];
+  bf16* kt = tiles;
+  bf16* vt = tiles + kLeaf * (D + 8);
   __shared__ float ls_all[4][32];
   __shared__ int64_t px_all[4][32];
 
@@ -320,19 +322,33 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
     px[col] = valid ? pi : -1;
     if (valid) plse[pi] = mx + __builtin_amdgcn_logf(sum);
   }
-  wave_sync();
+  // the normalised tile goes through LDS (the key and value tiles' space, free once every
+  // wavefront has finished its products) so that it leaves in 16-byte pieces
+  __syncthreads();
+  constexpr int OSR = D + 8;  // padded row of the staged output
+  bf16* os = tiles + wave * 32 * OSR;
+  static_assert(4 * 32 * (D + 8) <= kLeaf * (D + 8) + D * (kLeaf + 8), "output staging fits the tile space");
 #pragma unroll
   for (int w = 0; w < 16; ++w) {
     const int m = key_row(w, hh);
-    const int64_t pi = px[m];
-    if (pi < 0) continue;
-    const float inv = 1.f / ls[m];
+    const float inv = px[m] >= 0 ? 1.f / ls[m] : 0.f;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) po[pi * D + 32 * db + col] = (bf16)f2bf_rne(ao[db][w] * inv);
+    for (int db = 0; db < DB; ++db) os[m * OSR + 32 * db + col] = (bf16)f2bf_rne(ao[db][w] * inv);
+  }
+  wave_sync();
+#pragma unroll
+  for (int t = lane; t < 32 * (D / 8); t += 64) {
+    const int m = t / (D / 8), c8 = (t % (D / 8)) * 8;
+    const int64_t pi = px[m];
+    if (pi >= 0) *reinterpret_cast<u32x4*>(po + pi * D + c8) = *reinterpret_cast<const u32x4*>(os + m * OSR + c8);
   }
 }
 
-// One wavefront per query group: merges the K block partials of each head.
+// One wavefront per query group: merges the K block partials of each of its G heads.  All
+// of the row's loads leave together: lane t < K G reads the log2-sum-exp of (slot t / G,
+// head t % G), and every lane reads its dims of all K G partial rows (a slot without a
+// partial reads in-bounds workspace and gets weight 0 through a select, so no stale value
+// reaches the sum); the weights then come from shuffles.
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restrict__ idx, Geo geo,
                                                          const float* __restrict__ plse,
@@ -345,30 +361,62 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
   if (row >= (int64_t)geo.B * geo.Hkv * N) return;  // whole wavefront; no barrier follows
   const int bh = (int)(row / N), i = (int)(row % N);
   const int b = bh / geo.Hkv, h = bh % geo.Hkv, bq = i / geo.C;
-  const int my_blk = lane < K ? idx[row * K + lane] : -1;
+  const int KG = K * G;  // partials of the row, slot-major
+  const bf16* prow = po + row * KG * D + lane * DPL;
+  const float* lrow = plse + row * KG;
+  // lane t: log2-sum-exp of partial t (t < 64, then t - 64 < 64 in a second register;
+  // beyond 128 partials they are read directly), -inf where the slot names no block of the
+  // query's prefix
+  float x0 = -INFINITY, x1 = -INFINITY;
+  if (lane < KG) {
+    const int jb = idx[row * K + lane / G];
+    if (jb >= 0 && jb <= bq) x0 = lrow[lane];
+  }
+  if (lane + 64 < KG) {
+    const int jb = idx[row * K + (lane + 64) / G];
+    if (jb >= 0 && jb <= bq) x1 = lrow[lane + 64];
+  }
+  // partial t's log2-sum-exp in every lane (t is uniform across the wavefront)
+  auto xat = [&](int t) -> float {
+    if (t < 64) return __shfl(x0, t);
+    if (t < 128) return __shfl(x1, t - 64);
+    const int jb = idx[row * K + t / G];
+    return (jb >= 0 && jb <= bq) ? lrow[t] : -INFINITY;
+  };
 #pragma unroll 1
   for (int r = 0; r < G; ++r) {
-    float m = -INFINITY, l = 0.f, acc[DPL];
+    float mx = -INFINITY;
+    for (int u = 0; u < K; ++u) mx = fmaxf(mx, xat(u * G + r));
+    float l = 0.f, acc[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+#pragma unroll 8
     for (int u = 0; u < K; ++u) {
-      const int jb = __shfl(my_blk, u);
-      if (jb < 0 || jb > bq) continue;  // uniform
-      const int64_t pi = (row * K + u) * G + r;
-      const float x = plse[pi];
-      const float mn = fmaxf(m, x);
-      const float sc = __builtin_amdgcn_exp2f(m - mn), wgt = __builtin_amdgcn_exp2f(x - mn);
-      l = l * sc + wgt;
-      const bf16* o = po + pi * D + lane * DPL;
+      const int t = u * G + r;
+      const float xt = xat(t);
+      const float wu = xt > -INFINITY ? __builtin_amdgcn_exp2f(xt - mx) : 0.f;
+      l += wu;
+      const bf16* o = prow + (int64_t)t * D;
+      float ov[DPL];
+      if constexpr (DPL == 2) {
+        const uint32_t pr = *reinterpret_cast<const uint32_t*>(o);
+        ov[0] = bf2f(pr & 0xFFFFu);
+        ov[1] = bf2f(pr >> 16);
+      } else {
+        ov[0] = bf2f(o[0]);
+      }
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] = acc[e] * sc + wgt * bf2f(o[e]);
-      m = mn;
+      for (int e = 0; e < DPL; ++e) acc[e] += wu > 0.f ? wu * ov[e] : 0.f;
     }
     const int64_t orow = ((int64_t)b * geo.Hq + h * G + r) * N + i;
     const float inv = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) out[orow * D + lane * DPL + e] = (bf16)f2bf_rne(acc[e] * inv);
-    if (lse && lane == 0) lse[orow] = l > 0.f ? (m + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
+    if constexpr (DPL == 2) {
+      *reinterpret_cast<uint32_t*>(out + orow * D + lane * 2) =
+          f2bf_rne(acc[0] * inv) | (f2bf_rne(acc[1] * inv) << 16);
+    } else {
+      out[orow * D + lane] = (bf16)f2bf_rne(acc[0] * inv);
+    }
+    if (lse && lane == 0) lse[orow] = l > 0.f ? (mx + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
