@@ -344,29 +344,28 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   }
 }
 
-// One wavefront per query group: merges the K block partials of each of its G heads.  All
-// of the row's loads leave together: lane t < K G reads the log2-sum-exp of (slot t / G,
-// head t % G), and every lane reads its dims of all K G partial rows (a slot without a
-// partial reads in-bounds workspace and gets weight 0 through a select, so no stale value
-// reaches the sum); the weights then come from shuffles.
+// One wavefront per query group: merges the K block partials of each of its G heads.  A
+// head's row is D / 8 lanes x 16 bytes, so one pass covers HP = 64 / (D / 8) heads and each
+// slot's partial rows of those heads (contiguous: partials are slot-major, head-minor) come
+// in one 16-byte load per lane, the K slots' loads all in flight together.  Lane t < K G
+// first reads the log2-sum-exp of partial t (slot t / G, head t % G); each lane then takes
+// its head's weights by shuffles.  A slot without a partial reads in-bounds workspace and
+// gets weight 0 through a select, so no stale value reaches the sum.
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restrict__ idx, Geo geo,
                                                          const float* __restrict__ plse,
                                                          const bf16* __restrict__ po, bf16* __restrict__ out,
                                                          float* __restrict__ lse) {
-  constexpr int DPL = D / 64;  // dims per lane
+  constexpr int LPH = D / 8;       // lanes per head row (16 bytes each)
+  constexpr int HP = 64 / LPH;     // heads per pass
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = geo.N, K = geo.K;
   const int64_t row = (int64_t)blockIdx.x * 4 + wave;
   if (row >= (int64_t)geo.B * geo.Hkv * N) return;  // whole wavefront; no barrier follows
   const int bh = (int)(row / N), i = (int)(row % N);
   const int b = bh / geo.Hkv, h = bh % geo.Hkv, bq = i / geo.C;
-  const int KG = K * G;  // partials of the row, slot-major
-  const bf16* prow = po + row * KG * D + lane * DPL;
+  const int KG = K * G;
   const float* lrow = plse + row * KG;
-  // lane t: log2-sum-exp of partial t (t < 64, then t - 64 < 64 in a second register;
-  // beyond 128 partials they are read directly), -inf where the slot names no block of the
-  // query's prefix
   float x0 = -INFINITY, x1 = -INFINITY;
   if (lane < KG) {
     const int jb = idx[row * K + lane / G];
@@ -376,47 +375,49 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
     const int jb = idx[row * K + (lane + 64) / G];
     if (jb >= 0 && jb <= bq) x1 = lrow[lane + 64];
   }
-  // partial t's log2-sum-exp in every lane (t is uniform across the wavefront)
+  // partial t's log2-sum-exp for this lane (t may differ between lanes)
   auto xat = [&](int t) -> float {
-    if (t < 64) return __shfl(x0, t);
-    if (t < 128) return __shfl(x1, t - 64);
+    const float a = __shfl(x0, t & 63), c = __shfl(x1, t & 63);
+    if (t < 64) return a;
+    if (t < 128) return c;
     const int jb = idx[row * K + t / G];
     return (jb >= 0 && jb <= bq) ? lrow[t] : -INFINITY;
   };
+  const int hl = lane / LPH, dl = (lane % LPH) * 8;  // head within the pass, first dim
 #pragma unroll 1
-  for (int r = 0; r < G; ++r) {
+  for (int r0 = 0; r0 < G; r0 += HP) {
+    const int r = r0 + hl;
+    const bool live = r < G;
+    const int rr = live ? r : 0;  // idle lanes shadow head 0 so every lane takes part in the shuffles
     float mx = -INFINITY;
-    for (int u = 0; u < K; ++u) mx = fmaxf(mx, xat(u * G + r));
-    float l = 0.f, acc[DPL];
+    for (int u = 0; u < K; ++u) mx = fmaxf(mx, xat(u * G + rr));
+    float l = 0.f, acc[8];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll 8
     for (int u = 0; u < K; ++u) {
-      const int t = u * G + r;
+      const int t = u * G + rr;
       const float xt = xat(t);
       const float wu = xt > -INFINITY ? __builtin_amdgcn_exp2f(xt - mx) : 0.f;
       l += wu;
-      const bf16* o = prow + (int64_t)t * D;
-      float ov[DPL];
-      if constexpr (DPL == 2) {
-        const uint32_t pr = *reinterpret_cast<const uint32_t*>(o);
-        ov[0] = bf2f(pr & 0xFFFFu);
-        ov[1] = bf2f(pr >> 16);
-      } else {
-        ov[0] = bf2f(o[0]);
-      }
+      const u32x4 pr = *reinterpret_cast<const u32x4*>(po + (row * KG + t) * D + dl);
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) acc[e] += wu > 0.f ? wu * ov[e] : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf2f(pr[e] & 0xFFFFu), hi = bf2f(pr[e] >> 16);
+        acc[2 * e] += wu > 0.f ? wu * lo : 0.f;
+        acc[2 * e + 1] += wu > 0.f ? wu * hi : 0.f;
+      }
     }
-    const int64_t orow = ((int64_t)b * geo.Hq + h * G + r) * N + i;
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    if constexpr (DPL == 2) {
-      *reinterpret_cast<uint32_t*>(out + orow * D + lane * 2) =
-          f2bf_rne(acc[0] * inv) | (f2bf_rne(acc[1] * inv) << 16);
-    } else {
-      out[orow * D + lane] = (bf16)f2bf_rne(acc[0] * inv);
+    if (live) {
+      const int64_t orow = ((int64_t)b * geo.Hq + h * G + r) * N + i;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = f2bf_rne(acc[2 * e] * inv) | (f2bf_rne(acc[2 * e + 1] * inv) << 16);
+      *reinterpret_cast<u32x4*>(out + orow * D + dl) = o;
+      if (lse && lane % LPH == 0)
+        lse[orow] = l > 0.f ? (mx + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
     }
-    if (lse && lane == 0) lse[orow] = l > 0.f ? (mx + __builtin_amdgcn_logf(l)) * 0.6931471805599453f : -INFINITY;
   }
 }
 
