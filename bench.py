@@ -15,10 +15,10 @@ selection-kernel comparison at C=64, K=8, extended past 256K).
 
 Prints one JSON line.  Per-stage times come from HIP events recorded by the library on
 the stream its kernels run on (pisa_select_prefill_staged) and around pisa_build_pyramid.
-The roofline entry is for the stage with the largest average time (the dense upper-level
-routing launch); its algorithmic work per launch is stated in the design notes, and its
-HBM traffic comes from the committed counter summary under profiles/ while the kernel's
-sources still match it (else null).  ``cpu_baseline`` times the fp64 CPU oracle (test
+The roofline entry is for the stage with the largest average time, against its binding
+roof: the larger of its algorithmic bytes at the HBM peak and its algorithmic flops at the
+bf16 MFMA peak (Prefill.work); its HBM traffic comes from the committed counter summary
+under profiles/ while the kernel's sources still match it (else null).  ``cpu_baseline`` times the fp64 CPU oracle (test
 infrastructure) on a bounded sample of the 256K workload and scales it to the whole
 workload.
 """
@@ -36,7 +36,6 @@ import numpy as np
 METRIC = "pyramid selection latency ms @64K/256K prefill (C=64,K=8); decode µs/step"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-VALU_FP32_PEAK_TFLOPS = 157.3
 
 
 def log(*a):
@@ -96,26 +95,34 @@ def routing_dots_by_level(levels, K, bq):
     return out
 
 
-# Counter summary of the dominant kernel (HBM traffic per launch), valid while the
-# kernel's sources are unchanged.
+# Counter summary of the prefill kernels (HBM traffic per launch, FETCH_SIZE and WRITE_SIZE
+# scaled by a copy of known size); a stage's figure is valid while the sources of its
+# kernel hash to the recorded value.
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                            "route_dense_kernel_256k_hbm_traffic.md")
-TRAFFIC_SOURCES = ["k_route_dense.hip", "route_dev.h", "dev_common.h", "pisa_internal.h"]
+                            "prefill_256k_hbm_traffic.md")
+TRAFFIC_SOURCES = {
+    "route_upper": ["k_route_dense.hip", "final_dev.h", "route_dev.h", "tile_dev.h", "dev_common.h",
+                    "pisa_internal.h"],
+    "route_l2": ["k_route.hip", "route_dev.h", "dev_common.h", "pisa_internal.h"],
+    "leaf": ["k_leaf.hip", "final_dev.h", "dev_common.h", "pisa_internal.h"],
+}
 
 
-def kernel_sources_sha1():
+def kernel_sources_sha1(stage):
     import hashlib
     h = hashlib.sha1()
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "block_selection_pyramid_amd", "csrc")
-    for f in TRAFFIC_SOURCES:
+    for f in TRAFFIC_SOURCES[stage]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the dense routing kernel from the committed counter summary,
-    or None if there is none or the kernel changed since the counters were taken."""
+def recorded_traffic(stage):
+    """HBM bytes per launch of a stage's kernel from the committed counter summary, or None
+    if there is none or the kernel changed since the counters were taken."""
+    if stage not in TRAFFIC_SOURCES:
+        return None
     try:
         fields = {}
         with open(TRAFFIC_FILE) as fh:
@@ -123,9 +130,9 @@ def recorded_traffic():
                 if "=" in line and line.lstrip().startswith("- "):
                     k, v = line.lstrip()[2:].split("=", 1)
                     fields[k.strip()] = v.strip().strip("`")
-        if fields.get("sources_sha1") != kernel_sources_sha1():
+        if fields.get(stage + ".sources_sha1") != kernel_sources_sha1(stage):
             return None
-        return int(fields["hbm_bytes_per_launch"])
+        return int(fields[stage + ".hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -214,42 +221,55 @@ class Prefill:
         return {"ms": round(ms, 4), "pairs": pairs, "tile_GBps": round(tile_bytes / (ms * 1e-3) / 1e9, 1)}
 
     def work(self):
-        """Algorithmic work of each stage for one step (see the design notes)."""
+        """Algorithmic work of each stage for one step: (bytes, flops).  Bytes are the
+        unique HBM bytes the stage must move (each input read once, each output written
+        once); flops are the walk's dot products (2d per child and head) and the leaf and
+        forced-block key dots, however many the kernels execute."""
         p, w = self.p, self.w
         d, G, C, K = p.head_dim, p.n_q_heads // p.n_kv_heads, p.block, p.top_k
         L, levels, offs = self.pisa.levels(p)
         T = offs[-1]
-        BH = p.batch * p.n_kv_heads
-        bq = np.arange(p.seq_len) // C
+        BH, N = p.batch * p.n_kv_heads, p.seq_len
+        esz = 2 if p.dtype == self.pisa.BF16 else 4
+        bq = np.arange(N) // C
         by_level = routing_dots_by_level(levels, K, bq)
-        upper = int(sum(v.sum() for l, v in by_level.items() if l >= 3))
-        l2 = int(by_level[2].sum()) if 2 in by_level else 0
+        top, bot = self.pisa.dense_levels(p)  # (0, 0): every level by gathers
+        dense_l = [l for l in by_level if bot and l >= bot]
+        gather_l = [l for l in by_level if l not in dense_l]
+        dots = lambda ls: int(sum(by_level[l].sum() for l in ls))
+        copy = lambda ls: BH * sum(levels[l - 1] for l in ls) * d * 4  # child levels' routing copy
         pairs = self.pisa.routed_pairs(p, self.ws)
-        fkeys = int(forced_keys_per_query(p.seq_len, C).sum())
+        fflops = BH * int(forced_keys_per_query(N, C).sum()) * G * 2 * d
+        q_b, k_b = BH * G * N * d * esz, BH * N * d * esz
+        slots = BH * N * 2 * K * 4  # one int32 / fp32 per candidate slot
+        forced_in_route = bool(bot)
         return {
-            "build": ("hbm", BH * (p.seq_len * d * 2 + T * d * 8), "GB/s"),
-            "route_upper": ("mfma", BH * upper * G * 2 * d, "TFLOP/s"),
-            "route_l2": ("mfma", BH * l2 * G * 2 * d, "TFLOP/s"),
-            "leaf": ("mfma", pairs * G * C * 2 * d, "TFLOP/s"),
-            "final": ("mfma", BH * fkeys * G * 2 * d, "TFLOP/s"),
-            "group": ("hbm", BH * p.seq_len * 2 * K * 4 * 4, "GB/s"),
+            "build": (BH * N * d * esz + BH * T * d * 8, 0),
+            "route_upper": ((q_b + k_b + copy(dense_l) + slots + BH * N * 3 * 4, dots(dense_l) * BH * G * 2 * d
+                             + fflops) if forced_in_route else (0, 0)),
+            "route_l2": (q_b + (slots if forced_in_route else 0) + copy(gather_l) + slots,
+                         dots(gather_l) * BH * G * 2 * d),
+            "group": (BH * N * 2 * K * 4 * 4, 0),
+            "leaf": (q_b + k_b + 2 * slots, pairs * G * C * 2 * d),
+            "final": (BH * N * ((2 * K + 3) * 4 + K * 8) + (0 if forced_in_route else q_b + k_b),
+                      0 if forced_in_route else fflops),
             "_pairs": pairs,
-            "_route_dots": BH * (upper + l2),
         }
 
 
 def roofline(stage_ms, work):
-    dom = max((n for n in stage_ms if n in work), key=lambda n: stage_ms[n])
-    bound, amount, unit = work[dom]
+    """Roofline of the stage with the largest time: its binding roof is the larger of its
+    algorithmic bytes at the HBM peak and its algorithmic flops at the bf16 MFMA peak (each
+    kind of work charged to the unit that does it fastest); frac = that time / measured."""
+    dom = max((n for n in stage_ms if n in work and not n.startswith("_")), key=lambda n: stage_ms[n])
+    nbytes, flops = work[dom]
     t = stage_ms[dom] * 1e-3
-    if unit == "GB/s":
-        achieved, peak = amount / t / 1e9, HBM_PEAK_GBS
+    if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12):
+        bound, achieved, peak, unit = "hbm", nbytes / t / 1e9, HBM_PEAK_GBS, "GB/s"
     else:
-        achieved = amount / t / 1e12
-        peak = MFMA_BF16_PEAK_TFLOPS if bound == "mfma" else VALU_FP32_PEAK_TFLOPS
-    traffic = recorded_traffic() if dom == "route_upper" else None
+        bound, achieved, peak, unit = "mfma", flops / t / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s"
     return dom, {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                 "frac": round(achieved / peak, 4), "traffic": traffic}
+                 "frac": round(achieved / peak, 4), "traffic": recorded_traffic(dom)}
 
 
 def time_decode(torch, pisa, synth, steps):

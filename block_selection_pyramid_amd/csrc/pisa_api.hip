@@ -231,6 +231,19 @@ int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size
   return rc;
 }
 
+int pisa_prefill_dense_levels(const pisa_problem* p, int32_t* dense_top, int32_t* dense_bottom) {
+  Geo g;
+  int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (!dense_top || !dense_bottom) return PISA_ERR_INVALID_ARG;
+  rc = supported(g, p->dtype, PISA_PREFILL);
+  if (rc != PISA_OK) return rc;
+  const bool dense = route_scores_forced(g, p->dtype);  // bf16 with L >= 3
+  *dense_top = dense ? g.L : 0;
+  *dense_bottom = dense ? pisa::dense_bottom(g) : 0;
+  return PISA_OK;
+}
+
 int pisa_select_decode(const pisa_problem* p, const void* q, const void* k_cache, const float* pyramid,
                        void* workspace, size_t workspace_bytes, int32_t* out_idx, float* out_score,
                        pisa_stream_t stream) {

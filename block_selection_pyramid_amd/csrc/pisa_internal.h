@@ -80,8 +80,11 @@ inline bool route_scores_forced(const Geo& g, int dtype) { return dtype == PISA_
 // prefix of the child level, a gather's does not.  The dense launch covers levels L down
 // to dense_bottom(g), the highest routing levels whose child level has at most
 // kDenseMaxChildren nodes (n[L-1] <= 2gK always qualifies, so L >= 3 implies a dense
-// launch); the gather launch walks the levels below, down to 2.
-constexpr int kDenseMaxChildren = 2048;
+// launch); the gather launch walks the levels below, down to 2.  Measured at 256K-1M
+// tokens: a level over 2048 children costs a little more dense than gathered, one over
+// 1024 children clearly less (the dense cost halves with each level up, a gathered
+// level's stays the same).
+constexpr int kDenseMaxChildren = 1024;
 inline int dense_bottom(const Geo& g) {
   int l = 3;
   while (l < g.L && g.n[l - 1] > kDenseMaxChildren) ++l;

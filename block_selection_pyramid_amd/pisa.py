@@ -82,7 +82,8 @@ class Problem:
 _lib = None
 
 EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
-           "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs", "pisa_select_decode",
+           "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs",
+           "pisa_prefill_dense_levels", "pisa_select_decode",
            "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
            "pisa_attention_workspace_bytes",
            "pisa_status_string", "pisa_version")
@@ -109,6 +110,7 @@ def load(path: str | None = None):
     lib.pisa_select_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.pisa_select_prefill_staged.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp, ctypes.c_int32, vp]
     lib.pisa_prefill_routed_pairs.argtypes = [P, vp, sz, vp, vp]
+    lib.pisa_prefill_dense_levels.argtypes = [P, vp, vp]
     lib.pisa_select_decode.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.pisa_bsa_select_prefill.argtypes = [P, vp, vp, vp, vp, vp]
     lib.pisa_append_keys.argtypes = [P, vp, vp, vp, ctypes.c_int32, vp, vp]
@@ -318,6 +320,14 @@ def select_prefill_staged(p: Problem, q, k, pyramid, ws, out_idx, out_score, eve
     _check(load().pisa_select_prefill_staged(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, arr, 6,
                                              _stream(stream)), "pisa_select_prefill_staged")
     return out_idx, out_score
+
+
+def dense_levels(p: Problem) -> tuple[int, int]:
+    """(top, bottom) of the levels the bf16 prefill routes densely; (0, 0) if none."""
+    top, bot = ctypes.c_int32(), ctypes.c_int32()
+    _check(load().pisa_prefill_dense_levels(ctypes.byref(p.c()), ctypes.byref(top), ctypes.byref(bot)),
+           "pisa_prefill_dense_levels")
+    return top.value, bot.value
 
 
 def routed_pairs(p: Problem, ws: torch.Tensor, stream=None) -> int:

@@ -162,8 +162,9 @@ int pisa_select_decode(const pisa_problem* p, const void* q, const void* k_cache
  * Same as pisa_select_prefill, and additionally records caller-created HIP events
  * (hipEvent_t handles, e.g. from hipEventCreate) on `stream` at the stage boundaries:
  * events[0] before the first kernel, events[1] after counter clearing and the routing of
- * levels L..3 (bf16: the dense upper-level launch), events[2] after the routing of level
- * 2, events[3] after leaf grouping (scan + scatter), events[4] after leaf scoring,
+ * the upper levels (bf16: the dense launch, levels of pisa_prefill_dense_levels),
+ * events[2] after the routing of the levels below it down to level 2 (fp32: all levels),
+ * events[3] after leaf grouping (scan + scatter), events[4] after leaf scoring,
  * events[5] after forced blocks + final Top-K.  n_events must be 6.  Stages a problem does
  * not use (L < 3; fp32 inputs walk all levels in one launch and score leaves query-major
  * in stage 4) record their boundary events back to back.  For per-kernel timing of the
@@ -181,6 +182,17 @@ int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void*
  */
 int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size_t workspace_bytes,
                               int64_t* routed_pairs, pisa_stream_t stream);
+
+/*
+ * Host only: how pisa_select_prefill splits the routing walk for p.  The bf16 path scores
+ * levels *dense_top = L down to *dense_bottom densely, every visible node for all queries
+ * of a leaf block at once, and walks the levels below down to level 2 by per-query gathers;
+ * the dense launch covers a level while its child level has at most 1024 nodes.  Both are 0
+ * when there is no dense launch (L < 3, or fp32 inputs, which walk every level by gathers).
+ * The top-down walk and its result do not depend on the split.  Returns PISA_OK, or the
+ * status pisa_select_prefill would return for an invalid or unsupported p.
+ */
+int pisa_prefill_dense_levels(const pisa_problem* p, int32_t* dense_top, int32_t* dense_bottom);
 
 /* Static description of a status code. */
 /*

@@ -73,6 +73,34 @@ def test_sizes(pisa):
     assert pisa.workspace_bytes(p, pisa.DECODE) == 0
 
 
+@pytest.mark.parametrize("N,K", [(1024, 4), (4096, 8), (16384, 32), (65536, 8), (131072, 8), (131072 + 64, 8),
+                                 (262144, 8), (262144 + 1, 8), (300000, 8), (1 << 20, 8)])
+def test_dense_level_split(pisa, N, K):
+    # bf16: levels L .. bottom are scored densely, where bottom is the highest level >= 3
+    # whose child level has at most 1024 nodes (the top level always qualifies: its
+    # child level has at most 2gK <= 64 nodes); fp32 and L < 3 have no dense launch
+    nodes = oracle.levels(N, 64, K, 2)
+    L = len(nodes) - 1
+    bf = pisa.Problem(1, N, 4, 1, 128, 64, K, 2, dtype=pisa.BF16)
+    top, bot = pisa.dense_levels(bf)
+    if L < 3:
+        assert (top, bot) == (0, 0)
+    else:
+        want = min(l for l in range(3, L + 1) if nodes[l - 1] <= 1024 or l == L)
+        assert (top, bot) == (L, want)
+        assert 3 <= bot <= top
+    assert pisa.dense_levels(pisa.Problem(1, N, 4, 1, 128, 64, K, 2, dtype=pisa.F32)) == (0, 0)
+
+
+def test_dense_level_split_rejects_bad_arguments(pisa):
+    lib = pisa.load()
+    p = pisa.Problem(1, 4096, 4, 1, 128, 64, 8, 2)
+    t = ctypes.c_int32()
+    assert lib.pisa_prefill_dense_levels(ctypes.byref(p.c()), None, ctypes.byref(t)) == 1
+    bad = pisa.Problem(1, 0, 4, 1, 128, 64, 8, 2)
+    assert lib.pisa_prefill_dense_levels(ctypes.byref(bad.c()), ctypes.byref(t), ctypes.byref(t)) == 1
+
+
 def _call_prefill(pisa, p, ws_bytes=1 << 40, q=0x1000, k=0x1000, pyr=0x1000, ws=0x1000, oi=0x1000, os_=0x1000):
     lib = pisa.load()
     return lib.pisa_select_prefill(ctypes.byref(p.c()), q, k, pyr, ws, ws_bytes, oi, os_, None)

@@ -236,12 +236,12 @@ def test_prefill_workload_sampled(env, name, n_random):
 
 
 def test_prefill_gather_below_dense_levels(env):
-    # n_2 > 2048 (N > 256K tokens): the dense launch stops above level 3 and the gather
-    # launch walks levels 3 and 2
+    # n_3 > 1024 (N > 256K tokens): the dense launch stops above level 4 and the gather
+    # launch walks levels 4, 3 and 2 (at 256K it walks 3 and 2)
     w = synth.custom(name="300k-G4", batch=1, seq_len=300000, n_q_heads=4, n_kv_heads=1, head_dim=128, top_k=8,
                      seed=77, needles=1024)
     nodes = oracle.levels(w.seq_len, 64, 8, 2)
-    assert nodes[2] > 2048 and nodes[3] <= 2048
+    assert nodes[3] > 1024 and nodes[4] <= 1024
     p, op, q, k, needles, pyr, outs = gpu_prefill(env, w)
     opyr = oracle.build_pyramid(op, k)
     idx, sc = outs[0]
