@@ -128,6 +128,19 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
   }
   __syncthreads();
 
+  const T* keys = k + (int64_t)bh * kstride * D;
+  // one tile score into tsc[t], by the whole wavefront
+  auto score_tile = [&](int t, int j) {
+    float s;
+    if constexpr (std::is_same<T, bf16>::value) {
+      MfmaWalk<D, G, 1> tw;  // this wavefront's query fragments
+      tw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
+      s = score_tile_mfma<D, G>(keys, j, i, geo.N, geo.C, tw.qb[0], lane, geo.s, geo.s_log2e);
+    } else {
+      s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
+    }
+    if (lane == 0) tsc[t] = s;
+  };
   if (wave == 0) {
     int nx;
     const int32_t* X;
@@ -150,27 +163,15 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
       if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
       tj[lane] = leaf;
     }
-    if (lane < nf) tj[twoK + lane] = lane == 0 ? F[0] : (lane == 1 ? F[1] : F[2]);
+  } else if (wave <= nf) {
+    // the forced tiles are known up front: wavefronts 1..nf score them during the walk
+    score_tile(twoK + wave - 1, wave == 1 ? F[0] : (wave == 2 ? F[1] : F[2]));
   }
   __syncthreads();
-  const T* keys = k + (int64_t)bh * kstride * D;
-  if constexpr (std::is_same<T, bf16>::value) {
-    // every wavefront scores its tiles on the matrix cores with its own query fragments
-    MfmaWalk<D, G, 1> tw;
-    tw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
-    for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
-      const int j = tj[t];
-      if (j < 0) continue;
-      const float s = score_tile_mfma<D, G>(keys, j, i, geo.N, geo.C, tw.qb[0], lane, geo.s, geo.s_log2e);
-      if (lane == 0) tsc[t] = s;
-    }
-  } else {
-    for (int t = wave; t < twoK + nf; t += kDecodeWaves) {
-      const int j = tj[t];
-      if (j < 0) continue;
-      const float s = score_tile_valu<T, D, G>(keys, j, i, geo.N, geo.C, qs, lane, geo.s);
-      if (lane == 0) tsc[t] = s;
-    }
+  // the routed leaf candidates (forced blocks excluded), at most one tile per wavefront
+  for (int t = wave; t < twoK; t += kDecodeWaves) {
+    const int j = tj[t];
+    if (j >= 0) score_tile(t, j);
   }
   __syncthreads();
   if (wave == 0) {

@@ -290,10 +290,12 @@ struct MfmaWalk {
         my = xl < nx ? kg[xl] : 0ull;
         const float lo_x = xl < nx ? sg[xl] - eg[xl] : 0.f, up_x = xl < nx ? sg[xl] + eg[xl] : 0.f;
         int may = 0, sure = 0;  // others that may / surely score above this candidate
-        for (int y = 0; y < nx; ++y) {
-          if (y == xl || kg[y] == 0ull) continue;
-          may += sg[y] + eg[y] >= lo_x;
-          sure += sg[y] - eg[y] > up_x;
+#pragma unroll 8
+        for (int y = 0; y < nx; ++y) {  // branch-free and unrolled: the LDS reads go out together
+          const bool other = y != xl && kg[y] != 0ull;
+          const float sy = sg[y], ey = eg[y];
+          may += other && sy + ey >= lo_x;
+          sure += other && sy - ey > up_x;
         }
         const int cls = my == 0ull ? -1 : (may < K ? 2 : (sure >= K ? 0 : 1));
         const unsigned long long unc = __ballot(cls == 1);
@@ -319,6 +321,7 @@ struct MfmaWalk {
         w->key[lane] = xl < nx ? my : 0ull;
         wave_sync();
         const int32_t* cg = w->cls + gl * CW;
+#pragma unroll 8
         for (int y = 0; y < nx; ++y) rank += cg[y] > cls || (cg[y] == cls && kg[y] > my);
       } else {
         score<false>(geo, bq, l, nx, w->X, w->key, nullptr, nullptr, lane);
