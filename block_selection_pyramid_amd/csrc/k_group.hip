@@ -1,10 +1,13 @@
 // Leaf grouping: "groups queries that need the same leaf block and scores them together"
 // ("Block Sparse Attention with Log-Linear Complexity", rcap.io explainer, kernel
-// paragraph).  A counting sort over leaf blocks: the routing kernel histograms the
-// candidates per (batch, KV head, leaf block); here an exclusive scan turns the counts
-// into list offsets and into offsets of fixed-size work chunks, and a scatter writes each
-// (query, slot) candidate into its block's list.  Order inside a list does not affect any
-// result: every entry's score is computed on its own and written back to its slot.
+// paragraph).  A counting sort: the routing kernel histograms the routed pairs per
+// (batch, KV head, level-2 node), whose two children are adjacent leaf blocks that the
+// prefill leaf kernel scores together; here an exclusive scan turns the counts into list
+// offsets and into offsets of fixed-size work chunks, and a scatter writes each entry into
+// its list.  Block-sparse attention sorts its (query, block) pairs by single leaf blocks
+// with the same scan and scatter_hist_kernel / scatter_kernel.  Order inside a list does
+// not affect any result: every entry's score is computed on its own and written back to
+// its slot.
 #include "dev_common.h"
 
 namespace pisa {
@@ -104,7 +107,84 @@ __global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __rest
   }
 }
 
+// Leaf-pair lists: the children 2m, 2m+1 of a kept level-2 node m sit in slots 2r, 2r+1
+// of a query group's row (either may be -1: forced, not visible or missing).  Entry
+// (i << 6 | r) goes to list m once when either slot holds a block.
+__device__ __forceinline__ int pair_node(const int32_t* __restrict__ slots2) {
+  const int a = slots2[0], c = slots2[1];
+  return a >= 0 ? a >> 1 : (c >= 0 ? c >> 1 : -1);
+}
+
+__global__ __launch_bounds__(256) void scatter_pairs_kernel(const int32_t* __restrict__ cand, int64_t pairs,
+                                                            int32_t N, int32_t K, int32_t n1p,
+                                                            const int32_t* __restrict__ off,
+                                                            int32_t* __restrict__ cursor,
+                                                            int32_t* __restrict__ entries) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= pairs) return;
+  const int node = pair_node(cand + 2 * t);
+  if (node < 0) return;
+  const int r = (int)(t % K);
+  const int64_t qg = t / K;  // bh * N + i
+  const int bh = (int)(qg / N), i = (int)(qg % N);
+  const int list = bh * n1p + node;
+  const int pos = off[list] + atomicAdd(&cursor[list], 1);
+  entries[pos] = (i << 6) | r;
+}
+
+// Workgroup = kLeafQueries consecutive queries of one (b, h), as scatter_hist_kernel, over
+// level-2 nodes.
+__global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* __restrict__ cand, int32_t N,
+                                                                 int32_t BH, int32_t K, int32_t n1p,
+                                                                 const int32_t* __restrict__ off,
+                                                                 int32_t* __restrict__ cursor,
+                                                                 int32_t* __restrict__ entries) {
+  extern __shared__ int lds[];
+  int* hist = lds;         // n1p counts, then reserved bases
+  int* lcur = lds + n1p;   // n1p local cursors
+  const int bh = blockIdx.x % BH;
+  const int q0 = (blockIdx.x / BH) * kLeafQueries;
+  const int q1 = min(N, q0 + kLeafQueries);
+  for (int t = threadIdx.x; t < n1p; t += 256) {
+    hist[t] = 0;
+    lcur[t] = 0;
+  }
+  __syncthreads();
+  const int32_t* c = cand + ((int64_t)bh * N + q0) * 2 * K;
+  const int n = (q1 - q0) * K;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int node = pair_node(c + 2 * t);
+    if (node >= 0) atomicAdd(&hist[node], 1);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n1p; t += 256) {
+    const int h = hist[t];
+    if (h) hist[t] = off[bh * n1p + t] + atomicAdd(&cursor[bh * n1p + t], h);
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int node = pair_node(c + 2 * t);
+    if (node < 0) continue;
+    const int pos = hist[node] + atomicAdd(&lcur[node], 1);
+    entries[pos] = ((q0 + t / K) << 6) | (t % K);
+  }
+}
+
 }  // namespace
+
+int launch_scatter_pairs(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
+                         hipStream_t st) {
+  if (g.n1p <= kHistMaxBins) {
+    const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+    scatter_pairs_hist_kernel<<<grid, 256, 2 * sizeof(int) * (size_t)g.n1p, st>>>(cand, g.N, g.B * g.Hkv, g.K,
+                                                                                    g.n1p, off, cursor, entries);
+    return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+  }
+  const int64_t pairs = (int64_t)g.B * g.Hkv * g.N * g.K;
+  scatter_pairs_kernel<<<(unsigned)((pairs + 255) / 256), 256, 0, st>>>(cand, pairs, g.N, g.K, g.n1p, off, cursor,
+                                                                         entries);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
 
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st) {
   scan_kernel<<<1, kScanThreads, 0, st>>>(cnt, M, qc, off, choff);

@@ -7,13 +7,14 @@
 // (leaf LSE over raw keys; first, previous and current blocks forced in) and kernels
 // paragraph (GQA heads share the selection).
 //
-// The pages reuse a key tile across up to four queries.  Here a workgroup stages one
-// 64 x d bf16 key tile in LDS and streams the (query, slot) entries of that block's list
-// through v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from LDS, B = 16 dims x 32
-// columns where a column is one (query, head) pair of a listed entry (32/G entries per
-// wavefront), so every MFMA is dense.  The epilogue takes a 64-key LSE per column in
-// registers (one cross-lane exchange), sums the G heads of an entry with shuffles and
-// writes the score to the entry's slot.
+// The pages reuse a key tile across up to four queries.  Here the routed candidates are
+// grouped by level-2 node (its two children are adjacent leaf blocks, routed together): a
+// workgroup stages the node's two 64 x d bf16 key tiles in LDS and streams the entries of
+// that node's list through v_mfma_f32_32x32x16_bf16: A = 32 keys x 16 dims from LDS,
+// B = 16 dims x 32 columns where a column is one (query, head) pair of a listed entry
+// (32/G entries per column group), so every MFMA is dense.  The epilogue takes a 64-key
+// LSE per column and child in registers (one cross-lane exchange), sums the G heads of an
+// entry with DPP moves and writes the two scores to the entry's slots.
 //
 // MFMA operand layout (v_mfma_f32_32x32x16_bf16, wave64): lane l supplies row (l & 31)
 // of A and column (l & 31) of B, each with the 8 consecutive k of group (l >> 5); the
@@ -26,61 +27,108 @@ namespace pisa {
 
 namespace {
 
-// Workgroup = one chunk of a leaf block's list (QC = 128/G entries); each wavefront
-// scores 32/G entries (32 columns = (entry, head) pairs per MFMA tile).
+// Workgroup = one chunk of a level-2 node's list (QC = 4 kLeafColGroups 32/G entries):
+// the node's two leaf blocks (128 keys) are staged in LDS once, and each wavefront scores
+// kLeafColGroups column groups of 32 (entry, head) columns against both, loading the next
+// group's query fragments while it scores the current one.  A query that routed through
+// the node needs both children unless one is forced (scored elsewhere) or not visible;
+// both are scored, and the final Top-K reads only the slots that hold a routed block, so
+// one gather of the query rows serves two leaf scores.
+//
+// Chunk order is XCD-aware: workgroups are dispatched round-robin over the 8 XCDs
+// (blockIdx mod 8), so XCD x takes the contiguous chunk range [x per, (x + 1) per) in
+// order and the chunks of one list share one L2 (the node's key tiles are fetched once).
 template <int D, int G>
-__global__ __launch_bounds__(256) void leaf_mfma_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+__global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                         Geo geo, const int32_t* __restrict__ off,
                                                         const int32_t* __restrict__ choff,
                                                         const int32_t* __restrict__ entries, int32_t M,
                                                         float* __restrict__ lscore) {
-  constexpr int EW = 32 / G;   // entries per wavefront
-  constexpr int QC = 128 / G;  // entries per chunk (workgroup)
+  constexpr int CPG = 32 / G;  // entries per column group
+  constexpr int NCG = kLeafColGroups;
+  constexpr int QC = 4 * NCG * CPG;
   constexpr int KS = D / 16;
-  __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
+  constexpr int LDSR = D + 8;
+  __shared__ __attribute__((aligned(16))) bf16 kt[2 * kLeaf * LDSR];
 
-  const int c = blockIdx.x;
-  if (c >= choff[M]) return;  // uniform: grid is an upper bound on the chunk count
-  int lo = 0, hi = M;         // largest list whose first chunk is <= c
+  const int nch = choff[M];
+  const int per = (nch + 7) >> 3;
+  const int jx = (int)(blockIdx.x >> 3);
+  if (jx >= per) return;  // uniform: the grid is an upper bound on the chunk count
+  const int c = (int)(blockIdx.x & 7) * per + jx;
+  if (c >= nch) return;
+  int lo = 0, hi = M;  // largest list whose first chunk is <= c
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (choff[mid] <= c) lo = mid; else hi = mid;
   }
   const int list = lo;
-  const int bh = list / geo.n1, j = list % geo.n1;
+  const int bh = list / geo.n1p, m = list % geo.n1p;
   const int e0 = off[list] + (c - choff[list]) * QC;
   const int e1 = min(e0 + QC, off[list + 1]);
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
-  const int e = e0 + wave * EW + col / G;
   const int r = col % G;
-  const bool valid = e < e1;
-  const int ent = valid ? entries[e] : 0;
-  const int i = ent >> 6, slot = ent & 63;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-  // query fragments first: their latency overlaps the key-tile staging
+  const bf16* qh = q + ((int64_t)b * geo.Hq + h * G + r) * geo.N * D;
+  // entry of this lane's column in column group u of the wavefront (-1: none)
+  auto entry = [&](int u) {
+    const int e = e0 + (u * 4 + wave) * CPG + col / G;
+    return e < e1 ? entries[e] : -1;
+  };
+  int ent = entry(0);
   bf16x8 bq[KS];
-  load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * geo.N + i) * D, valid, hh, bq);
+  // query fragments first: their latency overlaps the key-tile staging
+  load_bfrag<D>(qh + (int64_t)(ent >> 6) * D, ent >= 0, hh, bq);
 
-  stage_tile<D>(k + (int64_t)bh * geo.N * D, j * kLeaf, geo.N, kt);
+  const bf16* kb = k + (int64_t)bh * geo.N * D;
+  const bool two = 2 * m + 1 < geo.n1;  // the node's second child exists
+  stage_tile<D>(kb, 2 * m * kLeaf, geo.N, kt);
+  if (two) stage_tile<D>(kb, (2 * m + 1) * kLeaf, geo.N, kt + kLeaf * LDSR);
   __syncthreads();
+  // keys present in each child (>= 1); only a short last block masks
+  const int live0 = min(kLeaf, geo.N - 2 * m * kLeaf);
+  const int live1 = two ? min(kLeaf, geo.N - (2 * m + 1) * kLeaf) : 0;
+  const int twoK = 2 * geo.K;
 
-  f32x16 acc0, acc1;
-  tile_mfma32<D>(kt, bq, lane, acc0, acc1);
-  // Routed blocks lie before the query's previous block, so all 64 keys exist and are
-  // causal; a short tail block is still masked for safety.
-  const int live = min(kLeaf, geo.N - j * kLeaf);
-  if (live < kLeaf) {
+  for (int u = 0; u < NCG; ++u) {
+    if (e0 + (u * 4 + wave) * CPG >= e1) break;  // uniform across the wavefront
+    const int ent_n = u + 1 < NCG ? entry(u + 1) : -1;
+    bf16x8 bqn[KS];
+    load_bfrag<D>(qh + (int64_t)(ent_n >> 6) * D, ent_n >= 0, hh, bqn);
+
+    f32x16 acc0, acc1;
+    tile_mfma32<D>(kt, bq, lane, acc0, acc1);
+    if (live0 < kLeaf) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      if (key_row(v, hh) >= live) acc0[v] = -INFINITY;
-      if (32 + key_row(v, hh) >= live) acc1[v] = -INFINITY;
+      for (int v = 0; v < 16; ++v) {
+        if (key_row(v, hh) >= live0) acc0[v] = -INFINITY;
+        if (32 + key_row(v, hh) >= live0) acc1[v] = -INFINITY;
+      }
     }
+    const float lse0 = group_sum<G>(column_lse32(acc0, acc1, geo.s, geo.s_log2e));
+    float lse1 = 0.f;
+    if (two) {
+      tile_mfma32<D>(kt + kLeaf * LDSR, bq, lane, acc0, acc1);
+      if (live1 < kLeaf) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (key_row(v, hh) >= live1) acc0[v] = -INFINITY;
+          if (32 + key_row(v, hh) >= live1) acc1[v] = -INFINITY;
+        }
+      }
+      lse1 = group_sum<G>(column_lse32(acc0, acc1, geo.s, geo.s_log2e));
+    }
+    if (hh == 0 && r == 0 && ent >= 0) {
+      float* dst = lscore + ((int64_t)bh * geo.N + (ent >> 6)) * twoK + 2 * (ent & 63);
+      dst[0] = lse0;
+      if (two) dst[1] = lse1;
+    }
+    ent = ent_n;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) bq[s2] = bqn[s2];
   }
-  float lse = column_lse32(acc0, acc1, geo.s, geo.s_log2e);
-  lse = group_sum<G>(lse);
-  if (hh == 0 && r == 0 && valid) lscore[((int64_t)bh * geo.N + i) * (2 * geo.K) + slot] = lse;
 }
 
 // Workgroup = one leaf block of queries (64) of one (b, h): stages the forced blocks'
@@ -217,16 +265,17 @@ template <int D>
 int leaf_d(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
            const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
   const int qc = chunk_entries(g.G);
-  const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
-  const int64_t grid = (slots + qc - 1) / qc + M;  // bound on sum over lists of ceil(count/qc)
+  const int64_t pairs = (int64_t)g.B * g.Hkv * g.N * g.K;
+  // bound on the sum over lists of ceil(count / qc), rounded up to whole XCD rounds
+  const int64_t grid = ((pairs + qc - 1) / qc + M + 7) / 8 * 8;
   const bf16* qq = (const bf16*)q;
   const bf16* kk = (const bf16*)k;
   switch (g.G) {
-    case 1: leaf_mfma_kernel<D, 1><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 2: leaf_mfma_kernel<D, 2><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 4: leaf_mfma_kernel<D, 4><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 8: leaf_mfma_kernel<D, 8><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 16: leaf_mfma_kernel<D, 16><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 1: leaf_pair_kernel<D, 1><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 2: leaf_pair_kernel<D, 2><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 4: leaf_pair_kernel<D, 4><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 8: leaf_pair_kernel<D, 8><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 16: leaf_pair_kernel<D, 16><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;

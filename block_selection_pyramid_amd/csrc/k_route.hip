@@ -1,12 +1,13 @@
 // Prefill routing (stage one of the two-stage prefill: walk levels L..2 per query group)
-// plus the histogram of leaf candidates per (batch, KV head, leaf block) that the leaf
-// grouping needs.  bf16 inputs: levels L..3 are scored densely per leaf block (separate
+// plus the histogram of routed (query group, level-2 node) pairs per (batch, KV head,
+// level-2 node) that the leaf grouping needs.  bf16 inputs: levels L..3 are scored densely per leaf block (separate
 // launch), level 2 here on the matrix cores from the pyramid's hi/lo routing copy, up to
 // four consecutive queries per wavefront; fp32 inputs: one wavefront per query group on
 // the VALU for the whole walk.
 //
 // Output per query group: 2K slots of leaf candidates that are not forced blocks (the
-// forced blocks are scored separately), -1 elsewhere.
+// forced blocks are scored separately), -1 elsewhere; slots 2r and 2r+1 are the children
+// of the kept level-2 node of rank r.
 #include <type_traits>
 
 #include "route_dev.h"
@@ -20,8 +21,7 @@ constexpr int kLowerQueries = 512;  // queries per level-2 routing workgroup
 // fp32 inputs: one wavefront per query group, VALU scorer.
 template <int D, int G>
 __global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict__ q, const float* __restrict__ pyr,
-                                                         Geo geo, int32_t* __restrict__ cand,
-                                                         int32_t* __restrict__ cnt) {
+                                                         Geo geo, int32_t* __restrict__ cand) {
   __shared__ float qs_all[4][G * (D + kQPad)];
   __shared__ WalkLds wl_all[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -44,7 +44,6 @@ __global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict
     int leaf = lane < nx ? w->X[lane] : -1;
     if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
     cand[((int64_t)bh * geo.N + i) * twoK + lane] = leaf;
-    if (leaf >= 0) atomicAdd(&cnt[bh * geo.n1 + leaf], 1);
   }
 }
 
@@ -63,16 +62,16 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
                                                          Geo geo, int32_t l_x, const int32_t* __restrict__ x2,
                                                          int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
   using Walk = MfmaWalk<D, G, GPW>;
-  // per-leaf-block histogram (when the blocks fit), flushed with one global add per bin
+  // per-level-2-node histogram (when the nodes fit), flushed with one global add per bin
   extern __shared__ __attribute__((aligned(16))) int hist[];
   __shared__ WalkLdsM<GPW> wl_all[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int BH = geo.B * geo.Hkv;
   const int bh = blockIdx.x % BH;
   const int qr0 = (blockIdx.x / BH) * kLowerQueries;
-  const bool lhist = geo.n1 <= kHistMaxBins;
+  const bool lhist = geo.n1p <= kHistMaxBins;
   if (lhist) {
-    for (int t = threadIdx.x; t < geo.n1; t += 256) hist[t] = 0;
+    for (int t = threadIdx.x; t < geo.n1p; t += 256) hist[t] = 0;
     __syncthreads();
   }
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
@@ -106,21 +105,26 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
     } else {
       nx = mw.init_level(geo, bq, 1, w, lane);
     }
+    int leaf = -1;
     if (xl < twoK && i < geo.N) {
-      int leaf = xl < nx ? w->X[gl * Walk::CW + xl] : -1;
+      leaf = xl < nx ? w->X[gl * Walk::CW + xl] : -1;
       if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
       __builtin_nontemporal_store(leaf, &cand[row * twoK + xl]);
-      if (leaf >= 0) {
-        if (lhist) atomicAdd(&hist[leaf], 1);
-        else atomicAdd(&cnt[bh * geo.n1 + leaf], 1);
-      }
+    }
+    // slots 2r and 2r+1 hold the two children of one kept level-2 node (or -1): count the
+    // pair once, in its even lane, under node = leaf >> 1
+    const int sib = __shfl_xor(leaf, 1);
+    if ((xl & 1) == 0 && (leaf >= 0 || sib >= 0)) {
+      const int node = (leaf >= 0 ? leaf : sib) >> 1;
+      if (lhist) atomicAdd(&hist[node], 1);
+      else atomicAdd(&cnt[bh * geo.n1p + node], 1);
     }
     wave_sync();
   }
   if (lhist) {
     __syncthreads();
-    for (int t = threadIdx.x; t < geo.n1; t += 256)
-      if (hist[t]) atomicAdd(&cnt[bh * geo.n1 + t], hist[t]);
+    for (int t = threadIdx.x; t < geo.n1p; t += 256)
+      if (hist[t]) atomicAdd(&cnt[bh * geo.n1p + t], hist[t]);
   }
 }
 
@@ -133,7 +137,7 @@ int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* p
   }
   if (mid && hipEventRecord(mid, st) != hipSuccess) return PISA_ERR_HIP;
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));
-  const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
+  const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
   const int l_x = g.L >= 3 ? dense_bottom(g) - 1 : 2;  // level of the candidates in x2
   route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, l_x, x2, cand, cnt);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
@@ -168,11 +172,11 @@ int route_d(const Geo& g, int dtype, const void* q, const void* k, const float* 
   dim3 grid((g.N + 3) / 4, g.B * g.Hkv);
   const float* qq = (const float*)q;
   switch (g.G) {
-    case 1: route_valu_kernel<D, 1><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 2: route_valu_kernel<D, 2><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 4: route_valu_kernel<D, 4><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 8: route_valu_kernel<D, 8><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
-    case 16: route_valu_kernel<D, 16><<<grid, 256, 0, st>>>(qq, pyr, g, cand, cnt); break;
+    case 1: route_valu_kernel<D, 1><<<grid, 256, 0, st>>>(qq, pyr, g, cand); break;
+    case 2: route_valu_kernel<D, 2><<<grid, 256, 0, st>>>(qq, pyr, g, cand); break;
+    case 4: route_valu_kernel<D, 4><<<grid, 256, 0, st>>>(qq, pyr, g, cand); break;
+    case 8: route_valu_kernel<D, 8><<<grid, 256, 0, st>>>(qq, pyr, g, cand); break;
+    case 16: route_valu_kernel<D, 16><<<grid, 256, 0, st>>>(qq, pyr, g, cand); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;

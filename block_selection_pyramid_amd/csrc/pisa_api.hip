@@ -43,6 +43,7 @@ int make_geo(const pisa_problem* p, Geo* g) {
   }
   g->L = L;
   g->n1 = g->n[1];
+  g->n1p = (g->n1 + 1) / 2;
   int64_t off = 0;
   for (int l = 1; l <= L; ++l) {
     g->off[l] = (int32_t)off;
@@ -70,7 +71,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 PrefillWs prefill_ws(const Geo& g) {
   PrefillWs w;
   w.slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
-  w.M = g.B * g.Hkv * g.n1;
+  w.M = g.B * g.Hkv * g.n1p;
   size_t o = 0;
   w.cand = o;    o = align256(o + sizeof(int32_t) * w.slots);
   w.lscore = o;  o = align256(o + sizeof(float) * w.slots);
@@ -177,7 +178,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
     return mark(5);
   }
   if ((rc = launch_scan(cnt, w.M, chunk_entries(g.G), off, choff, st)) != PISA_OK) return rc;
-  if ((rc = launch_scatter(g, 2 * g.K, cand, off, cursor, entries, st)) != PISA_OK) return rc;
+  if ((rc = launch_scatter_pairs(g, cand, off, cursor, entries, st)) != PISA_OK) return rc;
   if ((rc = mark(3)) != PISA_OK) return rc;
   if ((rc = launch_leaf_mfma(g, q, k, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
   if ((rc = mark(4)) != PISA_OK) return rc;
@@ -215,16 +216,16 @@ int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size
   if (workspace_bytes < w.total) return PISA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (hipStreamSynchronize(st) != hipSuccess) return PISA_ERR_HIP;
-  // the histogram of routed candidates (cnt) is complete after routing in both paths
-  const int32_t* cnt = (const int32_t*)((const char*)workspace + w.cnt);
+  // every routed leaf candidate holds a block id >= 0 in its slot (-1 elsewhere)
+  const int32_t* cand = (const int32_t*)((const char*)workspace + w.cand);
   int64_t total = 0;
-  const int32_t chunk = 1 << 16;
+  const int64_t chunk = 1 << 20;
   int32_t* host = new (std::nothrow) int32_t[chunk];
   if (!host) return PISA_ERR_INTERNAL;
-  for (int32_t o = 0; o < w.M && rc == PISA_OK; o += chunk) {
-    const int32_t n = w.M - o < chunk ? w.M - o : chunk;
-    if (hipMemcpy(host, cnt + o, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess) rc = PISA_ERR_HIP;
-    for (int32_t t = 0; t < n && rc == PISA_OK; ++t) total += host[t];
+  for (int64_t o = 0; o < w.slots && rc == PISA_OK; o += chunk) {
+    const int64_t n = w.slots - o < chunk ? w.slots - o : chunk;
+    if (hipMemcpy(host, cand + o, sizeof(int32_t) * n, hipMemcpyDeviceToHost) != hipSuccess) rc = PISA_ERR_HIP;
+    for (int64_t t = 0; t < n && rc == PISA_OK; ++t) total += host[t] >= 0;
   }
   delete[] host;
   if (rc == PISA_OK) *routed_pairs = total;

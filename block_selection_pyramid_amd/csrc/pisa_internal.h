@@ -16,6 +16,7 @@ constexpr int kMaxCand = 64;  // g*K <= 64 candidates per level (one per lane)
 // Geometry of one problem, passed by value to every kernel.
 struct Geo {
   int32_t B, Hq, Hkv, G, N, d, C, K, g, L, n1, T;
+  int32_t n1p;     // ceil(n1 / 2): level-2 nodes as leaf-block pairs (g = 2), one prefill leaf list each
   int32_t scorer;  // enum pisa_scorer of the routing levels
   float s;        // scale applied to every dot product
   float s_log2e;  // s * log2(e), for exp2-based LSE
@@ -30,13 +31,16 @@ struct Geo {
 struct PrefillWs {
   size_t cand, lscore, cnt, cursor, off, choff, entries, fsc, total;
   int64_t slots;  // B*Hkv*N*2K
-  int32_t M;      // B*Hkv*n1 leaf lists
+  int32_t M;      // B*Hkv*n1p leaf-pair lists
 };
 
 int make_geo(const pisa_problem* p, Geo* g);  // PISA_OK or PISA_ERR_INVALID_ARG
 int supported(const Geo& g, int dtype, int mode);
 PrefillWs prefill_ws(const Geo& g);
-inline int chunk_entries(int G) { return 128 / G; }  // leaf entries (query groups) per chunk
+// Leaf-pair entries (query groups) per chunk of the prefill leaf kernel: four wavefronts,
+// kLeafColGroups column groups of 32 (query, head) columns each.
+constexpr int kLeafColGroups = 4;
+inline int chunk_entries(int G) { return 4 * kLeafColGroups * 32 / G; }
 // Queries per workgroup of the level-2 routing launch and of the scatter; both keep a
 // per-leaf-block histogram in LDS when there are at most kHistMaxBins leaf blocks.
 constexpr int kLeafQueries = 2048;
@@ -94,6 +98,11 @@ int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t
 // scatter of per_row candidate slots per query group (-1 = none) into per-leaf-block lists
 int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
                    int32_t* entries, hipStream_t st);
+// scatter of the 2K routed leaf slots per query group into per-level-2-node lists: slots 2r
+// and 2r+1 (children of the kept node of rank r) give one entry (i << 6 | r) when either
+// holds a block
+int launch_scatter_pairs(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
+                         hipStream_t st);
 int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
                      const int32_t* entries, int32_t M, float* lscore, hipStream_t st);
 int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const float* fsc, int32_t* out_idx,
