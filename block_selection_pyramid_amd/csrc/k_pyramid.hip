@@ -5,9 +5,9 @@
 // to the routing copy, scaled by s log2(e) and split into bf16 hi + lo.
 //
 // One workgroup reduces a subtree: 16 consecutive nodes of level l0 (each the mean of
-// `fan` rows of the level below: C raw keys for l0 = 1, g nodes above that) and then the
+// FAN rows of the level below: C raw keys for l0 = 1, g nodes above that) and then the
 // up-to-4 levels above them from LDS.  For l0 = 1 the workgroup streams 16*C contiguous
-// key rows with 16-byte loads (16 rows per pass for d = 128 bf16), so k is read from HBM
+// key rows with 16-byte loads, four nodes' rows in flight at once, so k is read from HBM
 // exactly once.  A further launch with l0 = 6, 11, ... covers taller pyramids.
 #include "dev_common.h"
 
@@ -58,11 +58,67 @@ __device__ __forceinline__ float rows_mean(const Tin* s, int r0, int r1,
   return m;
 }
 
-template <typename Tin, int D>
+// Means of the nb <= NB consecutive nodes j0 .. j0+nb-1, node j over rows [j*FAN,
+// min(j*FAN + FAN, src_rows)) of s, with rows_mean's arithmetic for each node (a thread adds
+// its rows of the node in row order, then thread e < D adds the RPP partial sums in order
+// and divides), so a subtree build and an incremental append give the same bits.  Every
+// load of the NB nodes is issued before the first addition.  Returns the means in threads
+// e < D.  Every thread of the workgroup must call it (it synchronises twice).
+template <typename Tin, int D, int FAN, int NB>
+__device__ __forceinline__ void rows_mean_multi(const Tin* s, int j0, int nb, int src_rows,
+                                                float (&red)[NB][RowsShape<Tin, D>::RPP][D], int tid,
+                                                float (&m)[NB]) {
+  constexpr int VEC = RowsShape<Tin, D>::VEC, TPR = RowsShape<Tin, D>::TPR, RPP = RowsShape<Tin, D>::RPP;
+  constexpr int RPT = (FAN + RPP - 1) / RPP;  // rows of a node per thread (at most)
+  const int cseg = tid % TPR, rp = tid / TPR;
+  float x[NB][RPT][VEC];
+  bool ok[NB][RPT];
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    const int r0 = (j0 + u) * FAN, r1 = min(r0 + FAN, src_rows);
+#pragma unroll
+    for (int t = 0; t < RPT; ++t) {
+      const int r = r0 + rp + t * RPP;
+      ok[u][t] = u < nb && rp + t * RPP < FAN && r < r1;
+      Vec<Tin>::load(s + (int64_t)(ok[u][t] ? r : 0) * D + cseg * VEC, x[u][t]);  // row 0 always exists
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < NB; ++u) {
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int t = 0; t < RPT; ++t)
+      if (ok[u][t]) {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) acc[v] += x[u][t][v];
+      }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) red[u][rp][cseg * VEC + v] = acc[v];
+  }
+  __syncthreads();
+  if (tid < D) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      float t = 0.f;
+#pragma unroll 8
+      for (int p = 0; p < RPP; ++p) t += red[u][p][tid];
+      const int r0 = (j0 + u) * FAN;
+      m[u] = t / (float)(min(r0 + FAN, src_rows) - r0);
+    }
+  }
+  __syncthreads();
+}
+
+constexpr int kBuildNodes = 4;  // level-l0 nodes whose rows one workgroup loads at once
+
+// FAN: rows per level-l0 node (C raw keys for l0 = 1, g nodes above).
+template <typename Tin, int D, int FAN>
 __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ src, int64_t src_bh_stride,
-                                                      int32_t src_rows, int32_t fan, float* __restrict__ pyr,
-                                                      Geo geo, int32_t l0) {
-  __shared__ float red[RowsShape<Tin, D>::RPP][D];
+                                                      int32_t src_rows, float* __restrict__ pyr, Geo geo,
+                                                      int32_t l0) {
+  __shared__ float red[kBuildNodes][RowsShape<Tin, D>::RPP][D];
   __shared__ float lvl[2][kSub][D];
 
   const int tid = threadIdx.x;
@@ -72,15 +128,19 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
   const Tin* s = src + (int64_t)bh * src_bh_stride;
   float* P = pyr + (int64_t)bh * geo.T * D;
   bf16* R = reinterpret_cast<bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
-  for (int jb = 0; jb < nodes; ++jb) {
-    const int j = j0 + jb;
-    const int r0 = j * fan;
-    const int r1 = min(r0 + fan, src_rows);
-    const float m = rows_mean<Tin, D>(s, r0, r1, red, tid);
+  for (int jb0 = 0; jb0 < nodes; jb0 += kBuildNodes) {
+    const int nb = min(kBuildNodes, nodes - jb0);
+    float m[kBuildNodes];
+    rows_mean_multi<Tin, D, FAN, kBuildNodes>(s, j0 + jb0, nb, src_rows, red, tid, m);
     if (tid < D) {
-      P[(int64_t)(geo.off[l0] + j) * D + tid] = m;
-      store_rcopy<D>(R, geo.off[l0] + j, tid, m * geo.s_log2e);
-      lvl[0][jb][tid] = m;  // read back only by this thread
+#pragma unroll
+      for (int u = 0; u < kBuildNodes; ++u) {
+        if (u >= nb) break;
+        const int j = j0 + jb0 + u;
+        P[(int64_t)(geo.off[l0] + j) * D + tid] = m[u];
+        store_rcopy<D>(R, geo.off[l0] + j, tid, m[u] * geo.s_log2e);
+        lvl[0][jb0 + u][tid] = m[u];  // read back only by this thread
+      }
     }
   }
   __syncthreads();
@@ -116,10 +176,10 @@ int build_t(const Geo& g, const Tin* k, float* pyr, hipStream_t st) {
   for (int l0 = 1; l0 <= g.L; l0 += kSubLevels + 1) {
     dim3 grid((g.n[l0] + kSub - 1) / kSub, bhs);
     if (l0 == 1) {
-      pyr_sub_kernel<Tin, D><<<grid, 256, 0, st>>>(k, (int64_t)g.N * D, g.N, g.C, pyr, g, 1);
+      pyr_sub_kernel<Tin, D, kLeaf><<<grid, 256, 0, st>>>(k, (int64_t)g.N * D, g.N, pyr, g, 1);
     } else {
       const float* src = pyr + (int64_t)g.off[l0 - 1] * D;
-      pyr_sub_kernel<float, D><<<grid, 256, 0, st>>>(src, (int64_t)g.T * D, g.n[l0 - 1], g.g, pyr, g, l0);
+      pyr_sub_kernel<float, D, 2><<<grid, 256, 0, st>>>(src, (int64_t)g.T * D, g.n[l0 - 1], pyr, g, l0);
     }
     if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   }
