@@ -87,7 +87,10 @@ struct MfmaWalk {
   const char* lds = nullptr;           // staged copy of levels [stage_lo, L-1], or null
   int stage_lo = 1 << 30;              // lowest level held in LDS
   int stage_base = 0;                  // node offset of stage_lo in the pyramid
-  bf16x8 qb[GPW][KS];
+  // Four groups per wavefront use the mixed-row tiles of score_m, whose B operand is each
+  // lane's own query fragment: qb[0] only.  Fewer groups keep one zero-padded B per group.
+  static constexpr bool kMixed = GPW == 4;
+  bf16x8 qb[kMixed ? 1 : GPW][KS];
 
   // row(g, r): pointer to query head r of group g, or nullptr if the group is padding
   // (its columns stay zero; its results are never written).
@@ -95,8 +98,21 @@ struct MfmaWalk {
   __device__ void load_q(RowFn row, int lane) {
     const int n = lane & 15, kg = lane >> 4;
     const int gown = n / G, r = n % G;
+    if constexpr (kMixed) {
+      const bf16* p = gown < GPW ? row(gown, r) : nullptr;
 #pragma unroll
-    for (int g = 0; g < GPW; ++g) {
+      for (int s = 0; s < KS; ++s) {
+        if (p) {
+          qb[0][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 32 * s + 8 * kg));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qb[0][s][e] = (__bf16)0.f;
+        }
+      }
+      return;
+    }
+#pragma unroll
+    for (int g = 0; g < (kMixed ? 1 : GPW); ++g) {
       const bf16* p = (g == gown) ? row(g, r) : nullptr;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -184,18 +200,18 @@ struct MfmaWalk {
         for (int g = 0; g < GPW; ++g)
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[g][tb][s], qb[g][s], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[g][tb][s], qb[kMixed ? 0 : g][s], acc, 0, 0, 0);
             if constexpr (kApprox) {
               // |hi| and |q|: clear the bf16 sign bits (|q| formed at each use: keeping it
               // for the whole walk would cost a wavefront per SIMD)
-              u32x4 qa = __builtin_bit_cast(u32x4, qb[g][s]);
+              u32x4 qa = __builtin_bit_cast(u32x4, qb[kMixed ? 0 : g][s]);
               asm volatile("" : "+v"(qa));
               qa &= 0x7FFF7FFFu;
               const u32x4 ha = __builtin_bit_cast(u32x4, hi[g][tb][s]) & 0x7FFF7FFFu;
               acc2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ha),
                                                              __builtin_bit_cast(bf16x8, qa), acc2, 0, 0, 0);
             } else {
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[g][tb][s], qb[g][s], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[g][tb][s], qb[kMixed ? 0 : g][s], acc, 0, 0, 0);
             }
           }
         float lse[2], err[2];
@@ -244,13 +260,146 @@ struct MfmaWalk {
     wave_sync();
   }
 
+  // score_t for four groups per wavefront with mixed-row tiles.  Tile j (16 child rows)
+  // holds in row block rb (rows 4rb .. 4rb+3) the slots 4j .. 4j+3 (candidates 2j, 2j+1,
+  // two children each) of group (rb + j) mod 4, so one MFMA chain per tile takes every
+  // lane's own query fragment as B (no zero columns).  The MFMA result lane for column
+  // (gown, r) and row block kg = lane >> 4 holds its own group's rows in the tiles with
+  // j = gown - kg (mod 4): one tile of every four.  A level of nx candidates per group
+  // takes ceil(nx / 2) tiles; the hi-only pass loads four tiles per batch, the exact pass
+  // (hi + lo) two.
+  template <bool kLds, bool kApprox>
+  __device__ void score_m(const Geo& geo, int bq, int l, int nx, const int32_t* Xs, uint64_t* keys, float* sc,
+                          float* er, int lane) const {
+    static_assert(GPW == 4, "mixed-row tiles rotate four groups over four row blocks");
+    constexpr int TBM = kApprox ? 4 : 2;  // tiles per batch
+    const bf16* Rc = R + (int64_t)geo.off[l - 1] * 2 * D;
+    const char* Lc = kLds ? lds + (int64_t)(geo.off[l - 1] - stage_base) * kRecLds : nullptr;
+    const int nchild = geo.n[l - 1];
+    const int cshift = l - 2;
+    const int m = lane & 15, kg = lane >> 4;
+    const int gown = m / G, r = m % G;     // epilogue: this lane's column = (group, head)
+    const int rb = m >> 2, v = m & 3;      // loads: this lane's A row = row block, row in it
+    const int jo = (gown - kg) & 3;        // epilogue: tiles j = jo (mod 4) hold this lane's rows
+    const int ntiles = (nx + 1) >> 1;
+    for (int j0 = 0; j0 < ntiles; j0 += TBM) {
+      bf16x8 hi[TBM][KS], lo[TBM][KS];
+      // An invisible or missing child reads node 0 of the level instead (always present);
+      // its rows are masked to -inf in the epilogue, so the loads need no branches.
+#pragma unroll
+      for (int tb = 0; tb < TBM; ++tb) {
+        const int j = j0 + tb;
+        const int ga = (rb + j) & 3;
+        const int x = 2 * j + (v >> 1);
+        const int na = x < nx ? Xs[ga * CW + x] : -1;
+        const int c = na >= 0 ? 2 * na + (v & 1) : -1;
+        const int ca = child_visible(c, nchild, cshift, bq) ? c : 0;
+        if constexpr (kLds) {
+          const char* rp = Lc + (int64_t)ca * kRecLds + 16 * kg;
+#pragma unroll
+          for (int s2 = 0; s2 < KS; ++s2) {
+            hi[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 128 * s2);
+            if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 128 * s2 + 64);
+          }
+        } else {
+          const bf16* rp = Rc + (int64_t)ca * 2 * D + 8 * kg;
+#pragma unroll
+          for (int s2 = 0; s2 < KS; ++s2) {
+            hi[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 64 * s2);
+            if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 64 * s2 + 32);
+          }
+        }
+      }
+      f32x4 acc[TBM], acc2[TBM];
+#pragma unroll
+      for (int tb = 0; tb < TBM; ++tb) {
+        acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc2[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[tb][s2], qb[0][s2], acc[tb], 0, 0, 0);
+          if constexpr (kApprox) {
+            // |hi| and |q|: clear the bf16 sign bits (|q| formed at each use)
+            u32x4 qa = __builtin_bit_cast(u32x4, qb[0][s2]);
+            asm volatile("" : "+v"(qa));
+            qa &= 0x7FFF7FFFu;
+            const u32x4 ha = __builtin_bit_cast(u32x4, hi[tb][s2]) & 0x7FFF7FFFu;
+            acc2[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ha),
+                                                               __builtin_bit_cast(bf16x8, qa), acc2[tb], 0, 0, 0);
+          } else {
+            acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[tb][s2], qb[0][s2], acc[tb], 0, 0, 0);
+          }
+        }
+      }
+      // this lane's tile of the batch (if any): j = j0 + jj with j = jo (mod 4)
+      const int jj = (jo - j0) & 3;
+      const int j = j0 + jj;
+      const bool mine = jj < TBM && j < ntiles;
+      f32x4 a = acc[0], a2 = acc2[0];
+#pragma unroll
+      for (int tb = 1; tb < TBM; ++tb) {
+        a = jj == tb ? acc[tb] : a;
+        a2 = jj == tb ? acc2[tb] : a2;
+      }
+      float lse[2], err[2];
+      int node[2];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int x = 2 * j + p;  // candidate owning result rows 4kg + 2p, +1
+        node[p] = (mine && gown < GPW && x < nx) ? Xs[gown * CW + x] : -1;
+        float y[2], bnd[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int ch = node[p] >= 0 ? 2 * node[p] + c : -1;
+          const bool vis = child_visible(ch, nchild, cshift, bq);
+          y[c] = vis ? a[2 * p + c] : -INFINITY;
+          bnd[c] = vis ? a2[2 * p + c] : 0.f;
+        }
+        const float va = fmaxf(y[0], y[1]), vb = fminf(y[0], y[1]);
+        const float vv = geo.scorer == PISA_LSE ? va + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(vb - va))
+                                                : pair_trunc(va, vb, 1.f, trunc_c2(geo.scorer, true));
+        lse[p] = node[p] >= 0 ? vv : 0.f;
+        // the pair LSE moves by at most the larger child error; 2^-20 |score| more covers
+        // the differing fp32 rounding of the two evaluations
+        err[p] = node[p] >= 0 ? kLoBound * fmaxf(bnd[0], bnd[1]) + 9.6e-7f * fabsf(vv) : 0.f;
+      }
+      lse[0] = group_sum<G>(lse[0]);
+      lse[1] = group_sum<G>(lse[1]);
+      if constexpr (kApprox) {
+        err[0] = group_sum<G>(err[0]);
+        err[1] = group_sum<G>(err[1]);
+      }
+      if (r == 0 && gown < GPW && mine) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int x = 2 * j + p;
+          if (x < nx) {
+            keys[gown * CW + x] = node[p] >= 0 ? cand_key(lse[p], node[p]) : 0ull;
+            if constexpr (kApprox) {
+              sc[gown * CW + x] = lse[p];
+              er[gown * CW + x] = err[p];
+            }
+          }
+        }
+      }
+    }
+    wave_sync();
+  }
+
   template <bool kApprox>
   __device__ void score(const Geo& geo, int bq, int l, int nx, const int32_t* Xs, uint64_t* keys, float* sc,
                         float* er, int lane) const {
-    if (l - 1 >= stage_lo)
-      score_t<true, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
-    else
-      score_t<false, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
+    if constexpr (kMixed) {
+      if (l - 1 >= stage_lo)
+        score_m<true, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
+      else
+        score_m<false, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
+    } else {
+      if (l - 1 >= stage_lo)
+        score_t<true, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
+      else
+        score_t<false, kApprox>(geo, bq, l, nx, Xs, keys, sc, er, lane);
+    }
   }
 
   // Fills X with the visible nodes of level `l` (a prefix of the level) and returns nx.
