@@ -266,13 +266,16 @@ struct MfmaWalk {
   // lane's own query fragment as B (no zero columns).  The MFMA result lane for column
   // (gown, r) and row block kg = lane >> 4 holds its own group's rows in the tiles with
   // j = gown - kg (mod 4): one tile of every four.  A level of nx candidates per group
-  // takes ceil(nx / 2) tiles; the hi-only pass loads four tiles per batch, the exact pass
-  // (hi + lo) two.
+  // takes ceil(nx / 2) tiles; the hi-only pass loads two tiles per batch, the exact pass
+  // (hi + lo) one.
   template <bool kLds, bool kApprox>
   __device__ void score_m(const Geo& geo, int bq, int l, int nx, const int32_t* Xs, uint64_t* keys, float* sc,
                           float* er, int lane) const {
     static_assert(GPW == 4, "mixed-row tiles rotate four groups over four row blocks");
-    constexpr int TBM = kApprox ? 4 : 2;  // tiles per batch
+    // tiles per batch: small batches keep the launch at 126 VGPRs, four wavefronts per SIMD
+    // (256K, gather launch: hi-only batches of 2 and exact ones of 1 tile took 3.05 ms, 2/2
+    // 3.10, 1/1 3.13, 4/2 (three wavefronts per SIMD) 3.17, 8/2 3.37)
+    constexpr int TBM = kApprox ? 2 : 1;
     const bf16* Rc = R + (int64_t)geo.off[l - 1] * 2 * D;
     const char* Lc = kLds ? lds + (int64_t)(geo.off[l - 1] - stage_base) * kRecLds : nullptr;
     const int nchild = geo.n[l - 1];
@@ -331,53 +334,56 @@ struct MfmaWalk {
           }
         }
       }
-      // this lane's tile of the batch (if any): j = j0 + jj with j = jo (mod 4)
-      const int jj = (jo - j0) & 3;
-      const int j = j0 + jj;
-      const bool mine = jj < TBM && j < ntiles;
-      f32x4 a = acc[0], a2 = acc2[0];
+      // this lane's tile in each run of four tiles of the batch (if any): j = jo (mod 4)
 #pragma unroll
-      for (int tb = 1; tb < TBM; ++tb) {
-        a = jj == tb ? acc[tb] : a;
-        a2 = jj == tb ? acc2[tb] : a2;
-      }
-      float lse[2], err[2];
-      int node[2];
+      for (int sb = 0; sb < (TBM + 3) / 4; ++sb) {
+        const int jj = (jo - j0) & 3;
+        const int j = j0 + 4 * sb + jj;
+        const bool mine = jj < (TBM < 4 ? TBM : 4) && j < ntiles;
+        f32x4 a = acc[4 * sb], a2 = acc2[4 * sb];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int x = 2 * j + p;  // candidate owning result rows 4kg + 2p, +1
-        node[p] = (mine && gown < GPW && x < nx) ? Xs[gown * CW + x] : -1;
-        float y[2], bnd[2];
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int ch = node[p] >= 0 ? 2 * node[p] + c : -1;
-          const bool vis = child_visible(ch, nchild, cshift, bq);
-          y[c] = vis ? a[2 * p + c] : -INFINITY;
-          bnd[c] = vis ? a2[2 * p + c] : 0.f;
+        for (int tb = 1; tb < (TBM < 4 ? TBM : 4); ++tb) {
+          a = jj == tb ? acc[4 * sb + tb] : a;
+          a2 = jj == tb ? acc2[4 * sb + tb] : a2;
         }
-        const float va = fmaxf(y[0], y[1]), vb = fminf(y[0], y[1]);
-        const float vv = geo.scorer == PISA_LSE ? va + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(vb - va))
-                                                : pair_trunc(va, vb, 1.f, trunc_c2(geo.scorer, true));
-        lse[p] = node[p] >= 0 ? vv : 0.f;
-        // the pair LSE moves by at most the larger child error; 2^-20 |score| more covers
-        // the differing fp32 rounding of the two evaluations
-        err[p] = node[p] >= 0 ? kLoBound * fmaxf(bnd[0], bnd[1]) + 9.6e-7f * fabsf(vv) : 0.f;
-      }
-      lse[0] = group_sum<G>(lse[0]);
-      lse[1] = group_sum<G>(lse[1]);
-      if constexpr (kApprox) {
-        err[0] = group_sum<G>(err[0]);
-        err[1] = group_sum<G>(err[1]);
-      }
-      if (r == 0 && gown < GPW && mine) {
+        float lse[2], err[2];
+        int node[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const int x = 2 * j + p;
-          if (x < nx) {
-            keys[gown * CW + x] = node[p] >= 0 ? cand_key(lse[p], node[p]) : 0ull;
-            if constexpr (kApprox) {
-              sc[gown * CW + x] = lse[p];
-              er[gown * CW + x] = err[p];
+          const int x = 2 * j + p;  // candidate owning result rows 4kg + 2p, +1
+          node[p] = (mine && gown < GPW && x < nx) ? Xs[gown * CW + x] : -1;
+          float y[2], bnd[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int ch = node[p] >= 0 ? 2 * node[p] + c : -1;
+            const bool vis = child_visible(ch, nchild, cshift, bq);
+            y[c] = vis ? a[2 * p + c] : -INFINITY;
+            bnd[c] = vis ? a2[2 * p + c] : 0.f;
+          }
+          const float va = fmaxf(y[0], y[1]), vb = fminf(y[0], y[1]);
+          const float vv = geo.scorer == PISA_LSE ? va + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(vb - va))
+                                                  : pair_trunc(va, vb, 1.f, trunc_c2(geo.scorer, true));
+          lse[p] = node[p] >= 0 ? vv : 0.f;
+          // the pair LSE moves by at most the larger child error; 2^-20 |score| more covers
+          // the differing fp32 rounding of the two evaluations
+          err[p] = node[p] >= 0 ? kLoBound * fmaxf(bnd[0], bnd[1]) + 9.6e-7f * fabsf(vv) : 0.f;
+        }
+        lse[0] = group_sum<G>(lse[0]);
+        lse[1] = group_sum<G>(lse[1]);
+        if constexpr (kApprox) {
+          err[0] = group_sum<G>(err[0]);
+          err[1] = group_sum<G>(err[1]);
+        }
+        if (r == 0 && gown < GPW && mine) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int x = 2 * j + p;
+            if (x < nx) {
+              keys[gown * CW + x] = node[p] >= 0 ? cand_key(lse[p], node[p]) : 0ull;
+              if constexpr (kApprox) {
+                sc[gown * CW + x] = lse[p];
+                er[gown * CW + x] = err[p];
+              }
             }
           }
         }
