@@ -173,9 +173,10 @@ int attn_g(const Geo& g, const void* q, const void* k, const void* v, const int3
 
 // ---- key-major form (bf16 prefill) ----
 //
-// The (query group, selected block) pairs are sorted by block (counting sort, as for the
-// leaf scores), so each block's key and value tiles are staged in LDS once per chunk of
-// 128/G pairs instead of being gathered for every pair.  Per chunk, on
+// The (query group, selected block) pairs are sorted by block (counting sort), so each
+// block's key and value tiles are staged in LDS once per chunk of 4 kAttnColGroups 32/G
+// pairs (four wavefronts x kAttnColGroups column groups of 32 (pair, head) columns) instead
+// of being gathered for every pair.  Per chunk, on
 // v_mfma_f32_32x32x16_bf16: S = K Q^T (rows = 64 keys, columns = 32 (pair, head) per
 // wavefront), the block softmax in registers, then O = P^T V with the keys of each k-step
 // taken in the order the lane already holds its probabilities (k-step s, lane half hh,
@@ -216,6 +217,11 @@ __global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restric
   }
 }
 
+// Column groups of 32 (pair, head) columns each wavefront attends per chunk: the staged key
+// and value tiles serve 4 kAttnColGroups column groups of a block's list (256K, chunk
+// kernel plus merge: 1, 2, 4, 8 and 16 groups took 8.84, 8.46, 7.49, 6.98 and 6.71 ms).
+constexpr int kAttnColGroups = 16;
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                          const bf16* __restrict__ v, Geo geo,
@@ -223,14 +229,15 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
                                                          const int32_t* __restrict__ choff,
                                                          const int32_t* __restrict__ entries, int32_t M,
                                                          float* __restrict__ plse, bf16* __restrict__ po) {
-  constexpr int EW = 32 / G;   // pairs per wavefront
-  constexpr int QC = 128 / G;  // pairs per chunk (workgroup)
+  constexpr int EW = 32 / G;                    // pairs per column group
+  constexpr int NCG = kAttnColGroups;
+  constexpr int QC = 4 * NCG * EW;              // pairs per chunk (workgroup)
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int VTR = kLeaf + 8;  // padded row (keys) of the transposed value tile
-  // key tile, then the transposed value tile; later the staged outputs of the 4 wavefronts
-  __shared__ __attribute__((aligned(16))) bf16 tiles[kLeaf * (D + 8) + D * VTR];
-  bf16* kt = tiles;
-  bf16* vt = tiles + kLeaf * (D + 8);
+  constexpr int OSR = D + 8;      // padded row of a wavefront's staged output
+  __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
+  __shared__ __attribute__((aligned(16))) bf16 vt[D * VTR];
+  __shared__ __attribute__((aligned(16))) bf16 os_all[4][32 * OSR];
   __shared__ float ls_all[4][32];
   __shared__ int64_t px_all[4][32];
 
@@ -249,14 +256,17 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int col = lane & 31, hh = lane >> 5;
-  const int e = e0 + wave * EW + col / G;
   const int r = col % G;
-  const bool valid = e < e1;
-  const int ent = valid ? entries[e] : 0;
-  const int i = ent >> 6, slot = ent & 63;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  const bf16* qh = q + ((int64_t)b * geo.Hq + h * G + r) * N * D;
+  // entry of this lane's column in column group u of the wavefront (-1: none)
+  auto entry = [&](int u) {
+    const int e = e0 + (u * 4 + wave) * EW + col / G;
+    return e < e1 ? entries[e] : -1;
+  };
+  int ent = entry(0);
   bf16x8 bq[KS];
-  load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * N + i) * D, valid, hh, bq);
+  load_bfrag<D>(qh + (int64_t)max(ent >> 6, 0) * D, ent >= 0, hh, bq);
 
   stage_tile<D>(k + (int64_t)bh * N * D, j * kLeaf, N, kt);
   {  // value tile, transposed: vt[dim][key] (zeros past N)
@@ -274,73 +284,84 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   }
   __syncthreads();
 
-  f32x16 s0, s1;
-  tile_mfma32<D>(kt, bq, lane, s0, s1);
-  // block softmax of the column in log2 units; keys after the query or past N are masked
-  const float sl = geo.s_log2e;
-  float mx = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const int t0 = j * kLeaf + key_row(w, hh), t1 = t0 + 32;
-    s0[w] = (t0 <= i && t0 < N) ? s0[w] * sl : -INFINITY;
-    s1[w] = (t1 <= i && t1 < N) ? s1[w] * sl : -INFINITY;
-    mx = fmaxf(mx, fmaxf(s0[w], s1[w]));
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32));  // key 64 j <= i is live for a valid pair
-  if (!valid) mx = 0.f;                // padding columns: all probabilities 0, never written
-  float sum = 0.f;
-  bf16x8 pa[4];
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const float p0 = __builtin_amdgcn_exp2f(s0[w] - mx), p1 = __builtin_amdgcn_exp2f(s1[w] - mx);
-    sum += p0 + p1;
-    pa[w >> 3][w & 7] = (__bf16)p0;
-    pa[2 + (w >> 3)][w & 7] = (__bf16)p1;
-  }
-  sum += __shfl_xor(sum, 32);
-
-  f32x16 ao[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) {
-#pragma unroll
-    for (int w = 0; w < 16; ++w) ao[db][w] = 0.f;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16* vr = vt + (32 * db + col) * VTR + 32 * (s >> 1) + 16 * (s & 1) + 4 * hh;
-      const uint2 x0 = *reinterpret_cast<const uint2*>(vr), x1 = *reinterpret_cast<const uint2*>(vr + 8);
-      const u32x4 xv = {x0.x, x0.y, x1.x, x1.y};
-      ao[db] = mfma32(pa[s], __builtin_bit_cast(bf16x8, xv), ao[db]);
-    }
-  }
-
-  // lane (col, hh) holds O[column key_row(w, hh)][dim 32 db + col]
   float* ls = ls_all[wave];
   int64_t* px = px_all[wave];
-  if (hh == 0) {
-    ls[col] = sum;
-    const int64_t pi = ((((int64_t)bh * N + i) * K + slot) * G + r);
-    px[col] = valid ? pi : -1;
-    if (valid) plse[pi] = mx + __builtin_amdgcn_logf(sum);
-  }
-  // the normalised tile goes through LDS (the key and value tiles' space, free once every
-  // wavefront has finished its products) so that it leaves in 16-byte pieces
-  __syncthreads();
-  constexpr int OSR = D + 8;  // padded row of the staged output
-  bf16* os = tiles + wave * 32 * OSR;
-  static_assert(4 * 32 * (D + 8) <= kLeaf * (D + 8) + D * (kLeaf + 8), "output staging fits the tile space");
+  bf16* os = os_all[wave];
+  const float sl = geo.s_log2e;
+  for (int u = 0; u < NCG; ++u) {
+    if (e0 + (u * 4 + wave) * EW >= e1) break;  // uniform across the wavefront
+    const int ent_n = u + 1 < NCG ? entry(u + 1) : -1;
+    bf16x8 bqn[KS];
+    load_bfrag<D>(qh + (int64_t)max(ent_n >> 6, 0) * D, ent_n >= 0, hh, bqn);
+    const bool valid = ent >= 0;
+    const int i = valid ? ent >> 6 : 0, slot = valid ? ent & 63 : 0;
+
+    f32x16 s0, s1;
+    tile_mfma32<D>(kt, bq, lane, s0, s1);
+    // block softmax of the column in log2 units; keys after the query or past N are masked
+    float mx = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const int m = key_row(w, hh);
-    const float inv = px[m] >= 0 ? 1.f / ls[m] : 0.f;
+    for (int w = 0; w < 16; ++w) {
+      const int t0 = j * kLeaf + key_row(w, hh), t1 = t0 + 32;
+      s0[w] = (t0 <= i && t0 < N) ? s0[w] * sl : -INFINITY;
+      s1[w] = (t1 <= i && t1 < N) ? s1[w] * sl : -INFINITY;
+      mx = fmaxf(mx, fmaxf(s0[w], s1[w]));
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // key 64 j <= i is live for a valid pair
+    if (!valid) mx = 0.f;                // padding columns: all probabilities 0, never written
+    float sum = 0.f;
+    bf16x8 pa[4];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) os[m * OSR + 32 * db + col] = (bf16)f2bf_rne(ao[db][w] * inv);
-  }
-  wave_sync();
+    for (int w = 0; w < 16; ++w) {
+      const float p0 = __builtin_amdgcn_exp2f(s0[w] - mx), p1 = __builtin_amdgcn_exp2f(s1[w] - mx);
+      sum += p0 + p1;
+      pa[w >> 3][w & 7] = (__bf16)p0;
+      pa[2 + (w >> 3)][w & 7] = (__bf16)p1;
+    }
+    sum += __shfl_xor(sum, 32);
+
+    f32x16 ao[DB];
 #pragma unroll
-  for (int t = lane; t < 32 * (D / 8); t += 64) {
-    const int m = t / (D / 8), c8 = (t % (D / 8)) * 8;
-    const int64_t pi = px[m];
-    if (pi >= 0) *reinterpret_cast<u32x4*>(po + pi * D + c8) = *reinterpret_cast<const u32x4*>(os + m * OSR + c8);
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int w = 0; w < 16; ++w) ao[db][w] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16* vr = vt + (32 * db + col) * VTR + 32 * (s >> 1) + 16 * (s & 1) + 4 * hh;
+        const uint2 x0 = *reinterpret_cast<const uint2*>(vr), x1 = *reinterpret_cast<const uint2*>(vr + 8);
+        const u32x4 xv = {x0.x, x0.y, x1.x, x1.y};
+        ao[db] = mfma32(pa[s], __builtin_bit_cast(bf16x8, xv), ao[db]);
+      }
+    }
+
+    // lane (col, hh) holds O[column key_row(w, hh)][dim 32 db + col]
+    if (hh == 0) {
+      ls[col] = sum;
+      const int64_t pi = ((((int64_t)bh * N + i) * K + slot) * G + r);
+      px[col] = valid ? pi : -1;
+      if (valid) plse[pi] = mx + __builtin_amdgcn_logf(sum);
+    }
+    wave_sync();
+    // the normalised tile goes through this wavefront's LDS staging so that it leaves in
+    // 16-byte pieces
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int m = key_row(w, hh);
+      const float inv = px[m] >= 0 ? 1.f / ls[m] : 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) os[m * OSR + 32 * db + col] = (bf16)f2bf_rne(ao[db][w] * inv);
+    }
+    wave_sync();
+#pragma unroll
+    for (int t = lane; t < 32 * (D / 8); t += 64) {
+      const int m = t / (D / 8), c8 = (t % (D / 8)) * 8;
+      const int64_t pi = px[m];
+      if (pi >= 0) *reinterpret_cast<u32x4*>(po + pi * D + c8) = *reinterpret_cast<const u32x4*>(os + m * OSR + c8);
+    }
+    wave_sync();  // ls, px and os are rewritten by the next column group
+    ent = ent_n;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) bq[s2] = bqn[s2];
   }
 }
 
@@ -438,7 +459,7 @@ int attn_km_g(const Geo& g, const bf16* q, const bf16* k, const bf16* v, const i
   const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
   attn_cand_kernel<<<cgrid, 256, hbytes, st>>>(idx, g, cand, cnt);
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
-  const int qc = 128 / G;
+  const int qc = 4 * kAttnColGroups * 32 / G;  // pairs per chunk
   if ((rc = launch_scan(cnt, w.M, qc, off, choff, st)) != PISA_OK) return rc;
   if ((rc = launch_scatter(g, g.K, cand, off, cursor, entries, st)) != PISA_OK) return rc;
   const int64_t grid = (w.slots + qc - 1) / qc + w.M;  // bound on the chunk count
