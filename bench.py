@@ -247,8 +247,9 @@ class Prefill:
             "build": (BH * N * d * esz + BH * T * d * 8, 0),
             "route_upper": ((q_b + k_b + copy(dense_l) + slots + BH * N * 3 * 4, dots(dense_l) * BH * G * 2 * d
                              + fflops) if forced_in_route else (0, 0)),
-            "route_l2": (q_b + (slots if forced_in_route else 0) + copy(gather_l) + slots,
-                         dots(gather_l) * BH * G * 2 * d),
+            # no gathered level: the stage is the leaf-pair count over the candidate slots
+            "route_l2": ((q_b + (slots if forced_in_route else 0) + copy(gather_l) + slots,
+                          dots(gather_l) * BH * G * 2 * d) if gather_l else (slots, 0)),
             "group": (BH * N * 2 * K * 4 * 4, 0),
             "leaf": (q_b + k_b + 2 * slots, pairs * G * C * 2 * d),
             "final": (BH * N * ((2 * K + 3) * 4 + K * 8) + (0 if forced_in_route else q_b + k_b),

@@ -170,7 +170,43 @@ __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* 
   }
 }
 
+// Workgroup = kLeafQueries consecutive queries of one (b, h): the leaf-pair histogram of
+// their candidate slots, counted in LDS and flushed with one global add per non-empty
+// node (direct global adds when the nodes do not fit).
+__global__ __launch_bounds__(256) void count_pairs_kernel(const int32_t* __restrict__ cand, int32_t N, int32_t BH,
+                                                          int32_t K, int32_t n1p, int32_t* __restrict__ cnt) {
+  extern __shared__ int hist[];
+  const int bh = blockIdx.x % BH;
+  const int q0 = (blockIdx.x / BH) * kLeafQueries;
+  const int q1 = min(N, q0 + kLeafQueries);
+  const bool lhist = n1p <= kHistMaxBins;
+  if (lhist) {
+    for (int t = threadIdx.x; t < n1p; t += 256) hist[t] = 0;
+    __syncthreads();
+  }
+  const int32_t* c = cand + ((int64_t)bh * N + q0) * 2 * K;
+  const int n = (q1 - q0) * K;
+  for (int t = threadIdx.x; t < n; t += 256) {
+    const int node = pair_node(c + 2 * t);
+    if (node < 0) continue;
+    if (lhist) atomicAdd(&hist[node], 1);
+    else atomicAdd(&cnt[bh * n1p + node], 1);
+  }
+  if (lhist) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < n1p; t += 256)
+      if (hist[t]) atomicAdd(&cnt[bh * n1p + t], hist[t]);
+  }
+}
+
 }  // namespace
+
+int launch_count_pairs(const Geo& g, const int32_t* cand, int32_t* cnt, hipStream_t st) {
+  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+  const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
+  count_pairs_kernel<<<grid, 256, hbytes, st>>>(cand, g.N, g.B * g.Hkv, g.K, g.n1p, cnt);
+  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+}
 
 int launch_scatter_pairs(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                          hipStream_t st) {

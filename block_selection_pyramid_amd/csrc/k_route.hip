@@ -132,8 +132,14 @@ template <int D, int G, int GPW>
 int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
                       int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st) {
   if (g.L >= 3) {
-    const int rc = launch_route_upper_dense(g, q, pyr, k, x2, fsc, st);
+    // every routing level dense: the dense launch writes the leaf candidates
+    const bool all_dense = dense_bottom(g) == 2;
+    const int rc = launch_route_upper_dense(g, q, pyr, k, all_dense ? cand : x2, fsc, st);
     if (rc != PISA_OK) return rc;
+    if (all_dense) {
+      if (mid && hipEventRecord(mid, st) != hipSuccess) return PISA_ERR_HIP;
+      return launch_count_pairs(g, cand, cnt, st);
+    }
   }
   if (mid && hipEventRecord(mid, st) != hipSuccess) return PISA_ERR_HIP;
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));

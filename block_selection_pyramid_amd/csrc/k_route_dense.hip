@@ -22,7 +22,8 @@
 //
 // Output: per query group, the 2K candidate slots of level l_bot - 1 (children of the Top-K
 // nodes of level l_bot, -1 where a child does not exist or is not visible), the input of
-// the gather routing launch.  The same workgroup then scores its queries' forced leaf blocks
+// the gather routing launch; for l_bot = 2 the leaf candidates themselves, forced blocks
+// also -1.  The same workgroup then scores its queries' forced leaf blocks
 // ("Block Sparse Attention with Log-Linear Complexity", agihunt.info summary, LSE and
 // forced-block paragraph: first, previous and current block; leaf score = causal LSE over
 // the block's raw keys, summed over the G heads) with the query rows it already holds:
@@ -303,8 +304,12 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
     const int iq = it / KC, ir = it % KC, i = iw + iq;
     if (it < ITEMS && ir < K && i < N) {
       const int p = ip[m];
-      const int c0 = p >= 0 ? 2 * p : -1;
-      const int c1 = (p >= 0 && 2 * p + 1 < geo.n[lc] && ((int64_t)(2 * p + 1) << (lc - 1)) <= ibq[m]) ? 2 * p + 1 : -1;
+      int c0 = p >= 0 ? 2 * p : -1;
+      int c1 = (p >= 0 && 2 * p + 1 < geo.n[lc] && ((int64_t)(2 * p + 1) << (lc - 1)) <= ibq[m]) ? 2 * p + 1 : -1;
+      if (lc == 1) {  // leaf candidates: the forced blocks are scored on their own
+        if (c0 >= 0 && is_forced(c0, ibq[m])) c0 = -1;
+        if (c1 >= 0 && is_forced(c1, ibq[m])) c1 = -1;
+      }
       int32_t* dst = x2 + ((int64_t)bh * N + i) * twoK + 2 * ir;
       __builtin_nontemporal_store(c0, dst);
       __builtin_nontemporal_store(c1, dst + 1);

@@ -88,14 +88,19 @@ inline bool route_scores_forced(const Geo& g, int dtype) { return dtype == PISA_
 // launch); the gather launch walks the levels below, down to 2.  Measured at 256K-1M
 // tokens: a level over 2048 children costs a little more dense than gathered, one over
 // 1024 children clearly less (the dense cost halves with each level up, a gathered
-// level's stays the same).
+// level's stays the same).  With at most kDenseMaxChildren leaf blocks level 2 is dense
+// too (dense_bottom == 2): the dense launch then writes the leaf candidates itself, a
+// counting pass builds the leaf-pair histogram and the gather launch is skipped.
 constexpr int kDenseMaxChildren = 1024;
 inline int dense_bottom(const Geo& g) {
-  int l = 3;
+  int l = 2;
   while (l < g.L && g.n[l - 1] > kDenseMaxChildren) ++l;
   return l;
 }
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
+// histogram of the routed (query group, level-2 node) pairs of the 2K leaf slots per query
+// group into cnt [B*Hkv*n1p] (the counts the gather launch keeps when it runs)
+int launch_count_pairs(const Geo& g, const int32_t* cand, int32_t* cnt, hipStream_t st);
 // scatter of per_row candidate slots per query group (-1 = none) into per-leaf-block lists
 int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
                    int32_t* entries, hipStream_t st);
