@@ -132,10 +132,10 @@ __global__ __launch_bounds__(256) void scatter_pairs_kernel(const int32_t* __res
   entries[pos] = (i << 6) | r;
 }
 
-// Workgroup = kLeafQueries consecutive queries of one (b, h), as scatter_hist_kernel, over
-// level-2 nodes.
+// Workgroup = qpw consecutive queries of one (b, h), as scatter_hist_kernel, over level-2
+// nodes.
 __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* __restrict__ cand, int32_t N,
-                                                                 int32_t BH, int32_t K, int32_t n1p,
+                                                                 int32_t BH, int32_t K, int32_t n1p, int32_t qpw,
                                                                  const int32_t* __restrict__ off,
                                                                  int32_t* __restrict__ cursor,
                                                                  int32_t* __restrict__ entries) {
@@ -143,8 +143,8 @@ __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* 
   int* hist = lds;         // n1p counts, then reserved bases
   int* lcur = lds + n1p;   // n1p local cursors
   const int bh = blockIdx.x % BH;
-  const int q0 = (blockIdx.x / BH) * kLeafQueries;
-  const int q1 = min(N, q0 + kLeafQueries);
+  const int q0 = (blockIdx.x / BH) * qpw;
+  const int q1 = min(N, q0 + qpw);
   for (int t = threadIdx.x; t < n1p; t += 256) {
     hist[t] = 0;
     lcur[t] = 0;
@@ -170,15 +170,16 @@ __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* 
   }
 }
 
-// Workgroup = kLeafQueries consecutive queries of one (b, h): the leaf-pair histogram of
+// Workgroup = qpw consecutive queries of one (b, h): the leaf-pair histogram of
 // their candidate slots, counted in LDS and flushed with one global add per non-empty
 // node (direct global adds when the nodes do not fit).
 __global__ __launch_bounds__(256) void count_pairs_kernel(const int32_t* __restrict__ cand, int32_t N, int32_t BH,
-                                                          int32_t K, int32_t n1p, int32_t* __restrict__ cnt) {
+                                                          int32_t K, int32_t n1p, int32_t qpw,
+                                                          int32_t* __restrict__ cnt) {
   extern __shared__ int hist[];
   const int bh = blockIdx.x % BH;
-  const int q0 = (blockIdx.x / BH) * kLeafQueries;
-  const int q1 = min(N, q0 + kLeafQueries);
+  const int q0 = (blockIdx.x / BH) * qpw;
+  const int q1 = min(N, q0 + qpw);
   const bool lhist = n1p <= kHistMaxBins;
   if (lhist) {
     for (int t = threadIdx.x; t < n1p; t += 256) hist[t] = 0;
@@ -202,18 +203,20 @@ __global__ __launch_bounds__(256) void count_pairs_kernel(const int32_t* __restr
 }  // namespace
 
 int launch_count_pairs(const Geo& g, const int32_t* cand, int32_t* cnt, hipStream_t st) {
-  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+  const int qpw = group_queries(g);
+  const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + qpw - 1) / qpw));
   const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
-  count_pairs_kernel<<<grid, 256, hbytes, st>>>(cand, g.N, g.B * g.Hkv, g.K, g.n1p, cnt);
+  count_pairs_kernel<<<grid, 256, hbytes, st>>>(cand, g.N, g.B * g.Hkv, g.K, g.n1p, qpw, cnt);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 int launch_scatter_pairs(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                          hipStream_t st) {
   if (g.n1p <= kHistMaxBins) {
-    const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+    const int qpw = group_queries(g);
+    const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + qpw - 1) / qpw));
     scatter_pairs_hist_kernel<<<grid, 256, 2 * sizeof(int) * (size_t)g.n1p, st>>>(cand, g.N, g.B * g.Hkv, g.K,
-                                                                                    g.n1p, off, cursor, entries);
+                                                                                    g.n1p, qpw, off, cursor, entries);
     return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
   }
   const int64_t pairs = (int64_t)g.B * g.Hkv * g.N * g.K;

@@ -46,6 +46,13 @@ inline int chunk_entries(int G) { return 4 * kLeafColGroups * 32 / G; }
 // per-leaf-block histogram in LDS when there are at most kHistMaxBins leaf blocks.
 constexpr int kLeafQueries = 2048;
 constexpr int kHistMaxBins = 8192;
+// Queries per workgroup of the leaf-pair count and scatter: kLeafQueries, halved (down to
+// 64) while that leaves fewer than 1024 workgroups, so small problems fill the chip.
+inline int group_queries(const Geo& g) {
+  int qpw = kLeafQueries;
+  while (qpw > 64 && (int64_t)g.B * g.Hkv * ((g.N + qpw - 1) / qpw) < 1024) qpw >>= 1;
+  return qpw;
+}
 // Query groups one routing wavefront walks together: 2K candidate slots each within 64
 // lanes, one MFMA column per (group, head) within 16.
 inline int route_groups_per_wave(int G, int K) {
