@@ -258,9 +258,72 @@ __global__ __launch_bounds__(256) void append_up_kernel(Geo cap, const int32_t* 
   }
 }
 
+// One new key per sequence (max_new_keys == 1): the key's leaf block and its ancestors, one
+// node per level, in one workgroup per (b, h).  A single leaf block changed, so the path's
+// siblings are clean: each thread e < D loads element e of all of them before the first
+// addition and carries the path's means in a register, with a fresh build's arithmetic
+// (rows_mean for the leaf; a parent adds its children left to right and divides by their
+// count), up to the capacity's top level as append_up_kernel does.
+template <typename Tin, int D>
+__global__ __launch_bounds__(256) void append_path_kernel(const Tin* __restrict__ k, Geo cap,
+                                                          const int32_t* __restrict__ old_len,
+                                                          const int32_t* __restrict__ new_len,
+                                                          float* __restrict__ pyr) {
+  __shared__ float red[RowsShape<Tin, D>::RPP][D];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  int len, lo, hi;
+  if (!dirty_blocks(cap, old_len, new_len, bh / cap.Hkv, 1, &len, &lo, &hi)) return;  // whole workgroup
+  float* P = pyr + (int64_t)bh * cap.T * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.T * 2 * D;
+  const int n1 = (len + cap.C - 1) / cap.C;  // leaf blocks at this length
+  // sib[l]: element tid of the sibling of the path's level-l node (when it exists)
+  float sib[kMaxLevels + 1];
+  if (tid < D) {
+    int np = n1, pth = lo;
+#pragma unroll
+    for (int l = 1; l <= kMaxLevels; ++l) {
+      if (l < cap.L) {
+        const int sb = pth ^ 1;
+        sib[l] = sb < np ? P[(int64_t)(cap.off[l] + sb) * D + tid] : 0.f;
+        np = (np + 1) >> 1;
+        pth >>= 1;
+      }
+    }
+  }
+  float m = rows_mean<Tin, D>(k + (int64_t)bh * cap.N * D, lo * cap.C, min(lo * cap.C + cap.C, len), red, tid);
+  if (tid < D) {
+    P[(int64_t)(cap.off[1] + lo) * D + tid] = m;
+    store_rcopy<D>(R, cap.off[1] + lo, tid, m * cap.s_log2e);
+    int np = n1, pth = lo;
+#pragma unroll
+    for (int l = 2; l <= kMaxLevels; ++l) {
+      if (l <= cap.L) {
+        const int p = pth >> 1;
+        const int cnt = min(2 * p + 2, np) - 2 * p;  // children of p at this length
+        float a = 0.f;
+        if (cnt == 2) {
+          a += pth == 2 * p ? m : sib[l - 1];
+          a += pth == 2 * p ? sib[l - 1] : m;
+        } else {
+          a += m;
+        }
+        m = a / (float)cnt;
+        P[(int64_t)(cap.off[l] + p) * D + tid] = m;
+        store_rcopy<D>(R, cap.off[l] + p, tid, m * cap.s_log2e);
+        np = (np + 1) >> 1;
+        pth = p;
+      }
+    }
+  }
+}
+
 template <typename Tin, int D>
 int append_t(const Geo& cap, const Tin* k, const int32_t* old_len, const int32_t* new_len, int max_new,
              float* pyr, hipStream_t st) {
+  if (max_new == 1) {
+    append_path_kernel<Tin, D><<<cap.B * cap.Hkv, 256, 0, st>>>(k, cap, old_len, new_len, pyr);
+    return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+  }
   const int max_blocks = (max_new + cap.C - 1) / cap.C + 1;  // a range of max_new positions spans this many
   dim3 grid((max_blocks + kSub - 1) / kSub, cap.B * cap.Hkv);
   append_leaf_kernel<Tin, D><<<grid, 256, 0, st>>>(k, cap, old_len, new_len, max_blocks, pyr);

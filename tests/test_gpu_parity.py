@@ -491,6 +491,46 @@ def test_append_keys_matches_fresh_build(env, dt, d):
         old = new
 
 
+def test_append_single_keys_match_fresh_build(env):
+    # one key per sequence and step (the serving loop's append, max_new_keys = 1): lengths
+    # cross leaf-block boundaries and, at 4096 -> 4097 keys, a pyramid level (the level table
+    # grows); a sequence that does not grow is left alone.  Every node of each sequence's own
+    # level table stays bit-identical to a fresh build at its length.
+    torch, pisa = env
+    B, Hq, Hkv, d, K, cap = 3, 8, 2, 128, 8, 4200
+    dt = synth.BF16
+    w = synth.custom(name="append1", batch=B, seq_len=cap, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     dtype=dt, seed=77, needles=8, decode=True)
+    _, k, _ = synth.make_inputs(w)
+    p = pisa.Problem(B, cap, Hq, Hkv, d, 64, K, 2, dtype=dt)
+    kd = dev(torch, k)
+    pyr = torch.zeros(pisa.pyramid_shape(p), dtype=torch.float32, device="cuda")
+    _, _, coff = _levels_offsets(pisa, cap, B, Hq, Hkv, d, K, dt)
+    lengths = [62, 126, 4094]
+    lt = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+    pisa.append_keys(p, kd, torch.zeros_like(lt), lt, max(lengths), pyr)
+    for step in range(5):
+        new = [n + (0 if (step == 2 and b == 1) else 1) for b, n in enumerate(lengths)]
+        log("append1", "step %d: %s -> %s" % (step, lengths, new))
+        ot = torch.tensor(lengths, dtype=torch.int32, device="cuda")
+        nt = torch.tensor(new, dtype=torch.int32, device="cuda")
+        pisa.append_keys(p, kd, ot, nt, 1, pyr)
+        torch.cuda.synchronize()
+        app = pyr.cpu().numpy().view(np.uint32)
+        for b in range(B):
+            n = new[b]
+            pb = pisa.Problem(1, n, Hq, Hkv, d, 64, K, 2, dtype=dt)
+            fresh = pisa.build_pyramid(pb, kd[b:b + 1, :, :n].contiguous())
+            torch.cuda.synchronize()
+            fr = fresh.cpu().numpy().view(np.uint32)
+            L, nodes, foff = _levels_offsets(pisa, n, 1, Hq, Hkv, d, K, dt)
+            for l in range(1, L + 1):
+                a = app[:, b, :, coff[l - 1]:coff[l - 1] + nodes[l]]
+                f = fr[:, 0, :, foff[l - 1]:foff[l - 1] + nodes[l]]
+                assert np.array_equal(a, f), "step %d sequence %d length %d level %d differs" % (step, b, n, l)
+        lengths = new
+
+
 def _oracle_decode_rows(op_kw, q, k, lengths, b):
     n = int(lengths[b])
     kw = dict(op_kw, batch=1, seq_len=n)
