@@ -187,8 +187,10 @@ int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size
  * Host only: how pisa_select_prefill splits the routing walk for p.  The bf16 path scores
  * levels *dense_top = L down to *dense_bottom densely, every visible node for all queries
  * of a leaf block at once, and walks the levels below down to level 2 by per-query gathers;
- * the dense launch covers a level while its child level has at most 1024 nodes.  Both are 0
- * when there is no dense launch (L < 3, or fp32 inputs, which walk every level by gathers).
+ * the dense launch covers a level while its child level has at most 1024 nodes, so with at
+ * most 1024 leaf blocks every level down to 2 is dense (*dense_bottom = 2) and no gather
+ * launch runs.  Both are 0 when there is no dense launch (L < 3, or fp32 inputs, which walk
+ * every level by gathers).
  * The top-down walk and its result do not depend on the split.  Returns PISA_OK, or the
  * status pisa_select_prefill would return for an invalid or unsupported p.
  */
@@ -214,7 +216,8 @@ int pisa_prefill_dense_levels(const pisa_problem* p, int32_t* dense_top, int32_t
  * scratch.  old_lengths / new_lengths: device int32 [B] with 0 <= old <= new <= capacity
  * and new - old <= max_new_keys (host int, 0 <= max_new_keys <= capacity); values outside
  * that contract are clamped on the device and leave the pyramid unspecified, never an
- * out-of-bounds access.  Two launches on `stream`; no workspace.
+ * out-of-bounds access.  One launch on `stream` when max_new_keys == 1 (the changed path
+ * carried up in registers), two otherwise; no workspace.
  *
  * pisa_select_decode_varlen is pisa_select_decode for the query of sequence b at position
  * lengths[b] - 1 (device int32 [B], 1 <= lengths[b] <= capacity, clamped on the device),
