@@ -76,9 +76,10 @@ def test_sizes(pisa):
 @pytest.mark.parametrize("N,K", [(1024, 4), (4096, 8), (16384, 32), (65536, 8), (131072, 8), (131072 + 64, 8),
                                  (262144, 8), (262144 + 1, 8), (300000, 8), (1 << 20, 8)])
 def test_dense_level_split(pisa, N, K):
-    # bf16: levels L .. bottom are scored densely, where bottom is the highest level >= 3
+    # bf16: levels L .. bottom are scored densely, where bottom is the highest level >= 2
     # whose child level has at most 1024 nodes (the top level always qualifies: its
-    # child level has at most 2gK <= 64 nodes); fp32 and L < 3 have no dense launch
+    # child level has at most 2gK <= 64 nodes; bottom = 2 when there are at most 1024 leaf
+    # blocks); fp32 and L < 3 have no dense launch
     nodes = oracle.levels(N, 64, K, 2)
     L = len(nodes) - 1
     bf = pisa.Problem(1, N, 4, 1, 128, 64, K, 2, dtype=pisa.BF16)
@@ -86,9 +87,10 @@ def test_dense_level_split(pisa, N, K):
     if L < 3:
         assert (top, bot) == (0, 0)
     else:
-        want = min(l for l in range(3, L + 1) if nodes[l - 1] <= 1024 or l == L)
+        want = min(l for l in range(2, L + 1) if nodes[l - 1] <= 1024 or l == L)
         assert (top, bot) == (L, want)
-        assert 3 <= bot <= top
+        assert 2 <= bot <= top
+        assert (bot == 2) == (nodes[1] <= 1024)
     assert pisa.dense_levels(pisa.Problem(1, N, 4, 1, 128, 64, K, 2, dtype=pisa.F32)) == (0, 0)
 
 
