@@ -248,6 +248,26 @@ def test_prefill_gather_below_dense_levels(env):
     verify(op, q, k, opyr, sample_rows(w, needles, 2000, 17), idx, sc, what="300k-G4")
 
 
+def test_prefill_beyond_histogram_bins(env):
+    # more than 8192 level-2 nodes per (b, h) (N > 1M tokens at C = 64): the routing launch
+    # counts leaf pairs with global atomics instead of an LDS histogram, and the leaf-pair
+    # scatter places each entry with a global cursor; an odd leaf-block count leaves the last
+    # level-2 node one child
+    N = 64 * (2 * 8192 + 2) + 5
+    w = synth.custom(name="1m-G2", batch=1, seq_len=N, n_q_heads=2, n_kv_heads=1, head_dim=64, top_k=8,
+                     seed=91, needles=4096)
+    nodes = oracle.levels(N, 64, 8, 2)
+    assert (nodes[1] + 1) // 2 > 8192 and nodes[1] % 2 == 1
+    p, op, q, k, needles, pyr, outs = gpu_prefill(env, w)
+    opyr = oracle.build_pyramid(op, k)
+    idx, sc = outs[0]
+    K = w.top_k
+    nsel = (idx.reshape(-1, K) >= 0).sum(1)
+    assert np.array_equal(nsel, np.minimum(K, np.arange(N) // 64 + 1))
+    rows = np.unique(np.concatenate([sample_rows(w, needles, 1500, 23), [N - 1, N - 2, N - 70]]))
+    verify(op, q, k, opyr, rows, idx, sc, what="1m-G2")
+
+
 def gpu_decode(env, w):
     torch, pisa = env
     p, op = problems(pisa, w)
