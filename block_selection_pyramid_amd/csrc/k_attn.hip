@@ -178,12 +178,14 @@ int attn_g(const Geo& g, const void* q, const void* k, const void* v, const int3
 // pairs (four wavefronts x kAttnColGroups column groups of 32 (pair, head) columns) instead
 // of being gathered for every pair.  Per chunk, on
 // v_mfma_f32_32x32x16_bf16: S = K Q^T (rows = 64 keys, columns = 32 (pair, head) per
-// wavefront), the block softmax in registers, then O = P^T V with the keys of each k-step
+// wavefront), the block softmax in registers, then O^T = V^T P with the keys of each k-step
 // taken in the order the lane already holds its probabilities (k-step s, lane half hh,
 // element e <-> key 32 (s >> 1) + 16 (s & 1) + 8 (e >> 2) + 4 hh + (e & 3)), the value tile
-// staged transposed so that those keys are two 8-byte LDS reads.  Each pair writes its
-// block-normalised output (bf16) and log2-sum-exp; one wavefront per query group then
-// merges its K partials.
+// staged transposed so that those keys are two 8-byte LDS reads.  The transposed product
+// leaves each lane four consecutive dims of its own column's output row per result group:
+// each pair's block-normalised output (bf16) is staged in LDS in 8-byte pieces and leaves
+// in 16-byte pieces, with its log2-sum-exp; one wavefront per query group then merges its
+// K partials.
 
 // Candidate array of the pairs (per_row = K slots per query group, -1 where the slot is
 // padding or names a block after the query's own) and their count per (b, h, block).
@@ -238,7 +240,6 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 vt[D * VTR];
   __shared__ __attribute__((aligned(16))) bf16 os_all[4][32 * OSR];
-  __shared__ float ls_all[4][32];
   __shared__ int64_t px_all[4][32];
 
   const int c = blockIdx.x;
@@ -284,7 +285,6 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   }
   __syncthreads();
 
-  float* ls = ls_all[wave];
   int64_t* px = px_all[wave];
   bf16* os = os_all[wave];
   const float sl = geo.s_log2e;
@@ -330,26 +330,30 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
         const bf16* vr = vt + (32 * db + col) * VTR + 32 * (s >> 1) + 16 * (s & 1) + 4 * hh;
         const uint2 x0 = *reinterpret_cast<const uint2*>(vr), x1 = *reinterpret_cast<const uint2*>(vr + 8);
         const u32x4 xv = {x0.x, x0.y, x1.x, x1.y};
-        ao[db] = mfma32(pa[s], __builtin_bit_cast(bf16x8, xv), ao[db]);
+        ao[db] = mfma32(__builtin_bit_cast(bf16x8, xv), pa[s], ao[db]);
       }
     }
 
-    // lane (col, hh) holds O[column key_row(w, hh)][dim 32 db + col]
+    // O^T: lane (col, hh) holds dims 32 db + 8 a + 4 hh .. +3 of its own column's output
+    // row in ao[db][4a .. 4a+3]
     if (hh == 0) {
-      ls[col] = sum;
       const int64_t pi = ((((int64_t)bh * N + i) * K + slot) * G + r);
       px[col] = valid ? pi : -1;
       if (valid) plse[pi] = mx + __builtin_amdgcn_logf(sum);
     }
-    wave_sync();
-    // the normalised tile goes through this wavefront's LDS staging so that it leaves in
-    // 16-byte pieces
+    // the normalised rows go through this wavefront's LDS staging (8-byte pieces in) so that
+    // they leave in 16-byte pieces
+    {
+      const float inv = valid ? 1.f / sum : 0.f;
 #pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int m = key_row(w, hh);
-      const float inv = px[m] >= 0 ? 1.f / ls[m] : 0.f;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) os[m * OSR + 32 * db + col] = (bf16)f2bf_rne(ao[db][w] * inv);
+        for (int a = 0; a < 4; ++a) {
+          uint2 o;
+          o.x = f2bf_rne(ao[db][4 * a] * inv) | (f2bf_rne(ao[db][4 * a + 1] * inv) << 16);
+          o.y = f2bf_rne(ao[db][4 * a + 2] * inv) | (f2bf_rne(ao[db][4 * a + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(os + col * OSR + 32 * db + 8 * a + 4 * hh) = o;
+        }
     }
     wave_sync();
 #pragma unroll
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
       const int64_t pi = px[m];
       if (pi >= 0) *reinterpret_cast<u32x4*>(po + pi * D + c8) = *reinterpret_cast<const u32x4*>(os + m * OSR + c8);
     }
-    wave_sync();  // ls, px and os are rewritten by the next column group
+    wave_sync();  // px and os are rewritten by the next column group
     ent = ent_n;
 #pragma unroll
     for (int s2 = 0; s2 < KS; ++s2) bq[s2] = bqn[s2];
