@@ -85,7 +85,10 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   const float c2 = trunc_c2(geo.scorer, true);
   const int BH = geo.B * geo.Hkv;
   const int bh = blockIdx.x % BH;  // workgroups of one XCD (w mod 8) share few heads
-  const int iwg = (blockIdx.x / BH) * (kDenseWaves * QPW);
+  // longest visible prefixes (highest leaf blocks) first, so the heaviest workgroups do not
+  // form the launch's tail (64K: 0.74 -> ~0.69 ms)
+  const int nwg = (geo.N + kDenseWaves * QPW - 1) / (kDenseWaves * QPW);
+  const int iwg = (nwg - 1 - (int)(blockIdx.x / BH)) * (kDenseWaves * QPW);
   const int iw = iwg + wave * QPW;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
   const int bqmax = (min(N, iwg + kDenseWaves * QPW) - 1) / C;
