@@ -221,8 +221,9 @@ __global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restric
 
 // Column groups of 32 (pair, head) columns each wavefront attends per chunk: the staged key
 // and value tiles serve 4 kAttnColGroups column groups of a block's list (256K, chunk
-// kernel plus merge: 1, 2, 4, 8 and 16 groups took 8.84, 8.46, 7.49, 6.98 and 6.71 ms).
-constexpr int kAttnColGroups = 16;
+// kernel plus merge: 1, 2, 4, 8 and 16 groups took 8.84, 8.46, 7.49, 6.98 and 6.71 ms; with
+// the transposed value product, 16 and 32 groups 6.37 and 6.20 ms).
+constexpr int kAttnColGroups = 32;
 
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,

@@ -38,9 +38,9 @@ int make_geo(const pisa_problem* p, Geo* g);  // PISA_OK or PISA_ERR_INVALID_ARG
 int supported(const Geo& g, int dtype, int mode);
 PrefillWs prefill_ws(const Geo& g);
 // Leaf-pair entries (query groups) per chunk of the prefill leaf kernel: four wavefronts,
-// kLeafColGroups column groups of 32 (query, head) columns each (256K prefill: 2, 4, 8 and
-// 16 groups took 2.45, 2.02, 1.82 and 1.73 ms).
-constexpr int kLeafColGroups = 16;
+// kLeafColGroups column groups of 32 (query, head) columns each (256K prefill: 2, 4, 8, 16
+// and 32 groups took 2.45, 2.02, 1.82, 1.73 and ~1.69 ms).
+constexpr int kLeafColGroups = 32;
 inline int chunk_entries(int G) { return 4 * kLeafColGroups * 32 / G; }
 // Queries per workgroup of the level-2 routing launch and of the scatter; both keep a
 // per-leaf-block histogram in LDS when there are at most kHistMaxBins leaf blocks.
