@@ -1,9 +1,10 @@
 // Prefill routing (stage one of the two-stage prefill: walk levels L..2 per query group)
 // plus the histogram of routed (query group, level-2 node) pairs per (batch, KV head,
-// level-2 node) that the leaf grouping needs.  bf16 inputs: levels L..3 are scored densely per leaf block (separate
-// launch), level 2 here on the matrix cores from the pyramid's hi/lo routing copy, up to
-// four consecutive queries per wavefront; fp32 inputs: one wavefront per query group on
-// the VALU for the whole walk.
+// level-2 node) that the leaf grouping needs.  bf16 inputs: the upper levels are scored
+// densely per leaf block (separate launch, down to level 2 itself when there are at most
+// kDenseMaxChildren leaf blocks), the levels below by per-query gathers on the matrix
+// cores from the pyramid's hi/lo routing copy, up to four consecutive queries per
+// wavefront; fp32 inputs: one wavefront per query group on the VALU for the whole walk.
 //
 // Output per query group: 2K slots of leaf candidates that are not forced blocks (the
 // forced blocks are scored separately), -1 elsewhere; slots 2r and 2r+1 are the children

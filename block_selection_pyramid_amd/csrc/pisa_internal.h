@@ -42,8 +42,10 @@ PrefillWs prefill_ws(const Geo& g);
 // and 32 groups took 2.45, 2.02, 1.82, 1.73 and ~1.69 ms).
 constexpr int kLeafColGroups = 32;
 inline int chunk_entries(int G) { return 4 * kLeafColGroups * 32 / G; }
-// Queries per workgroup of the level-2 routing launch and of the scatter; both keep a
-// per-leaf-block histogram in LDS when there are at most kHistMaxBins leaf blocks.
+// Queries per workgroup of block-sparse attention's candidate pass and scatter, and the
+// most the leaf-pair count and scatter take (group_queries); the histograms of those passes
+// and of the gather routing launch live in LDS while they have at most kHistMaxBins bins
+// (leaf blocks or level-2 nodes).
 constexpr int kLeafQueries = 2048;
 constexpr int kHistMaxBins = 8192;
 // Queries per workgroup of the leaf-pair count and scatter: kLeafQueries, halved (down to
@@ -109,6 +111,7 @@ int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t
 // group into cnt [B*Hkv*n1p] (the counts the gather launch keeps when it runs)
 int launch_count_pairs(const Geo& g, const int32_t* cand, int32_t* cnt, hipStream_t st);
 // scatter of per_row candidate slots per query group (-1 = none) into per-leaf-block lists
+// (block-sparse attention's (query group, block) pairs)
 int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
                    int32_t* entries, hipStream_t st);
 // scatter of the 2K routed leaf slots per query group into per-level-2-node lists: slots 2r
