@@ -361,7 +361,11 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
     for (int t = lane; t < 32 * (D / 8); t += 64) {
       const int m = t / (D / 8), c8 = (t % (D / 8)) * 8;
       const int64_t pi = px[m];
-      if (pi >= 0) *reinterpret_cast<u32x4*>(po + pi * D + c8) = *reinterpret_cast<const u32x4*>(os + m * OSR + c8);
+      // streamed out (read back once, by the merge): non-temporal stores keep the key and
+      // value tiles and query rows in the caches (256K attention 6.20 -> 5.73 ms)
+      if (pi >= 0)
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(os + m * OSR + c8),
+                                    reinterpret_cast<u32x4*>(po + pi * D + c8));
     }
     wave_sync();  // px and os are rewritten by the next column group
     ent = ent_n;
