@@ -188,7 +188,8 @@ int attn_g(const Geo& g, const void* q, const void* k, const void* v, const int3
 // K partials.
 
 // Candidate array of the pairs (per_row = K slots per query group, -1 where the slot is
-// padding or names a block after the query's own) and their count per (b, h, block).
+// padding, names a block after the query's own or one of its forced blocks) and their
+// count per (b, h, block).
 __global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restrict__ idx, Geo geo,
                                                         int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
   extern __shared__ __attribute__((aligned(16))) int hist[];
@@ -205,7 +206,8 @@ __global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restric
   for (int t = threadIdx.x; t < n; t += 256) {
     const int i = q0 + t / K;
     const int j = idx[base + t];
-    const bool ok = j >= 0 && j <= i / geo.C;
+    // the forced blocks of the query's leaf block are attended densely (attn_forced_kernel)
+    const bool ok = j >= 0 && j <= i / geo.C && !is_forced(j, i / geo.C);
     cand[base + t] = ok ? j : -1;
     if (ok) {
       if (lhist) atomicAdd(&hist[j], 1);
@@ -374,6 +376,208 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   }
 }
 
+// The forced blocks {0, b-1, b} of leaf block b, shared by its 64 queries.  Workgroup =
+// kForcedRun consecutive leaf blocks of one (b, h), eight wavefronts: key tiles and
+// transposed value tiles live in LDS slots, tile 0 in slot 0 for the whole run and tile j >= 1
+// in slot 1 + j % 3, so that moving from block b to b + 1 stages one new tile (b + 1), whose
+// global loads are issued into registers before block b is computed and written to its slot
+// (that of b - 2, no longer read) after it.  Each wavefront takes column groups of 32
+// (query, head) columns (the next group's query fragments loaded ahead) and runs an online
+// softmax over the block's forced tiles (a tile the query's selection does not name, and
+// keys after the query, are masked), with S = K Q^T and O^T = V^T P as in
+// attn_chunk_kernel.  Writes one combined partial per (query, head): the output over its
+// forced keys normalised by their sum (bf16) and their log2-sum-exp (-inf without such keys).
+constexpr int kForcedRun = 8;
+
+template <int D>
+struct ForcedTile {
+  static constexpr int PER = kLeaf * (D / 8) / 512;  // 16-byte pieces per thread and tensor
+  u32x4 kx[PER], vx[PER];
+  __device__ __forceinline__ void load(const bf16* kb, const bf16* vb, int f, int N) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = threadIdx.x + 512 * p;
+      const int key = t / (D / 8), d8 = (t % (D / 8)) * 8;
+      kx[p] = {0u, 0u, 0u, 0u};
+      vx[p] = {0u, 0u, 0u, 0u};
+      if (f * kLeaf + key < N) {
+        kx[p] = *reinterpret_cast<const u32x4*>(kb + (int64_t)(f * kLeaf + key) * D + d8);
+        vx[p] = *reinterpret_cast<const u32x4*>(vb + (int64_t)(f * kLeaf + key) * D + d8);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(bf16* kt, bf16* vt) const {
+    constexpr int VTR = kLeaf + 8;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int t = threadIdx.x + 512 * p;
+      const int key = t / (D / 8), d8 = (t % (D / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&kt[key * (D + 8) + d8]) = kx[p];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vt[(d8 + 2 * w) * VTR + key] = (bf16)(vx[p][w] & 0xFFFFu);
+        vt[(d8 + 2 * w + 1) * VTR + key] = (bf16)(vx[p][w] >> 16);
+      }
+    }
+  }
+};
+
+__device__ __forceinline__ int forced_slot(int j) { return j == 0 ? 0 : 1 + j % 3; }
+
+template <int D, int G>
+__global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                          const bf16* __restrict__ v, Geo geo,
+                                                          const int32_t* __restrict__ idx, float* __restrict__ pfl,
+                                                          bf16* __restrict__ pfo) {
+  static_assert(D % 64 == 0, "ForcedTile spreads a tile over 512 threads in whole pieces");
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int VTR = kLeaf + 8;
+  __shared__ __attribute__((aligned(16))) bf16 kt[4][kLeaf * (D + 8)];
+  __shared__ __attribute__((aligned(16))) bf16 vt[4][D * VTR];
+  __shared__ uint32_t pres[2][kLeaf];  // bit x: the query's selection names forced block x
+  const int bh = blockIdx.y;
+  const int N = geo.N, K = geo.K;
+  const int b = bh / geo.Hkv, h = bh % geo.Hkv;
+  const int bs = blockIdx.x * kForcedRun, be = min(bs + kForcedRun, geo.n1);
+  const bf16* kb = k + (int64_t)bh * N * D;
+  const bf16* vb = v + (int64_t)bh * N * D;
+  auto presence = [&](int bq, uint32_t* dst) {
+    if (threadIdx.x < kLeaf) {
+      const int i = bq * kLeaf + threadIdx.x;
+      uint32_t pm = 0;
+      if (i < N) {
+        const int32_t* sel = idx + ((int64_t)bh * N + i) * K;
+        for (int u = 0; u < K; ++u) {
+          const int j = sel[u];
+          pm |= (j == 0 ? 1u : 0u) | (bq >= 2 && j == bq - 1 ? 2u : 0u) | (bq >= 1 && j == bq ? 4u : 0u);
+        }
+      }
+      dst[threadIdx.x] = pm;
+    }
+  };
+  {  // the run's first block: tiles 0, bs - 1 and bs
+    ForcedTile<D> t;
+    t.load(kb, vb, 0, N);
+    t.store(kt[0], vt[0]);
+    if (bs >= 2) {
+      t.load(kb, vb, bs - 1, N);
+      t.store(kt[forced_slot(bs - 1)], vt[forced_slot(bs - 1)]);
+    }
+    if (bs >= 1) {
+      t.load(kb, vb, bs, N);
+      t.store(kt[forced_slot(bs)], vt[forced_slot(bs)]);
+    }
+    presence(bs, pres[bs & 1]);
+  }
+  __syncthreads();
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = lane & 31, hh = lane >> 5;
+  const float sl = geo.s_log2e;
+  // query fragments of column group cg of block bq (zeros past N)
+  auto load_q = [&](int bq, int cg, bf16x8* dst) {
+    const int gc = cg * 32 + col;
+    const int i = bq * kLeaf + gc / G, r = gc % G;
+    const bool valid = i < N;
+    load_bfrag<D>(q + (((int64_t)b * geo.Hq + h * G + r) * N + (valid ? i : 0)) * D, valid, hh, dst);
+  };
+  bf16x8 bqf[KS];
+  if (wave < 2 * G) load_q(bs, wave, bqf);
+  for (int bq = bs; bq < be; ++bq) {
+    const bool more = bq + 1 < be;
+    ForcedTile<D> nt;
+    if (more) {
+      nt.load(kb, vb, bq + 1, N);
+      presence(bq + 1, pres[(bq + 1) & 1]);
+    }
+    int F[3];
+    const int nf = forced_blocks(bq, F);
+    for (int cg = wave; cg < 2 * G; cg += 8) {
+      // the next column group of this wavefront, in this block or the next
+      const int ncg = cg + 8 < 2 * G ? cg + 8 : wave;
+      const int nbq = cg + 8 < 2 * G ? bq : bq + 1;
+      bf16x8 bqn[KS];
+      if (nbq < be) load_q(nbq, ncg, bqn);
+      const int gc = cg * 32 + col;
+      const int ql = gc / G, r = gc % G;
+      const int i = bq * kLeaf + ql;
+      const bool valid = i < N;
+      const uint32_t pm = valid ? pres[bq & 1][ql] : 0u;
+      float mrun = -INFINITY, lrun = 0.f;
+      f32x16 ao[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int w = 0; w < 16; ++w) ao[db][w] = 0.f;
+      for (int x = 0; x < nf; ++x) {
+        const int f = x == 0 ? F[0] : (x == 1 ? F[1] : F[2]);
+        const int fs = forced_slot(f);
+        // presence bit of block f: 0 -> bit 0, bq - 1 -> bit 1, bq -> bit 2
+        const bool named = (pm >> (f == 0 ? 0 : (f == bq ? 2 : 1))) & 1u;
+        f32x16 s0, s1;
+        tile_mfma32<D>(kt[fs], bqf, lane, s0, s1);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+          const int t0 = f * kLeaf + key_row(w, hh), t1 = t0 + 32;
+          s0[w] = (named && t0 <= i && t0 < N) ? s0[w] * sl : -INFINITY;
+          s1[w] = (named && t1 <= i && t1 < N) ? s1[w] * sl : -INFINITY;
+          mx = fmaxf(mx, fmaxf(s0[w], s1[w]));
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(mrun, mx);
+        // running maximum still -inf: every key so far is masked and contributes nothing
+        const float base = mnew == -INFINITY ? 0.f : mnew;
+        const float alpha = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - base);
+        float sum = 0.f;
+        bf16x8 pa[4];
+#pragma unroll
+        for (int w = 0; w < 16; ++w) {
+          const float p0 = __builtin_amdgcn_exp2f(s0[w] - base), p1 = __builtin_amdgcn_exp2f(s1[w] - base);
+          sum += p0 + p1;
+          pa[w >> 3][w & 7] = (__bf16)p0;
+          pa[2 + (w >> 3)][w & 7] = (__bf16)p1;
+        }
+        sum += __shfl_xor(sum, 32);
+        lrun = lrun * alpha + sum;
+        mrun = mnew;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+#pragma unroll
+          for (int w = 0; w < 16; ++w) ao[db][w] *= alpha;
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            const bf16* vr = &vt[fs][(32 * db + col) * VTR + 32 * (s2 >> 1) + 16 * (s2 & 1) + 4 * hh];
+            const uint2 x0 = *reinterpret_cast<const uint2*>(vr), x1 = *reinterpret_cast<const uint2*>(vr + 8);
+            const u32x4 xv = {x0.x, x0.y, x1.x, x1.y};
+            ao[db] = mfma32(__builtin_bit_cast(bf16x8, xv), pa[s2], ao[db]);
+          }
+        }
+      }
+      if (valid) {
+        const int64_t prow = ((int64_t)bh * N + i) * G + r;
+        if (hh == 0) pfl[prow] = lrun > 0.f ? mrun + __builtin_amdgcn_logf(lrun) : -INFINITY;
+        const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+        bf16* dst = pfo + prow * D + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            uint2 o;
+            o.x = f2bf_rne(ao[db][4 * a] * inv) | (f2bf_rne(ao[db][4 * a + 1] * inv) << 16);
+            o.y = f2bf_rne(ao[db][4 * a + 2] * inv) | (f2bf_rne(ao[db][4 * a + 3] * inv) << 16);
+            *reinterpret_cast<uint2*>(dst + 32 * db + 8 * a) = o;
+          }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2) bqf[s2] = bqn[s2];
+    }
+    // slot of bq + 1 = slot of bq - 2, read last by the previous block (before the barrier)
+    if (more) nt.store(kt[forced_slot(bq + 1)], vt[forced_slot(bq + 1)]);
+    __syncthreads();
+  }
+}
+
 // One wavefront per query group: merges the K block partials of each of its G heads.  A
 // head's row is D / 8 lanes x 16 bytes, so one pass covers HP = 64 / (D / 8) heads and each
 // slot's partial rows of those heads (contiguous: partials are slot-major, head-minor) come
@@ -384,7 +588,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restrict__ idx, Geo geo,
                                                          const float* __restrict__ plse,
-                                                         const bf16* __restrict__ po, bf16* __restrict__ out,
+                                                         const bf16* __restrict__ po,
+                                                         const float* __restrict__ pfl,
+                                                         const bf16* __restrict__ pfo, bf16* __restrict__ out,
                                                          float* __restrict__ lse) {
   constexpr int LPH = D / 8;       // lanes per head row (16 bytes each)
   constexpr int HP = 64 / LPH;     // heads per pass
@@ -399,11 +605,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
   float x0 = -INFINITY, x1 = -INFINITY;
   if (lane < KG) {
     const int jb = idx[row * K + lane / G];
-    if (jb >= 0 && jb <= bq) x0 = lrow[lane];
+    if (jb >= 0 && jb <= bq && !is_forced(jb, bq)) x0 = lrow[lane];
   }
   if (lane + 64 < KG) {
     const int jb = idx[row * K + (lane + 64) / G];
-    if (jb >= 0 && jb <= bq) x1 = lrow[lane + 64];
+    if (jb >= 0 && jb <= bq && !is_forced(jb, bq)) x1 = lrow[lane + 64];
   }
   // partial t's log2-sum-exp for this lane (t may differ between lanes)
   auto xat = [&](int t) -> float {
@@ -411,7 +617,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
     if (t < 64) return a;
     if (t < 128) return c;
     const int jb = idx[row * K + t / G];
-    return (jb >= 0 && jb <= bq) ? lrow[t] : -INFINITY;
+    return (jb >= 0 && jb <= bq && !is_forced(jb, bq)) ? lrow[t] : -INFINITY;
   };
   const int hl = lane / LPH, dl = (lane % LPH) * 8;  // head within the pass, first dim
 #pragma unroll 1
@@ -419,18 +625,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
     const int r = r0 + hl;
     const bool live = r < G;
     const int rr = live ? r : 0;  // idle lanes shadow head 0 so every lane takes part in the shuffles
-    float mx = -INFINITY;
+    // the forced blocks' combined partial of this head (attn_forced_kernel)
+    const float lf = pfl[row * G + rr];
+    const u32x4 fr = *reinterpret_cast<const u32x4*>(pfo + (row * G + rr) * D + dl);
+    float mx = lf;
     for (int u = 0; u < K; ++u) mx = fmaxf(mx, xat(u * G + rr));
     float l = 0.f, acc[8];
+    {
+      const float wf = lf > -INFINITY ? __builtin_amdgcn_exp2f(lf - mx) : 0.f;
+      l = wf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = wf > 0.f ? wf * bf2f(fr[e] & 0xFFFFu) : 0.f;
+        acc[2 * e + 1] = wf > 0.f ? wf * bf2f(fr[e] >> 16) : 0.f;
+      }
+    }
 #pragma unroll 8
     for (int u = 0; u < K; ++u) {
       const int t = u * G + rr;
       const float xt = xat(t);
       const float wu = xt > -INFINITY ? __builtin_amdgcn_exp2f(xt - mx) : 0.f;
       l += wu;
-      const u32x4 pr = *reinterpret_cast<const u32x4*>(po + (row * KG + t) * D + dl);
+      // slots without a partial (forced blocks, padding, blocks after the query's) are not
+      // read: the slot's block is the same for every lane, so this is uniform in practice
+      u32x4 pr = {0u, 0u, 0u, 0u};
+      if (wu > 0.f) pr = *reinterpret_cast<const u32x4*>(po + (row * KG + t) * D + dl);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = bf2f(pr[e] & 0xFFFFu), hi = bf2f(pr[e] >> 16);
@@ -474,8 +693,13 @@ int attn_km_g(const Geo& g, const bf16* q, const bf16* k, const bf16* v, const i
   const int64_t grid = (w.slots + qc - 1) / qc + w.M;  // bound on the chunk count
   attn_chunk_kernel<D, G><<<(unsigned)grid, 256, 0, st>>>(q, k, v, g, off, choff, entries, w.M, plse, po);
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  float* pfl = (float*)(ws + w.pfl);
+  bf16* pfo = (bf16*)(ws + w.pfo);
+  attn_forced_kernel<D, G><<<dim3((g.n1 + kForcedRun - 1) / kForcedRun, g.B * g.Hkv), 512, 0, st>>>(q, k, v, g, idx,
+                                                                                                  pfl, pfo);
+  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   const int64_t rows = (int64_t)g.B * g.Hkv * g.N;
-  attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, out, lse);
+  attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, pfl, pfo, out, lse);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
@@ -514,6 +738,9 @@ AttnWs attention_ws(const Geo& g) {
   w.entries = o; o = align256(o + sizeof(int32_t) * w.slots);
   w.plse = o;    o = align256(o + sizeof(float) * w.slots * g.G);
   w.po = o;      o = align256(o + sizeof(uint16_t) * w.slots * g.G * g.d);
+  const size_t rows = (size_t)g.B * g.Hkv * g.N;
+  w.pfl = o;     o = align256(o + sizeof(float) * rows * g.G);
+  w.pfo = o;     o = align256(o + sizeof(uint16_t) * rows * g.G * g.d);
   w.total = o;
   return w;
 }

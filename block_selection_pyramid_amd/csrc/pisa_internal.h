@@ -68,7 +68,7 @@ int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hip
 // block-sparse attention over selected blocks (decode != 0: one query per sequence at N-1);
 // bf16 prefill runs key-major and needs the workspace laid out by attention_ws
 struct AttnWs {
-  size_t cand, cnt, cursor, off, choff, entries, plse, po, total;
+  size_t cand, cnt, cursor, off, choff, entries, plse, po, pfl, pfo, total;
   int64_t slots;  // B*Hkv*N*K
   int32_t M;      // B*Hkv*n1 block lists
 };
