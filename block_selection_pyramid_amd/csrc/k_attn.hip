@@ -376,8 +376,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   }
 }
 
-// The forced blocks {0, b-1, b} of leaf block b, shared by its 64 queries.  Workgroup =
-// kForcedRun consecutive leaf blocks of one (b, h), eight wavefronts: key tiles and
+// The forced blocks {0, b-1, b} of leaf block b, shared by its 64 queries.  Workgroup = a
+// run of consecutive leaf blocks of one (b, h), eight wavefronts: key tiles and
 // transposed value tiles live in LDS slots, tile 0 in slot 0 for the whole run and tile j >= 1
 // in slot 1 + j % 3, so that moving from block b to b + 1 stages one new tile (b + 1), whose
 // global loads are issued into registers before block b is computed and written to its slot
@@ -387,7 +387,13 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
 // keys after the query, are masked), with S = K Q^T and O^T = V^T P as in
 // attn_chunk_kernel.  Writes one combined partial per (query, head): the output over its
 // forced keys normalised by their sum (bf16) and their log2-sum-exp (-inf without such keys).
-constexpr int kForcedRun = 8;
+// Run length: about two workgroups per compute unit (one fits, by LDS), at most 32 blocks
+// (256K, runs of 4, 8, 16 and 32 blocks: attention 5.07, 5.02, 5.01 and 4.98 ms).
+constexpr int kForcedMaxRun = 32;
+inline int forced_run(const Geo& g) {
+  const int64_t lists = (int64_t)g.B * g.Hkv * g.n1;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kForcedMaxRun, lists / 512));
+}
 
 template <int D>
 struct ForcedTile {
@@ -427,8 +433,8 @@ __device__ __forceinline__ int forced_slot(int j) { return j == 0 ? 0 : 1 + j % 
 template <int D, int G>
 __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, Geo geo,
-                                                          const int32_t* __restrict__ idx, float* __restrict__ pfl,
-                                                          bf16* __restrict__ pfo) {
+                                                          const int32_t* __restrict__ idx, int run,
+                                                          float* __restrict__ pfl, bf16* __restrict__ pfo) {
   static_assert(D % 64 == 0, "ForcedTile spreads a tile over 512 threads in whole pieces");
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int VTR = kLeaf + 8;
@@ -438,7 +444,7 @@ __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict
   const int bh = blockIdx.y;
   const int N = geo.N, K = geo.K;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-  const int bs = blockIdx.x * kForcedRun, be = min(bs + kForcedRun, geo.n1);
+  const int bs = blockIdx.x * run, be = min(bs + run, geo.n1);
   const bf16* kb = k + (int64_t)bh * N * D;
   const bf16* vb = v + (int64_t)bh * N * D;
   auto presence = [&](int bq, uint32_t* dst) {
@@ -695,8 +701,9 @@ int attn_km_g(const Geo& g, const bf16* q, const bf16* k, const bf16* v, const i
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   float* pfl = (float*)(ws + w.pfl);
   bf16* pfo = (bf16*)(ws + w.pfo);
-  attn_forced_kernel<D, G><<<dim3((g.n1 + kForcedRun - 1) / kForcedRun, g.B * g.Hkv), 512, 0, st>>>(q, k, v, g, idx,
-                                                                                                  pfl, pfo);
+  const int run = forced_run(g);
+  attn_forced_kernel<D, G><<<dim3((g.n1 + run - 1) / run, g.B * g.Hkv), 512, 0, st>>>(q, k, v, g, idx, run, pfl,
+                                                                                      pfo);
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   const int64_t rows = (int64_t)g.B * g.Hkv * g.N;
   attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, pfl, pfo, out, lse);

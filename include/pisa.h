@@ -242,9 +242,11 @@ int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* 
  * group; entries < 0 or after the query's own block are skipped; entries must be distinct,
  * as pisa_select_* produce them).  k and v [B, Hkv, N, d] of q's dtype; out has q's dtype
  * (bf16 rounded to nearest even from fp32 accumulation); lse fp32, may be NULL.  A row
- * with no attended key gets out = 0, lse = -inf.  bf16 prefill sorts the (query group,
- * block) pairs by block, attends each block's staged key and value tiles on the matrix
- * cores and merges per-block partial outputs (kept in bf16 in the workspace); it needs
+ * with no attended key gets out = 0, lse = -inf.  bf16 prefill attends the blocks
+ * {0, b-1, b} of each leaf block b for all its queries at once (each query masked by
+ * whether its selection names them), sorts the other (query group, block) pairs by block,
+ * attends each block's staged key and value tiles on the matrix cores and merges the
+ * partial outputs (kept in bf16 in the workspace); it needs
  * pisa_attention_workspace_bytes(p, mode) bytes of 16-byte aligned device workspace
  * (PISA_ERR_WORKSPACE if smaller).  fp32 inputs and decode need none (workspace may be
  * NULL).
