@@ -671,6 +671,10 @@ ATT_CASES = [
     ("G16-d64-padded", 2048 + 9, 16, 1, 64, 7, synth.BF16, 1, False, "random-pad"),
     ("G1-K32", 5000, 2, 2, 128, 32, synth.BF16, 1, False, "random"),
     ("G4-some-forced-dropped", 3000 + 41, 8, 2, 128, 8, synth.BF16, 2, False, "random-dropforced"),
+    # 8 KV heads x 131 leaf blocks: the forced-block kernel walks runs of 2 blocks, the last
+    # run a single ragged block
+    ("G2-runs-of-2-ragged", 64 * 130 + 17, 16, 8, 128, 8, synth.BF16, 1, False, "random"),
+    ("G8-d64-ragged", 4096 + 100, 16, 2, 64, 6, synth.BF16, 1, False, "random"),
     ("decode-G4", 9000, 8, 2, 128, 8, synth.BF16, 3, True, "oracle"),
     ("decode-f32-G8", 777, 8, 1, 64, 4, synth.F32, 2, True, "random"),
 ]
