@@ -441,10 +441,11 @@ __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict
   __shared__ __attribute__((aligned(16))) bf16 kt[4][kLeaf * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 vt[4][D * VTR];
   __shared__ uint32_t pres[2][kLeaf];  // bit x: the query's selection names forced block x
-  const int bh = blockIdx.y;
+  const int nruns = (geo.n1 + run - 1) / run;
+  const int bh = blockIdx.x / nruns;  // one-dimensional grid: B * Hkv may exceed a y extent
   const int N = geo.N, K = geo.K;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-  const int bs = blockIdx.x * run, be = min(bs + run, geo.n1);
+  const int bs = (blockIdx.x % nruns) * run, be = min(bs + run, geo.n1);
   const bf16* kb = k + (int64_t)bh * N * D;
   const bf16* vb = v + (int64_t)bh * N * D;
   auto presence = [&](int bq, uint32_t* dst) {
@@ -702,8 +703,8 @@ int attn_km_g(const Geo& g, const bf16* q, const bf16* k, const bf16* v, const i
   float* pfl = (float*)(ws + w.pfl);
   bf16* pfo = (bf16*)(ws + w.pfo);
   const int run = forced_run(g);
-  attn_forced_kernel<D, G><<<dim3((g.n1 + run - 1) / run, g.B * g.Hkv), 512, 0, st>>>(q, k, v, g, idx, run, pfl,
-                                                                                      pfo);
+  const unsigned fgrid = (unsigned)(((g.n1 + run - 1) / run) * (int64_t)g.B * g.Hkv);
+  attn_forced_kernel<D, G><<<fgrid, 512, 0, st>>>(q, k, v, g, idx, run, pfl, pfo);
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   const int64_t rows = (int64_t)g.B * g.Hkv * g.N;
   attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, pfl, pfo, out, lse);
