@@ -184,8 +184,10 @@ int attn_g(const Geo& g, const void* q, const void* k, const void* v, const int3
 // staged transposed so that those keys are two 8-byte LDS reads.  The transposed product
 // leaves each lane four consecutive dims of its own column's output row per result group:
 // each pair's block-normalised output (bf16) is staged in LDS in 8-byte pieces and leaves
-// in 16-byte pieces, with its log2-sum-exp; one wavefront per query group then merges its
-// K partials.
+// in 16-byte pieces, with its log2-sum-exp.  The forced blocks {0, b-1, b} of leaf block b
+// are shared by all its queries: they are left out of the pairs and attended per leaf block
+// by attn_forced_kernel, which writes one combined partial per (query, head).  One
+// wavefront per query group then merges that partial with its other slots' partials.
 
 // Candidate array of the pairs (per_row = K slots per query group, -1 where the slot is
 // padding, names a block after the query's own or one of its forced blocks) and their
@@ -585,13 +587,14 @@ __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict
   }
 }
 
-// One wavefront per query group: merges the K block partials of each of its G heads.  A
-// head's row is D / 8 lanes x 16 bytes, so one pass covers HP = 64 / (D / 8) heads and each
-// slot's partial rows of those heads (contiguous: partials are slot-major, head-minor) come
-// in one 16-byte load per lane, the K slots' loads all in flight together.  Lane t < K G
-// first reads the log2-sum-exp of partial t (slot t / G, head t % G); each lane then takes
-// its head's weights by shuffles.  A slot without a partial reads in-bounds workspace and
-// gets weight 0 through a select, so no stale value reaches the sum.
+// One wavefront per query group: merges, for each of its G heads, the forced blocks'
+// combined partial and the partials of the other selected blocks.  A head's row is D / 8
+// lanes x 16 bytes, so one pass covers HP = 64 / (D / 8) heads and each slot's partial rows
+// of those heads (contiguous: partials are slot-major, head-minor) come in one 16-byte load
+// per lane, the K slots' loads all in flight together.  Lane t < K G first reads the
+// log2-sum-exp of partial t (slot t / G, head t % G); each lane then takes its head's
+// weights by shuffles.  A slot without a partial (forced, padding, or after the query's
+// block) gets weight 0 and is not loaded, so no stale value reaches the sum.
 template <int D, int G>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restrict__ idx, Geo geo,
                                                          const float* __restrict__ plse,
