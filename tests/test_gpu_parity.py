@@ -675,6 +675,9 @@ ATT_CASES = [
     # run a single ragged block
     ("G2-runs-of-2-ragged", 64 * 130 + 17, 16, 8, 128, 8, synth.BF16, 1, False, "random"),
     ("G8-d64-ragged", 4096 + 100, 16, 2, 64, 6, synth.BF16, 1, False, "random"),
+    # every selected block forced: no (query group, block) pair reaches the chunk kernel
+    ("tiny-N5-all-forced", 5, 8, 2, 64, 4, synth.BF16, 2, False, "random"),
+    ("tiny-N70-two-blocks", 70, 8, 2, 128, 4, synth.BF16, 2, False, "random"),
     ("decode-G4", 9000, 8, 2, 128, 8, synth.BF16, 3, True, "oracle"),
     ("decode-f32-G8", 777, 8, 1, 64, 4, synth.F32, 2, True, "random"),
 ]
