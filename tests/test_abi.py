@@ -155,6 +155,21 @@ def test_attention_host_checks(pisa):
     assert lib.pisa_sparse_attention(P, pisa.PREFILL, 0, *a[1:], 0x1000, need, 0x1000, None, None) == 1
 
 
+@pytest.mark.parametrize("B,N,Hq,Hkv,d,K", [(1, 262144, 16, 4, 128, 8), (2, 3000 + 17, 8, 2, 64, 6), (1, 5, 8, 2, 64, 4)])
+def test_attention_workspace_regions(pisa, B, N, Hq, Hkv, d, K):
+    # bf16 prefill: per slot (K per query group) a candidate, a list entry, G log2-sum-exp
+    # partials and G bf16 output rows; per (KV head, leaf block) list a count, a cursor, an
+    # offset and a chunk offset (+1 each for the offsets); per query group the forced
+    # blocks' G log2-sum-exp partials and G bf16 output rows; eleven 256-byte aligned regions
+    lib = pisa.load()
+    p = pisa.Problem(B, N, Hq, Hkv, d, 64, K, 2)
+    G, rows, n1 = Hq // Hkv, B * Hkv * N, -(-N // 64)
+    slots, lists = rows * K, B * Hkv * n1
+    need = slots * (4 + 4 + 4 * G + 2 * G * d) + lists * 4 * 4 + 2 * 4 + rows * G * (4 + 2 * d)
+    got = lib.pisa_attention_workspace_bytes(ctypes.byref(p.c()), pisa.PREFILL)
+    assert need <= got < need + 11 * 256
+
+
 def test_bsa_host_checks(pisa):
     lib = pisa.load()
     p = pisa.Problem(1, 4096, 16, 4, 128)
