@@ -7,6 +7,11 @@ not know that feature, which is harmless.  Matrix-core results are kept in ordin
 VGPRs (``-amdgpu-mfma-vgpr-form``) so that the epilogues read them without accvgpr
 moves.
 
+Every compile also asks for the compiler's per-kernel resource report; the build writes it
+to ``_build/kernel_resources.txt`` (VGPRs, scratch bytes per lane, waves per SIMD) and
+fails when a kernel instantiation on the 16/4-head, d = 128 bf16 path spills to scratch
+(``HEADLINE``): a spill there costs HBM traffic on every launch.
+
 Usage: ``python -m block_selection_pyramid_amd.build [--force] [-j N]``.
 """
 from __future__ import annotations
@@ -14,6 +19,7 @@ from __future__ import annotations
 import argparse
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -33,6 +39,52 @@ CXXFLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
+
+
+RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
+
+# Kernel instantiations of the d = 128, G = 4 bf16 path (prefill selection and decode) that
+# must not spill: demangled-name prefixes.
+HEADLINE = (
+    "pisa::(anonymous namespace)::route_dense_kernel<128, 4, 8, false>",
+    "pisa::(anonymous namespace)::route_sub_kernel<128,",
+    "pisa::(anonymous namespace)::route_mfma_kernel<128, 4,",
+    "pisa::(anonymous namespace)::leaf_pair_kernel<128, 4>",
+    "pisa::(anonymous namespace)::final_kernel",
+    "pisa::(anonymous namespace)::scatter_pairs_hist_kernel",
+    "pisa::(anonymous namespace)::pyr_sub_kernel<unsigned short, 128",
+    "pisa::(anonymous namespace)::decode_kernel<unsigned short, 128, 4",
+)
+
+
+def _demangle(names: list[str]) -> list[str]:
+    exe = shutil.which("c++filt") or shutil.which("llvm-cxxfilt") or "/opt/rocm/llvm/bin/llvm-cxxfilt"
+    try:
+        r = subprocess.run([exe], input="\n".join(names), capture_output=True, text=True, check=True)
+        out = r.stdout.splitlines()
+        return out if len(out) == len(names) else names
+    except (OSError, subprocess.CalledProcessError):
+        return names
+
+
+def _resources(stderr: str) -> list[tuple[str, int, int, int]]:
+    """(kernel, VGPRs, scratch bytes per lane, waves per SIMD) from the compiler remarks."""
+    rows, cur = [], None
+    for line in stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = [m.group(1), -1, -1, -1]
+            rows.append(cur)
+            continue
+        if cur is None:
+            continue
+        for i, key in ((1, r"\bVGPRs: (\d+)"), (2, r"ScratchSize \[bytes/lane\]: (\d+)"),
+                       (3, r"Occupancy \[waves/SIMD\]: (\d+)")):
+            m = re.search(key, line)
+            if m:
+                cur[i] = int(m.group(1))
+    names = _demangle([r[0] for r in rows])
+    return [(n, r[1], r[2], r[3]) for n, r in zip(names, rows)]
 
 
 def hipcc() -> str:
@@ -59,11 +111,11 @@ def up_to_date() -> bool:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [hipcc(), *CXXFLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *CXXFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
-    return obj
+    return obj, _resources(r.stderr)
 
 
 def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> str:
@@ -73,7 +125,16 @@ def build(force: bool = True, jobs: int | None = None, verbose: bool = False) ->
     os.makedirs(BUILD_DIR, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, sources()))
+        done = list(ex.map(_compile, sources()))
+    objs = [o for o, _ in done]
+    res = sorted(r for _, rs in done for r in rs)
+    with open(RESOURCES, "w") as f:
+        for name, vgpr, scratch, occ in res:
+            f.write("%4d VGPRs %5d B scratch %2d waves/SIMD  %s\n" % (vgpr, scratch, occ, name))
+    spills = [r for r in res if r[2] > 0 and r[0].startswith(HEADLINE)]
+    if spills:
+        raise RuntimeError("headline kernels spill to scratch (see %s):\n%s" % (
+            RESOURCES, "\n".join("%d B/lane  %s" % (r[2], r[0]) for r in spills)))
     tmp = OUT + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

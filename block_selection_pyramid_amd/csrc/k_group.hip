@@ -1,6 +1,6 @@
-// Leaf grouping: "groups queries that need the same leaf block and scores them together"
-// ("Block Sparse Attention with Log-Linear Complexity", rcap.io explainer, kernel
-// paragraph).  A counting sort: the routing kernel histograms the routed pairs per
+// Leaf grouping: the second prefill stage collects the queries routed to one leaf block
+// so that the block is scored for all of them at once ("Block Sparse Attention with
+// Log-Linear Complexity", rcap.io explainer, kernel paragraph).  A counting sort: the routing kernel histograms the routed pairs per
 // (batch, KV head, level-2 node), whose two children are adjacent leaf blocks that the
 // prefill leaf kernel scores together; here an exclusive scan turns the counts into list
 // offsets and into offsets of fixed-size work chunks, and a scatter writes each entry into

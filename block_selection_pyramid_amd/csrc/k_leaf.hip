@@ -2,8 +2,8 @@
 // local blocks plus final Top-K.
 //
 // "Block Sparse Attention with Log-Linear Complexity": rcap.io explainer, kernel
-// paragraph (stage two groups queries that need the same leaf block so that each leaf key
-// tile is loaded once and reused); agihunt.info summary, LSE and forced-block paragraph
+// paragraph: the second stage gathers the queries routed to a leaf block, so one load of
+// its key tile serves all of them); agihunt.info summary, LSE and forced-block paragraph
 // (leaf LSE over raw keys; first, previous and current blocks forced in) and kernels
 // paragraph (GQA heads share the selection).
 //

@@ -1,5 +1,5 @@
 // Pyramid construction ("Block Sparse Attention with Log-Linear Complexity", agihunt.info
-// summary, pyramid paragraph; rcap.io explainer, "think of the keys as leaves of a tree"):
+// summary, pyramid paragraph; rcap.io explainer, tree paragraph):
 // level 1 node j = mean of the keys of leaf block j, level l node j = mean of level l-1
 // nodes 2j, 2j+1 (g = 2), unweighted over the children that exist.  Every mean also goes
 // to the routing copy, scaled by s log2(e) and split into bf16 hi + lo.

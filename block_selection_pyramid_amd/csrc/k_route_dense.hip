@@ -145,9 +145,6 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[cg][v] = 0.f;
-    // raised wave priority while the MFMAs issue, so a wavefront in its contraction goes
-    // ahead of one in its epilogue on the same SIMD (256K: route_upper 2.73 -> 2.67 ms)
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks) * 64 + lane) * 16);
@@ -158,7 +155,6 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
         acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[cg][ks], acc[cg], 0, 0, 0);
       }
     }
-    __builtin_amdgcn_s_setprio(0);
     const int nchild = geo.n[l - 1], cshift = l - 2;
     // Epilogue.  Result row (child) 8a + 4hh + 2p (+1) sits in acc[4a + 2p] (+1); node
     // 4a + 2hh + p of the tile owns that pair.  Per head, with d = a0 - a1: mx = a0 -

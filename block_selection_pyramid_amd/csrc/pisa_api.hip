@@ -60,9 +60,13 @@ int supported(const Geo& g, int dtype, int mode) {
   if (g.d != 64 && g.d != 128) return PISA_ERR_UNSUPPORTED;
   if (g.C != kLeaf || g.g != 2 || g.K > 32) return PISA_ERR_UNSUPPORTED;
   if (g.G != 1 && g.G != 2 && g.G != 4 && g.G != 8 && g.G != 16) return PISA_ERR_UNSUPPORTED;
-  if (g.N >= (1 << 25)) return PISA_ERR_UNSUPPORTED;  // leaf entries pack (i << 6 | slot)
-  const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
-  if (slots >= ((int64_t)1 << 31) - 1) return PISA_ERR_UNSUPPORTED;  // int32 list offsets
+  if (mode == PISA_PREFILL) {
+    // only the prefill workspace holds per-(query, slot) lists: entries pack (i << 6 | slot)
+    // and list offsets are int32
+    if (g.N >= (1 << 25)) return PISA_ERR_UNSUPPORTED;
+    const int64_t slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
+    if (slots >= ((int64_t)1 << 31) - 1) return PISA_ERR_UNSUPPORTED;
+  }
   return PISA_OK;
 }
 
@@ -108,6 +112,20 @@ int pisa_levels(const pisa_problem* p, int32_t* n_levels, int64_t* level_nodes, 
   return PISA_OK;
 }
 
+int pisa_pyramid_layout(const pisa_problem* p, int32_t* n_levels, int32_t* nodes, int64_t* node_offset) {
+  Geo g;
+  const int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (n_levels) *n_levels = g.L;
+  if (nodes) {
+    for (int i = 0; i < PISA_MAX_LEVELS; ++i) nodes[i] = i < g.L ? g.n[i + 1] : 0;
+  }
+  if (node_offset) {
+    for (int i = 0; i <= PISA_MAX_LEVELS; ++i) node_offset[i] = i <= g.L ? g.off[i + 1] : 0;
+  }
+  return PISA_OK;
+}
+
 int pisa_supported(const pisa_problem* p, int mode) {
   Geo g;
   const int rc = make_geo(p, &g);
@@ -134,7 +152,8 @@ int pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyramid, pis
   int rc = make_geo(p, &g);
   if (rc != PISA_OK) return rc;
   if (!k || !pyramid || !aligned16(k) || !aligned16(pyramid)) return PISA_ERR_INVALID_ARG;
-  rc = supported(g, p->dtype, PISA_PREFILL);
+  // the build uses no workspace lists: the decode support matrix (no prefill list limits)
+  rc = supported(g, p->dtype, PISA_DECODE);
   if (rc != PISA_OK) return rc;
   return launch_build_pyramid(g, p->dtype, k, pyramid, (hipStream_t)stream);
 }

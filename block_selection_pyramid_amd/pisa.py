@@ -81,7 +81,7 @@ class Problem:
 
 _lib = None
 
-EXPORTS = ("pisa_levels", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
+EXPORTS = ("pisa_levels", "pisa_pyramid_layout", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs",
            "pisa_prefill_dense_levels", "pisa_select_decode",
            "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
@@ -101,6 +101,7 @@ def load(path: str | None = None):
     P = ctypes.POINTER(_CProblem)
     vp, sz = ctypes.c_void_p, ctypes.c_size_t
     lib.pisa_levels.argtypes = [P, vp, vp, vp]
+    lib.pisa_pyramid_layout.argtypes = [P, vp, vp, vp]
     lib.pisa_supported.argtypes = [P, ctypes.c_int]
     lib.pisa_pyramid_bytes.argtypes = [P]
     lib.pisa_pyramid_bytes.restype = sz
@@ -139,6 +140,16 @@ def levels(p: Problem):
     _check(load().pisa_levels(ctypes.byref(p.c()), ctypes.byref(n), nodes, offs), "pisa_levels")
     L = n.value
     return L, list(nodes[: L + 1]), list(offs[1: L + 2])
+
+
+def pyramid_layout(p: Problem):
+    """(L, [n_1..n_L], [offset of level 1..L, T]) from pisa_pyramid_layout."""
+    n = (ctypes.c_int32)()
+    nodes = (ctypes.c_int32 * MAX_LEVELS)()
+    offs = (ctypes.c_int64 * (MAX_LEVELS + 1))()
+    _check(load().pisa_pyramid_layout(ctypes.byref(p.c()), ctypes.byref(n), nodes, offs), "pisa_pyramid_layout")
+    L = n.value
+    return L, list(nodes[:L]), list(offs[: L + 1])
 
 
 def supported(p: Problem, mode: int = PREFILL) -> int:

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shaped like the pages' selection workloads.
 
-The paper's timing runs ("selection kernels at C=64, K=8", 4K-256K tokens) name no
-dataset, so every workload here is synthetic: q and k are i.i.d. N(0, 1) from a
+The paper's timing runs (the selection kernels alone at C=64 and K=8, 4K-256K tokens)
+name no dataset, so every workload here is synthetic: q and k are i.i.d. N(0, 1) from a
 counter-based generator (SplitMix64 hash of (seed, tensor id, flat index), then
 Box-Muller; see ``csrc/synth.c``), rounded to bf16 with round-to-nearest-even for the
 bf16 workloads, plus planted "needle" keys equal to 3x a later query row of a head in

@@ -7,7 +7,7 @@
  *
  *   - keys are mean-pooled into a pyramid: level 1 holds one mean per leaf block of C
  *     keys, each coarser level holds the mean of g adjacent nodes of the level below
- *     (agihunt.info, pyramid paragraph; rcap.io, "think of the keys as leaves of a tree");
+ *     (agihunt.info, pyramid paragraph; rcap.io, tree paragraph);
  *   - the walk starts at the coarsest stored level, scores each candidate node by the
  *     LogSumExp over its children of the scaled dot products q.child, keeps the Top-K and
  *     expands only their children, so each level scores at most g*K candidates (rcap.io,
@@ -118,6 +118,16 @@ typedef struct {
  * be NULL.  Returns PISA_OK or PISA_ERR_INVALID_ARG.
  */
 int pisa_levels(const pisa_problem* p, int32_t* n_levels, int64_t* level_nodes, int64_t* level_offset);
+
+/*
+ * The same level table in the pyramid's own terms, leaf level first: nodes[i] = n_{i+1}
+ * for i = 0..L-1 and node_offset[i] = offset of level i+1 inside one (batch, KV head)
+ * pyramid for i = 0..L, so node_offset[L] = T, the nodes per (batch, KV head); entries
+ * past those are set to 0.  nodes must hold PISA_MAX_LEVELS entries, node_offset
+ * PISA_MAX_LEVELS + 1; either may be NULL.  Host only.  Returns PISA_OK or
+ * PISA_ERR_INVALID_ARG.
+ */
+int pisa_pyramid_layout(const pisa_problem* p, int32_t* n_levels, int32_t* nodes, int64_t* node_offset);
 
 /* PISA_OK if the kernels support this problem in this mode, else the error code. */
 int pisa_supported(const pisa_problem* p, int mode);

@@ -12,11 +12,10 @@
  *      top-down walk, bounded candidate set), paragraph on LSE scoring and
  *      the forced first/previous/current leaf blocks, paragraph on the
  *      kernels and GQA sharing.
- *  [B] rcap.io explainer of the same paper: the "think of the keys as leaves
- *      of a tree" paragraph (pooling with g = 2), the "selection walks the
- *      tree top-down" paragraph (at most g*K candidates per level), the
- *      "scoring rule matters" paragraph (LSE over child summaries, Jensen),
- *      and the selection-walk sketch that follows it.
+ *  [B] rcap.io explainer of the same paper: the tree paragraph (keys as
+ *      leaves, pooling with g = 2), the top-down walk paragraph (at most g*K
+ *      candidates per level), the scoring-rule paragraph (LSE over child
+ *      summaries, Jensen), and the selection-walk sketch that follows it.
  *
  * Readings taken where the pages are silent (each is also listed in the
  * design notes):
@@ -704,8 +703,8 @@ int orc_check_rows(const orc_problem* P, const void* qp, const void* k, const do
 
 /*
  * The full-scan selector the pages compare the pyramid against ([A] first
- * paragraphs and baselines paragraph; [B] "the catch is the picking step"
- * paragraph and the comparison-point paragraph: standard block-sparse
+ * paragraphs and baselines paragraph; [B] picking-step paragraph and the
+ * comparison-point paragraph: standard block-sparse
  * attention scores every query against every block summary, O(N^2/C); the
  * baseline is NSA's selected branch with mean-pooled block summaries).
  * Readings (also in the design notes):

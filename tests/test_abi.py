@@ -59,6 +59,16 @@ def test_level_table_matches_oracle(pisa, N, K):
     assert nodes == oracle.levels(N, 64, K, 2)
     assert offs[0] == 0 and offs[-1] == sum(nodes[1:])
     assert pisa.pyramid_bytes(p) == 2 * 4 * offs[-1] * 128
+    L2, nodes2, offs2 = pisa.pyramid_layout(p)
+    assert L2 == L and nodes2 == nodes[1:] and offs2 == offs
+
+
+def test_decode_k32_at_full_decode_shape_is_supported(pisa):
+    # 32 sequences x 256K keys, 16/4 heads: B*Hkv*N*2K = 2^31 is past the prefill list limit,
+    # which decode, its pyramid build and the append path do not use
+    p = pisa.Problem(32, 262144, 16, 4, 128, 64, 32, 2)
+    assert pisa.supported(p, pisa.DECODE) == 0
+    assert pisa.supported(p, pisa.PREFILL) == 2
 
 
 def test_sizes(pisa):
