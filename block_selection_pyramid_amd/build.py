@@ -131,7 +131,7 @@ def build(force: bool = True, jobs: int | None = None, verbose: bool = False) ->
     with open(RESOURCES, "w") as f:
         for name, vgpr, scratch, occ in res:
             f.write("%4d VGPRs %5d B scratch %2d waves/SIMD  %s\n" % (vgpr, scratch, occ, name))
-    spills = [r for r in res if r[2] > 0 and r[0].startswith(HEADLINE)]
+    spills = [r for r in res if r[2] > 0 and r[0].removeprefix("void ").startswith(HEADLINE)]
     if spills:
         raise RuntimeError("headline kernels spill to scratch (see %s):\n%s" % (
             RESOURCES, "\n".join("%d B/lane  %s" % (r[2], r[0]) for r in spills)))

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256, 2) void bsa_kernel(const bf16* __restrict__ q,
   const int iw = iwg + wave * QPW;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
   const int bqmax = (min(N, iwg + QW) - 1) / C;
-  const char* Rb = reinterpret_cast<const char*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * (4 * D);
+  const char* Rb = reinterpret_cast<const char*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * (4 * D);
 
   const int j = lane & 31, hh = lane >> 5, r = j % G;
   bf16x8 qf[NCG][KS];

@@ -126,8 +126,8 @@ __global__ __launch_bounds__(256) void pyr_sub_kernel(const Tin* __restrict__ sr
   const int j0 = blockIdx.x * kSub;
   const int nodes = min(kSub, geo.n[l0] - j0);
   const Tin* s = src + (int64_t)bh * src_bh_stride;
-  float* P = pyr + (int64_t)bh * geo.T * D;
-  bf16* R = reinterpret_cast<bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+  float* P = pyr + (int64_t)bh * geo.Tp * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * 2 * D;
   for (int jb0 = 0; jb0 < nodes; jb0 += kBuildNodes) {
     const int nb = min(kBuildNodes, nodes - jb0);
     float m[kBuildNodes];
@@ -179,7 +179,7 @@ int build_t(const Geo& g, const Tin* k, float* pyr, hipStream_t st) {
       pyr_sub_kernel<Tin, D, kLeaf><<<grid, 256, 0, st>>>(k, (int64_t)g.N * D, g.N, pyr, g, 1);
     } else {
       const float* src = pyr + (int64_t)g.off[l0 - 1] * D;
-      pyr_sub_kernel<float, D, 2><<<grid, 256, 0, st>>>(src, (int64_t)g.T * D, g.n[l0 - 1], pyr, g, l0);
+      pyr_sub_kernel<float, D, 2><<<grid, 256, 0, st>>>(src, (int64_t)g.Tp * D, g.n[l0 - 1], pyr, g, l0);
     }
     if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   }
@@ -219,8 +219,8 @@ __global__ __launch_bounds__(256) void append_leaf_kernel(const Tin* __restrict_
   if (!dirty_blocks(cap, old_len, new_len, bh / cap.Hkv, max_blocks, &len, &lo, &hi)) return;  // whole workgroup
   const int j0 = lo + blockIdx.x * kSub;
   const Tin* s = k + (int64_t)bh * cap.N * D;
-  float* P = pyr + (int64_t)bh * cap.T * D;
-  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.T * 2 * D;
+  float* P = pyr + (int64_t)bh * cap.Tp * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.Tp * 2 * D;
   for (int j = j0; j < j0 + kSub && j <= hi; ++j) {
     const float m = rows_mean<Tin, D>(s, j * cap.C, min(j * cap.C + cap.C, len), red, tid);
     if (tid < D) {
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(256) void append_up_kernel(Geo cap, const int32_t* 
   const int tid = threadIdx.x, bh = blockIdx.x;
   int len, lo, hi;
   if (!dirty_blocks(cap, old_len, new_len, bh / cap.Hkv, max_blocks, &len, &lo, &hi)) return;  // whole workgroup
-  float* P = pyr + (int64_t)bh * cap.T * D;
-  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.T * 2 * D;
+  float* P = pyr + (int64_t)bh * cap.Tp * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.Tp * 2 * D;
   int nprev = (len + cap.C - 1) / cap.C;  // nodes of level l - 1 at this length
   for (int l = 2; l <= cap.L; ++l) {
     const int ncur = (nprev + 1) >> 1;
@@ -273,8 +273,8 @@ __global__ __launch_bounds__(256) void append_path_kernel(const Tin* __restrict_
   const int tid = threadIdx.x, bh = blockIdx.x;
   int len, lo, hi;
   if (!dirty_blocks(cap, old_len, new_len, bh / cap.Hkv, 1, &len, &lo, &hi)) return;  // whole workgroup
-  float* P = pyr + (int64_t)bh * cap.T * D;
-  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.T * 2 * D;
+  float* P = pyr + (int64_t)bh * cap.Tp * D;
+  bf16* R = reinterpret_cast<bf16*>(pyr + cap.means_floats()) + (int64_t)bh * cap.Tp * 2 * D;
   const int n1 = (len + cap.C - 1) / cap.C;  // leaf blocks at this length
   // sib[l]: element tid of the sibling of the path's level-l node (when it exists)
   float sib[kMaxLevels + 1];

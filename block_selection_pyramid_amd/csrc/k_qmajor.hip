@@ -112,7 +112,7 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
       for (int v = 0; v < VEC; ++v) qs[r * (D + kQPad) + e + v] = x[v];
     }
   }
-  const bf16* R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+  const bf16* R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * 2 * D;
   int sbase = 0;
   if constexpr (std::is_same<T, bf16>::value) {
     using Walk = MfmaWalk<D, G, 1>;
@@ -121,8 +121,8 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
     constexpr int kChunks = Walk::kRec / 16;  // 16-byte pieces per node
     for (int t = threadIdx.x; t < snodes * kChunks; t += 64 * kDecodeWaves) {
       const int nd = t / kChunks, c = t % kChunks;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(R) +
-                                                      (int64_t)(sbase + nd) * Walk::kRec + 16 * c);
+      const u32x4 v =
+          *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(R) + rc_piece_bytes(sbase + nd, c, D));
       *reinterpret_cast<u32x4*>(stage + nd * Walk::kRecLds + 16 * c) = v;
     }
   }
@@ -154,7 +154,7 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
       nx = mw.walk(geo, bq, &wlm, lane);
       X = wlm.X;
     } else {
-      ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.T * D, qs};
+      ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.Tp * D, qs};
       nx = route_walk(geo, sc, bq, &wl, lane);
       X = wl.X;
     }

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void route_valu_kernel(const float* __restrict
   float* qs = qs_all[wave];
   load_qrows<float, D, G>(rows, qs, lane);
   wave_sync();
-  ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.T * D, qs};
+  ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.Tp * D, qs};
   const int nx = route_walk(geo, sc, bq, w, lane);
   const int twoK = 2 * geo.K;
   if (lane < twoK) {
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
   }
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
   Walk mw;
-  mw.R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * 2 * D;
+  mw.R = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * 2 * D;
 
   WalkLdsM<GPW>* w = &wl_all[wave];
   const int64_t qbase = ((int64_t)b * geo.Hq + h * G) * geo.N;
@@ -146,6 +146,7 @@ int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* p
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));
   const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
   const int l_x = g.L >= 3 ? dense_bottom(g) - 1 : 2;  // level of the candidates in x2
+  if (route_sub_supported(g, l_x)) return launch_route_sub(g, l_x, q, pyr, x2, cand, cnt, st);
   route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, l_x, x2, cand, cnt);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }

@@ -44,6 +44,15 @@ constexpr size_t dense_lds_bytes() {
 // Forced key tile f (64 raw keys) into fragment-major LDS: fragment fi = rb KS + ks holds
 // keys 64 f + 32 rb + (lane & 31), dims 16 ks + 8 (lane >> 5) .. +8; keys past N read
 // zeros (the row index is clamped and the value replaced, so no load sits behind a branch).
+// Fragments fi = wave + 4 u of dense_load_keys into LDS slot lane of fragment fi.
+template <int D, int NU>
+__device__ __forceinline__ void dense_store_keys(char* lds, int buf, int wave, int lane, const u32x4 (&stg)[NU]) {
+  constexpr int TILE = 2 * (D / 16) * 1024;
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    *reinterpret_cast<u32x4*>(lds + buf * TILE + ((wave + kDenseWaves * u) * 64 + lane) * 16) = stg[u];
+}
+
 template <int D, int NU>
 __device__ __forceinline__ void dense_load_keys(const bf16* kb, int N, int f, int wave, int lane, u32x4 (&stg)[NU]) {
   constexpr int KS = D / 16;
@@ -92,7 +101,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   const int iw = iwg + wave * QPW;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
   const int bqmax = (min(N, iwg + kDenseWaves * QPW) - 1) / C;
-  const char* Rb = reinterpret_cast<const char*>(pyr + geo.means_floats()) + (int64_t)bh * geo.T * (4 * D);
+  const char* Rb = reinterpret_cast<const char*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * (4 * D);
 
   // B operand: lane column j <-> (query j / G, head j % G) of column group cg, dims
   // 16 ks + 8 hh .. +8 of k-step ks.
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   const bf16* kb = k + (int64_t)bh * N * D;
   __syncthreads();  // the staging buffers are free again
   dense_load_keys<D>(kb, N, ft[0], wave, lane, stg);
-  dense_store_tile<D>(lds, 0, wave, lane, stg);
+  dense_store_keys<D>(lds, 0, wave, lane, stg);
   __syncthreads();
   int nfw = 0;  // |F| of this wavefront's leaf block
   {
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (x + 1 < nft) dense_store_tile<D>(lds, (x + 1) & 1, wave, lane, stg);
+    if (x + 1 < nft) dense_store_keys<D>(lds, (x + 1) & 1, wave, lane, stg);
     __syncthreads();
   }
 }

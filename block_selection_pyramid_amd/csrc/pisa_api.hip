@@ -51,6 +51,7 @@ int make_geo(const pisa_problem* p, Geo* g) {
   }
   g->off[L + 1] = (int32_t)off;
   g->T = (int32_t)off;
+  g->Tp = (int32_t)((off + 1) & ~(int64_t)1);  // sibling pairs of the routing copy stay within one (b, h)
   return PISA_OK;
 }
 
@@ -136,7 +137,7 @@ int pisa_supported(const pisa_problem* p, int mode) {
 size_t pisa_pyramid_bytes(const pisa_problem* p) {
   Geo g;
   if (make_geo(p, &g) != PISA_OK) return 0;
-  return 2 * sizeof(float) * (size_t)g.B * g.Hkv * g.T * g.d;  // fp32 means + bf16 hi/lo copy
+  return 2 * sizeof(float) * (size_t)g.B * g.Hkv * g.Tp * g.d;  // fp32 means + bf16 hi/lo copy
 }
 
 size_t pisa_workspace_bytes(const pisa_problem* p, int mode) {

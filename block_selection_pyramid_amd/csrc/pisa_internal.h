@@ -16,6 +16,7 @@ constexpr int kMaxCand = 64;  // g*K <= 64 candidates per level (one per lane)
 // Geometry of one problem, passed by value to every kernel.
 struct Geo {
   int32_t B, Hq, Hkv, G, N, d, C, K, g, L, n1, T;
+  int32_t Tp;      // node stride of one (b, h) pyramid in the buffer: T rounded up to even
   int32_t n1p;     // ceil(n1 / 2): level-2 nodes as leaf-block pairs (g = 2), one prefill leaf list each
   int32_t scorer;  // enum pisa_scorer of the routing levels
   float s;        // scale applied to every dot product
@@ -24,7 +25,7 @@ struct Geo {
   int32_t off[kMaxLevels + 2];  // node offset of level l in one (b, h) pyramid
 
   // floats of fp32 means before the routing copy in the pyramid buffer
-  __host__ __device__ int64_t means_floats() const { return (int64_t)B * Hkv * T * d; }
+  __host__ __device__ int64_t means_floats() const { return (int64_t)B * Hkv * Tp * d; }
 };
 
 // Prefill workspace carve-up (byte offsets, 256-aligned).
@@ -106,6 +107,12 @@ inline int dense_bottom(const Geo& g) {
   while (l < g.L && g.n[l - 1] > kDenseMaxChildren) ++l;
   return l;
 }
+// The gather levels in one launch from leaf-block means (G = 4, gather levels l_x .. 2 with
+// l_x = 3 or 2; x2 holds the level-l_x candidates); writes cand and histograms into cnt
+// like the gather walk.
+bool route_sub_supported(const Geo& g, int l_x);
+int launch_route_sub(const Geo& g, int l_x, const void* q, const float* pyr, const int32_t* x2, int32_t* cand,
+                     int32_t* cnt, hipStream_t st);
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
 // histogram of the routed (query group, level-2 node) pairs of the 2K leaf slots per query
 // group into cnt [B*Hkv*n1p] (the counts the gather launch keeps when it runs)

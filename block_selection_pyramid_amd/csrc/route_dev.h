@@ -133,7 +133,7 @@ struct MfmaWalk {
   static constexpr int TB = GPW == 1 ? 2 : 1;  // tiles per batch
 
   template <bool kLds, bool kLo>
-  __device__ __forceinline__ void load_batch(const Geo& geo, const bf16* Rc, const char* Lc, int bq, int l,
+  __device__ __forceinline__ void load_batch(const Geo& geo, const char* Lc, int bq, int l,
                                              int nx, int t0, const int32_t* Xs, int lane,
                                              bf16x8 (&hi)[GPW][TB][KS], bf16x8 (&lo)[GPW][TB][KS]) const {
     const int nchild = geo.n[l - 1];
@@ -164,11 +164,11 @@ struct MfmaWalk {
             if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
           }
         } else {
-          const bf16* rp = Rc + (int64_t)ca[g][tb] * 2 * D + 8 * kg;
+          const bf16* rp = R + rc_node(geo.off[l - 1] + ca[g][tb], D) + 8 * kg;
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
-            hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s);
-            if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 64 * s + 32);
+            hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s);
+            if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
           }
         }
       }
@@ -181,7 +181,6 @@ struct MfmaWalk {
   template <bool kLds, bool kApprox>
   __device__ void score_t(const Geo& geo, int bq, int l, int nx, const int32_t* Xs, uint64_t* keys, float* sc,
                           float* er, int lane) const {
-    const bf16* Rc = R + (int64_t)geo.off[l - 1] * 2 * D;
     const char* Lc = kLds ? lds + (int64_t)(geo.off[l - 1] - stage_base) * kRecLds : nullptr;
     const int nchild = geo.n[l - 1];
     const int cshift = l - 2;
@@ -190,7 +189,7 @@ struct MfmaWalk {
     const int ntiles = (2 * nx + 15) >> 4;
     for (int t0 = 0; t0 < ntiles; t0 += TB) {
       bf16x8 hi[GPW][TB][KS], lo[GPW][TB][KS];
-      load_batch<kLds, !kApprox>(geo, Rc, Lc, bq, l, nx, t0, Xs, lane, hi, lo);
+      load_batch<kLds, !kApprox>(geo, Lc, bq, l, nx, t0, Xs, lane, hi, lo);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int t = t0 + tb;
@@ -276,7 +275,6 @@ struct MfmaWalk {
     // (256K, gather launch: hi-only batches of 2 and exact ones of 1 tile took 3.05 ms, 2/2
     // 3.10, 1/1 3.13, 4/2 (three wavefronts per SIMD) 3.17, 8/2 3.37)
     constexpr int TBM = kApprox ? 2 : 1;
-    const bf16* Rc = R + (int64_t)geo.off[l - 1] * 2 * D;
     const char* Lc = kLds ? lds + (int64_t)(geo.off[l - 1] - stage_base) * kRecLds : nullptr;
     const int nchild = geo.n[l - 1];
     const int cshift = l - 2;
@@ -305,11 +303,11 @@ struct MfmaWalk {
             if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 128 * s2 + 64);
           }
         } else {
-          const bf16* rp = Rc + (int64_t)ca * 2 * D + 8 * kg;
+          const bf16* rp = R + rc_node(geo.off[l - 1] + ca, D) + 8 * kg;
 #pragma unroll
           for (int s2 = 0; s2 < KS; ++s2) {
-            hi[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 64 * s2);
-            if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 64 * s2 + 32);
+            hi[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 128 * s2);
+            if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 128 * s2 + 64);
           }
         }
       }

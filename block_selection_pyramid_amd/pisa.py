@@ -182,15 +182,17 @@ def _stream(stream) -> int:
 
 
 def pyramid_shape(p: Problem):
-    """Shape of the fp32 pyramid buffer: [2, B, Hkv, T, d]; [0] holds the fp32 means, [1]
-    the bf16 hi/lo routing copy (its bytes, see include/pisa.h)."""
+    """Shape of the fp32 pyramid buffer: [2, B, Hkv, Tp, d] with Tp = T rounded up to even
+    (one unused node per (b, h) when T is odd); [0] holds the fp32 means, [1] the bf16 hi/lo
+    routing copy (its bytes, see include/pisa.h)."""
     L, nodes, offs = levels(p)
-    return (2, p.batch, p.n_kv_heads, offs[-1], p.head_dim)
+    return (2, p.batch, p.n_kv_heads, offs[-1] + (offs[-1] & 1), p.head_dim)
 
 
-def pyramid_means(pyramid: torch.Tensor) -> torch.Tensor:
+def pyramid_means(p: Problem, pyramid: torch.Tensor) -> torch.Tensor:
     """The fp32 means [B, Hkv, T, d] inside a pyramid buffer."""
-    return pyramid[0]
+    L, nodes, offs = levels(p)
+    return pyramid[0][:, :, : offs[-1]]
 
 
 def build_pyramid(p: Problem, k: torch.Tensor, pyramid: torch.Tensor | None = None, stream=None) -> torch.Tensor:

@@ -36,13 +36,16 @@
  *   q (prefill)   [B, Hq, N, d]     dtype of the problem (fp32 or bf16)
  *   q (decode)    [B, Hq, d]        the new token's query, at position N-1
  *   k / k_cache   [B, Hkv, N, d]    dtype of the problem
- *   pyramid       pisa_pyramid_bytes() bytes: first the fp32 means [B, Hkv, T, d]
- *                 (T = sum of level sizes, level 1 (leaves) first, see pisa_levels),
- *                 then an equally sized routing copy: each mean times s * log2(e)
- *                 (fp32 product, s as resolved from the problem) split into bf16 hi +
- *                 bf16 lo (hi + lo equals that product to 2^-18 relative), laid out per
- *                 node as d/32 chunks of [hi(32) | lo(32)]; the copy is therefore tied
- *                 to the problem's scale
+ *   pyramid       pisa_pyramid_bytes() bytes: first the fp32 means [B, Hkv, Tp, d]
+ *                 (T = sum of level sizes, level 1 (leaves) first, see pisa_levels;
+ *                 Tp = T rounded up to even, the last node unused when T is odd), then an
+ *                 equally sized routing copy: each mean times s * log2(e) (fp32 product,
+ *                 s as resolved from the problem) split into bf16 hi + bf16 lo (hi + lo
+ *                 equals that product to 2^-18 relative).  In each (b, h) block of the copy
+ *                 nodes n and n ^ 1 share a record of 4d bf16: per 32-dim chunk,
+ *                 [hi(32) of the even node | hi(32) of the odd node | lo(32) even |
+ *                 lo(32) odd], so one 128-byte line holds the same dims of two sibling
+ *                 nodes.  The copy is tied to the problem's scale
  *   out_idx       [B, Hkv, N, K] (prefill) or [B, Hkv, K] (decode), int32: selected leaf
  *                 block ids in ascending order, padded with -1
  *   out_score     same shape, fp32: each selected block's group-summed causal leaf LSE,
@@ -114,7 +117,8 @@ typedef struct {
  * Level table.  level_nodes[l] (l = 0..L) holds n_l with n_0 = N, n_1 = ceil(N/C),
  * n_l = ceil(n_{l-1}/g), L = first level with n_L <= g*K.  level_offset[l] (l = 1..L+1) is
  * the node offset of level l inside one (batch, KV head) pyramid (level_offset[1] = 0,
- * level_offset[L+1] = T).  Both arrays must hold PISA_MAX_LEVELS + 2 entries; either may
+ * level_offset[L+1] = T; the pyramid buffer's node stride per (batch, KV head) is T rounded
+ * up to even).  Both arrays must hold PISA_MAX_LEVELS + 2 entries; either may
  * be NULL.  Returns PISA_OK or PISA_ERR_INVALID_ARG.
  */
 int pisa_levels(const pisa_problem* p, int32_t* n_levels, int64_t* level_nodes, int64_t* level_offset);
@@ -132,8 +136,8 @@ int pisa_pyramid_layout(const pisa_problem* p, int32_t* n_levels, int32_t* nodes
 /* PISA_OK if the kernels support this problem in this mode, else the error code. */
 int pisa_supported(const pisa_problem* p, int mode);
 
-/* Bytes of the pyramid buffer (fp32 means + routing copy, 2 * 4*B*Hkv*T*d); 0 for an
- * invalid problem. */
+/* Bytes of the pyramid buffer (fp32 means + routing copy, 2 * 4*B*Hkv*Tp*d with Tp = T
+ * rounded up to even); 0 for an invalid problem. */
 size_t pisa_pyramid_bytes(const pisa_problem* p);
 
 /* Bytes of device workspace a call in `mode` needs (may be 0); 0 for an invalid problem. */

@@ -88,8 +88,20 @@ def verify(op, q, k, opyr, rows, idx, sc, decode=False, what=""):
                     % (what, len(bad), len(rows), rows[r], oracle.CHECK_STATUS[st[r]], gi[r], gs[r], oi[0], os_[0]))
 
 
+def decode_rcopy(pyr, d):
+    """Routing copy of a pyramid buffer [2, B, Hkv, Tp, d] (fp32 view) as bf16 bits
+    [B, Hkv, Tp, 2, d] (hi, lo per node).  Layout: nodes n and n ^ 1 of one (b, h) share a
+    record; per 32-dim chunk, [hi even | hi odd | lo even | lo odd], 32 bf16 each."""
+    B, H, Tp = pyr.shape[1:4]
+    r = np.ascontiguousarray(pyr[1]).view(np.uint16).reshape(B, H, Tp // 2, d // 32, 2, 2, 32)
+    return r.transpose(0, 1, 2, 5, 4, 3, 6).reshape(B, H, Tp, 2, d)
+
+
 def check_pyramid(op, k, pyr, what):
     opyr = oracle.build_pyramid(op, k)
+    # the buffer's node stride per (b, h) is the node count rounded up to even
+    assert pyr.shape[2] in (opyr.shape[2], opyr.shape[2] + 1) and pyr.shape[2] % 2 == 0
+    pyr = pyr[:, :, :opyr.shape[2]]
     assert pyr.shape == opyr.shape
     err = np.abs(pyr.astype(np.float64) - opyr)
     tol = 4e-6 + 1e-6 * np.abs(opyr)
@@ -110,9 +122,9 @@ def test_routing_copy_is_hi_lo_of_means(env, d):
     torch.cuda.synchronize()
     a = pyr.cpu().numpy()
     means = a[0]
-    bits = a[1].view(np.uint16).reshape(means.shape[:-1] + (d // 32, 2, 32))
-    hi = synth.bf16_bits_to_f32(bits[..., 0, :]).reshape(means.shape)
-    lo = synth.bf16_bits_to_f32(bits[..., 1, :]).reshape(means.shape)
+    bits = decode_rcopy(a, d)
+    hi = synth.bf16_bits_to_f32(bits[..., 0, :])
+    lo = synth.bf16_bits_to_f32(bits[..., 1, :])
     # the copy holds fp32(s * log2(e)) * mean, s = 1/sqrt(d) in fp32 (the default scale)
     s = np.float32(1.0) / np.sqrt(np.float32(d))
     c = np.float32(s * np.float32(1.4426950408889634))
@@ -248,6 +260,52 @@ def test_prefill_gather_below_dense_levels(env):
     verify(op, q, k, opyr, sample_rows(w, needles, 2000, 17), idx, sc, what="300k-G4")
 
 
+# The gather levels below the dense launch run from the leaf-block means under each kept
+# node (G = 4): levels 3 and 2 when the dense launch stops at level 4 (2048 < n_1 <= 4096
+# leaf blocks), level 2 alone when it stops at level 3 (1024 < n_1 <= 2048).  Cases: both
+# depths, the three scorers, K not a multiple of four (partly empty tile batches), K = 16
+# with d = 64, and leaf counts that leave the last level-3 node with one, two or three
+# leaf blocks; every row of the last 80 leaf blocks is checked besides the sample.
+GATHER_CASES = [
+    # name, N, Hq, Hkv, d, K, scorer, gather levels
+    ("128k-K5-pisa1", 131072, 4, 1, 128, 5, oracle.PISA1, 1),
+    ("128k-ragged-lse", 64 * 2046 + 5, 8, 2, 128, 8, oracle.LSE, 1),
+    ("256k-ragged1-pisa2", 64 * 4092 + 7, 4, 1, 128, 8, oracle.PISA2, 2),
+    ("256k-ragged2-K16-d64", 64 * 4094, 8, 2, 64, 16, oracle.LSE, 2),
+    ("256k-ragged3-K5", 64 * 4094 + 9, 4, 1, 128, 5, oracle.LSE, 2),
+    ("256k-pisa1-K6", 262144, 4, 1, 128, 6, oracle.PISA1, 2),
+]
+
+
+@pytest.mark.parametrize("case", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_gather_levels_from_leaf_means(env, case):
+    torch, pisa = env
+    name, N, Hq, Hkv, d, K, scorer, nlev = case
+    w = synth.custom(name=name, batch=1, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     seed=1300 + N % 997, needles=N // 256)
+    p, op = problems(pisa, w, scorer=scorer)
+    top, bot = pisa.dense_levels(p)
+    assert bot - 2 == nlev, (top, bot)
+    q, k, needles = synth.make_inputs(w)
+    if scorer != oracle.LSE:
+        k = synth.add_block_offsets(w, k, 2.0)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log(name, "gather levels %d, scorer %d: launching" % (nlev, scorer))
+    pyr = pisa.build_pyramid(p, kd)
+    idx, sc = pisa.select_prefill(p, qd, kd, pyr, pisa.workspace(p))
+    torch.cuda.synchronize()
+    idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+    nsel = (idx.reshape(-1, K) >= 0).sum(1)
+    bq = np.tile(np.arange(N) // 64, Hkv)
+    assert np.array_equal(nsel, np.minimum(K, bq + 1))
+    opyr = oracle.build_pyramid(op, k)
+    tail = np.concatenate([hk * N + np.arange(max(0, N - 80 * 64), N) for hk in range(Hkv)])
+    rows = np.unique(np.concatenate([sample_rows(w, needles, 1500, 29), tail]))
+    verify(op, q, k, opyr, rows, idx, sc, what=name)
+    if scorer != oracle.LSE:
+        assert scorer_sensitive(op, q, k, opyr, rows[:2000], False) > 0
+
+
 def test_prefill_beyond_histogram_bins(env):
     # more than 8192 level-2 nodes per (b, h) (N > 1M tokens at C = 64): the routing launch
     # counts leaf pairs with global atomics instead of an LDS histogram, and the leaf-pair
@@ -307,7 +365,7 @@ def test_decode_workload_full_size(env):
     w = synth.WORKLOADS["decode"]
     p, op, q, k, qd, kd, pyr, idx, sc = gpu_decode(env, w)
     opyr = oracle.build_pyramid(op, k)
-    gp = pyr.cpu().numpy()[0]
+    gp = pyr.cpu().numpy()[0][:, :, :opyr.shape[2]]
     assert np.max(np.abs(gp - opyr)) <= 1e-5
     verify(op, q, k, opyr, np.arange(w.batch * w.n_kv_heads), idx, sc, decode=True, what="decode-full")
 
@@ -475,6 +533,18 @@ def _levels_offsets(pisa, N, B, Hq, Hkv, d, K, dtype):
     return L, nodes, offs
 
 
+def assert_same_levels(app, b, coff, fr, foff, nodes, L, d, what):
+    """Every node of levels 1..L of sequence b in the appended capacity pyramid `app` (level
+    offsets coff) holds the same bits as in the fresh build `fr` (offsets foff): fp32 means
+    and routing-copy hi/lo."""
+    am, fm = app[0].view(np.uint32), fr[0].view(np.uint32)
+    ar, frc = decode_rcopy(app, d), decode_rcopy(fr, d)
+    for l in range(1, L + 1):
+        sa, sf = slice(coff[l - 1], coff[l - 1] + nodes[l]), slice(foff[l - 1], foff[l - 1] + nodes[l])
+        assert np.array_equal(am[b, :, sa], fm[0, :, sf]), "%s level %d means differ" % (what, l)
+        assert np.array_equal(ar[b, :, sa], frc[0, :, sf]), "%s level %d routing copy differs" % (what, l)
+
+
 @pytest.mark.parametrize("dt,d", [(synth.BF16, 128), (synth.F32, 64)])
 def test_append_keys_matches_fresh_build(env, dt, d):
     # appends of assorted sizes (single keys, block boundaries, long runs, none) leave every
@@ -496,18 +566,15 @@ def test_append_keys_matches_fresh_build(env, dt, d):
         nt = torch.tensor(new, dtype=torch.int32, device="cuda")
         pisa.append_keys(p, kd, ot, nt, max(n - o for n, o in zip(new, old)), pyr)
         torch.cuda.synchronize()
-        app = pyr.cpu().numpy().view(np.uint32)
+        app = pyr.cpu().numpy()
         for b in range(B):
             n = new[b]
             pb = pisa.Problem(1, n, Hq, Hkv, d, 64, K, 2, dtype=dt)
             fresh = pisa.build_pyramid(pb, kd[b:b + 1, :, :n].contiguous())
             torch.cuda.synchronize()
-            fr = fresh.cpu().numpy().view(np.uint32)
             L, nodes, foff = _levels_offsets(pisa, n, 1, Hq, Hkv, d, K, dt)
-            for l in range(1, L + 1):
-                a = app[:, b, :, coff[l - 1]:coff[l - 1] + nodes[l]]
-                f = fr[:, 0, :, foff[l - 1]:foff[l - 1] + nodes[l]]
-                assert np.array_equal(a, f), "sequence %d length %d level %d differs" % (b, n, l)
+            assert_same_levels(app, b, coff, fresh.cpu().numpy(), foff, nodes, L, d,
+                               "sequence %d length %d" % (b, n))
         old = new
 
 
@@ -536,18 +603,15 @@ def test_append_single_keys_match_fresh_build(env):
         nt = torch.tensor(new, dtype=torch.int32, device="cuda")
         pisa.append_keys(p, kd, ot, nt, 1, pyr)
         torch.cuda.synchronize()
-        app = pyr.cpu().numpy().view(np.uint32)
+        app = pyr.cpu().numpy()
         for b in range(B):
             n = new[b]
             pb = pisa.Problem(1, n, Hq, Hkv, d, 64, K, 2, dtype=dt)
             fresh = pisa.build_pyramid(pb, kd[b:b + 1, :, :n].contiguous())
             torch.cuda.synchronize()
-            fr = fresh.cpu().numpy().view(np.uint32)
             L, nodes, foff = _levels_offsets(pisa, n, 1, Hq, Hkv, d, K, dt)
-            for l in range(1, L + 1):
-                a = app[:, b, :, coff[l - 1]:coff[l - 1] + nodes[l]]
-                f = fr[:, 0, :, foff[l - 1]:foff[l - 1] + nodes[l]]
-                assert np.array_equal(a, f), "step %d sequence %d length %d level %d differs" % (step, b, n, l)
+            assert_same_levels(app, b, coff, fresh.cpu().numpy(), foff, nodes, L, d,
+                               "step %d sequence %d length %d" % (step, b, n))
         lengths = new
 
 
