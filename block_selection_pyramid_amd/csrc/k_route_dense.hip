@@ -44,15 +44,6 @@ constexpr size_t dense_lds_bytes() {
 // Forced key tile f (64 raw keys) into fragment-major LDS: fragment fi = rb KS + ks holds
 // keys 64 f + 32 rb + (lane & 31), dims 16 ks + 8 (lane >> 5) .. +8; keys past N read
 // zeros (the row index is clamped and the value replaced, so no load sits behind a branch).
-// Fragments fi = wave + 4 u of dense_load_keys into LDS slot lane of fragment fi.
-template <int D, int NU>
-__device__ __forceinline__ void dense_store_keys(char* lds, int buf, int wave, int lane, const u32x4 (&stg)[NU]) {
-  constexpr int TILE = 2 * (D / 16) * 1024;
-#pragma unroll
-  for (int u = 0; u < NU; ++u)
-    *reinterpret_cast<u32x4*>(lds + buf * TILE + ((wave + kDenseWaves * u) * 64 + lane) * 16) = stg[u];
-}
-
 template <int D, int NU>
 __device__ __forceinline__ void dense_load_keys(const bf16* kb, int N, int f, int wave, int lane, u32x4 (&stg)[NU]) {
   constexpr int KS = D / 16;
@@ -81,6 +72,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   constexpr int M = (ITEMS + 63) / 64;
   constexpr int SLOTS = 2 * KC;
   static_assert(F % kDenseWaves == 0, "fragments split evenly over the wavefronts");
+  static_assert((KC & (KC - 1)) == 0, "items index queries by it / KC");
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -89,7 +81,8 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   uint64_t* key = reinterpret_cast<uint64_t*>(wl + QPW * 64);           // [QPW][SLOTS]
   int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (64 + 16 * KC));  // [QPW][KC]
 
-  const int N = geo.N, C = geo.C, K = geo.K, L = geo.L;
+  const int N = geo.N, K = geo.K, L = geo.L;
+  constexpr int C = kLeaf;  // leaf block size (the only one the kernels support)
   constexpr bool trunc = TRUNC;
   const float c2 = trunc_c2(geo.scorer, true);
   const int BH = geo.B * geo.Hkv;
@@ -262,13 +255,13 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
       for (int m = 0; m < M; ++m) {
         const int it = lane + 64 * m;
         if (it < ITEMS) {
-          const int iq = it / KC, ir = it % KC;
+          // item it = (query it / KC, rank it % KC): key slots 2 it, 2 it + 1 (SLOTS = 2 KC)
           const int n0 = 2 * ip[m], n1 = n0 + 1;
           const bool v0 = ip[m] >= 0;
           const bool v1 = v0 && n1 < nl && ((int64_t)n1 << (l - 1)) <= ibq[m];
-          key[iq * SLOTS + 2 * ir] = v0 ? cand_key(sc[m][0], n0) : 0ull;
-          key[iq * SLOTS + 2 * ir + 1] = v1 ? cand_key(sc[m][1], n1) : 0ull;
-          np[iq * KC + ir] = -1;
+          key[2 * it] = v0 ? cand_key(sc[m][0], n0) : 0ull;
+          key[2 * it + 1] = v1 ? cand_key(sc[m][1], n1) : 0ull;
+          np[it] = -1;
         }
       }
       wave_sync();
@@ -276,9 +269,8 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
       for (int m = 0; m < M; ++m) {
         const int it = lane + 64 * m;
         if (it < ITEMS) {
-          const int iq = it / KC, ir = it % KC;
-          const uint64_t* kq = key + iq * SLOTS;
-          const uint64_t k0 = kq[2 * ir], k1 = kq[2 * ir + 1];
+          const uint64_t* kq = key + (it & ~(KC - 1)) * 2;  // the query's SLOTS keys
+          const uint64_t k0 = key[2 * it], k1 = key[2 * it + 1];
           int r0 = 0, r1 = 0;
 #pragma unroll 4
           for (int s = 0; s < SLOTS; s += 2) {
@@ -286,15 +278,15 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
             r0 += (kk.x > k0) + (kk.y > k0);
             r1 += (kk.x > k1) + (kk.y > k1);
           }
-          if (k0 != 0ull && r0 < K) np[iq * KC + r0] = 2 * ip[m];
-          if (k1 != 0ull && r1 < K) np[iq * KC + r1] = 2 * ip[m] + 1;
+          if (k0 != 0ull && r0 < K) np[(it & ~(KC - 1)) + r0] = 2 * ip[m];
+          if (k1 != 0ull && r1 < K) np[(it & ~(KC - 1)) + r1] = 2 * ip[m] + 1;
         }
       }
       wave_sync();
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int it = lane + 64 * m;
-        if (it < ITEMS) ip[m] = np[(it / KC) * KC + it % KC];
+        if (it < ITEMS) ip[m] = np[it];
       }
       wave_sync();
     }
@@ -339,7 +331,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   const bf16* kb = k + (int64_t)bh * N * D;
   __syncthreads();  // the staging buffers are free again
   dense_load_keys<D>(kb, N, ft[0], wave, lane, stg);
-  dense_store_keys<D>(lds, 0, wave, lane, stg);
+  dense_store_tile<D>(lds, 0, wave, lane, stg);
   __syncthreads();
   int nfw = 0;  // |F| of this wavefront's leaf block
   {
@@ -386,7 +378,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (x + 1 < nft) dense_store_keys<D>(lds, (x + 1) & 1, wave, lane, stg);
+    if (x + 1 < nft) dense_store_tile<D>(lds, (x + 1) & 1, wave, lane, stg);
     __syncthreads();
   }
 }

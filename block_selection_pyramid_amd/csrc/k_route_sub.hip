@@ -34,6 +34,9 @@ namespace pisa {
 namespace {
 
 constexpr int kSubQueries = 512;  // queries per workgroup
+// Tiles per batch of gathers (256K, levels 3-2: 1, 2 and 4 tiles took 1.49, 1.51 and
+// 1.51 ms at 4, 3 and 2 wavefronts per SIMD).
+constexpr int kSubTB = 1;
 
 template <int KC, int NLEV>
 struct SubLds {
@@ -127,21 +130,41 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
       yf[u] = y;
     }
   };
-  bf16x8 qn[KS];
+  // Gathers of tiles t0 .. t0+TB-1 (a batch: 2 TB KS loads per lane, all issued before the
+  // first MFMA that needs them: left to itself the compiler keeps two in flight and waits
+  // on each, a dependent chain of L2 round trips).
+  auto load_batch = [&](int t0, bf16x8 (&hi)[kSubTB][KS], bf16x8 (&lo)[kSubTB][KS]) {
+#pragma unroll
+    for (int u = 0; u < kSubTB; ++u) {
+      const int j = t0 + u;
+      const int y = j < ntile ? w->Y[(rb + j) & 3][j] : -1;
+      const int leaf = 4 * y + v;
+      // a missing leaf (or an empty tile) reads leaf 0 instead; its rows are never used
+      // k-step s, lane group kg <-> 8-dim piece 4 s + kg (hi, then lo 32 bf16 later)
+      const bf16* rp = R1 + rc_node((y >= 0 && leaf < n1) ? leaf : 0, D) + 64 * kg;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
+        lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 32);
+      }
+    }
+  };
+
+  bf16x8 qb[KS], qn[KS];
   int yn[YPL];
   fetch(wave, qn, yn);
 
+#pragma unroll 1
   for (int quad = wave; quad < kSubQueries / 4; quad += 4) {
     const int i0 = qr0 + quad * 4;
     if (i0 >= N) break;          // uniform across the wavefront
-    const int bq = i0 / geo.C;   // four consecutive queries share one leaf block (4 | C)
-    bf16x8 qb[KS];
+    const int bq = i0 / kLeaf;   // four consecutive queries share one leaf block (C = kLeaf)
 #pragma unroll
     for (int s = 0; s < KS; ++s) qb[s] = qn[s];
 #pragma unroll
     for (int u = 0; u < YPL; ++u)
       if (xl + 16 * u < S::NT) w->Y[gl][xl + 16 * u] = yn[u];
-    fetch(quad + 4, qn, yn);
+    fetch(quad + 4, qn, yn);  // the next quad's query fragments and tile nodes
     const int i = i0 + gl;  // the query of this lane's ranking group
     const int64_t row = (int64_t)bh * N + i;
     for (int x = xl; x < 2 * KC; x += 16) {
@@ -152,32 +175,22 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
     wave_sync();
 
     for (int t0 = 0; t0 < ntile; t0 += 4) {
-      // the batch's 8 KS gathers all go out before its first MFMA (left to itself the
-      // compiler keeps two in flight and waits on each: a dependent chain of L2 round trips)
-      bf16x8 hi[4][KS], lo[4][KS];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int j = t0 + u;
-        const int y = j < ntile ? w->Y[(rb + j) & 3][j] : -1;
-        const int leaf = 4 * y + v;
-        // a missing leaf (or an empty tile) reads leaf 0 instead; its rows are never used
-        const bf16* rp = R1 + rc_node((y >= 0 && leaf < n1) ? leaf : 0, D) + 8 * kg;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s);
-          lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
       f32x4 acc[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t1 = 0; t1 < 4; t1 += kSubTB) {
+        bf16x8 hi[kSubTB][KS], lo[kSubTB][KS];
+        load_batch(t0 + t1, hi, lo);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[u][s], qb[s], acc[u], 0, 0, 0);
-          acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[u][s], qb[s], acc[u], 0, 0, 0);
+        for (int u = 0; u < kSubTB; ++u) {
+          acc[t1 + u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[u][s], qb[s], acc[t1 + u], 0, 0, 0);
+            acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[u][s], qb[s], acc[t1 + u], 0, 0, 0);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       // this lane's tile of the four: leaf dots a[0..3] of leaves 4y .. 4y+3, head r
       f32x4 a = acc[0];

@@ -51,7 +51,7 @@ int make_geo(const pisa_problem* p, Geo* g) {
   }
   g->off[L + 1] = (int32_t)off;
   g->T = (int32_t)off;
-  g->Tp = (int32_t)((off + 1) & ~(int64_t)1);  // sibling pairs of the routing copy stay within one (b, h)
+  g->Tp = (int32_t)((off + 3) & ~(int64_t)3);  // node quads of the routing copy stay within one (b, h)
   return PISA_OK;
 }
 

@@ -16,7 +16,7 @@ constexpr int kMaxCand = 64;  // g*K <= 64 candidates per level (one per lane)
 // Geometry of one problem, passed by value to every kernel.
 struct Geo {
   int32_t B, Hq, Hkv, G, N, d, C, K, g, L, n1, T;
-  int32_t Tp;      // node stride of one (b, h) pyramid in the buffer: T rounded up to even
+  int32_t Tp;      // node stride of one (b, h) pyramid in the buffer: T rounded up to a multiple of 4
   int32_t n1p;     // ceil(n1 / 2): level-2 nodes as leaf-block pairs (g = 2), one prefill leaf list each
   int32_t scorer;  // enum pisa_scorer of the routing levels
   float s;        // scale applied to every dot product

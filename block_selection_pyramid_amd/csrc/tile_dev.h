@@ -19,31 +19,28 @@ struct DenseShape {
 };
 
 // Staging of child tile t of level l - 1 (children 32t .. 32t+31) into fragment-major LDS:
-// fragment f = 2 ks + hi/lo, lane slot = child + 32 h for dims 16 ks + 8 h .. +8, so every
-// MFMA A-operand read is one conflict-free 16-byte row per lane.  Wavefront w loads the hi
-// (w < 2) or lo half of every 32-dim chunk u of the children 16 (w & 1) .. +15: lane
-// 16 kg + r takes child 16 (w & 1) + r, bytes 16 kg .. of the half-chunk, so one load covers
-// whole lines of sibling pairs in the routing copy.  Piece kg of chunk u holds dims
-// 32 u + 8 kg .., i.e. k-step 2 u + (kg >> 1), half kg & 1: fragment 4 u + 2 (kg >> 1) + hl.
-static_assert(kDenseWaves == 4, "hi / lo x two halves of the tile's children");
+// fragment f = 2 ks + hi/lo, lane slot = child (lane & 31) and dims 8 (lane >> 5) .. of
+// k-step ks, so every MFMA A-operand read is one conflict-free 16-byte row per lane.  The
+// wavefronts of the workgroup take fragments wave, wave + 4, ...  A fragment's lane reads
+// 8-dim piece 2 ks + (lane >> 5) of its child, so each four consecutive lanes read one node
+// quad's 64 contiguous bytes of the routing copy.
 template <int D, int NU>
 __device__ __forceinline__ void dense_load_tile(const char* Rb, const Geo& geo, int l, int t, int wave, int lane,
                                                 u32x4 (&stg)[NU]) {
-  static_assert(NU == D / 32, "one load per 32-dim chunk");
-  const int child = 16 * (wave & 1) + (lane & 15);
-  const int node = geo.off[l - 1] + min(32 * t + child, geo.n[l - 1] - 1);  // a missing child reads a real node
-  const char* p = Rb + 2 * rc_node(node, D) + 128 * (wave >> 1) + 16 * (lane >> 4);
+  const int node = geo.off[l - 1] + min(32 * t + (lane & 31), geo.n[l - 1] - 1);  // a missing child reads a real node
+  // fragment wave + 4 u: k-step 2 u + (wave >> 1), hi / lo = wave & 1
+  const char* base = Rb + 2 * rc_node(node, D) + 128 * (lane >> 5) + 256 * (wave >> 1) + 64 * (wave & 1);
 #pragma unroll
-  for (int u = 0; u < NU; ++u) stg[u] = *reinterpret_cast<const u32x4*>(p + 256 * u);
+  for (int u = 0; u < NU; ++u) stg[u] = *reinterpret_cast<const u32x4*>(base + 512 * u);
 }
 template <int D, int NU>
 __device__ __forceinline__ void dense_store_tile(char* lds, int buf, int wave, int lane, const u32x4 (&stg)[NU]) {
   constexpr int TILE = 2 * (D / 16) * 1024;
-  const int kg = lane >> 4;
-  const int slot = 16 * (wave & 1) + (lane & 15) + 32 * (kg & 1);
-  char* p = lds + buf * TILE + ((2 * (kg >> 1) + (wave >> 1)) * 64 + slot) * 16;
 #pragma unroll
-  for (int u = 0; u < NU; ++u) *reinterpret_cast<u32x4*>(p + u * 4 * 64 * 16) = stg[u];
+  for (int u = 0; u < NU; ++u) {
+    const int f = wave + kDenseWaves * u;
+    *reinterpret_cast<u32x4*>(lds + buf * TILE + (f * 64 + lane) * 16) = stg[u];
+  }
 }
 
 // B operand of the queries iw .. iw + QPW - 1 of (b, h): lane column j = lane & 31 of
@@ -58,7 +55,7 @@ __device__ __forceinline__ void load_query_cols(const bf16* q, const Geo& geo, i
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     const int i = iw + cg * (32 / G) + j / G;
-    bqc[cg] = min(i, N - 1) / geo.C;
+    bqc[cg] = min(i, N - 1) / kLeaf;  // C = kLeaf
     if (i < N) {
       const bf16* p = q + (((int64_t)b * geo.Hq + h * G + j % G) * N + i) * D + 8 * hh;
 #pragma unroll

@@ -182,11 +182,11 @@ def _stream(stream) -> int:
 
 
 def pyramid_shape(p: Problem):
-    """Shape of the fp32 pyramid buffer: [2, B, Hkv, Tp, d] with Tp = T rounded up to even
-    (one unused node per (b, h) when T is odd); [0] holds the fp32 means, [1] the bf16 hi/lo
-    routing copy (its bytes, see include/pisa.h)."""
+    """Shape of the fp32 pyramid buffer: [2, B, Hkv, Tp, d] with Tp = T rounded up to a
+    multiple of 4 (up to three unused nodes per (b, h)); [0] holds the fp32 means, [1] the
+    bf16 hi/lo routing copy (its bytes, see include/pisa.h)."""
     L, nodes, offs = levels(p)
-    return (2, p.batch, p.n_kv_heads, offs[-1] + (offs[-1] & 1), p.head_dim)
+    return (2, p.batch, p.n_kv_heads, (offs[-1] + 3) // 4 * 4, p.head_dim)
 
 
 def pyramid_means(p: Problem, pyramid: torch.Tensor) -> torch.Tensor:

@@ -38,14 +38,13 @@
  *   k / k_cache   [B, Hkv, N, d]    dtype of the problem
  *   pyramid       pisa_pyramid_bytes() bytes: first the fp32 means [B, Hkv, Tp, d]
  *                 (T = sum of level sizes, level 1 (leaves) first, see pisa_levels;
- *                 Tp = T rounded up to even, the last node unused when T is odd), then an
+ *                 Tp = T rounded up to a multiple of 4, the nodes past T unused), then an
  *                 equally sized routing copy: each mean times s * log2(e) (fp32 product,
  *                 s as resolved from the problem) split into bf16 hi + bf16 lo (hi + lo
  *                 equals that product to 2^-18 relative).  In each (b, h) block of the copy
- *                 nodes n and n ^ 1 share a record of 4d bf16: per 32-dim chunk,
- *                 [hi(32) of the even node | hi(32) of the odd node | lo(32) even |
- *                 lo(32) odd], so one 128-byte line holds the same dims of two sibling
- *                 nodes.  The copy is tied to the problem's scale
+ *                 nodes 4Q .. 4Q+3 share a record of 8d bf16: per 8-dim piece, one
+ *                 128-byte line [hi(8) of the four nodes | lo(8) of the four nodes].  The
+ *                 copy is tied to the problem's scale
  *   out_idx       [B, Hkv, N, K] (prefill) or [B, Hkv, K] (decode), int32: selected leaf
  *                 block ids in ascending order, padded with -1
  *   out_score     same shape, fp32: each selected block's group-summed causal leaf LSE,
@@ -118,7 +117,7 @@ typedef struct {
  * n_l = ceil(n_{l-1}/g), L = first level with n_L <= g*K.  level_offset[l] (l = 1..L+1) is
  * the node offset of level l inside one (batch, KV head) pyramid (level_offset[1] = 0,
  * level_offset[L+1] = T; the pyramid buffer's node stride per (batch, KV head) is T rounded
- * up to even).  Both arrays must hold PISA_MAX_LEVELS + 2 entries; either may
+ * up to a multiple of 4).  Both arrays must hold PISA_MAX_LEVELS + 2 entries; either may
  * be NULL.  Returns PISA_OK or PISA_ERR_INVALID_ARG.
  */
 int pisa_levels(const pisa_problem* p, int32_t* n_levels, int64_t* level_nodes, int64_t* level_offset);
@@ -137,7 +136,7 @@ int pisa_pyramid_layout(const pisa_problem* p, int32_t* n_levels, int32_t* nodes
 int pisa_supported(const pisa_problem* p, int mode);
 
 /* Bytes of the pyramid buffer (fp32 means + routing copy, 2 * 4*B*Hkv*Tp*d with Tp = T
- * rounded up to even); 0 for an invalid problem. */
+ * rounded up to a multiple of 4); 0 for an invalid problem. */
 size_t pisa_pyramid_bytes(const pisa_problem* p);
 
 /* Bytes of device workspace a call in `mode` needs (may be 0); 0 for an invalid problem. */

@@ -58,7 +58,7 @@ def test_level_table_matches_oracle(pisa, N, K):
     L, nodes, offs = pisa.levels(p)
     assert nodes == oracle.levels(N, 64, K, 2)
     assert offs[0] == 0 and offs[-1] == sum(nodes[1:])
-    assert pisa.pyramid_bytes(p) == 2 * 4 * (offs[-1] + (offs[-1] & 1)) * 128
+    assert pisa.pyramid_bytes(p) == 2 * 4 * ((offs[-1] + 3) // 4 * 4) * 128
     L2, nodes2, offs2 = pisa.pyramid_layout(p)
     assert L2 == L and nodes2 == nodes[1:] and offs2 == offs
 
