@@ -36,6 +36,8 @@ import numpy as np
 METRIC = "pyramid selection latency ms @64K/256K prefill (C=64,K=8); decode µs/step"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# exp2 / log2 issue at a quarter of the fp32 lane rate: 256 CUs x 4 SIMDs x 16 lanes / 4 x 2.4 GHz
+TRANS_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9
 
 
 def log(*a):
@@ -55,7 +57,10 @@ def parse():
     ap.add_argument("--no-attention", action="store_true", help="skip the block-sparse attention timing")
     ap.add_argument("--no-scorers", action="store_true",
                     help="skip the PISA-1 / PISA-2 ablation timings at 256K")
-    ap.add_argument("--cpu-sample-rows", type=int, default=393216)
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="query groups the oracle selects for the CPU baseline (0: all 1048576)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the tiny, 4K, 16K (K = 32) and 128K prefill timings")
     ap.add_argument("--only", choices=["256k", "64k", "decode", "bsa"], default=None,
                     help="time one workload only (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -103,7 +108,7 @@ TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profile
 TRAFFIC_SOURCES = {
     "route_upper": ["k_route_dense.hip", "final_dev.h", "route_dev.h", "tile_dev.h", "dev_common.h",
                     "pisa_internal.h"],
-    "route_l2": ["k_route.hip", "route_dev.h", "dev_common.h", "pisa_internal.h"],
+    "route_l2": ["k_route_sub.hip", "route_dev.h", "dev_common.h", "pisa_internal.h"],
     "leaf": ["k_leaf.hip", "final_dev.h", "dev_common.h", "pisa_internal.h"],
 }
 
@@ -243,7 +248,11 @@ class Prefill:
         q_b, k_b = BH * G * N * d * esz, BH * N * d * esz
         slots = BH * N * 2 * K * 4  # one int32 / fp32 per candidate slot
         forced_in_route = bool(bot)
+        step_bytes = q_b + 2 * k_b + 2 * BH * T * d * 4 + BH * N * K * 8
+        step_flops = (dots(by_level) * BH * G * 2 * d + pairs * G * C * 2 * d + fflops)
         return {
+            "_step": (step_bytes, step_flops),
+            "_d": d,
             "build": (BH * N * d * esz + BH * T * d * 8, 0),
             "route_upper": ((q_b + k_b + copy(dense_l) + slots + BH * N * 3 * 4, dots(dense_l) * BH * G * 2 * d
                              + fflops) if forced_in_route else (0, 0)),
@@ -258,11 +267,30 @@ class Prefill:
         }
 
 
+def step_roofline(work, ms_per_step):
+    """Roofline of the whole step: T_roof = max(unique HBM bytes / HBM peak, the walk's dot
+    flops / bf16 MFMA peak, its exponentials / transcendental rate), each kind of work
+    charged to the unit that does it fastest; frac = T_roof / measured step time.  Bytes:
+    q and k read once, the pyramid written and read once, the outputs written once (k is
+    read by the build and again by the leaf and forced stages: 2 k).  Flops: every routing
+    child dot, routed leaf key and forced key (2 d per key and head).  Exponentials: one per
+    such dot."""
+    nbytes, flops = work["_step"]
+    exps = flops / (2 * work["_d"])
+    t = {"hbm": nbytes / (HBM_PEAK_GBS * 1e9), "mfma": flops / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+         "exp": exps / TRANS_PEAK_PER_S}
+    bound = max(t, key=t.get)
+    return {"bound": bound, "t_roof_ms": round(t[bound] * 1e3, 4), "ms_per_step": round(ms_per_step, 4),
+            "frac": round(t[bound] * 1e3 / ms_per_step, 4), "bytes": int(nbytes), "flops": int(flops),
+            "exps": int(exps), "t_hbm_ms": round(t["hbm"] * 1e3, 4), "t_mfma_ms": round(t["mfma"] * 1e3, 4),
+            "t_exp_ms": round(t["exp"] * 1e3, 4)}
+
+
 def roofline(stage_ms, work):
     """Roofline of the stage with the largest time: its binding roof is the larger of its
     algorithmic bytes at the HBM peak and its algorithmic flops at the bf16 MFMA peak (each
     kind of work charged to the unit that does it fastest); frac = that time / measured."""
-    dom = max((n for n in stage_ms if n in work and not n.startswith("_")), key=lambda n: stage_ms[n])
+    dom = max((n for n in stage_ms if n in work), key=lambda n: stage_ms[n])
     nbytes, flops = work[dom]
     t = stage_ms[dom] * 1e-3
     if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12):
@@ -426,24 +454,53 @@ def extra_rooflines(extra):
     return out
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth, sample_rows):
+    """The fp64 C oracle (OpenMP over query groups) on the 256K prefill workload: pyramid
+    build plus the selection of every query group (or of a random sample, scaled up)."""
     import oracle
     w = synth.WORKLOADS["256k"]
     q, k, _ = synth.make_inputs(w)
     op = oracle.Problem(**w.shape())
     cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count() or 1)
+    total_rows = w.batch * w.n_kv_heads * w.seq_len
+    full = sample_rows <= 0 or sample_rows >= total_rows
     t0 = time.perf_counter()
     pyr = oracle.build_pyramid(op, k)
     t1 = time.perf_counter()
-    total_rows = w.batch * w.n_kv_heads * w.seq_len
-    rows = np.sort(np.random.default_rng(0).choice(total_rows, sample_rows, replace=False))
-    oracle.select(op, q, k, pyr, rows=rows)
+    if full:
+        oracle.select(op, q, k, pyr)
+        n_rows = total_rows
+    else:
+        rows = np.sort(np.random.default_rng(0).choice(total_rows, sample_rows, replace=False))
+        oracle.select(op, q, k, pyr, rows=rows)
+        n_rows = sample_rows
     t2 = time.perf_counter()
-    est_ms = ((t1 - t0) + (t2 - t1) * total_rows / sample_rows) * 1e3
-    return {"value": round(est_ms, 1), "unit": "ms", "cores": cores, "kind": "oracle",
-            "sample": "fp64 C oracle: full pyramid build + selection of %d random query groups of %d "
-                      "(256K prefill, 16/4 heads), select time scaled by %d/%d; measured %.1fs" % (
-                          sample_rows, total_rows, total_rows, sample_rows, t2 - t0)}
+    ms = ((t1 - t0) + (t2 - t1) * total_rows / n_rows) * 1e3
+    what = ("every one of the %d query groups" % total_rows if full else
+            "%d random query groups of %d, select time scaled by %d/%d" % (n_rows, total_rows, total_rows, n_rows))
+    return {"value": round(ms, 1), "unit": "ms", "cores": cores, "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": "fp64 C oracle, 256K prefill (16/4 heads, d = 128, K = 8): full pyramid build + "
+                      "selection of %s; measured %.1fs" % (what, t2 - t0)}
+
+
+def time_config(torch, pisa, synth, name, steps, warmup):
+    """Prefill (pyramid build + selection) of one more workload, wall ms per step."""
+    b = Prefill(torch, pisa, synth, name)
+    wall, stages, _ = b.run(steps, warmup)
+    del b
+    torch.cuda.empty_cache()
+    return round(wall, 4), {k: round(v, 4) for k, v in stages.items()}
 
 
 def main():
@@ -500,6 +557,13 @@ def main():
         log("64k: wall %.3f ms/step; stages %s" % (wall64, extra["prefill_64k_stages_ms"]))
         del b
         torch.cuda.empty_cache()
+    if a.only is None and not a.no_configs:
+        # the other prefill workloads: tiny fp32 (K = 4), 4K (K = 8), 16K (K = 32), 128K (K = 8)
+        for name in ("tiny", "4k", "16k", "128k"):
+            ms, st = time_config(torch, pisa, synth, name, max(a.steps, 20), a.warmup)
+            extra["prefill_%s_ms" % name] = ms
+            extra["prefill_%s_stages_ms" % name] = st
+            log("%s: wall %.3f ms/step; stages %s" % (name, ms, st))
     if a.only in (None, "decode") and not a.no_decode:
         cold, warm, vcold, vwarm = time_decode(torch, pisa, synth, a.decode_steps)
         extra["decode_us_per_step"] = round(cold, 2)
@@ -525,6 +589,7 @@ def main():
                    "block": w.block, "top_k": w.top_k, "branch": w.branch, "parallelism": "single-gpu"},
         "roofline": roof,
         "roofline_kernel": dom,
+        "roofline_step": step_roofline(work, wall_ms),
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "event_ms_per_step": round(ev_ms, 4),
         "routed_pairs": work["_pairs"],

@@ -69,13 +69,19 @@ def gpu_prefill(env, w, reps=1):
     return p, op, q, k, needles, pyr.cpu().numpy()[0], outs
 
 
-def verify(op, q, k, opyr, rows, idx, sc, decode=False, what=""):
+def verify(op, q, k, opyr, rows, idx, sc, decode=False, what="", tau5_rows=None):
+    """The tie-tolerant check (tau = 1e-3) on every listed row; the tau = 1e-5 pass rate
+    (a diagnostic: how often the GPU resolves even near-ties like the oracle) on all of them
+    or on the first tau5_rows of a seeded shuffle."""
     K = op.top_k
     gi = idx.reshape(-1, K)[rows]
     gs = sc.reshape(-1, K)[rows]
     t = time.time()
     st, br = oracle.check(op, q, k, opyr, rows, gi, gs, tau=TAU, rtol=RTOL, decode=decode)
-    st5, _ = oracle.check(op, q, k, opyr, rows, gi, gs, tau=1e-5, rtol=RTOL, decode=decode)
+    sub = np.arange(len(rows))
+    if tau5_rows is not None and tau5_rows < len(rows):
+        sub = np.sort(np.random.default_rng(5).choice(len(rows), tau5_rows, replace=False))
+    st5, _ = oracle.check(op, q, k, opyr, rows[sub], gi[sub], gs[sub], tau=1e-5, rtol=RTOL, decode=decode)
     counts = {oracle.CHECK_STATUS[s]: int(c) for s, c in enumerate(np.bincount(st, minlength=6)) if c}
     log(what, "rows=%d status=%s branches(max)=%d pass@tau1e-5=%.4f (%.1fs)" % (
         len(rows), counts, br.max() if len(br) else 0, float(np.mean(st5 == 0)) if len(st5) else 1.0,
@@ -232,19 +238,21 @@ def sample_rows(w, needles, n_random, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
-@pytest.mark.parametrize("name,n_random", [("16k", 3000), ("64k", 1500), ("128k", 1500), ("256k", 2000)])
-def test_prefill_workload_sampled(env, name, n_random):
+@pytest.mark.parametrize("name", ["16k", "64k", "128k", "256k"])
+def test_prefill_workload_every_row(env, name):
+    # the full-size workloads in bench.py's launch configuration, every query row against
+    # the oracle (256K: 1048576 rows, about a minute of the oracle on 16 cores)
     w = synth.WORKLOADS[name]
     p, op, q, k, needles, pyr, outs = gpu_prefill(env, w)
     opyr = check_pyramid(op, k, pyr, name)
     idx, sc = outs[0]
-    # every row: shape invariants
     K = w.top_k
     flat = idx.reshape(-1, K)
     nsel = (flat >= 0).sum(1)
     bq = np.tile(np.arange(w.seq_len) // 64, w.batch * w.n_kv_heads)
     assert np.array_equal(nsel, np.minimum(K, bq + 1))
-    verify(op, q, k, opyr, sample_rows(w, needles, n_random, 7), idx, sc, what=name)
+    rows = np.arange(w.batch * w.n_kv_heads * w.seq_len)
+    verify(op, q, k, opyr, rows, idx, sc, what=name + "-every-row", tau5_rows=20000)
 
 
 def test_prefill_gather_below_dense_levels(env):
