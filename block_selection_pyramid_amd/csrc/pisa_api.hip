@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "pisa_internal.h"
@@ -91,6 +92,27 @@ PrefillWs prefill_ws(const Geo& g) {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Scratch of pisa_select_prefill_noalloc: one copy per device, held until the process ends.
+// In host code `scratch` names a host-side stand-in; kernels get the device address that
+// hipGetSymbolAddress returns for the current device (looked up once per device).
+static __device__ __align__(256) unsigned char scratch[PISA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void* scratch_dev[kMaxDevices];
+
+// Device address of the current device's scratch, or null (HIP error or device id out of range).
+static void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_dev[dev] = ptr;
+  }
+  return scratch_dev[dev];
+}
 static bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 }  // namespace pisa
@@ -221,6 +243,22 @@ int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void*
   for (int i = 0; i < 6; ++i)
     if (!events[i]) return PISA_ERR_INVALID_ARG;
   return select_prefill_impl(p, q, k, pyramid, workspace, workspace_bytes, out_idx, out_score, events,
+                             (hipStream_t)stream);
+}
+
+int pisa_select_prefill_noalloc(const pisa_problem* p, const void* q, const void* k, const float* pyramid,
+                                int32_t* out_idx, float* out_score, pisa_stream_t stream) {
+  Geo g;
+  int rc = make_geo(p, &g);
+  if (rc != PISA_OK) return rc;
+  if (!q || !k || !pyramid || !out_idx || !out_score) return PISA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(pyramid)) return PISA_ERR_INVALID_ARG;
+  rc = supported(g, p->dtype, PISA_PREFILL);
+  if (rc != PISA_OK) return rc;
+  if (prefill_ws(g).total > (size_t)PISA_NOALLOC_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return PISA_ERR_HIP;
+  return select_prefill_impl(p, q, k, pyramid, ws, (size_t)PISA_NOALLOC_SCRATCH_BYTES, out_idx, out_score, nullptr,
                              (hipStream_t)stream);
 }
 

@@ -83,7 +83,7 @@ _lib = None
 
 EXPORTS = ("pisa_levels", "pisa_pyramid_layout", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs",
-           "pisa_prefill_dense_levels", "pisa_select_decode",
+           "pisa_prefill_dense_levels", "pisa_select_decode", "pisa_select_prefill_noalloc",
            "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
            "pisa_attention_workspace_bytes",
            "pisa_status_string", "pisa_version")
@@ -110,6 +110,7 @@ def load(path: str | None = None):
     lib.pisa_build_pyramid.argtypes = [P, vp, vp, vp]
     lib.pisa_select_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.pisa_select_prefill_staged.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp, ctypes.c_int32, vp]
+    lib.pisa_select_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.pisa_prefill_routed_pairs.argtypes = [P, vp, sz, vp, vp]
     lib.pisa_prefill_dense_levels.argtypes = [P, vp, vp]
     lib.pisa_select_decode.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
@@ -229,6 +230,24 @@ def select_prefill(p: Problem, q: torch.Tensor, k: torch.Tensor, pyramid: torch.
     sp = _dev(out_score, "out_score", torch.float32, oshape)
     _check(load().pisa_select_prefill(ctypes.byref(p.c()), qp, kp, pp, wp, ws.numel(), ip, sp, _stream(stream)),
            "pisa_select_prefill")
+    return out_idx, out_score
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PISA_NOALLOC_SCRATCH_BYTES
+
+
+def select_prefill_noalloc(p: Problem, q: torch.Tensor, k: torch.Tensor, pyramid: torch.Tensor,
+                           out_idx: torch.Tensor, out_score: torch.Tensor, stream=None):
+    """pisa_select_prefill_noalloc: the selection on the library's own device scratch (no
+    workspace, nothing allocated); the caller passes the outputs."""
+    oshape = (p.batch, p.n_kv_heads, p.seq_len, p.top_k)
+    qp = _dev(q, "q", p.torch_dtype, (p.batch, p.n_q_heads, p.seq_len, p.head_dim))
+    kp = _dev(k, "k", p.torch_dtype, (p.batch, p.n_kv_heads, p.seq_len, p.head_dim))
+    pp = _dev(pyramid, "pyramid", torch.float32, pyramid_shape(p))
+    ip = _dev(out_idx, "out_idx", torch.int32, oshape)
+    sp = _dev(out_score, "out_score", torch.float32, oshape)
+    _check(load().pisa_select_prefill_noalloc(ctypes.byref(p.c()), qp, kp, pp, ip, sp, _stream(stream)),
+           "pisa_select_prefill_noalloc")
     return out_idx, out_score
 
 

@@ -188,6 +188,23 @@ int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void*
                                void* const* events, int32_t n_events, pisa_stream_t stream);
 
 /*
+ * pisa_select_prefill for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument;
+ * the call runs on a scratch array of PISA_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each device it runs on until the process ends (its address is looked up on the first
+ * call on a device), and allocates nothing.  Problems whose prefill workspace
+ * (pisa_workspace_bytes(p, PISA_PREFILL)) exceeds it return PISA_ERR_WORKSPACE: 64 MiB
+ * covers, for example, 64K tokens with 4 KV heads at K = 8.  Every call on a device shares
+ * that device's scratch, so calls that overlap on one GPU (several streams, several host
+ * threads) race: the caller orders them, e.g. on one stream.  The scratch needs no clearing
+ * (each call clears its own counters with a kernel, not a memset).  Results equal
+ * pisa_select_prefill's.
+ */
+#define PISA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pisa_select_prefill_noalloc(const pisa_problem* p, const void* q, const void* k, const float* pyramid,
+                                int32_t* out_idx, float* out_score, pisa_stream_t stream);
+
+/*
  * Diagnostic, blocking: after a bf16 pisa_select_prefill on `stream` with `workspace`,
  * waits for the stream and reports how many (query group, leaf block) pairs the routing
  * walk sent to leaf scoring (forced blocks excluded).  fp32 problems report the number of
