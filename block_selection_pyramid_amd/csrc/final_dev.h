@@ -54,6 +54,21 @@ __device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool v
   }
 }
 
+// B fragments of one column: k-step s at p + s * step (p already at the lane's 8 dims).
+template <int D>
+__device__ __forceinline__ void load_bfrag_step(const bf16* __restrict__ p, bool valid, int step, bf16x8* bq) {
+  constexpr int KS = D / 16;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (valid) {
+      bq[s] = *reinterpret_cast<const bf16x8*>(p + step * s);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
+    }
+  }
+}
+
 // 64 keys (LDS tile, two M-tiles of 32) x 32 columns: acc0/acc1[v] of lane l hold keys
 // key_row(v, l >> 5) and 32 + key_row(v, l >> 5) against column l & 31.
 template <int D>

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
                                                         Geo geo, const int32_t* __restrict__ off,
                                                         const int32_t* __restrict__ choff,
                                                         const int32_t* __restrict__ entries, int32_t M,
-                                                        float* __restrict__ lscore) {
+                                                        float* __restrict__ lscore, const bf16* __restrict__ qg) {
   constexpr int CPG = 32 / G;  // entries per column group
   constexpr int NCG = kLeafColGroups;
   constexpr int QC = 4 * NCG * CPG;
@@ -69,7 +69,13 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   const int col = lane & 31, hh = lane >> 5;
   const int r = col % G;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-  const bf16* qh = q + ((int64_t)b * geo.Hq + h * G + r) * geo.N * D;
+  // The lane's query rows (head h G + r of each entry's query), dims 16 s + 8 hh of k-step
+  // s: from the regrouped copy when the dense launch wrote one (the group's heads adjacent
+  // per 8-dim piece, so G consecutive lanes read G * 16 contiguous bytes), else from q.
+  const bf16* qh = qg ? qg + (int64_t)bh * geo.N * (G * D) + (hh * G + r) * 8
+                      : q + ((int64_t)b * geo.Hq + h * G + r) * geo.N * D + 8 * hh;
+  const int64_t qrow = qg ? G * D : D;
+  const int qstep = qg ? 16 * G : 16;
   // entry of this lane's column in column group u of the wavefront (-1: none)
   auto entry = [&](int u) {
     const int e = e0 + (u * 4 + wave) * CPG + col / G;
@@ -78,7 +84,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   int ent = entry(0);
   bf16x8 bq[KS];
   // query fragments first: their latency overlaps the key-tile staging
-  load_bfrag<D>(qh + (int64_t)(ent >> 6) * D, ent >= 0, hh, bq);
+  load_bfrag_step<D>(qh + (ent >> 6) * qrow, ent >= 0, qstep, bq);
 
   const bf16* kb = k + (int64_t)bh * geo.N * D;
   const bool two = 2 * m + 1 < geo.n1;  // the node's second child exists
@@ -94,7 +100,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
     if (e0 + (u * 4 + wave) * CPG >= e1) break;  // uniform across the wavefront
     const int ent_n = u + 1 < NCG ? entry(u + 1) : -1;
     bf16x8 bqn[KS];
-    load_bfrag<D>(qh + (int64_t)(ent_n >> 6) * D, ent_n >= 0, hh, bqn);
+    load_bfrag_step<D>(qh + (ent_n >> 6) * qrow, ent_n >= 0, qstep, bqn);
 
     f32x16 acc0, acc1;
     tile_mfma32<D>(kt, bq, lane, acc0, acc1);
@@ -260,7 +266,7 @@ __global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __re
 }
 
 template <int D>
-int leaf_d(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
+int leaf_d(const Geo& g, const void* q, const void* k, const void* qg, const int32_t* off, const int32_t* choff,
            const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
   const int qc = chunk_entries(g.G);
   const int64_t pairs = (int64_t)g.B * g.Hkv * g.N * g.K;
@@ -268,11 +274,11 @@ int leaf_d(const Geo& g, const void* q, const void* k, const int32_t* off, const
   const bf16* qq = (const bf16*)q;
   const bf16* kk = (const bf16*)k;
   switch (g.G) {
-    case 1: leaf_pair_kernel<D, 1><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 2: leaf_pair_kernel<D, 2><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 4: leaf_pair_kernel<D, 4><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 8: leaf_pair_kernel<D, 8><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
-    case 16: leaf_pair_kernel<D, 16><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore); break;
+    case 1: leaf_pair_kernel<D, 1><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore, (const bf16*)qg); break;
+    case 2: leaf_pair_kernel<D, 2><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore, (const bf16*)qg); break;
+    case 4: leaf_pair_kernel<D, 4><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore, (const bf16*)qg); break;
+    case 8: leaf_pair_kernel<D, 8><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore, (const bf16*)qg); break;
+    case 16: leaf_pair_kernel<D, 16><<<(unsigned)grid, 256, 0, st>>>(qq, kk, g, off, choff, entries, M, lscore, (const bf16*)qg); break;
     default: return PISA_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
@@ -306,10 +312,10 @@ int forced_d(const Geo& g, const void* q, const void* k, const int32_t* cand, co
 
 }  // namespace
 
-int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
-                     const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
-  if (g.d == 128) return leaf_d<128>(g, q, k, off, choff, entries, M, lscore, st);
-  if (g.d == 64) return leaf_d<64>(g, q, k, off, choff, entries, M, lscore, st);
+int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const void* qg, const int32_t* off,
+                     const int32_t* choff, const int32_t* entries, int32_t M, float* lscore, hipStream_t st) {
+  if (g.d == 128) return leaf_d<128>(g, q, k, qg, off, choff, entries, M, lscore, st);
+  if (g.d == 64) return leaf_d<64>(g, q, k, qg, off, choff, entries, M, lscore, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -63,7 +63,8 @@ __device__ __forceinline__ void dense_load_keys(const bf16* kb, int N, int f, in
 template <int D, int G, int KC, bool TRUNC>
 __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
                                                           const bf16* __restrict__ k, Geo geo, int32_t l_bot,
-                                                          int32_t* __restrict__ x2, float* __restrict__ fsc) {
+                                                          int32_t* __restrict__ x2, float* __restrict__ fsc,
+                                                          bf16* __restrict__ qg) {
   constexpr int NCG = DenseShape<G>::NCG, QPW = DenseShape<G>::QPW;
   constexpr int KS = D / 16;         // k-steps of 16 dims
   constexpr int F = 2 * KS;          // 1 KB fragments of a staged child tile (hi, lo per k-step)
@@ -103,6 +104,20 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   int bqc[NCG];
   const int bqw = min(iw, N - 1) / C;  // bq of this wavefront's first (smallest) query
   load_query_cols<D, G, NCG>(q, geo, b, h, iw, lane, qf, bqc);
+  // The regrouped query copy for the gather and leaf launches: query i's G heads of every
+  // 8-dim piece adjacent, [b, h, i][piece][head][8 dims]; lane (j, hh) holds pieces
+  // 2 ks + hh of column j, so each G consecutive lanes write G * 16 contiguous bytes.
+  if (qg) {
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) {
+      const int i = iw + cg * (32 / G) + j / G;
+      if (i < N) {
+        bf16* dst = qg + ((int64_t)bh * N + i) * (G * D) + (hh * G + j % G) * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<bf16x8*>(dst + ks * 16 * G) = qf[cg][ks];
+      }
+    }
+  }
 
   // Walk state.  Item (query iq, rank r) = lane + 64 m holds the node ip kept at rank r one
   // level up; its candidates are ip's two children, with scores sc.  At the top level the
@@ -385,33 +400,35 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
 
 template <int D, int G, int KC>
 int dense_launch(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc,
-                 hipStream_t st) {
+                 bf16* qg, hipStream_t st) {
   constexpr int QW = kDenseWaves * DenseShape<G>::QPW;  // queries per workgroup
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + QW - 1) / QW));
   if (g.scorer == PISA_LSE)
     route_dense_kernel<D, G, KC, false>
-        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, dense_bottom(g), x2, fsc);
+        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, dense_bottom(g), x2, fsc, qg);
   else
     route_dense_kernel<D, G, KC, true>
-        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, dense_bottom(g), x2, fsc);
+        <<<grid, 64 * kDenseWaves, dense_lds_bytes<D, G, KC>(), st>>>(q, pyr, k, g, dense_bottom(g), x2, fsc, qg);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 template <int D, int G>
-int dense_k(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc, hipStream_t st) {
-  if (g.K <= 8) return dense_launch<D, G, 8>(g, q, pyr, k, x2, fsc, st);
-  if (g.K <= 16) return dense_launch<D, G, 16>(g, q, pyr, k, x2, fsc, st);
-  return dense_launch<D, G, 32>(g, q, pyr, k, x2, fsc, st);
+int dense_k(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc, bf16* qg,
+            hipStream_t st) {
+  if (g.K <= 8) return dense_launch<D, G, 8>(g, q, pyr, k, x2, fsc, qg, st);
+  if (g.K <= 16) return dense_launch<D, G, 16>(g, q, pyr, k, x2, fsc, qg, st);
+  return dense_launch<D, G, 32>(g, q, pyr, k, x2, fsc, qg, st);
 }
 
 template <int D>
-int dense_g(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc, hipStream_t st) {
+int dense_g(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_t* x2, float* fsc, bf16* qg,
+            hipStream_t st) {
   switch (g.G) {
-    case 1: return dense_k<D, 1>(g, q, pyr, k, x2, fsc, st);
-    case 2: return dense_k<D, 2>(g, q, pyr, k, x2, fsc, st);
-    case 4: return dense_k<D, 4>(g, q, pyr, k, x2, fsc, st);
-    case 8: return dense_k<D, 8>(g, q, pyr, k, x2, fsc, st);
-    case 16: return dense_k<D, 16>(g, q, pyr, k, x2, fsc, st);
+    case 1: return dense_k<D, 1>(g, q, pyr, k, x2, fsc, qg, st);
+    case 2: return dense_k<D, 2>(g, q, pyr, k, x2, fsc, qg, st);
+    case 4: return dense_k<D, 4>(g, q, pyr, k, x2, fsc, qg, st);
+    case 8: return dense_k<D, 8>(g, q, pyr, k, x2, fsc, qg, st);
+    case 16: return dense_k<D, 16>(g, q, pyr, k, x2, fsc, qg, st);
     default: return PISA_ERR_UNSUPPORTED;
   }
 }
@@ -419,10 +436,10 @@ int dense_g(const Geo& g, const bf16* q, const float* pyr, const bf16* k, int32_
 }  // namespace
 
 int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, const void* k, int32_t* x2, float* fsc,
-                              hipStream_t st) {
+                              void* qg, hipStream_t st) {
   if (g.L < 3 || g.K > 32) return PISA_ERR_UNSUPPORTED;
-  if (g.d == 128) return dense_g<128>(g, (const bf16*)q, pyr, (const bf16*)k, x2, fsc, st);
-  if (g.d == 64) return dense_g<64>(g, (const bf16*)q, pyr, (const bf16*)k, x2, fsc, st);
+  if (g.d == 128) return dense_g<128>(g, (const bf16*)q, pyr, (const bf16*)k, x2, fsc, (bf16*)qg, st);
+  if (g.d == 64) return dense_g<64>(g, (const bf16*)q, pyr, (const bf16*)k, x2, fsc, (bf16*)qg, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -68,7 +68,8 @@ __device__ __forceinline__ float sub_pair(float y0, float y1, float c2) {
 template <int D, int KC, int NLEV, bool TRUNC>
 __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
                                                         Geo geo, const int32_t* __restrict__ x2,
-                                                        int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
+                                                        int32_t* __restrict__ cand, int32_t* __restrict__ cnt,
+                                                        const bf16* __restrict__ qg) {
   constexpr int G = 4, KS = D / 32;
   using S = SubLds<KC, NLEV>;
   extern __shared__ __attribute__((aligned(16))) int hist[];
@@ -104,9 +105,13 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
     const int f0 = qr0 + qd * 4;
     const int ii = f0 + gown;
     if (qd < kSubQueries / 4 && ii < N) {
-      const bf16* p = q + (qbase + (int64_t)r * N + ii) * D + 8 * kg;
+      // piece 4 s + kg of head r: from the regrouped copy (the group's heads adjacent per
+      // piece) when the dense launch wrote one, else from q's own rows
+      const bf16* p = qg ? qg + ((int64_t)bh * N + ii) * (G * D) + (kg * G + r) * 8
+                         : q + (qbase + (int64_t)r * N + ii) * D + 8 * kg;
+      const int step = qg ? 32 * G : 32;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + 32 * s));
+      for (int s = 0; s < KS; ++s) qf[s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p + step * s));
     } else {
 #pragma unroll
       for (int s = 0; s < KS; ++s)
@@ -293,22 +298,22 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
 
 template <int D, int KC, int NLEV>
 int sub_launch(const Geo& g, const void* q, const float* pyr, const int32_t* x2, int32_t* cand, int32_t* cnt,
-               hipStream_t st) {
+               const void* qg, hipStream_t st) {
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kSubQueries - 1) / kSubQueries));
   const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
   if (g.scorer == PISA_LSE)
-    route_sub_kernel<D, KC, NLEV, false><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt);
+    route_sub_kernel<D, KC, NLEV, false><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt, (const bf16*)qg);
   else
-    route_sub_kernel<D, KC, NLEV, true><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt);
+    route_sub_kernel<D, KC, NLEV, true><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt, (const bf16*)qg);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 template <int D, int NLEV>
 int sub_k(const Geo& g, const void* q, const float* pyr, const int32_t* x2, int32_t* cand, int32_t* cnt,
-          hipStream_t st) {
-  if (g.K <= 8) return sub_launch<D, 8, NLEV>(g, q, pyr, x2, cand, cnt, st);
-  if (g.K <= 16) return sub_launch<D, 16, NLEV>(g, q, pyr, x2, cand, cnt, st);
-  return sub_launch<D, 32, NLEV>(g, q, pyr, x2, cand, cnt, st);
+          const void* qg, hipStream_t st) {
+  if (g.K <= 8) return sub_launch<D, 8, NLEV>(g, q, pyr, x2, cand, cnt, qg, st);
+  if (g.K <= 16) return sub_launch<D, 16, NLEV>(g, q, pyr, x2, cand, cnt, qg, st);
+  return sub_launch<D, 32, NLEV>(g, q, pyr, x2, cand, cnt, qg, st);
 }
 
 }  // namespace
@@ -318,10 +323,10 @@ bool route_sub_supported(const Geo& g, int l_x) {
 }
 
 int launch_route_sub(const Geo& g, int l_x, const void* q, const float* pyr, const int32_t* x2, int32_t* cand,
-                     int32_t* cnt, hipStream_t st) {
+                     int32_t* cnt, const void* qg, hipStream_t st) {
   if (!route_sub_supported(g, l_x)) return PISA_ERR_UNSUPPORTED;
-  if (g.d == 128) return l_x == 3 ? sub_k<128, 2>(g, q, pyr, x2, cand, cnt, st) : sub_k<128, 1>(g, q, pyr, x2, cand, cnt, st);
-  return l_x == 3 ? sub_k<64, 2>(g, q, pyr, x2, cand, cnt, st) : sub_k<64, 1>(g, q, pyr, x2, cand, cnt, st);
+  if (g.d == 128) return l_x == 3 ? sub_k<128, 2>(g, q, pyr, x2, cand, cnt, qg, st) : sub_k<128, 1>(g, q, pyr, x2, cand, cnt, qg, st);
+  return l_x == 3 ? sub_k<64, 2>(g, q, pyr, x2, cand, cnt, qg, st) : sub_k<64, 1>(g, q, pyr, x2, cand, cnt, qg, st);
 }
 
 }  // namespace pisa

@@ -74,7 +74,7 @@ int supported(const Geo& g, int dtype, int mode) {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-PrefillWs prefill_ws(const Geo& g) {
+PrefillWs prefill_ws(const Geo& g, int dtype) {
   PrefillWs w;
   w.slots = (int64_t)g.B * g.Hkv * g.N * 2 * g.K;
   w.M = g.B * g.Hkv * g.n1p;
@@ -87,6 +87,9 @@ PrefillWs prefill_ws(const Geo& g) {
   w.choff = o;   o = align256(o + sizeof(int32_t) * (w.M + 1));
   w.entries = o; o = align256(o + sizeof(int32_t) * w.slots);
   w.fsc = o;     o = align256(o + sizeof(float) * 3 * (size_t)g.B * g.Hkv * g.N);
+  w.total_min = o;
+  w.qg = o;
+  if (route_scores_forced(g, dtype)) o = align256(o + 2 * (size_t)g.B * g.Hq * g.N * g.d);  // bf16, q's size
   w.total = o;
   return w;
 }
@@ -167,7 +170,13 @@ size_t pisa_workspace_bytes(const pisa_problem* p, int mode) {
   if (make_geo(p, &g) != PISA_OK) return 0;
   if (mode == PISA_DECODE) return 0;
   if (mode != PISA_PREFILL) return 0;
-  return prefill_ws(g).total;
+  return prefill_ws(g, p->dtype).total;
+}
+
+size_t pisa_prefill_workspace_min_bytes(const pisa_problem* p) {
+  Geo g;
+  if (make_geo(p, &g) != PISA_OK) return 0;
+  return prefill_ws(g, p->dtype).total_min;
 }
 
 int pisa_build_pyramid(const pisa_problem* p, const void* k, float* pyramid, pisa_stream_t stream) {
@@ -191,9 +200,10 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(pyramid) || !aligned16(workspace)) return PISA_ERR_INVALID_ARG;
   rc = supported(g, p->dtype, PISA_PREFILL);
   if (rc != PISA_OK) return rc;
-  const PrefillWs w = prefill_ws(g);
-  if (workspace_bytes < w.total) return PISA_ERR_WORKSPACE;
+  const PrefillWs w = prefill_ws(g, p->dtype);
+  if (workspace_bytes < w.total_min) return PISA_ERR_WORKSPACE;
   char* ws = (char*)workspace;
+  void* qg = (w.total > w.total_min && workspace_bytes >= w.total) ? ws + w.qg : nullptr;
   int32_t* cand = (int32_t*)(ws + w.cand);
   float* lscore = (float*)(ws + w.lscore);
   int32_t* cnt = (int32_t*)(ws + w.cnt);
@@ -209,7 +219,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   // counters are contiguous: cnt then cursor (each 256-aligned)
   if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
   // the entries region is free until the scatter: it carries the level-2 candidates
-  if ((rc = launch_route(g, p->dtype, q, k, pyramid, entries, fsc, cand, cnt, ev ? (hipEvent_t)ev[1] : nullptr,
+  if ((rc = launch_route(g, p->dtype, q, k, pyramid, entries, fsc, cand, cnt, qg, ev ? (hipEvent_t)ev[1] : nullptr,
                         st)) != PISA_OK)
     return rc;
   if ((rc = mark(2)) != PISA_OK) return rc;
@@ -222,7 +232,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   if ((rc = launch_scan(cnt, w.M, chunk_entries(g.G), off, choff, st)) != PISA_OK) return rc;
   if ((rc = launch_scatter_pairs(g, cand, off, cursor, entries, st)) != PISA_OK) return rc;
   if ((rc = mark(3)) != PISA_OK) return rc;
-  if ((rc = launch_leaf_mfma(g, q, k, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
+  if ((rc = launch_leaf_mfma(g, q, k, qg, off, choff, entries, w.M, lscore, st)) != PISA_OK) return rc;
   if ((rc = mark(4)) != PISA_OK) return rc;
   rc = route_scores_forced(g, p->dtype) ? launch_final(g, cand, lscore, fsc, out_idx, out_score, st)
                                         : launch_forced_final(g, q, k, cand, lscore, out_idx, out_score, st);
@@ -255,7 +265,8 @@ int pisa_select_prefill_noalloc(const pisa_problem* p, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(pyramid)) return PISA_ERR_INVALID_ARG;
   rc = supported(g, p->dtype, PISA_PREFILL);
   if (rc != PISA_OK) return rc;
-  if (prefill_ws(g).total > (size_t)PISA_NOALLOC_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
+  // without room for the regrouped query copy the call reads q itself
+  if (prefill_ws(g, p->dtype).total_min > (size_t)PISA_NOALLOC_SCRATCH_BYTES) return PISA_ERR_WORKSPACE;
   void* ws = scratch_address();
   if (!ws) return PISA_ERR_HIP;
   return select_prefill_impl(p, q, k, pyramid, ws, (size_t)PISA_NOALLOC_SCRATCH_BYTES, out_idx, out_score, nullptr,
@@ -270,7 +281,7 @@ int pisa_prefill_routed_pairs(const pisa_problem* p, const void* workspace, size
   if (!workspace || !routed_pairs) return PISA_ERR_INVALID_ARG;
   rc = supported(g, p->dtype, PISA_PREFILL);
   if (rc != PISA_OK) return rc;
-  const PrefillWs w = prefill_ws(g);
+  const PrefillWs w = prefill_ws(g, p->dtype);
   if (workspace_bytes < w.total) return PISA_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (hipStreamSynchronize(st) != hipSuccess) return PISA_ERR_HIP;

@@ -28,16 +28,20 @@ struct Geo {
   __host__ __device__ int64_t means_floats() const { return (int64_t)B * Hkv * Tp * d; }
 };
 
-// Prefill workspace carve-up (byte offsets, 256-aligned).
+// Prefill workspace carve-up (byte offsets, 256-aligned).  qg: the queries regrouped by
+// (b, KV head, position) with the G heads of each 8-dim piece adjacent, written by the dense
+// routing launch (bf16 with L >= 3) for the gather and leaf launches; total includes it,
+// total_min does not (a workspace of at least total_min but less than total runs without
+// the copy, reading q itself).
 struct PrefillWs {
-  size_t cand, lscore, cnt, cursor, off, choff, entries, fsc, total;
+  size_t cand, lscore, cnt, cursor, off, choff, entries, fsc, qg, total_min, total;
   int64_t slots;  // B*Hkv*N*2K
   int32_t M;      // B*Hkv*n1p leaf-pair lists
 };
 
 int make_geo(const pisa_problem* p, Geo* g);  // PISA_OK or PISA_ERR_INVALID_ARG
 int supported(const Geo& g, int dtype, int mode);
-PrefillWs prefill_ws(const Geo& g);
+PrefillWs prefill_ws(const Geo& g, int dtype);
 // Leaf-pair entries (query groups) per chunk of the prefill leaf kernel: four wavefronts,
 // kLeafColGroups column groups of 32 (query, head) columns each (256K prefill: 2, 4, 8, 16
 // and 32 groups took 2.45, 2.02, 1.82, 1.73 and ~1.69 ms).
@@ -83,12 +87,14 @@ int launch_zero(int32_t* a, int64_t n, hipStream_t st);
 // x2: scratch of B*Hkv*N*2K int32 (level-2 candidates between the two routing launches);
 // fsc: forced-block scores, written when route_scores_forced(); mid (may be null) is
 // recorded between the upper-level and the level-2 launch
+// qg (may be null): the regrouped query copy, written by the dense launch and read by the
+// gather launch
 int launch_route(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2,
-                 float* fsc, int32_t* cand, int32_t* cnt, hipEvent_t mid, hipStream_t st);
+                 float* fsc, int32_t* cand, int32_t* cnt, void* qg, hipEvent_t mid, hipStream_t st);
 // Levels L..dense_bottom(g) of the bf16 walk (L >= 3), scored densely per leaf block; writes x2 and the
 // forced blocks' scores fsc [B*Hkv*N*3] (ascending forced-block order).
 int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, const void* k, int32_t* x2, float* fsc,
-                              hipStream_t st);
+                              void* qg, hipStream_t st);
 // true when launch_route scores the forced blocks (into fsc) for this problem
 inline bool route_scores_forced(const Geo& g, int dtype) { return dtype == PISA_BF16 && g.L >= 3; }
 // Dense scoring pays while a level is small: its cost per query grows with the visible
@@ -112,7 +118,7 @@ inline int dense_bottom(const Geo& g) {
 // like the gather walk.
 bool route_sub_supported(const Geo& g, int l_x);
 int launch_route_sub(const Geo& g, int l_x, const void* q, const float* pyr, const int32_t* x2, int32_t* cand,
-                     int32_t* cnt, hipStream_t st);
+                     int32_t* cnt, const void* qg, hipStream_t st);
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
 // histogram of the routed (query group, level-2 node) pairs of the 2K leaf slots per query
 // group into cnt [B*Hkv*n1p] (the counts the gather launch keeps when it runs)
@@ -126,8 +132,8 @@ int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t
 // holds a block
 int launch_scatter_pairs(const Geo& g, const int32_t* cand, const int32_t* off, int32_t* cursor, int32_t* entries,
                          hipStream_t st);
-int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const int32_t* off, const int32_t* choff,
-                     const int32_t* entries, int32_t M, float* lscore, hipStream_t st);
+int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const void* qg, const int32_t* off,
+                     const int32_t* choff, const int32_t* entries, int32_t M, float* lscore, hipStream_t st);
 int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const float* fsc, int32_t* out_idx,
                  float* out_score, hipStream_t st);
 int launch_forced_final(const Geo& g, const void* q, const void* k, const int32_t* cand, const float* lscore,

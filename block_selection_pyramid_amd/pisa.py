@@ -84,6 +84,7 @@ _lib = None
 EXPORTS = ("pisa_levels", "pisa_pyramid_layout", "pisa_supported", "pisa_pyramid_bytes", "pisa_workspace_bytes", "pisa_build_pyramid",
            "pisa_select_prefill", "pisa_select_prefill_staged", "pisa_prefill_routed_pairs",
            "pisa_prefill_dense_levels", "pisa_select_decode", "pisa_select_prefill_noalloc",
+           "pisa_prefill_workspace_min_bytes",
            "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
            "pisa_attention_workspace_bytes",
            "pisa_status_string", "pisa_version")
@@ -107,6 +108,8 @@ def load(path: str | None = None):
     lib.pisa_pyramid_bytes.restype = sz
     lib.pisa_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.pisa_workspace_bytes.restype = sz
+    lib.pisa_prefill_workspace_min_bytes.argtypes = [P]
+    lib.pisa_prefill_workspace_min_bytes.restype = sz
     lib.pisa_build_pyramid.argtypes = [P, vp, vp, vp]
     lib.pisa_select_prefill.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.pisa_select_prefill_staged.argtypes = [P, vp, vp, vp, vp, sz, vp, vp, vp, ctypes.c_int32, vp]
@@ -163,6 +166,10 @@ def pyramid_bytes(p: Problem) -> int:
 
 def workspace_bytes(p: Problem, mode: int = PREFILL) -> int:
     return load().pisa_workspace_bytes(ctypes.byref(p.c()), mode)
+
+
+def prefill_workspace_min_bytes(p: Problem) -> int:
+    return load().pisa_prefill_workspace_min_bytes(ctypes.byref(p.c()))
 
 
 def _dev(t: torch.Tensor, name: str, dtype, shape=None) -> int:

@@ -139,8 +139,14 @@ int pisa_supported(const pisa_problem* p, int mode);
  * rounded up to a multiple of 4); 0 for an invalid problem. */
 size_t pisa_pyramid_bytes(const pisa_problem* p);
 
-/* Bytes of device workspace a call in `mode` needs (may be 0); 0 for an invalid problem. */
+/* Bytes of device workspace a call in `mode` needs (may be 0); 0 for an invalid problem.
+ * For bf16 prefill with L >= 3 this includes room for a copy of q regrouped so that the G
+ * heads of a KV head sit together per 8-dim piece, which the routing launch writes and the
+ * gather and leaf launches read (their query loads then take whole cache lines); a
+ * workspace of at least pisa_prefill_workspace_min_bytes runs without that copy, with the
+ * same results. */
 size_t pisa_workspace_bytes(const pisa_problem* p, int mode);
+size_t pisa_prefill_workspace_min_bytes(const pisa_problem* p);
 
 /*
  * Builds the pyramid of k [B, Hkv, N, d] into `pyramid` (agihunt.info, pyramid paragraph:
@@ -193,8 +199,9 @@ int pisa_select_prefill_staged(const pisa_problem* p, const void* q, const void*
  * the call runs on a scratch array of PISA_NOALLOC_SCRATCH_BYTES that the library holds on
  * each device it runs on until the process ends (its address is looked up on the first
  * call on a device), and allocates nothing.  Problems whose prefill workspace
- * (pisa_workspace_bytes(p, PISA_PREFILL)) exceeds it return PISA_ERR_WORKSPACE: 64 MiB
- * covers, for example, 64K tokens with 4 KV heads at K = 8.  Every call on a device shares
+ * (pisa_prefill_workspace_min_bytes(p)) exceeds it return PISA_ERR_WORKSPACE: 64 MiB
+ * covers, for example, 78K tokens with 4 KV heads at K = 8 (the regrouped query copy is
+ * used when it fits as well).  Every call on a device shares
  * that device's scratch, so calls that overlap on one GPU (several streams, several host
  * threads) race: the caller orders them, e.g. on one stream.  The scratch needs no clearing
  * (each call clears its own counters with a kernel, not a memset).  Results equal

@@ -79,7 +79,13 @@ def test_sizes(pisa):
     # candidates, leaf scores and list entries per slot; counts, cursors, offsets and
     # chunk offsets per (KV head, leaf block) list; three forced-block scores per query group
     need = slots * 12 + 4 * 262144 * 3 * 4
-    assert ws >= need and ws < need + 4 * 4 * 4096 * 4 + 4096
+    qcopy = 16 * 262144 * 128 * 2  # the regrouped query copy (bf16, q's size)
+    assert ws >= need + qcopy and ws < need + qcopy + 4 * 4 * 4096 * 4 + 4096
+    wmin = pisa.prefill_workspace_min_bytes(p)
+    assert wmin >= need and wmin < need + 4 * 4 * 4096 * 4 + 4096
+    # no copy without a dense routing launch (fp32)
+    pf = pisa.Problem(1, 262144, 16, 4, 128, 64, 8, 2, dtype=pisa.F32)
+    assert pisa.workspace_bytes(pf, pisa.PREFILL) == pisa.prefill_workspace_min_bytes(pf)
     assert pisa.workspace_bytes(p, pisa.DECODE) == 0
 
 
@@ -212,8 +218,10 @@ def test_unsupported_problems(pisa, kw):
 
 
 def test_workspace_too_small(pisa):
+    # below the minimum (no room even without the regrouped query copy): rejected on the host
     p = pisa.Problem(1, 4096, 16, 4, 128)
-    need = pisa.workspace_bytes(p)
+    need = pisa.prefill_workspace_min_bytes(p)
+    assert 0 < need < pisa.workspace_bytes(p)
     assert _call_prefill(pisa, p, ws_bytes=need - 1) == 3
 
 

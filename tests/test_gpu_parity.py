@@ -217,6 +217,28 @@ def test_staged_call_matches_plain_call(env):
         pisa.select_prefill_staged(p, qd, kd, pyr, ws, i2, s2, ev[:5])
 
 
+@pytest.mark.parametrize("N,Hq,Hkv,d,K", [(4096 + 37, 8, 2, 64, 5), (64 * 2046 + 5, 4, 1, 128, 8),
+                                          (262144, 4, 1, 128, 8)])
+def test_min_workspace_matches_full_workspace(env, N, Hq, Hkv, d, K):
+    # a workspace of pisa_prefill_workspace_min_bytes reads q itself; the full one adds the
+    # regrouped query copy for the gather and leaf launches: the same bits either way
+    torch, pisa = env
+    w = synth.custom(name="ws-min", batch=1, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     seed=60 + N % 31, needles=8)
+    p, _ = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    qd, kd = dev(torch, q), dev(torch, k)
+    log("ws-min", "N=%d: launching" % N)
+    pyr = pisa.build_pyramid(p, kd)
+    full = pisa.workspace_bytes(p)
+    wmin = pisa.prefill_workspace_min_bytes(p)
+    assert wmin < full
+    i1, s1 = pisa.select_prefill(p, qd, kd, pyr, torch.empty(full, dtype=torch.uint8, device="cuda"))
+    i2, s2 = pisa.select_prefill(p, qd, kd, pyr, torch.empty(wmin, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
 @pytest.mark.parametrize("name", ["tiny", "4k"])
 def test_prefill_workload_all_rows(env, name):
     w = synth.WORKLOADS[name]

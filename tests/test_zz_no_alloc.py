@@ -38,7 +38,7 @@ def test_noalloc_matches_workspace_call_twice():
                          head_dim=128, top_k=5, seed=42, needles=8)
     for w in (big, small):
         p = pisa.Problem(**w.shape())
-        assert pisa.workspace_bytes(p) <= pisa.NOALLOC_SCRATCH_BYTES
+        assert pisa.prefill_workspace_min_bytes(p) <= pisa.NOALLOC_SCRATCH_BYTES
         print("[noalloc]", w.name, "N=%d: launching" % w.seq_len, flush=True)
         ri, rs, oi, os_ = _run(torch, pisa, w)
         assert np.array_equal(ri, oi), w.name
@@ -50,7 +50,7 @@ def test_noalloc_rejects_problems_past_the_scratch():
     from block_selection_pyramid_amd import pisa
     pisa.load()
     p = pisa.Problem(1, 262144, 16, 4, 128, 64, 8, 2)
-    assert pisa.workspace_bytes(p) > pisa.NOALLOC_SCRATCH_BYTES
+    assert pisa.prefill_workspace_min_bytes(p) > pisa.NOALLOC_SCRATCH_BYTES
     # host-side rejection: no kernel runs, so tiny placeholder tensors suffice for the shapes
     # the binding checks are bypassed by calling the C entry point directly
     lib = pisa.load()
