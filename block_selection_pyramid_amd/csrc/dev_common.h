@@ -27,22 +27,25 @@ __device__ __forceinline__ uint32_t f2bf_rne(float f) {
 // and lo = bf16(v - hi), so that a dot product with a query row is the scaled score in log2
 // units.  It follows the fp32 means in the pyramid buffer.  Layout: the nodes of one (b, h)
 // (node stride a multiple of 4) form aligned quads 4Q .. 4Q+3, each a record of 8*D bf16;
-// for every 8-dim piece p (dims 8p .. 8p+7) the record holds one 128-byte line
-// [hi of nodes 4Q .. 4Q+3 | lo of nodes 4Q .. 4Q+3], 16 bytes per node and half.  The matrix
-// cores' operand layout puts 16 consecutive nodes on 16 consecutive lanes that each take 16
-// bytes of one piece, so every four consecutive lanes then read 64 contiguous bytes: an L1
-// pays per line per group of four lanes (L2-resident gathers on this chip: 33 TB/s when
-// four lanes share a line, 19 when they span two, 9.7 when they span four).
-// rc_node: bf16 offset of node n's hi piece 0; piece p's hi at + 64 p, lo at + 32.
+// for every two 8-dim pieces 2j, 2j+1 (dims 16j .. 16j+15) the record holds a 128-byte hi
+// line [piece 2j of nodes 4Q .. 4Q+3 | piece 2j+1 of nodes 4Q .. 4Q+3] (16 bytes per node
+// and piece), then the lo line laid out alike.  The matrix cores' operand layout puts
+// consecutive nodes on consecutive lanes that each take 16 bytes of one piece, so every
+// four consecutive lanes read 64 contiguous bytes and the lanes of two adjacent pieces fill
+// whole lines: an L1 pays per line per group of four lanes (L2-resident gathers on this
+// chip, this layout's operand loads: 34 TB/s; four lanes on four lines: 9.7).
+// rc_node: bf16 offset of node n's hi piece 0; piece p's hi at + 128 (p >> 1) + 32 (p & 1),
+// its lo 64 bf16 further.
 __host__ __device__ __forceinline__ int64_t rc_node(int64_t n, int D) { return (n >> 2) * 8 * D + (n & 3) * 8; }
+__host__ __device__ __forceinline__ int64_t rc_piece(int p) { return 128 * (p >> 1) + 32 * (p & 1); }
 __host__ __device__ __forceinline__ int64_t rcopy_index(int64_t node, int e, int D) {
-  return rc_node(node, D) + (e >> 3) * 64 + (e & 7);
+  return rc_node(node, D) + rc_piece(e >> 3) + (e & 7);
 }
 // Byte offset of 16-byte piece c of node n in the order of a node-contiguous record (the
 // layout staged in LDS): d/32 chunks of [hi(32 dims) | lo(32 dims)], 8 pieces each.
 __host__ __device__ __forceinline__ int64_t rc_piece_bytes(int64_t n, int c, int D) {
   const int p = 4 * (c >> 3) + (c & 3);  // 8-dim piece
-  return 2 * rc_node(n, D) + 128 * p + 64 * ((c >> 2) & 1);
+  return 2 * (rc_node(n, D) + rc_piece(p) + 64 * ((c >> 2) & 1));
 }
 template <int D>
 __device__ __forceinline__ void store_rcopy(bf16* R, int64_t node, int e, float v) {
@@ -50,7 +53,7 @@ __device__ __forceinline__ void store_rcopy(bf16* R, int64_t node, int e, float 
   const float rest = v - bf2f(hi);
   const int64_t i = rcopy_index(node, e, D);
   R[i] = (bf16)hi;
-  R[i + 32] = (bf16)f2bf_rne(rest);
+  R[i + 64] = (bf16)f2bf_rne(rest);
 }
 
 // Load 16 bytes of input starting at element e of row r and widen to float.

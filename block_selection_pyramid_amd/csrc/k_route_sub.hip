@@ -145,12 +145,12 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
       const int y = j < ntile ? w->Y[(rb + j) & 3][j] : -1;
       const int leaf = 4 * y + v;
       // a missing leaf (or an empty tile) reads leaf 0 instead; its rows are never used
-      // k-step s, lane group kg <-> 8-dim piece 4 s + kg (hi, then lo 32 bf16 later)
-      const bf16* rp = R1 + rc_node((y >= 0 && leaf < n1) ? leaf : 0, D) + 64 * kg;
+      // k-step s, lane group kg <-> 8-dim piece 4 s + kg (hi, then lo 64 bf16 later)
+      const bf16* rp = R1 + rc_node((y >= 0 && leaf < n1) ? leaf : 0, D) + rc_piece(kg);
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
-        lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 32);
+        lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
       }
     }
   };

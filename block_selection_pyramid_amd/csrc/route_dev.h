@@ -164,11 +164,11 @@ struct MfmaWalk {
             if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
           }
         } else {
-          const bf16* rp = R + rc_node(geo.off[l - 1] + ca[g][tb], D) + 64 * kg;  // piece 4 s + kg
+          const bf16* rp = R + rc_node(geo.off[l - 1] + ca[g][tb], D) + rc_piece(kg);  // piece 4 s + kg
 #pragma unroll
           for (int s = 0; s < KS; ++s) {
             hi[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
-            if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 32);
+            if constexpr (kLo) lo[g][tb][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
           }
         }
       }
@@ -303,11 +303,11 @@ struct MfmaWalk {
             if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 128 * s2 + 64);
           }
         } else {
-          const bf16* rp = R + rc_node(geo.off[l - 1] + ca, D) + 64 * kg;  // piece 4 s2 + kg
+          const bf16* rp = R + rc_node(geo.off[l - 1] + ca, D) + rc_piece(kg);  // piece 4 s2 + kg
 #pragma unroll
           for (int s2 = 0; s2 < KS; ++s2) {
             hi[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 256 * s2);
-            if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 256 * s2 + 32);
+            if constexpr (!kApprox) lo[tb][s2] = *reinterpret_cast<const bf16x8*>(rp + 256 * s2 + 64);
           }
         }
       }

@@ -23,13 +23,14 @@ struct DenseShape {
 // k-step ks, so every MFMA A-operand read is one conflict-free 16-byte row per lane.  The
 // wavefronts of the workgroup take fragments wave, wave + 4, ...  A fragment's lane reads
 // 8-dim piece 2 ks + (lane >> 5) of its child, so each four consecutive lanes read one node
-// quad's 64 contiguous bytes of the routing copy.
+// quad's 64 contiguous bytes of the routing copy and the two halves of the lanes fill the
+// k-step's hi (or lo) lines.
 template <int D, int NU>
 __device__ __forceinline__ void dense_load_tile(const char* Rb, const Geo& geo, int l, int t, int wave, int lane,
                                                 u32x4 (&stg)[NU]) {
   const int node = geo.off[l - 1] + min(32 * t + (lane & 31), geo.n[l - 1] - 1);  // a missing child reads a real node
   // fragment wave + 4 u: k-step 2 u + (wave >> 1), hi / lo = wave & 1
-  const char* base = Rb + 2 * rc_node(node, D) + 128 * (lane >> 5) + 256 * (wave >> 1) + 64 * (wave & 1);
+  const char* base = Rb + 2 * rc_node(node, D) + 64 * (lane >> 5) + 256 * (wave >> 1) + 128 * (wave & 1);
 #pragma unroll
   for (int u = 0; u < NU; ++u) stg[u] = *reinterpret_cast<const u32x4*>(base + 512 * u);
 }

@@ -42,8 +42,9 @@
  *                 equally sized routing copy: each mean times s * log2(e) (fp32 product,
  *                 s as resolved from the problem) split into bf16 hi + bf16 lo (hi + lo
  *                 equals that product to 2^-18 relative).  In each (b, h) block of the copy
- *                 nodes 4Q .. 4Q+3 share a record of 8d bf16: per 8-dim piece, one
- *                 128-byte line [hi(8) of the four nodes | lo(8) of the four nodes].  The
+ *                 nodes 4Q .. 4Q+3 share a record of 8d bf16: per 16 dims 16j .. 16j+15,
+ *                 a 128-byte line of hi halves [dims 16j..+8 of the four nodes | dims
+ *                 16j+8..+8 of the four nodes], then the line of lo halves alike.  The
  *                 copy is tied to the problem's scale
  *   out_idx       [B, Hkv, N, K] (prefill) or [B, Hkv, K] (decode), int32: selected leaf
  *                 block ids in ascending order, padded with -1

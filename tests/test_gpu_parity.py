@@ -97,10 +97,12 @@ def verify(op, q, k, opyr, rows, idx, sc, decode=False, what="", tau5_rows=None)
 def decode_rcopy(pyr, d):
     """Routing copy of a pyramid buffer [2, B, Hkv, Tp, d] (fp32 view) as bf16 bits
     [B, Hkv, Tp, 2, d] (hi, lo per node).  Layout: nodes 4Q .. 4Q+3 of one (b, h) share a
-    record; per 8-dim piece, [hi of the four nodes | lo of the four nodes], 8 bf16 each."""
+    record; per two 8-dim pieces 2j, 2j+1: the hi line [piece 2j of the four nodes | piece
+    2j+1 of the four nodes], then the lo line alike, 8 bf16 per node and piece."""
     B, H, Tp = pyr.shape[1:4]
-    r = np.ascontiguousarray(pyr[1]).view(np.uint16).reshape(B, H, Tp // 4, d // 8, 2, 4, 8)
-    return r.transpose(0, 1, 2, 5, 4, 3, 6).reshape(B, H, Tp, 2, d)
+    r = np.ascontiguousarray(pyr[1]).view(np.uint16).reshape(B, H, Tp // 4, d // 16, 2, 2, 4, 8)
+    # axes: quad, piece pair j, hi/lo, piece parity, node, dim -> quad, node, hi/lo, j, parity, dim
+    return r.transpose(0, 1, 2, 6, 4, 3, 5, 7).reshape(B, H, Tp, 2, d)
 
 
 def check_pyramid(op, k, pyr, what):
