@@ -494,6 +494,58 @@ def cpu_baseline(synth, sample_rows):
                       "selection of %s; measured %.1fs" % (what, t2 - t0)}
 
 
+def bruteforce_selection(q, k, K, C, s):
+    """Brute-force all-leaf selection for one KV head with G query heads (q [G, N, d],
+    k [N, d], fp64): every causal block scored by the group-summed causal LSE over its raw
+    keys, the forced blocks {0, b-1, b} kept, then the K - |F| best other blocks (score
+    descending, lower index first).  Returns a list of sets per query."""
+    G, N, d = q.shape
+    logits = s * np.einsum("gid,td->git", q, k)  # [G, N, N]
+    out = []
+    for i in range(N):
+        b = i // C
+        sc = np.zeros(b + 1)
+        for j in range(b + 1):
+            x = logits[:, i, j * C:min(i + 1, (j + 1) * C)]
+            m = x.max(axis=1, keepdims=True)
+            sc[j] = float(np.sum(m[:, 0] + np.log(np.exp(x - m).sum(axis=1))))
+        forced = {f for f in (0, b - 1, b) if 0 <= f <= b}
+        rest = sorted((j for j in range(b + 1) if j not in forced), key=lambda j: (-sc[j], j))
+        out.append(forced | set(rest[:max(0, K - len(forced))]))
+    return out
+
+
+def tiny_diagnostics(torch, pisa, synth):
+    """The tiny workload (1024 tokens, 16 leaf blocks, K = 4, fp32): how much of the
+    brute-force all-leaf ranking the pruned walk on the GPU keeps (recall averaged over query
+    positions), and how often each planted needle's block is selected by the query it was
+    planted for, by the walk and by brute force."""
+    w = synth.WORKLOADS["tiny"]
+    q, k, needles = synth.make_inputs(w)
+    p = pisa.Problem(**w.shape())
+    qd, kd = dev(torch, q), dev(torch, k)
+    pyr = pisa.build_pyramid(p, kd)
+    idx, _ = pisa.select_prefill(p, qd, kd, pyr)
+    idx = idx.cpu().numpy()
+    s = 1.0 / np.sqrt(w.head_dim)
+    G = w.n_q_heads // w.n_kv_heads
+    recall, hits, bf_hits = [], 0, 0
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            bf = bruteforce_selection(q[b, h * G:(h + 1) * G].astype(np.float64), k[b, h].astype(np.float64),
+                                      w.top_k, w.block, s)
+            for i in range(w.seq_len):
+                got = {int(x) for x in idx[b, h, i] if x >= 0}
+                recall.append(len(got & bf[i]) / len(bf[i]))
+            for nb, nh, npos, _nq, nj in needles:
+                if nb == b and nh == h:
+                    hits += int(npos // w.block in set(idx[b, h, nj].tolist()))
+                    bf_hits += int(npos // w.block in bf[nj])
+    n = max(len(needles), 1)
+    return {"recall_vs_bruteforce": round(float(np.mean(recall)), 4), "needles": int(len(needles)),
+            "needle_hit_rate": round(hits / n, 4), "needle_hit_rate_bruteforce": round(bf_hits / n, 4)}
+
+
 def time_config(torch, pisa, synth, name, steps, warmup):
     """Prefill (pyramid build + selection) of one more workload, wall ms per step."""
     b = Prefill(torch, pisa, synth, name)
@@ -564,6 +616,8 @@ def main():
             extra["prefill_%s_ms" % name] = ms
             extra["prefill_%s_stages_ms" % name] = st
             log("%s: wall %.3f ms/step; stages %s" % (name, ms, st))
+        extra["tiny_diagnostics"] = tiny_diagnostics(torch, pisa, synth)
+        log("tiny diagnostics: %s" % extra["tiny_diagnostics"])
     if a.only in (None, "decode") and not a.no_decode:
         cold, warm, vcold, vwarm = time_decode(torch, pisa, synth, a.decode_steps)
         extra["decode_us_per_step"] = round(cold, 2)

@@ -12,7 +12,13 @@ to ``_build/kernel_resources.txt`` (VGPRs, scratch bytes per lane, waves per SIM
 fails when a kernel instantiation on the 16/4-head, d = 128 bf16 path spills to scratch
 (``HEADLINE``): a spill there costs HBM traffic on every launch.
 
-Usage: ``python -m block_selection_pyramid_amd.build [--force] [-j N]``.
+``build(sanitize=True)`` (``--sanitize``) makes a second library,
+``_build/san/libpisa_san.so``, whose host code (argument validation, workspace carving,
+launch set-up) is instrumented with AddressSanitizer and UndefinedBehaviorSanitizer; the
+device code is built as usual, without sanitizers.  It needs the ASan runtime preloaded and
+is meant for the CPU tests, which load it through ``PISA_LIB``.
+
+Usage: ``python -m block_selection_pyramid_amd.build [--force] [--sanitize] [-j N]``.
 """
 from __future__ import annotations
 
@@ -40,6 +46,12 @@ CXXFLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]
 
+
+# host-side sanitizers only: each flag goes to the host compile through -Xarch_host
+SAN_FLAGS = [f for x in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+                         "-fno-omit-frame-pointer", "-g") for f in ("-Xarch_host", x)]
+SAN_DIR = os.path.join(BUILD_DIR, "san")
+SAN_OUT = os.path.join(SAN_DIR, "libpisa_san.so")
 
 RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
 
@@ -102,31 +114,36 @@ def _deps() -> list[str]:
     return sources() + glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(INCLUDE, "*.h"))
 
 
-def up_to_date() -> bool:
-    if not os.path.exists(OUT):
+def up_to_date(out: str = OUT) -> bool:
+    if not os.path.exists(out):
         return False
-    t = os.path.getmtime(OUT)
+    t = os.path.getmtime(out)
     return all(os.path.getmtime(p) <= t for p in _deps())
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [hipcc(), *CXXFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_DIR if sanitize else BUILD_DIR, os.path.basename(src).replace(".hip", ".o"))
+    extra = SAN_FLAGS if sanitize else []
+    cmd = [hipcc(), *CXXFLAGS, *extra, "-Rpass-analysis=kernel-resource-usage", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr[-6000:]))
     return obj, _resources(r.stderr)
 
 
-def build(force: bool = True, jobs: int | None = None, verbose: bool = False) -> str:
-    """Compiles every HIP source for gfx950 and links libpisa.so.  Returns its path."""
-    if not force and up_to_date():
-        return OUT
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(force: bool = True, jobs: int | None = None, verbose: bool = False, sanitize: bool = False) -> str:
+    """Compiles every HIP source for gfx950 and links libpisa.so (with ``sanitize``, the
+    host-sanitized ``_build/san/libpisa_san.so``).  Returns its path."""
+    out = SAN_OUT if sanitize else OUT
+    if not force and up_to_date(out):
+        return out
+    os.makedirs(SAN_DIR if sanitize else BUILD_DIR, exist_ok=True)
     jobs = jobs or min(8, os.cpu_count() or 4)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        done = list(ex.map(_compile, sources()))
+        done = list(ex.map(lambda s: _compile(s, sanitize), sources()))
     objs = [o for o, _ in done]
+    if sanitize:
+        return _link(objs, out, SAN_FLAGS, verbose)
     res = sorted(r for _, rs in done for r in rs)
     with open(RESOURCES, "w") as f:
         for name, vgpr, scratch, occ in res:
@@ -135,23 +152,29 @@ def build(force: bool = True, jobs: int | None = None, verbose: bool = False) ->
     if spills:
         raise RuntimeError("headline kernels spill to scratch (see %s):\n%s" % (
             RESOURCES, "\n".join("%d B/lane  %s" % (r[2], r[0]) for r in spills)))
-    tmp = OUT + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    return _link(objs, OUT, [], verbose)
+
+
+def _link(objs: list[str], out: str, extra: list[str], verbose: bool) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-4000:]))
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print("built", OUT)
-    return OUT
+        print("built", out)
+    return out
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--force", action="store_true")
+    ap.add_argument("--sanitize", action="store_true", help="build the host-sanitized library instead")
     ap.add_argument("-j", type=int, default=None)
     a = ap.parse_args(argv)
-    build(force=a.force or not up_to_date(), jobs=a.j, verbose=True)
+    out = SAN_OUT if a.sanitize else OUT
+    build(force=a.force or not up_to_date(out), jobs=a.j, verbose=True, sanitize=a.sanitize)
 
 
 if __name__ == "__main__":

@@ -24,7 +24,9 @@ F32, BF16 = 0, 1
 PREFILL, DECODE = 0, 1
 LSE, PISA1, PISA2 = 0, 1, 2  # enum pisa_scorer
 MAX_LEVELS = 32
-LIB_PATH = _build.OUT
+# PISA_LIB names another build of the same sources to load instead (the CPU tests load the
+# host-sanitized build through it); without it, the in-tree libpisa.so
+LIB_PATH = os.environ.get("PISA_LIB") or _build.OUT
 
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error",
            5: "internal error"}
@@ -97,6 +99,8 @@ def load(path: str | None = None):
         return _lib
     p = path or LIB_PATH
     if not os.path.exists(p):
+        if p != _build.OUT:
+            raise FileNotFoundError("PISA_LIB names a missing library: %s" % p)
         _build.build(force=True)
     lib = ctypes.CDLL(p)
     P = ctypes.POINTER(_CProblem)

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(pisa):
         assert hasattr(lib, f), f
     assert set(pisa.EXPORTS) == set(declared_functions())
     # exported names are plain C symbols (extern "C")
-    out = os.popen("nm -D --defined-only %s" % pbuild.OUT).read()
+    out = os.popen("nm -D --defined-only %s" % pisa.LIB_PATH).read()
     for f in declared_functions():
         assert re.search(r"\bT %s$" % f, out, flags=re.M), f
 

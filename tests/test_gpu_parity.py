@@ -565,6 +565,22 @@ def _levels_offsets(pisa, N, B, Hq, Hkv, d, K, dtype):
     return L, nodes, offs
 
 
+def assert_levels_match_oracle(app, b, coff, k, n, w, what):
+    """The means of sequence b in the appended capacity pyramid `app` (level offsets coff)
+    against the fp64 oracle's pyramid of its first n keys, level by level, to the pyramid
+    tolerance (4e-6 absolute + 1e-6 relative)."""
+    op = oracle.Problem(batch=1, seq_len=n, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                        block=64, top_k=w.top_k, branch=2, dtype=w.dtype)
+    opyr = oracle.build_pyramid(op, np.ascontiguousarray(k[b:b + 1, :, :n]))
+    nodes = oracle.levels(n, 64, w.top_k, 2)
+    ooff = np.cumsum([0] + nodes[1:])
+    for l in range(1, len(nodes)):
+        a = app[0][b, :, coff[l - 1]:coff[l - 1] + nodes[l]].astype(np.float64)
+        o = opyr[0, :, ooff[l - 1]:ooff[l - 1] + nodes[l]]
+        err = np.abs(a - o)
+        assert np.all(err <= 4e-6 + 1e-6 * np.abs(o)), "%s level %d: max err %.3g" % (what, l, err.max())
+
+
 def assert_same_levels(app, b, coff, fr, foff, nodes, L, d, what):
     """Every node of levels 1..L of sequence b in the appended capacity pyramid `app` (level
     offsets coff) holds the same bits as in the fresh build `fr` (offsets foff): fp32 means
@@ -607,6 +623,7 @@ def test_append_keys_matches_fresh_build(env, dt, d):
             L, nodes, foff = _levels_offsets(pisa, n, 1, Hq, Hkv, d, K, dt)
             assert_same_levels(app, b, coff, fresh.cpu().numpy(), foff, nodes, L, d,
                                "sequence %d length %d" % (b, n))
+            assert_levels_match_oracle(app, b, coff, k, n, w, "sequence %d length %d" % (b, n))
         old = new
 
 
@@ -644,6 +661,7 @@ def test_append_single_keys_match_fresh_build(env):
             L, nodes, foff = _levels_offsets(pisa, n, 1, Hq, Hkv, d, K, dt)
             assert_same_levels(app, b, coff, fresh.cpu().numpy(), foff, nodes, L, d,
                                "step %d sequence %d length %d" % (step, b, n))
+            assert_levels_match_oracle(app, b, coff, k, n, w, "step %d sequence %d length %d" % (step, b, n))
         lengths = new
 
 
