@@ -98,10 +98,12 @@ __device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1
 #pragma unroll
   for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(a0[v], a1[v]));
   m = fmaxf(m, __shfl_xor(m, 32));
+  // exp(s (a - m)) as 2^(a s log2(e) - m s log2(e)): one fused multiply-add per key
+  const float ms = m * s_log2e;
   float sum = 0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v)
-    sum += __builtin_amdgcn_exp2f((a0[v] - m) * s_log2e) + __builtin_amdgcn_exp2f((a1[v] - m) * s_log2e);
+    sum += __builtin_amdgcn_exp2f(fmaf(a0[v], s_log2e, -ms)) + __builtin_amdgcn_exp2f(fmaf(a1[v], s_log2e, -ms));
   sum += __shfl_xor(sum, 32);
   return s * m + logf(sum);
 }

@@ -552,11 +552,12 @@ __device__ __forceinline__ float score_tile_mfma(const bf16* __restrict__ keys, 
     }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));  // key jC <= i is live, so mx is finite
+  const float ms = mx * s_log2e;
   float sum = 0.f;
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f((acc[rb][v] - mx) * s_log2e);
+    for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][v], s_log2e, -ms));
   sum += __shfl_xor(sum, 16);
   sum += __shfl_xor(sum, 32);
   const float lse = group_sum<G>(s * mx + logf(sum));  // lanes 0 .. G-1: the group's heads
