@@ -57,7 +57,8 @@
  * error before any HIP call), enqueue kernels on `stream` and return without
  * synchronising.  Faults inside kernels surface at the caller's next synchronisation.
  * Calls on one stream are ordered; concurrent calls must not share a workspace.  The
- * library keeps no state between calls and no C++ exception crosses this interface.
+ * library keeps no state between calls (apart from the device scratch of
+ * pisa_select_prefill_noalloc) and no C++ exception crosses this interface.
  */
 #ifndef PISA_H_
 #define PISA_H_
