@@ -7,13 +7,15 @@
 //
 // Decode ("Block Sparse Attention with Log-Linear Complexity", agihunt.info summary,
 // kernels paragraph: a single-stage kernel for decode avoids launch overhead; rcap.io
-// explainer: one query at a time leaves no cross-query tile reuse): one workgroup of 16
+// explainer: one query at a time leaves no cross-query tile reuse): one workgroup of 8
 // wavefronts per (sequence, KV head).  All of them first load the query rows and stage
 // the top pyramid levels' routing copy in LDS (one parallel burst); wavefront 0 then walks
-// the pyramid for the new query at position N-1, its top levels from LDS; then every
-// wavefront scores one of the <= 2K + 3 candidate and forced tiles (so their loads are in
-// flight together; bf16 on the matrix cores, 16 keys x 32 dims per MFMA against the G
-// head columns), and wavefront 0 writes the selection.  One launch per step.  With
+// the pyramid for the new query at position N-1, its top levels from LDS and two levels
+// per round of gathers below them (bf16: MfmaWalk::pair_step), while wavefronts 1..3 score
+// the forced tiles (known up front); then every wavefront scores two of the <= 2K routed
+// tiles with both tiles' loads in flight together (bf16 on the matrix cores, 16 keys x 32
+// dims per MFMA against the G head columns), and wavefront 0 writes the selection.  One
+// launch per step.  With
 // per-sequence lengths each workgroup first re-derives its sequence's level table in LDS
 // (node offsets stay those of the capacity layout that pisa_append_keys maintains).
 #include <type_traits>
@@ -62,7 +64,9 @@ __global__ __launch_bounds__(256) void qmajor_kernel(const T* __restrict__ q, co
   finalize_row(leaf, sc, F, nf, scs + twoK, geo.K, twoK, lane, out_idx + row * geo.K, out_score + row * geo.K);
 }
 
-constexpr int kDecodeWaves = 16;
+// Eight wavefronts: the two-level gathers of the walk (pair_step) and two routed tiles per
+// wavefront need up to 256 VGPRs per lane.
+constexpr int kDecodeWaves = 8;
 constexpr int64_t kDecodeStageBytes = 64 * 1024;  // LDS for the staged top levels
 
 template <int D, int G>
@@ -100,8 +104,9 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
 #pragma unroll
   for (int r = 0; r < G; ++r) rows[r] = q + ((int64_t)b * geo.Hq + h * G + r) * D;
 
-  // query rows (fp32, for the tile scoring) and the staged top levels, by all wavefronts
-  {
+  // query rows (fp32 in LDS for the VALU scoring of fp32 inputs; the bf16 path reads its
+  // MFMA fragments from q itself) and the staged top levels, by all wavefronts
+  if constexpr (!std::is_same<T, bf16>::value) {
     constexpr int VEC = Vec<T>::N;
     constexpr int PER_ROW = D / VEC;
     for (int t = threadIdx.x; t < G * PER_ROW; t += 64 * kDecodeWaves) {
@@ -119,11 +124,23 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
     sbase = stage_lo < geo.L ? geo.off[stage_lo] : 0;
     const int snodes = stage_lo < geo.L ? geo.off[geo.L] - sbase : 0;
     constexpr int kChunks = Walk::kRec / 16;  // 16-byte pieces per node
-    for (int t = threadIdx.x; t < snodes * kChunks; t += 64 * kDecodeWaves) {
-      const int nd = t / kChunks, c = t % kChunks;
-      const u32x4 v =
-          *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(R) + rc_piece_bytes(sbase + nd, c, D));
-      *reinterpret_cast<u32x4*>(stage + nd * Walk::kRecLds + 16 * c) = v;
+    constexpr int NT = 64 * kDecodeWaves;
+    // every thread's pieces loaded before the first is stored: one round trip, not one per
+    // piece (the staged levels fit kDecodeStageBytes, so kIt pieces per thread suffice)
+    constexpr int kIt = (int)(((kDecodeStageBytes / Walk::kRecLds) * kChunks + NT - 1) / NT);
+    const int npieces = snodes * kChunks;
+    u32x4 v[kIt];
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      const int t = threadIdx.x + u * NT;
+      v[u] = t < npieces ? *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(R) +
+                                                          rc_piece_bytes(sbase + t / kChunks, t % kChunks, D))
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kIt; ++u) {
+      const int t = threadIdx.x + u * NT;
+      if (t < npieces) *reinterpret_cast<u32x4*>(stage + (t / kChunks) * Walk::kRecLds + 16 * (t % kChunks)) = v[u];
     }
   }
   __syncthreads();
@@ -151,7 +168,7 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
       mw.stage_lo = stage_lo < geo.L ? stage_lo : 1 << 30;
       mw.stage_base = sbase;
       mw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
-      nx = mw.walk(geo, bq, &wlm, lane);
+      nx = mw.walk_pairs(geo, bq, &wlm, lane);
       X = wlm.X;
     } else {
       ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.Tp * D, qs};
@@ -168,10 +185,27 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
     score_tile(twoK + wave - 1, wave == 1 ? F[0] : (wave == 2 ? F[1] : F[2]));
   }
   __syncthreads();
-  // the routed leaf candidates (forced blocks excluded), at most one tile per wavefront
-  for (int t = wave; t < twoK; t += kDecodeWaves) {
-    const int j = tj[t];
-    if (j >= 0) score_tile(t, j);
+  // the routed leaf candidates (forced blocks excluded): tiles t and t + kDecodeWaves of a
+  // wavefront scored together (bf16), so their loads are in flight at once
+  for (int t = wave; t < twoK; t += 2 * kDecodeWaves) {
+    const int t2 = t + kDecodeWaves;
+    const int j0 = tj[t], j1 = t2 < twoK ? tj[t2] : -1;
+    if constexpr (std::is_same<T, bf16>::value) {
+      if (j0 >= 0 || j1 >= 0) {
+        MfmaWalk<D, G, 1> tw;
+        tw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
+        const int jt[2] = {j0, j1};
+        float sc2[2];
+        score_tiles_mfma<D, G, 2>(keys, jt, i, geo.N, geo.C, tw.qb[0], lane, geo.s, geo.s_log2e, sc2);
+        if (lane == 0) {
+          if (j0 >= 0) tsc[t] = sc2[0];
+          if (j1 >= 0) tsc[t2] = sc2[1];
+        }
+      }
+    } else {
+      if (j0 >= 0) score_tile(t, j0);
+      if (j1 >= 0) score_tile(t2, j1);
+    }
   }
   __syncthreads();
   if (wave == 0) {

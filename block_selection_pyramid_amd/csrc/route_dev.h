@@ -50,7 +50,7 @@ __device__ __forceinline__ uint64_t cand_key(float score, int node) {
 }
 
 template <int GPW>
-struct WalkLdsM {
+struct alignas(16) WalkLdsM {  // 16-byte aligned: key arrays are read two keys at a time
   int32_t X[kMaxCand];   // GPW groups x (64 / GPW) candidate slots
   uint64_t key[kMaxCand];
   // bounded-approximation walk (walk_levels<true>): approximate scores and their error
@@ -190,6 +190,11 @@ struct MfmaWalk {
     for (int t0 = 0; t0 < ntiles; t0 += TB) {
       bf16x8 hi[GPW][TB][KS], lo[GPW][TB][KS];
       load_batch<kLds, !kApprox>(geo, Lc, bq, l, nx, t0, Xs, lane, hi, lo);
+      // every load of the batch goes out before the first MFMA: left to itself the compiler
+      // interleaves them with the products and waits on the first few, so one level costs
+      // several round trips to L2 or HBM instead of one (G <= 4: with more heads per group
+      // the decode kernel would spill)
+      if constexpr (G <= 4) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb) {
         const int t = t0 + tb;
@@ -514,54 +519,227 @@ struct MfmaWalk {
     const int nx = init_level(geo, bq, geo.L, w, lane);
     return geo.L == 1 ? nx : walk_levels(geo, bq, geo.L, 2, nx, w, lane);
   }
+
+  // One query group per wavefront (decode): levels l and l - 1 (l >= 3) from one gather.
+  // A pyramid node is the plain mean of its children, so q.(child mean) is the mean of q
+  // over the grandchildren's means: the dots of the four level-(l-2) grandchildren
+  // 4y .. 4y+3 of every level-l candidate y give its score (LSE over its two children's
+  // averaged dots) and the scores of both of its children (LSE over their own children's
+  // dots), so the level-l Top-K and the level-(l-1) Top-K over the kept nodes' children
+  // need one round of gathers instead of two.  Tile t holds in row block rb the four
+  // grandchildren of candidate 4t + rb; lane (column m = head, row block kg) then holds
+  // candidate 4t + kg's four dots for head m.  X holds the level-l candidates on entry
+  // (nx slots) and the level-(l-2) candidates (children of the level-(l-1) nodes kept) on
+  // return; the function returns their slot count.  Uses key, sc, er, key2 and U of w.
+  template <bool kLds>
+  __device__ int pair_step(const Geo& geo, int bq, int l, int nx, WalkLdsM<GPW>* w, int lane) const {
+    static_assert(GPW == 1, "one query group per wavefront");
+    constexpr int PT = 4;  // tiles (16 candidates) per batch of gathers
+    const int K = geo.K;
+    const int lb = l - 2;  // level of the gathered nodes (>= 1)
+    const int nb = geo.n[lb];
+    const int sh = lb - 1;  // a level-lb node g covers leaf blocks from g << sh
+    const char* Lc = kLds ? lds + (int64_t)(geo.off[lb] - stage_base) * kRecLds : nullptr;
+    const int m = lane & 15, kg = lane >> 4;
+    const int rb = m >> 2, v = m & 3;  // loads: row block (candidate of the tile), grandchild
+    const float c2 = trunc_c2(geo.scorer, true);
+    const bool lse = geo.scorer == PISA_LSE;
+    auto pair = [&](float y0, float y1) {  // y0: a visible child's dot; y1: -inf if absent
+      const float a = fmaxf(y0, y1), b = fminf(y0, y1);
+      return lse ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a)) : pair_trunc(a, b, 1.f, c2);
+    };
+    const int ntiles = (nx + 3) >> 2;
+    for (int t0 = 0; t0 < ntiles; t0 += PT) {
+      bf16x8 hi[PT][KS], lo[PT][KS];
+      int ye[PT];  // epilogue: candidate 4 (t0 + tb) + kg of this lane, read with the loads
+#pragma unroll
+      for (int tb = 0; tb < PT; ++tb) {
+        const int xe = 4 * (t0 + tb) + kg;
+        ye[tb] = xe < nx ? w->X[xe] : -1;
+        const int x = 4 * (t0 + tb) + rb;
+        const int y = x < nx ? w->X[x] : -1;
+        const int gc = y >= 0 ? 4 * y + v : -1;
+        const int ca = (gc >= 0 && gc < nb) ? gc : 0;  // a missing grandchild reads node 0, never used
+        if constexpr (kLds) {
+          const char* rp = Lc + (int64_t)ca * kRecLds + 16 * kg;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            hi[tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s);
+            lo[tb][s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
+          }
+        } else {
+          const bf16* rp = R + rc_node(geo.off[lb] + ca, D) + rc_piece(kg);  // piece 4 s + kg
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            hi[tb][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
+            lo[tb][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the whole batch in flight before the first product
+      // every tile of the batch (those past the candidates gathered node 0 and are never
+      // written), with no branch between them so that their MFMA chains and epilogues
+      // interleave
+      f32x4 acc[PT];
+#pragma unroll
+      for (int tb = 0; tb < PT; ++tb) {
+        acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[tb][s], qb[0][s], acc[tb], 0, 0, 0);
+          acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[tb][s], qb[0][s], acc[tb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int tb = 0; tb < PT; ++tb) {
+        const f32x4 a = acc[tb];
+        const int x = 4 * (t0 + tb) + kg;
+        const int y = ye[tb];
+        const int g0 = 4 * y;
+        const bool e1 = g0 + 1 < nb, e2 = g0 + 2 < nb, e3 = g0 + 3 < nb;
+        const bool v1 = e1 && ((int64_t)(g0 + 1) << sh) <= bq;
+        const bool v2 = e2 && ((int64_t)(g0 + 2) << sh) <= bq;
+        const bool v3 = e3 && ((int64_t)(g0 + 3) << sh) <= bq;
+        // children 2y and 2y+1 (the latter exists iff 4y+2 does, is visible iff 4y+2 is):
+        // their dots are the means of their existing children's dots
+        const float d0 = e1 ? 0.5f * (a[0] + a[1]) : a[0];
+        const float d1 = e3 ? 0.5f * (a[2] + a[3]) : a[2];
+        const float sl = group_sum<G>(pair(d0, v2 ? d1 : -INFINITY));  // y at level l
+        const float s0 = group_sum<G>(pair(a[0], v1 ? a[1] : -INFINITY));  // 2y at level l - 1
+        const float s1 = group_sum<G>(pair(a[2], v3 ? a[3] : -INFINITY));  // 2y+1 (if v2)
+        if (m == 0 && x < nx) {
+          w->key[x] = y >= 0 ? cand_key(sl, y) : 0ull;
+          w->sc[x] = s0;
+          w->er[x] = s1;
+        }
+      }
+    }
+    w->key2[lane] = 0ull;
+    w->U[lane] = -1;
+    wave_sync();
+    // Top-K of level l; the kept node of rank r opens level-(l-1) slots 2r, 2r+1 (key[x] for
+    // x in [nx, nx rounded up to even) is 0 here or holds a candidate past nx: never larger)
+    {
+      const uint64_t my = lane < nx ? w->key[lane] : 0ull;
+      int rank = 0;
+#pragma unroll 4
+      for (int y = 0; y < nx; y += 2) {
+        const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(w->key + y);
+        rank += (kk.x > my) + (y + 1 < nx && kk.y > my);
+      }
+      if (my != 0ull && rank < K) {
+        const int y = w->X[lane];
+        const bool vis1 = child_visible(2 * y + 1, geo.n[l - 1], l - 2, bq);
+        w->U[2 * rank] = 2 * y;
+        w->key2[2 * rank] = cand_key(w->sc[lane], 2 * y);
+        w->U[2 * rank + 1] = vis1 ? 2 * y + 1 : -1;
+        w->key2[2 * rank + 1] = vis1 ? cand_key(w->er[lane], 2 * y + 1) : 0ull;
+      }
+    }
+    wave_sync();
+    // Top-K of level l - 1; the kept node of rank r opens level-(l-2) slots 2r, 2r+1
+    const uint64_t my = w->key2[lane];
+    int rank = 0;
+#pragma unroll 4
+    for (int y = 0; y < 2 * K && y < kMaxCand; y += 2) {
+      const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(w->key2 + y);
+      rank += (kk.x > my) + (kk.y > my);
+    }
+    const int z = w->U[lane];
+    const int nk = min(K, (int)__popcll(__ballot(my != 0ull)));
+    w->X[lane] = -1;
+    wave_sync();
+    if (my != 0ull && rank < K) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = 2 * z + c;
+        w->X[2 * rank + c] = child_visible(ch, geo.n[l - 2], l - 3, bq) ? ch : -1;
+      }
+    }
+    wave_sync();
+    return 2 * nk;
+  }
+
+  // The whole walk for one query group per wavefront, two levels per gather while at
+  // least two routing levels remain (pair_step), then the last one alone.
+  __device__ int walk_pairs(const Geo& geo, int bq, WalkLdsM<GPW>* w, int lane) const {
+    int nx = init_level(geo, bq, geo.L, w, lane);
+    int l = geo.L;
+    for (; l >= 3; l -= 2)
+      nx = l - 2 >= stage_lo ? pair_step<true>(geo, bq, l, nx, w, lane) : pair_step<false>(geo, bq, l, nx, w, lane);
+    return l == 2 ? walk_levels(geo, bq, 2, 2, nx, w, lane) : nx;
+  }
 };
 
-// Leaf score of tile j for one query group on the matrix cores (decode): A = 16 raw keys
-// x 32 dims of the tile (bf16 inputs are exact), B = the group's G head columns in the
+// Leaf scores of tiles j[0..NT) for one query group on the matrix cores (decode): A = 16 raw
+// keys x 32 dims of a tile (bf16 inputs are exact), B = the group's G head columns in the
 // MfmaWalk<D, G, 1> layout (column n = head n; k-step s, lane group kg = lane >> 4 <-> dims
 // 32s + 8kg .. +8; columns >= G are zero), four row blocks of 16 keys.  Lane l then holds
-// head l & 15 for keys 16rb + 4(l >> 4) + v.  Returns the head-summed causal LSE over the
-// keys t <= i (t < N) of the block, in natural units, in every lane.
+// head l & 15 for keys 16rb + 4(l >> 4) + v.  out[u] = the head-summed causal LSE over the
+// keys t <= i (t < N) of block j[u], in natural units, in every lane (a tile with j[u] < 0
+// reads block 0 and its result is meaningless).  Every tile's loads go out before the
+// first product, so the NT tiles cost one round trip.
+template <int D, int G, int NT>
+__device__ __forceinline__ void score_tiles_mfma(const bf16* __restrict__ keys, const int (&jt)[NT], int i, int N,
+                                                 int C, const bf16x8 (&qb)[D / 32], int lane, float s, float s_log2e,
+                                                 float (&out)[NT]) {
+  constexpr int KS = D / 32;
+  const int m = lane & 15, kg = lane >> 4;
+  bf16x8 a[NT][4][KS];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int j = jt[u] >= 0 ? jt[u] : 0;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const int t = min(j * C + 16 * rb + m, N - 1);  // rows past N read a real key; masked below
+#pragma unroll
+      for (int k = 0; k < KS; ++k) a[u][rb][k] = *reinterpret_cast<const bf16x8*>(keys + (int64_t)t * D + 32 * k + 8 * kg);
+    }
+  }
+  // the tiles' loads in flight before the first product (G <= 4: with more heads the
+  // decode kernel would spill)
+  if constexpr (G <= 4) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int j = jt[u] >= 0 ? jt[u] : 0;
+    f32x4 acc[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KS; ++k) acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][rb][k], qb[k], acc[rb], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = j * C + 16 * rb + 4 * kg + v;
+        if (t > i || t >= N) acc[rb][v] = -INFINITY;
+        mx = fmaxf(mx, acc[rb][v]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // key jC <= i is live, so mx is finite
+    const float ms = mx * s_log2e;
+    float sum = 0.f;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][v], s_log2e, -ms));
+    sum += __shfl_xor(sum, 16);
+    sum += __shfl_xor(sum, 32);
+    const float lse = group_sum<G>(s * mx + logf(sum));  // lanes 0 .. G-1: the group's heads
+    out[u] = __shfl(lse, 0);
+  }
+}
+
 template <int D, int G>
 __device__ __forceinline__ float score_tile_mfma(const bf16* __restrict__ keys, int j, int i, int N, int C,
                                                  const bf16x8 (&qb)[D / 32], int lane, float s, float s_log2e) {
-  constexpr int KS = D / 32;
-  const int m = lane & 15, kg = lane >> 4;
-  bf16x8 a[4][KS];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const int t = min(j * C + 16 * rb + m, N - 1);  // rows past N read a real key; masked below
-#pragma unroll
-    for (int k = 0; k < KS; ++k) a[rb][k] = *reinterpret_cast<const bf16x8*>(keys + (int64_t)t * D + 32 * k + 8 * kg);
-  }
-  f32x4 acc[4];
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < KS; ++k) acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb][k], qb[k], acc[rb], 0, 0, 0);
-  }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int t = j * C + 16 * rb + 4 * kg + v;
-      if (t > i || t >= N) acc[rb][v] = -INFINITY;
-      mx = fmaxf(mx, acc[rb][v]);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));  // key jC <= i is live, so mx is finite
-  const float ms = mx * s_log2e;
-  float sum = 0.f;
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][v], s_log2e, -ms));
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
-  const float lse = group_sum<G>(s * mx + logf(sum));  // lanes 0 .. G-1: the group's heads
-  return __shfl(lse, 0);
+  const int jt[1] = {j};
+  float out[1];
+  score_tiles_mfma<D, G, 1>(keys, jt, i, N, C, qb, lane, s, s_log2e, out);
+  return out[0];
 }
 
 // ---------------------------------------------------------------- VALU scorer
