@@ -242,6 +242,12 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int VTR = kLeaf + 8;  // padded row (keys) of the transposed value tile
   constexpr int OSR = D + 8;      // padded row of a wavefront's staged output
+  // the chunk's entries (-1 past its end) in LDS while they take at most 4 KB (G >= 4); with
+  // fewer heads per group the chunk is longer and its copy would cost a workgroup per CU
+  constexpr bool kLdsEnt = QC <= 1024;
+  constexpr int EPT = kLdsEnt ? QC / 256 : 1;
+  static_assert(!kLdsEnt || QC % 256 == 0, "the chunk's entries split evenly over the threads");
+  __shared__ int32_t ents[kLdsEnt ? QC : 1];
   __shared__ __attribute__((aligned(16))) bf16 kt[kLeaf * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 vt[D * VTR];
   __shared__ __attribute__((aligned(16))) bf16 os_all[4][32 * OSR];
@@ -265,7 +271,9 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   const int r = col % G;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
   const bf16* qh = q + ((int64_t)b * geo.Hq + h * G + r) * N * D;
-  // entry of this lane's column in column group u of the wavefront (-1: none)
+  // entry of this lane's column in column group u of the wavefront (-1: none): the first
+  // from global memory, the others from the chunk's copy in LDS (loaded with the tiles, so
+  // no column group waits on a global round trip for its entry index)
   auto entry = [&](int u) {
     const int e = e0 + (u * 4 + wave) * EW + col / G;
     return e < e1 ? entries[e] : -1;
@@ -273,6 +281,14 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   int ent = entry(0);
   bf16x8 bq[KS];
   load_bfrag<D>(qh + (int64_t)max(ent >> 6, 0) * D, ent >= 0, hh, bq);
+  int ev[EPT];
+  if constexpr (kLdsEnt) {
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) {
+      const int t = threadIdx.x + 256 * x;
+      ev[x] = e0 + t < e1 ? entries[e0 + t] : -1;
+    }
+  }
 
   stage_tile<D>(k + (int64_t)bh * N * D, j * kLeaf, N, kt);
   {  // value tile, transposed: vt[dim][key] (zeros past N)
@@ -288,6 +304,10 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
       }
     }
   }
+  if constexpr (kLdsEnt) {
+#pragma unroll
+    for (int x = 0; x < EPT; ++x) ents[threadIdx.x + 256 * x] = ev[x];
+  }
   __syncthreads();
 
   int64_t* px = px_all[wave];
@@ -295,7 +315,8 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   const float sl = geo.s_log2e;
   for (int u = 0; u < NCG; ++u) {
     if (e0 + (u * 4 + wave) * EW >= e1) break;  // uniform across the wavefront
-    const int ent_n = u + 1 < NCG ? entry(u + 1) : -1;
+    int ent_n = -1;
+    if (u + 1 < NCG) ent_n = kLdsEnt ? ents[((u + 1) * 4 + wave) * EW + col / G] : entry(u + 1);
     bf16x8 bqn[KS];
     load_bfrag<D>(qh + (int64_t)max(ent_n >> 6, 0) * D, ent_n >= 0, hh, bqn);
     const bool valid = ent >= 0;

@@ -51,7 +51,10 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   constexpr int QC = 4 * NCG * CPG;
   constexpr int KS = D / 16;
   constexpr int LDSR = D + 8;
+  constexpr int EPT = QC / 256;  // chunk entries per thread
+  static_assert(QC % 256 == 0, "the chunk's entries split evenly over the threads");
   __shared__ __attribute__((aligned(16))) bf16 kt[2 * kLeaf * LDSR];
+  __shared__ int32_t ents[QC];  // the chunk's entries (-1 past its end)
 
   const int c = blockIdx.x;
   if (c >= choff[M]) return;  // uniform: the grid is an upper bound on the chunk count
@@ -76,7 +79,9 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
                       : q + ((int64_t)b * geo.Hq + h * G + r) * geo.N * D + 8 * hh;
   const int64_t qrow = qg ? G * D : D;
   const int qstep = qg ? 16 * G : 16;
-  // entry of this lane's column in column group u of the wavefront (-1: none)
+  // entry of this lane's column in column group u of the wavefront (-1: none): the first
+  // from global memory, the others from the chunk's copy in LDS (loaded with the key
+  // tiles, so no column group waits on a global round trip for its entry index)
   auto entry = [&](int u) {
     const int e = e0 + (u * 4 + wave) * CPG + col / G;
     return e < e1 ? entries[e] : -1;
@@ -85,11 +90,19 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   bf16x8 bq[KS];
   // query fragments first: their latency overlaps the key-tile staging
   load_bfrag_step<D>(qh + (ent >> 6) * qrow, ent >= 0, qstep, bq);
+  int ev[EPT];
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) {
+    const int t = threadIdx.x + 256 * x;
+    ev[x] = e0 + t < e1 ? entries[e0 + t] : -1;
+  }
 
   const bf16* kb = k + (int64_t)bh * geo.N * D;
   const bool two = 2 * m + 1 < geo.n1;  // the node's second child exists
   stage_tile<D>(kb, 2 * m * kLeaf, geo.N, kt);
   if (two) stage_tile<D>(kb, (2 * m + 1) * kLeaf, geo.N, kt + kLeaf * LDSR);
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) ents[threadIdx.x + 256 * x] = ev[x];
   __syncthreads();
   // keys present in each child (>= 1); only a short last block masks
   const int live0 = min(kLeaf, geo.N - 2 * m * kLeaf);
@@ -98,7 +111,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
 
   for (int u = 0; u < NCG; ++u) {
     if (e0 + (u * 4 + wave) * CPG >= e1) break;  // uniform across the wavefront
-    const int ent_n = u + 1 < NCG ? entry(u + 1) : -1;
+    const int ent_n = u + 1 < NCG ? ents[((u + 1) * 4 + wave) * CPG + col / G] : -1;
     bf16x8 bqn[KS];
     load_bfrag_step<D>(qh + (ent_n >> 6) * qrow, ent_n >= 0, qstep, bqn);
 
