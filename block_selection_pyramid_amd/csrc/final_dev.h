@@ -22,15 +22,35 @@ __device__ __forceinline__ int key_row(int v, int hh) { return 8 * (v >> 2) + 4 
 
 // Stages rows [row0, row0 + 64) of one (b,h)'s keys into LDS (zero past N).
 template <int D>
-__device__ __forceinline__ void stage_tile(const bf16* __restrict__ kb, int row0, int N, bf16* kt) {
-  constexpr int LDSR = D + 8;
-  constexpr int TPR = D / 8;
-  for (int t = threadIdx.x; t < kLeaf * TPR; t += 256) {
-    const int r = t / TPR, c = (t % TPR) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row0 + r < N) v = *reinterpret_cast<const uint4*>(kb + (int64_t)(row0 + r) * D + c);
-    *reinterpret_cast<uint4*>(kt + r * LDSR + c) = v;
+// A key tile staged by a workgroup of 256 threads in two phases, so that several tiles'
+// loads (and other loads of the caller) are in flight together before the first store.
+template <int D>
+struct KeyTile {
+  static constexpr int LDSR = D + 8;
+  static constexpr int TPR = D / 8;                 // 16-byte pieces per key row
+  static constexpr int NP = kLeaf * TPR / 256;      // pieces per thread
+  static_assert(kLeaf * TPR % 256 == 0, "a tile splits evenly over 256 threads");
+  uint4 v[NP];
+  __device__ __forceinline__ void load(const bf16* __restrict__ kb, int row0, int N) {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int t = threadIdx.x + 256 * u, r = t / TPR, c = (t % TPR) * 8;
+      v[u] = row0 + r < N ? *reinterpret_cast<const uint4*>(kb + (int64_t)(row0 + r) * D + c) : make_uint4(0, 0, 0, 0);
+    }
   }
+  __device__ __forceinline__ void store(bf16* kt) const {
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int t = threadIdx.x + 256 * u, r = t / TPR, c = (t % TPR) * 8;
+      *reinterpret_cast<uint4*>(kt + r * LDSR + c) = v[u];
+    }
+  }
+};
+template <int D>
+__device__ __forceinline__ void stage_tile(const bf16* __restrict__ kb, int row0, int N, bf16* kt) {
+  KeyTile<D> t;
+  t.load(kb, row0, N);
+  t.store(kt);
 }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {

@@ -99,8 +99,11 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
 
   const bf16* kb = k + (int64_t)bh * geo.N * D;
   const bool two = 2 * m + 1 < geo.n1;  // the node's second child exists
-  stage_tile<D>(kb, 2 * m * kLeaf, geo.N, kt);
-  if (two) stage_tile<D>(kb, (2 * m + 1) * kLeaf, geo.N, kt + kLeaf * LDSR);
+  KeyTile<D> ta, tb;  // both tiles' loads in flight before either is stored
+  ta.load(kb, 2 * m * kLeaf, geo.N);
+  if (two) tb.load(kb, (2 * m + 1) * kLeaf, geo.N);
+  ta.store(kt);
+  if (two) tb.store(kt + kLeaf * LDSR);
 #pragma unroll
   for (int x = 0; x < EPT; ++x) ents[threadIdx.x + 256 * x] = ev[x];
   __syncthreads();
@@ -182,10 +185,15 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
   float cv[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
+    // the slot's candidate and score loaded together (the score is only used where the
+    // slot holds a candidate; elsewhere it reads an in-bounds stale value)
     const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
-    const int64_t row = (int64_t)bh * geo.N + i;
-    cl[p] = (i < geo.N && slot < twoK) ? cand[row * twoK + slot] : -1;
-    cv[p] = cl[p] >= 0 ? lscore[row * twoK + slot] : -INFINITY;
+    const bool in = i < geo.N && slot < twoK;
+    const int64_t e = in ? ((int64_t)bh * geo.N + i) * twoK + slot : 0;
+    const int c = cand[e];
+    const float v = lscore[e];
+    cl[p] = in ? c : -1;
+    cv[p] = cl[p] >= 0 ? v : -INFINITY;
   }
 
   // 64 queries x G heads = 2G groups of 32 columns; this wavefront takes cg = wave + 4m
@@ -198,7 +206,15 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
   load_bfrag<D>(qrow(wave), qvalid(wave), hh, bfr);
 
   const bf16* kb = k + (int64_t)bh * geo.N * D;
-  for (int f = 0; f < nf; ++f) stage_tile<D>(kb, F[f] * kLeaf, geo.N, kt[f]);
+  {  // the forced tiles' loads all in flight before the first is stored
+    KeyTile<D> tl[3];
+#pragma unroll
+    for (int f = 0; f < 3; ++f)
+      if (f < nf) tl[f].load(kb, F[f] * kLeaf, geo.N);
+#pragma unroll
+    for (int f = 0; f < 3; ++f)
+      if (f < nf) tl[f].store(kt[f]);
+  }
   __syncthreads();
 
   for (int cg = wave; cg < 2 * G; cg += 4) {
@@ -263,10 +279,15 @@ __global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __re
   float cv[PASSES];
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
+    // the slot's candidate and score loaded together (the score is only used where the
+    // slot holds a candidate; elsewhere it reads an in-bounds stale value)
     const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
-    const int64_t row = (int64_t)bh * geo.N + i;
-    cl[p] = (i < geo.N && slot < twoK) ? cand[row * twoK + slot] : -1;
-    cv[p] = cl[p] >= 0 ? lscore[row * twoK + slot] : -INFINITY;
+    const bool in = i < geo.N && slot < twoK;
+    const int64_t e = in ? ((int64_t)bh * geo.N + i) * twoK + slot : 0;
+    const int c = cand[e];
+    const float v = lscore[e];
+    cl[p] = in ? c : -1;
+    cv[p] = cl[p] >= 0 ? v : -INFINITY;
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
