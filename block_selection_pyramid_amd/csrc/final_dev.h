@@ -20,10 +20,9 @@ __device__ __forceinline__ int key_row(int v, int hh) { return 8 * (v >> 2) + 4 
 // (l >> 5); its 16 results are column (l & 31), rows key_row(v, l >> 5).  The head
 // dimension is walked as k-step s, group hh -> dims 16s + 8hh .. +8 for A and B alike.
 
-// Stages rows [row0, row0 + 64) of one (b,h)'s keys into LDS (zero past N).
-template <int D>
-// A key tile staged by a workgroup of 256 threads in two phases, so that several tiles'
-// loads (and other loads of the caller) are in flight together before the first store.
+// Rows [row0, row0 + 64) of one (b,h)'s keys (zero past N) staged into LDS by a workgroup
+// of 256 threads in two phases, so that several tiles' loads (and other loads of the
+// caller) are in flight together before the first store.
 template <int D>
 struct KeyTile {
   static constexpr int LDSR = D + 8;
