@@ -210,20 +210,26 @@ class Prefill:
         self.step()
         out = torch.empty_like(self.q)
         lse = torch.empty(self.q.shape[:-1], dtype=torch.float32, device="cuda")
-        aws = torch.empty(max(pisa.attention_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
-        for _ in range(warmup):
-            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse, ws=aws)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(steps):
-            pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse, ws=aws)
-        b.record()
-        b.synchronize()
-        ms = a.elapsed_time(b) / steps
+        res = {}
+        # the one-pass workspace, then a 2 GiB one (passes over query ranges)
+        for tag, nbytes in (("", pisa.attention_workspace_bytes(p)), ("_2gib_ws", min(2 << 30, pisa.attention_workspace_bytes(p)))):
+            aws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+            for _ in range(warmup):
+                pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse, ws=aws)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(steps):
+                pisa.sparse_attention(p, self.q, self.k, v, self.oi, out=out, lse=lse, ws=aws)
+            b.record()
+            b.synchronize()
+            res["ms" + tag] = round(a.elapsed_time(b) / steps, 4)
+            res["workspace_GB" + tag] = round(nbytes / 1e9, 3)
+            del aws
         pairs = int((self.oi >= 0).sum().item())
         tile_bytes = pairs * 2 * p.block * p.head_dim * 2
-        return {"ms": round(ms, 4), "pairs": pairs, "tile_GBps": round(tile_bytes / (ms * 1e-3) / 1e9, 1)}
+        res.update({"pairs": pairs, "tile_GBps": round(tile_bytes / (res["ms"] * 1e-3) / 1e9, 1)})
+        return res
 
     def work(self):
         """Algorithmic work of each stage for one step: (bytes, flops).  Bytes are the

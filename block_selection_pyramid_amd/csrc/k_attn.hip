@@ -191,13 +191,15 @@ int attn_g(const Geo& g, const void* q, const void* k, const void* v, const int3
 
 // Candidate array of the pairs (per_row = K slots per query group, -1 where the slot is
 // padding, names a block after the query's own or one of its forced blocks) and their
-// count per (b, h, block).
-__global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restrict__ idx, Geo geo,
+// count per list (range, b h, block): query i belongs to range i / R (R a multiple of
+// kLeafQueries, so a workgroup's queries share one range).
+__global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restrict__ idx, Geo geo, int32_t R,
                                                         int32_t* __restrict__ cand, int32_t* __restrict__ cnt) {
   extern __shared__ __attribute__((aligned(16))) int hist[];
   const int BH = geo.B * geo.Hkv, K = geo.K;
   const int bh = blockIdx.x % BH;
   const int q0 = (blockIdx.x / BH) * kLeafQueries, q1 = min(geo.N, q0 + kLeafQueries);
+  const int lrow = (q0 / R) * BH + bh;  // this workgroup's lists: lrow * n1 + block
   const bool lhist = geo.n1 <= kHistMaxBins;
   if (lhist) {
     for (int t = threadIdx.x; t < geo.n1; t += 256) hist[t] = 0;
@@ -213,13 +215,13 @@ __global__ __launch_bounds__(256) void attn_cand_kernel(const int32_t* __restric
     cand[base + t] = ok ? j : -1;
     if (ok) {
       if (lhist) atomicAdd(&hist[j], 1);
-      else atomicAdd(&cnt[bh * geo.n1 + j], 1);
+      else atomicAdd(&cnt[lrow * geo.n1 + j], 1);
     }
   }
   if (lhist) {
     __syncthreads();
     for (int t = threadIdx.x; t < geo.n1; t += 256)
-      if (hist[t]) atomicAdd(&cnt[bh * geo.n1 + t], hist[t]);
+      if (hist[t]) atomicAdd(&cnt[lrow * geo.n1 + t], hist[t]);
   }
 }
 
@@ -234,8 +236,11 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
                                                          const bf16* __restrict__ v, Geo geo,
                                                          const int32_t* __restrict__ off,
                                                          const int32_t* __restrict__ choff,
-                                                         const int32_t* __restrict__ entries, int32_t M,
+                                                         const int32_t* __restrict__ entries, int32_t Mlo,
+                                                         int32_t Mhi, int32_t i0, int32_t R,
                                                          float* __restrict__ plse, bf16* __restrict__ po) {
+  // one query range: lists [Mlo, Mhi) (those of queries i0 .. i0 + R - 1); the partials of
+  // query i of (b, h) sit at row b h * R + (i - i0) of the range's partial buffers
   constexpr int EW = 32 / G;                    // pairs per column group
   constexpr int NCG = kAttnColGroups;
   constexpr int QC = 4 * NCG * EW;              // pairs per chunk (workgroup)
@@ -253,15 +258,15 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
   __shared__ __attribute__((aligned(16))) bf16 os_all[4][32 * OSR];
   __shared__ int64_t px_all[4][32];
 
-  const int c = blockIdx.x;
-  if (c >= choff[M]) return;  // uniform: grid is an upper bound on the chunk count
-  int lo = 0, hi = M;         // largest list whose first chunk is <= c
+  const int c = choff[Mlo] + blockIdx.x;
+  if (c >= choff[Mhi]) return;  // uniform: grid is an upper bound on the range's chunk count
+  int lo = Mlo, hi = Mhi;        // largest list whose first chunk is <= c
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (choff[mid] <= c) lo = mid; else hi = mid;
   }
   const int list = lo;
-  const int bh = list / geo.n1, j = list % geo.n1;
+  const int bh = (list / geo.n1) % (geo.B * geo.Hkv), j = list % geo.n1;
   const int e0 = off[list] + (c - choff[list]) * QC;
   const int e1 = min(e0 + QC, off[list + 1]);
   const int N = geo.N, K = geo.K;
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
     // O^T: lane (col, hh) holds dims 32 db + 8 a + 4 hh .. +3 of its own column's output
     // row in ao[db][4a .. 4a+3]
     if (hh == 0) {
-      const int64_t pi = ((((int64_t)bh * N + i) * K + slot) * G + r);
+      const int64_t pi = ((((int64_t)bh * R + (i - i0)) * K + slot) * G + r);
       px[col] = valid ? pi : -1;
       if (valid) plse[pi] = mx + __builtin_amdgcn_logf(sum);
     }
@@ -456,19 +461,22 @@ __device__ __forceinline__ int forced_slot(int j) { return j == 0 ? 0 : 1 + j % 
 template <int D, int G>
 __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                           const bf16* __restrict__ v, Geo geo,
-                                                          const int32_t* __restrict__ idx, int run,
-                                                          float* __restrict__ pfl, bf16* __restrict__ pfo) {
+                                                          const int32_t* __restrict__ idx, int run, int b0,
+                                                          int b1, int i0, int R, float* __restrict__ pfl,
+                                                          bf16* __restrict__ pfo) {
+  // one query range: leaf blocks [b0, b1) (queries i0 .. i0 + R - 1); the partial of query i
+  // of (b, h) sits at row b h * R + (i - i0) of the range's buffers
   static_assert(D % 64 == 0, "ForcedTile spreads a tile over 512 threads in whole pieces");
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int VTR = kLeaf + 8;
   __shared__ __attribute__((aligned(16))) bf16 kt[4][kLeaf * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 vt[4][D * VTR];
   __shared__ uint32_t pres[2][kLeaf];  // bit x: the query's selection names forced block x
-  const int nruns = (geo.n1 + run - 1) / run;
+  const int nruns = (b1 - b0 + run - 1) / run;
   const int bh = blockIdx.x / nruns;  // one-dimensional grid: B * Hkv may exceed a y extent
   const int N = geo.N, K = geo.K;
   const int b = bh / geo.Hkv, h = bh % geo.Hkv;
-  const int bs = (blockIdx.x % nruns) * run, be = min(bs + run, geo.n1);
+  const int bs = b0 + (blockIdx.x % nruns) * run, be = min(bs + run, b1);
   const bf16* kb = k + (int64_t)bh * N * D;
   const bf16* vb = v + (int64_t)bh * N * D;
   auto presence = [&](int bq, uint32_t* dst) {
@@ -585,7 +593,7 @@ __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict
         }
       }
       if (valid) {
-        const int64_t prow = ((int64_t)bh * N + i) * G + r;
+        const int64_t prow = ((int64_t)bh * R + (i - i0)) * G + r;
         if (hh == 0) pfl[prow] = lrun > 0.f ? mrun + __builtin_amdgcn_logf(lrun) : -INFINITY;
         const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
         bf16* dst = pfo + prow * D + 4 * hh;
@@ -622,17 +630,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
                                                          const bf16* __restrict__ po,
                                                          const float* __restrict__ pfl,
                                                          const bf16* __restrict__ pfo, bf16* __restrict__ out,
-                                                         float* __restrict__ lse) {
+                                                         float* __restrict__ lse, int i0, int nq, int R) {
+  // one query range: queries i0 .. i0 + nq - 1 of every (b, h); their partials sit at rows
+  // b h * R + (i - i0) of the range's buffers
   constexpr int LPH = D / 8;       // lanes per head row (16 bytes each)
   constexpr int HP = 64 / LPH;     // heads per pass
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int N = geo.N, K = geo.K;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-  if (row >= (int64_t)geo.B * geo.Hkv * N) return;  // whole wavefront; no barrier follows
-  const int bh = (int)(row / N), i = (int)(row % N);
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave;
+  if (w >= (int64_t)geo.B * geo.Hkv * nq) return;  // whole wavefront; no barrier follows
+  const int bh = (int)(w / nq), i = i0 + (int)(w % nq);
+  const int64_t row = (int64_t)bh * N + i;       // the selection's row
+  const int64_t prow = (int64_t)bh * R + (i - i0);  // the partials' row
   const int b = bh / geo.Hkv, h = bh % geo.Hkv, bq = i / geo.C;
   const int KG = K * G;
-  const float* lrow = plse + row * KG;
+  const float* lrow = plse + prow * KG;
   float x0 = -INFINITY, x1 = -INFINITY;
   if (lane < KG) {
     const int jb = idx[row * K + lane / G];
@@ -657,8 +669,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
     const bool live = r < G;
     const int rr = live ? r : 0;  // idle lanes shadow head 0 so every lane takes part in the shuffles
     // the forced blocks' combined partial of this head (attn_forced_kernel)
-    const float lf = pfl[row * G + rr];
-    const u32x4 fr = *reinterpret_cast<const u32x4*>(pfo + (row * G + rr) * D + dl);
+    const float lf = pfl[prow * G + rr];
+    const u32x4 fr = *reinterpret_cast<const u32x4*>(pfo + (prow * G + rr) * D + dl);
     float mx = lf;
     for (int u = 0; u < K; ++u) mx = fmaxf(mx, xat(u * G + rr));
     float l = 0.f, acc[8];
@@ -680,7 +692,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const int32_t* __restri
       // slots without a partial (forced blocks, padding, blocks after the query's) are not
       // read: the slot's block is the same for every lane, so this is uniform in practice
       u32x4 pr = {0u, 0u, 0u, 0u};
-      if (wu > 0.f) pr = *reinterpret_cast<const u32x4*>(po + (row * KG + t) * D + dl);
+      if (wu > 0.f) pr = *reinterpret_cast<const u32x4*>(po + (prow * KG + t) * D + dl);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = bf2f(pr[e] & 0xFFFFu), hi = bf2f(pr[e] >> 16);
@@ -712,33 +724,47 @@ int attn_km_g(const Geo& g, const bf16* q, const bf16* k, const bf16* v, const i
   int32_t* entries = (int32_t*)(ws + w.entries);
   float* plse = (float*)(ws + w.plse);
   bf16* po = (bf16*)(ws + w.po);
+  float* pfl = (float*)(ws + w.pfl);
+  bf16* pfo = (bf16*)(ws + w.pfo);
+  const int BH = g.B * g.Hkv, R = w.R;
   int rc;
   if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
-  const unsigned cgrid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
+  const unsigned cgrid = (unsigned)(BH * ((g.N + kLeafQueries - 1) / kLeafQueries));
   const size_t hbytes = g.n1 <= kHistMaxBins ? sizeof(int) * (size_t)g.n1 : 0;
-  attn_cand_kernel<<<cgrid, 256, hbytes, st>>>(idx, g, cand, cnt);
+  attn_cand_kernel<<<cgrid, 256, hbytes, st>>>(idx, g, R, cand, cnt);
   if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
   const int qc = 4 * kAttnColGroups * 32 / G;  // pairs per chunk
   if ((rc = launch_scan(cnt, w.M, qc, off, choff, st)) != PISA_OK) return rc;
-  if ((rc = launch_scatter(g, g.K, cand, off, cursor, entries, st)) != PISA_OK) return rc;
-  const int64_t grid = (w.slots + qc - 1) / qc + w.M;  // bound on the chunk count
-  attn_chunk_kernel<D, G><<<(unsigned)grid, 256, 0, st>>>(q, k, v, g, off, choff, entries, w.M, plse, po);
-  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
-  float* pfl = (float*)(ws + w.pfl);
-  bf16* pfo = (bf16*)(ws + w.pfo);
+  if ((rc = launch_scatter(g, g.K, R, cand, off, cursor, entries, st)) != PISA_OK) return rc;
   const int run = forced_run(g);
-  const unsigned fgrid = (unsigned)(((g.n1 + run - 1) / run) * (int64_t)g.B * g.Hkv);
-  attn_forced_kernel<D, G><<<fgrid, 512, 0, st>>>(q, k, v, g, idx, run, pfl, pfo);
-  if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
-  const int64_t rows = (int64_t)g.B * g.Hkv * g.N;
-  attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, pfl, pfo, out, lse);
-  return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
+  // one pass per query range (one in all with the full workspace): the chunk kernel writes
+  // the range's pair partials, the forced kernel its forced partials, the merge its output
+  for (int i0 = 0; i0 < g.N; i0 += R) {
+    const int i1 = std::min(g.N, i0 + R), nq = i1 - i0;
+    const int32_t Mlo = (i0 / R) * BH * g.n1, Mhi = Mlo + BH * g.n1;
+    // chunks of the range: at most its pairs / qc plus one per list that can be non-empty
+    // (blocks up to the range's last query)
+    const int64_t lists = (int64_t)BH * std::min(g.n1, (i1 - 1) / kLeaf + 1);
+    const int64_t grid = ((int64_t)BH * nq * g.K + qc - 1) / qc + lists;
+    attn_chunk_kernel<D, G><<<(unsigned)grid, 256, 0, st>>>(q, k, v, g, off, choff, entries, Mlo, Mhi, i0, R, plse,
+                                                            po);
+    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+    const int b0 = i0 / kLeaf, b1 = std::min(g.n1, (i1 + kLeaf - 1) / kLeaf);
+    const unsigned fgrid = (unsigned)(((b1 - b0 + run - 1) / run) * (int64_t)BH);
+    attn_forced_kernel<D, G><<<fgrid, 512, 0, st>>>(q, k, v, g, idx, run, b0, b1, i0, R, pfl, pfo);
+    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+    const int64_t rows = (int64_t)BH * nq;
+    attn_merge_kernel<D, G><<<(unsigned)((rows + 3) / 4), 256, 0, st>>>(idx, g, plse, po, pfl, pfo, out, lse, i0, nq,
+                                                                          R);
+    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  }
+  return PISA_OK;
 }
 
 template <int D>
 int attn_km_d(const Geo& g, const void* q, const void* k, const void* v, const int32_t* idx, void* ws,
-              void* out, float* lse, hipStream_t st) {
-  const AttnWs w = attention_ws(g);
+              int32_t R, void* out, float* lse, hipStream_t st) {
+  const AttnWs w = attention_ws(g, R);
   const bf16 *qq = (const bf16*)q, *kk = (const bf16*)k, *vv = (const bf16*)v;
   bf16* oo = (bf16*)out;
   char* wc = (char*)ws;
@@ -756,11 +782,19 @@ int attn_km_d(const Geo& g, const void* q, const void* k, const void* v, const i
 
 bool attention_key_major(const Geo& g, int dtype, int decode) { return dtype == PISA_BF16 && !decode; }
 
-AttnWs attention_ws(const Geo& g) {
+AttnWs attention_ws(const Geo& g, int32_t R) {
   AttnWs w;
   auto align256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  w.slots = (int64_t)g.B * g.Hkv * g.N * g.K;
-  w.M = g.B * g.Hkv * g.n1;
+  const int64_t BH = (int64_t)g.B * g.Hkv;
+  w.R = R;
+  w.slots = BH * g.N * g.K;
+  const int64_t M = ((g.N + R - 1) / R) * BH * g.n1;
+  if (R <= 0 || M >= (int64_t)1 << 30) {  // list indices must stay int32: too many ranges
+    w.M = 0;
+    w.total = SIZE_MAX;
+    return w;
+  }
+  w.M = (int32_t)M;
   size_t o = 0;
   w.cand = o;    o = align256(o + sizeof(int32_t) * w.slots);
   w.cnt = o;     o = align256(o + sizeof(int32_t) * w.M);
@@ -768,20 +802,35 @@ AttnWs attention_ws(const Geo& g) {
   w.off = o;     o = align256(o + sizeof(int32_t) * (w.M + 1));
   w.choff = o;   o = align256(o + sizeof(int32_t) * (w.M + 1));
   w.entries = o; o = align256(o + sizeof(int32_t) * w.slots);
-  w.plse = o;    o = align256(o + sizeof(float) * w.slots * g.G);
-  w.po = o;      o = align256(o + sizeof(uint16_t) * w.slots * g.G * g.d);
-  const size_t rows = (size_t)g.B * g.Hkv * g.N;
+  const size_t rows = (size_t)BH * R;  // one range's (b h, query) rows
+  w.plse = o;    o = align256(o + sizeof(float) * rows * g.K * g.G);
+  w.po = o;      o = align256(o + sizeof(uint16_t) * rows * g.K * g.G * g.d);
   w.pfl = o;     o = align256(o + sizeof(float) * rows * g.G);
   w.pfo = o;     o = align256(o + sizeof(uint16_t) * rows * g.G * g.d);
   w.total = o;
   return w;
 }
 
+int32_t attention_full_range(const Geo& g) {
+  return (int32_t)(((int64_t)g.N + kLeafQueries - 1) / kLeafQueries * kLeafQueries);
+}
+
+int32_t attention_range(const Geo& g, size_t bytes) {
+  int lo = 0, hi = attention_full_range(g) / kLeafQueries;  // largest m with total(m * kLeafQueries) <= bytes
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (attention_ws(g, mid * kLeafQueries).total <= bytes) lo = mid; else hi = mid - 1;
+  }
+  return lo * kLeafQueries;
+}
+
 int launch_attention(const Geo& g, int dtype, const void* q, const void* k, const void* v, const int32_t* idx,
-                     int decode, void* ws, void* out, float* lse, hipStream_t st) {
+                     int decode, void* ws, size_t ws_bytes, void* out, float* lse, hipStream_t st) {
   if (attention_key_major(g, dtype, decode)) {
-    if (g.d == 128) return attn_km_d<128>(g, q, k, v, idx, ws, out, lse, st);
-    if (g.d == 64) return attn_km_d<64>(g, q, k, v, idx, ws, out, lse, st);
+    const int32_t R = attention_range(g, ws_bytes);  // as many queries per pass as the workspace holds
+    if (R <= 0) return PISA_ERR_WORKSPACE;
+    if (g.d == 128) return attn_km_d<128>(g, q, k, v, idx, ws, R, out, lse, st);
+    if (g.d == 64) return attn_km_d<64>(g, q, k, v, idx, ws, R, out, lse, st);
     return PISA_ERR_UNSUPPORTED;
   }
   if (dtype == PISA_BF16) {

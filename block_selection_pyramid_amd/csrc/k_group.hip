@@ -54,9 +54,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(const int32_t* __res
   }
 }
 
+// Lists are numbered (range, b h, block): query i belongs to range i / R (R a multiple of
+// kLeafQueries; R >= N gives one range, list = bh * n1 + block).
 __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ cand, int64_t slots, int32_t N,
-                                                      int32_t twoK, int32_t n1, const int32_t* __restrict__ off,
-                                                      int32_t* __restrict__ cursor, int32_t* __restrict__ entries) {
+                                                      int32_t twoK, int32_t n1, int32_t BH, int32_t R,
+                                                      const int32_t* __restrict__ off, int32_t* __restrict__ cursor,
+                                                      int32_t* __restrict__ entries) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= slots) return;
   const int leaf = cand[t];
@@ -64,7 +67,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   const int slot = (int)(t % twoK);
   const int64_t qg = t / twoK;  // bh * N + i
   const int bh = (int)(qg / N), i = (int)(qg % N);
-  const int list = bh * n1 + leaf;
+  const int list = ((i / R) * BH + bh) * n1 + leaf;
   const int pos = off[list] + atomicAdd(&cursor[list], 1);
   entries[pos] = (i << 6) | slot;
 }
@@ -73,21 +76,25 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
 // leaf block in LDS, reserve one range per non-empty block with a single returning global
 // add, then place each entry with an LDS counter.
 __global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __restrict__ cand, int32_t N, int32_t BH,
-                                                           int32_t twoK, int32_t n1, const int32_t* __restrict__ off,
+                                                           int32_t twoK, int32_t n1, int32_t R,
+                                                           const int32_t* __restrict__ off,
                                                            int32_t* __restrict__ cursor,
                                                            int32_t* __restrict__ entries) {
   extern __shared__ int lds[];
   int* hist = lds;        // n1 counts, then reserved bases
   int* lcur = lds + n1;   // n1 local cursors
-  const int bh = blockIdx.x % BH;
+  const int bh0 = blockIdx.x % BH;
   const int q0 = (blockIdx.x / BH) * kLeafQueries;
   const int q1 = min(N, q0 + kLeafQueries);
+  // the workgroup's queries share one range (R is a multiple of kLeafQueries): its lists
+  // are those of "row" (range, b h)
+  const int lrow = (q0 / R) * BH + bh0;
   for (int t = threadIdx.x; t < n1; t += 256) {
     hist[t] = 0;
     lcur[t] = 0;
   }
   __syncthreads();
-  const int32_t* c = cand + ((int64_t)bh * N + q0) * twoK;
+  const int32_t* c = cand + ((int64_t)bh0 * N + q0) * twoK;
   const int n = (q1 - q0) * twoK;
   for (int t = threadIdx.x; t < n; t += 256) {
     const int leaf = c[t];
@@ -96,7 +103,7 @@ __global__ __launch_bounds__(256) void scatter_hist_kernel(const int32_t* __rest
   __syncthreads();
   for (int t = threadIdx.x; t < n1; t += 256) {
     const int h = hist[t];
-    if (h) hist[t] = off[bh * n1 + t] + atomicAdd(&cursor[bh * n1 + t], h);
+    if (h) hist[t] = off[lrow * n1 + t] + atomicAdd(&cursor[lrow * n1 + t], h);
   }
   __syncthreads();
   for (int t = threadIdx.x; t < n; t += 256) {
@@ -230,17 +237,18 @@ int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
-int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
+int launch_scatter(const Geo& g, int per_row, int32_t R, const int32_t* cand, const int32_t* off, int32_t* cursor,
                    int32_t* entries, hipStream_t st) {
+  if (R <= 0 || R % kLeafQueries != 0) return PISA_ERR_INVALID_ARG;
   if (g.n1 <= kHistMaxBins) {
     const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLeafQueries - 1) / kLeafQueries));
     scatter_hist_kernel<<<grid, 256, 2 * sizeof(int) * (size_t)g.n1, st>>>(cand, g.N, g.B * g.Hkv, per_row, g.n1,
-                                                                            off, cursor, entries);
+                                                                            R, off, cursor, entries);
     return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
   }
   const int64_t slots = (int64_t)g.B * g.Hkv * g.N * per_row;
-  scatter_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(cand, slots, g.N, per_row, g.n1, off, cursor,
-                                                                   entries);
+  scatter_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(cand, slots, g.N, per_row, g.n1, g.B * g.Hkv, R,
+                                                                   off, cursor, entries);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 

@@ -359,7 +359,19 @@ int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* 
 size_t pisa_attention_workspace_bytes(const pisa_problem* p, int32_t mode) {
   Geo g;
   if (make_geo(p, &g) != PISA_OK || (mode != PISA_PREFILL && mode != PISA_DECODE)) return 0;
-  return attention_key_major(g, p->dtype, mode == PISA_DECODE) ? attention_ws(g).total : 0;
+  return attention_key_major(g, p->dtype, mode == PISA_DECODE) ? attention_ws(g, attention_full_range(g)).total : 0;
+}
+
+size_t pisa_attention_workspace_min_bytes(const pisa_problem* p, int32_t mode) {
+  Geo g;
+  if (make_geo(p, &g) != PISA_OK || (mode != PISA_PREFILL && mode != PISA_DECODE)) return 0;
+  if (!attention_key_major(g, p->dtype, mode == PISA_DECODE)) return 0;
+  // the smallest range whose list numbering fits (at most the full range)
+  for (int32_t R = kLeafQueries; R <= attention_full_range(g); R += kLeafQueries) {
+    const size_t t = attention_ws(g, R).total;
+    if (t != SIZE_MAX) return t;
+  }
+  return attention_ws(g, attention_full_range(g)).total;
 }
 
 int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, const void* k, const void* v,
@@ -376,9 +388,9 @@ int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, co
   if (rc != PISA_OK) return rc;
   if (attention_key_major(g, p->dtype, mode == PISA_DECODE)) {
     if (!workspace || !aligned16(workspace)) return PISA_ERR_INVALID_ARG;
-    if (workspace_bytes < attention_ws(g).total) return PISA_ERR_WORKSPACE;
+    if (attention_range(g, workspace_bytes) <= 0) return PISA_ERR_WORKSPACE;
   }
-  return launch_attention(g, p->dtype, q, k, v, idx, mode == PISA_DECODE, workspace, out, lse,
+  return launch_attention(g, p->dtype, q, k, v, idx, mode == PISA_DECODE, workspace, workspace_bytes, out, lse,
                           (hipStream_t)stream);
 }
 

@@ -71,16 +71,20 @@ inline int route_groups_per_wave(int G, int K) {
 // ---- launchers (each returns PISA_OK or PISA_ERR_HIP) ----
 int launch_build_pyramid(const Geo& g, int dtype, const void* k, float* pyr, hipStream_t st);
 // block-sparse attention over selected blocks (decode != 0: one query per sequence at N-1);
-// bf16 prefill runs key-major and needs the workspace laid out by attention_ws
+// bf16 prefill runs key-major in passes over query ranges of R queries (R a multiple of
+// kLeafQueries) and needs the workspace laid out by attention_ws(g, R)
 struct AttnWs {
   size_t cand, cnt, cursor, off, choff, entries, plse, po, pfl, pfo, total;
   int64_t slots;  // B*Hkv*N*K
-  int32_t M;      // B*Hkv*n1 block lists
+  int32_t M;      // ceil(N / R) * B*Hkv*n1 block lists, numbered (range, b h, block)
+  int32_t R;      // queries per range
 };
 bool attention_key_major(const Geo& g, int dtype, int decode);
-AttnWs attention_ws(const Geo& g);
+AttnWs attention_ws(const Geo& g, int32_t R);
+int32_t attention_full_range(const Geo& g);           // one range: N rounded up to kLeafQueries
+int32_t attention_range(const Geo& g, size_t bytes);  // largest R whose workspace fits, 0 if none
 int launch_attention(const Geo& g, int dtype, const void* q, const void* k, const void* v, const int32_t* idx,
-                     int decode, void* ws, void* out, float* lse, hipStream_t st);
+                     int decode, void* ws, size_t ws_bytes, void* out, float* lse, hipStream_t st);
 // full-scan BSA selection (bf16): out_idx / out_score [B, Hkv, N, K]
 int launch_bsa(const Geo& g, const void* q, const float* pyr, int32_t* out_idx, float* out_score, hipStream_t st);
 int launch_zero(int32_t* a, int64_t n, hipStream_t st);
@@ -125,7 +129,7 @@ int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t
 int launch_count_pairs(const Geo& g, const int32_t* cand, int32_t* cnt, hipStream_t st);
 // scatter of per_row candidate slots per query group (-1 = none) into per-leaf-block lists
 // (block-sparse attention's (query group, block) pairs)
-int launch_scatter(const Geo& g, int per_row, const int32_t* cand, const int32_t* off, int32_t* cursor,
+int launch_scatter(const Geo& g, int per_row, int32_t R, const int32_t* cand, const int32_t* off, int32_t* cursor,
                    int32_t* entries, hipStream_t st);
 // scatter of the 2K routed leaf slots per query group into per-level-2-node lists: slots 2r
 // and 2r+1 (children of the kept node of rank r) give one entry (i << 6 | r) when either

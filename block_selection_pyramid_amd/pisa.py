@@ -88,7 +88,7 @@ EXPORTS = ("pisa_levels", "pisa_pyramid_layout", "pisa_supported", "pisa_pyramid
            "pisa_prefill_dense_levels", "pisa_select_decode", "pisa_select_prefill_noalloc",
            "pisa_prefill_workspace_min_bytes",
            "pisa_bsa_select_prefill", "pisa_append_keys", "pisa_select_decode_varlen", "pisa_sparse_attention",
-           "pisa_attention_workspace_bytes",
+           "pisa_attention_workspace_bytes", "pisa_attention_workspace_min_bytes",
            "pisa_status_string", "pisa_version")
 
 
@@ -127,6 +127,8 @@ def load(path: str | None = None):
     lib.pisa_sparse_attention.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, sz, vp, vp, vp]
     lib.pisa_attention_workspace_bytes.argtypes = [P, ctypes.c_int32]
     lib.pisa_attention_workspace_bytes.restype = sz
+    lib.pisa_attention_workspace_min_bytes.argtypes = [P, ctypes.c_int32]
+    lib.pisa_attention_workspace_min_bytes.restype = sz
     lib.pisa_status_string.argtypes = [ctypes.c_int]
     lib.pisa_status_string.restype = ctypes.c_char_p
     lib.pisa_version.restype = ctypes.c_char_p
@@ -296,7 +298,13 @@ def select_decode_varlen(p: Problem, q: torch.Tensor, k_cache: torch.Tensor, pyr
 
 
 def attention_workspace_bytes(p: Problem, decode: bool = False) -> int:
+    """Workspace for one pass over the whole sequence (bf16 prefill; 0 otherwise)."""
     return int(load().pisa_attention_workspace_bytes(ctypes.byref(p.c()), DECODE if decode else PREFILL))
+
+
+def attention_workspace_min_bytes(p: Problem, decode: bool = False) -> int:
+    """Smallest workspace pisa_sparse_attention accepts (passes over 2048-query ranges)."""
+    return int(load().pisa_attention_workspace_min_bytes(ctypes.byref(p.c()), DECODE if decode else PREFILL))
 
 
 def sparse_attention(p: Problem, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,

@@ -285,12 +285,16 @@ int pisa_select_decode_varlen(const pisa_problem* p, const void* q, const void* 
  * {0, b-1, b} of each leaf block b for all its queries at once (each query masked by
  * whether its selection names them), sorts the other (query group, block) pairs by block,
  * attends each block's staged key and value tiles on the matrix cores and merges the
- * partial outputs (kept in bf16 in the workspace); it needs
- * pisa_attention_workspace_bytes(p, mode) bytes of 16-byte aligned device workspace
- * (PISA_ERR_WORKSPACE if smaller).  fp32 inputs and decode need none (workspace may be
- * NULL).
+ * partial outputs (kept in bf16 in the workspace).  The partials of one query range at a
+ * time live in the workspace: with pisa_attention_workspace_bytes(p, mode) bytes (16-byte
+ * aligned device memory) the whole sequence is one range; with less, but at least
+ * pisa_attention_workspace_min_bytes(p, mode), the call takes as few passes over ranges of
+ * consecutive queries (multiples of 2048) as the given size allows, with the same results
+ * (PISA_ERR_WORKSPACE below the minimum).  fp32 inputs and decode need none (workspace may
+ * be NULL; both sizes are 0).
  */
 size_t pisa_attention_workspace_bytes(const pisa_problem* p, int32_t mode);
+size_t pisa_attention_workspace_min_bytes(const pisa_problem* p, int32_t mode);
 int pisa_sparse_attention(const pisa_problem* p, int32_t mode, const void* q, const void* k, const void* v,
                           const int32_t* idx, void* workspace, size_t workspace_bytes, void* out, float* lse,
                           pisa_stream_t stream);

@@ -161,29 +161,44 @@ def test_attention_host_checks(pisa):
     p = pisa.Problem(1, 4096, 16, 4, 128)
     P = ctypes.byref(p.c())
     need = lib.pisa_attention_workspace_bytes(P, pisa.PREFILL)
-    assert need > 0 and lib.pisa_attention_workspace_bytes(P, pisa.DECODE) == 0
+    least = lib.pisa_attention_workspace_min_bytes(P, pisa.PREFILL)
+    assert 0 < least < need and lib.pisa_attention_workspace_bytes(P, pisa.DECODE) == 0
     f32 = pisa.Problem(1, 4096, 16, 4, 128, dtype=pisa.F32)
     assert lib.pisa_attention_workspace_bytes(ctypes.byref(f32.c()), pisa.PREFILL) == 0
     a = (0x1000, 0x1000, 0x1000, 0x1000)
     assert lib.pisa_sparse_attention(P, pisa.PREFILL, *a, None, need, 0x1000, None, None) == 1       # no workspace
-    assert lib.pisa_sparse_attention(P, pisa.PREFILL, *a, 0x1000, need - 1, 0x1000, None, None) == 3  # too small
+    assert lib.pisa_sparse_attention(P, pisa.PREFILL, *a, 0x1000, least - 1, 0x1000, None, None) == 3  # too small
     assert lib.pisa_sparse_attention(P, 7, *a, 0x1000, need, 0x1000, None, None) == 1                 # bad mode
     assert lib.pisa_sparse_attention(P, pisa.PREFILL, 0, *a[1:], 0x1000, need, 0x1000, None, None) == 1
 
 
 @pytest.mark.parametrize("B,N,Hq,Hkv,d,K", [(1, 262144, 16, 4, 128, 8), (2, 3000 + 17, 8, 2, 64, 6), (1, 5, 8, 2, 64, 4)])
 def test_attention_workspace_regions(pisa, B, N, Hq, Hkv, d, K):
-    # bf16 prefill: per slot (K per query group) a candidate, a list entry, G log2-sum-exp
-    # partials and G bf16 output rows; per (KV head, leaf block) list a count, a cursor, an
-    # offset and a chunk offset (+1 each for the offsets); per query group the forced
-    # blocks' G log2-sum-exp partials and G bf16 output rows; eleven 256-byte aligned regions
+    # bf16 prefill, queries in ranges of R (a multiple of 2048): per slot (K per query group)
+    # a candidate and a list entry; per (range, KV head, leaf block) list a count, a cursor,
+    # an offset and a chunk offset (+1 each for the offsets); per query group of one range
+    # K G log2-sum-exp partials and K G bf16 output rows for the slots, G and G for the
+    # forced blocks; ten 256-byte aligned regions.  The full size is one range (R = N
+    # rounded up to 2048), the minimum R = 2048.
     lib = pisa.load()
     p = pisa.Problem(B, N, Hq, Hkv, d, 64, K, 2)
-    G, rows, n1 = Hq // Hkv, B * Hkv * N, -(-N // 64)
-    slots, lists = rows * K, B * Hkv * n1
-    need = slots * (4 + 4 + 4 * G + 2 * G * d) + lists * 4 * 4 + 2 * 4 + rows * G * (4 + 2 * d)
+    G, BH, n1 = Hq // Hkv, B * Hkv, -(-N // 64)
+    slots = BH * N * K
+
+    def need(R):
+        nr = -(-N // R)
+        return slots * 8 + nr * BH * n1 * 4 * 4 + 2 * 4 + BH * R * (K + 1) * G * (4 + 2 * d)
+
+    full = need(-(-N // 2048) * 2048)
     got = lib.pisa_attention_workspace_bytes(ctypes.byref(p.c()), pisa.PREFILL)
-    assert need <= got < need + 11 * 256
+    assert full <= got < full + 10 * 256
+    got_min = lib.pisa_attention_workspace_min_bytes(ctypes.byref(p.c()), pisa.PREFILL)
+    assert need(2048) <= got_min < need(2048) + 10 * 256
+    assert got_min <= got
+    if N > 2048:
+        assert got_min < got
+    # decode and fp32 take no workspace
+    assert lib.pisa_attention_workspace_min_bytes(ctypes.byref(p.c()), pisa.DECODE) == 0
 
 
 def test_bsa_host_checks(pisa):

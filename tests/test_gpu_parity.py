@@ -827,6 +827,36 @@ def test_sparse_attention_parity(env, case):
     attn_verify(op, q, k, v, idx, rows, o, lse.cpu().numpy(), decode, dt, "attn-" + name)
 
 
+def test_sparse_attention_query_ranges_match_one_pass(env):
+    # a workspace smaller than the one-pass size splits the bf16 prefill into passes over
+    # ranges of 2048 queries: the same kernels per pair, so the same bits, at the minimum
+    # size (5 ranges, the last ragged), at an intermediate size and at the full size
+    torch, pisa = env
+    N, B, Hq, Hkv, d, K = 64 * 130 + 17, 2, 16, 4, 128, 8
+    w = synth.custom(name="ranges", batch=B, seq_len=N, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     seed=77, needles=6)
+    p, op = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    v = synth.make_values(w)
+    idx = synth.random_selection(w, 13)
+    qd, kd, vd = dev(torch, q), dev(torch, k), dev(torch, v)
+    idd = torch.from_numpy(idx).cuda()
+    full, least = pisa.attention_workspace_bytes(p), pisa.attention_workspace_min_bytes(p)
+    assert least < full
+    outs = []
+    for nbytes in (full, (full + least) // 2, least):
+        log("ranges", "attention with a %d-byte workspace: launching" % nbytes)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        out, lse = pisa.sparse_attention(p, qd, kd, vd, idd, ws=ws)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu().numpy(), lse.cpu().numpy()))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l.view(np.int32), outs[0][1].view(np.int32))
+    rows = np.sort(np.random.default_rng(3).choice(B * Hkv * N, 1500, replace=False))
+    attn_verify(op, q, k, v, idx, rows, synth.bf16_bits_to_f32(outs[2][0].view(np.uint16)), outs[2][1], False,
+                synth.BF16, "attn-ranges-min")
+
+
 def test_sparse_attention_256k_sampled(env):
     # the full-size workload in bench.py's launch configuration, on a random valid selection
     torch, pisa = env
