@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pisa_internal.h"
 
 namespace pisa {
@@ -126,6 +128,47 @@ __device__ __forceinline__ float group_prod(float v) {
   if constexpr (G >= 8) v *= dpp_move<0x141>(v);
   if constexpr (G >= 16) v *= dpp_move<0x140>(v);
   return v;
+}
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
+
+// Sum (or product) of NV values per lane over the G lanes of a query group, scattered:
+// afterwards lane r of the group holds the results for values (r % GE) VPL .. + VPL - 1 in
+// v[0 .. VPL), GE = min(G, NV), VPL = NV / GE.  The exchanges run from the highest lane bit
+// down: while the group spans more lanes than there are values left to split, both partners
+// combine everything; below that each step sends the half of the values the partner keeps
+// and combines the half it keeps, so a value crosses lanes once per step, not once per step
+// per result.  The partner of lane bit b (quad_perm for bits 0 and 1, half-row and row
+// mirrors for bits 2 and 3) agrees with the lane on every higher bit, so both hold the same
+// sub-range of values when they exchange.
+template <int CTRL, bool PROD>
+__device__ __forceinline__ float dpp_combine(float keep, float send) {
+  return PROD ? keep * dpp_move<CTRL>(send) : keep + dpp_move<CTRL>(send);
+}
+template <int G, int NV, bool PROD>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[NV], int r) {
+  constexpr int LG = ilog2(G), H = LG < ilog2(NV) ? LG : ilog2(NV);
+  static_assert((1 << LG) == G && (1 << ilog2(NV)) == NV, "powers of two");
+  auto step = [&](auto bitc) {
+    constexpr int b = decltype(bitc)::value;
+    constexpr int CTRL = b == 0 ? 0xB1 : b == 1 ? 0x4E : b == 2 ? 0x141 : 0x140;
+    if constexpr (b >= H) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[i] = dpp_combine<CTRL, PROD>(v[i], v[i]);
+    } else {
+      constexpr int n = NV >> (H - 1 - b);  // values still held
+      const bool up = (r >> b) & 1;
+#pragma unroll
+      for (int i = 0; i < n / 2; ++i) {
+        const float lo = v[i], hi = v[i + n / 2];
+        v[i] = dpp_combine<CTRL, PROD>(up ? hi : lo, up ? lo : hi);
+      }
+    }
+  };
+  if constexpr (LG > 3) step(std::integral_constant<int, 3>{});
+  if constexpr (LG > 2) step(std::integral_constant<int, 2>{});
+  if constexpr (LG > 1) step(std::integral_constant<int, 1>{});
+  if constexpr (LG > 0) step(std::integral_constant<int, 0>{});
 }
 
 // Forced leaf blocks of a query in leaf block bq: {0, bq-1, bq} that exist, ascending.

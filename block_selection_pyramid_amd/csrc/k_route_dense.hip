@@ -16,9 +16,13 @@
 // held in registers; the routing copy is pre-scaled by s log2(e), so the products are the
 // scores in log2 units).  The epilogue forms the pair LSE of each node's two children (or,
 // for the PISA-1 / PISA-2 ablations, its truncation about their mean) and the head sum,
-// and each wavefront keeps only the scores of its own queries' candidates.  The
-// staged child tiles do not depend on the walk, so the next tile is fetched from L2 while
-// the current one is scored, across level boundaries too.
+// and each wavefront keeps only the scores of its own queries' candidates.  Because a
+// node's dot is the mean of its children's dots, one sweep over the tiles of level l - 2
+// scores both level l - 1 (pairs of tile nodes) and level l (pairs of those pair means):
+// the levels are scored two per sweep, so the tiles of every other level are never read.
+// The staged tiles do not depend on the walk, so the next tile is fetched straight into
+// the other LDS buffer (no registers in flight) while the current one is scored, across
+// level boundaries too.
 //
 // Output: per query group, the 2K candidate slots of level l_bot - 1 (children of the Top-K
 // nodes of level l_bot, -1 where a child does not exist or is not visible), the input of
@@ -28,6 +32,8 @@
 // forced-block paragraph: first, previous and current block; leaf score = causal LSE over
 // the block's raw keys, summed over the G heads) with the query rows it already holds:
 // each forced key tile is staged in LDS once and contracted on the matrix cores.
+#include <type_traits>
+
 #include "final_dev.h"
 #include "route_dev.h"
 #include "tile_dev.h"
@@ -38,7 +44,7 @@ namespace {
 
 template <int D, int G, int KC>
 constexpr size_t dense_lds_bytes() {
-  return 2 * (size_t)(2 * (D / 16) * 1024) + (size_t)kDenseWaves * DenseShape<G>::QPW * (64 + 20 * KC);
+  return 2 * (size_t)(2 * (D / 16) * 1024) + (size_t)kDenseWaves * DenseShape<G>::QPW * (96 + 20 * KC);
 }
 
 // Forced key tile f (64 raw keys) into fragment-major LDS: fragment fi = rb KS + ks holds
@@ -76,11 +82,11 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   static_assert((KC & (KC - 1)) == 0, "items index queries by it / KC");
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  char* wl = lds + 2 * TILE + wave * (QPW * (64 + 20 * KC));
-  float* Sx = reinterpret_cast<float*>(wl);                             // [QPW][16] node scores
-  uint64_t* key = reinterpret_cast<uint64_t*>(wl + QPW * 64);           // [QPW][SLOTS]
-  int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (64 + 16 * KC));  // [QPW][KC]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  char* wl = lds + 2 * TILE + wave * (QPW * (96 + 20 * KC));
+  float* Sx = reinterpret_cast<float*>(wl);                             // [QPW][24] node scores
+  uint64_t* key = reinterpret_cast<uint64_t*>(wl + QPW * 96);           // [QPW][SLOTS]
+  int32_t* np = reinterpret_cast<int32_t*>(wl + QPW * (96 + 16 * KC));  // [QPW][KC]
 
   const int N = geo.N, K = geo.K, L = geo.L;
   constexpr int C = kLeaf;  // leaf block size (the only one the kernels support)
@@ -134,28 +140,42 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
     sc[m][0] = sc[m][1] = 0.f;
   }
 
-  u32x4 stg[F / kDenseWaves];
-  auto ntiles = [&](int l) {
-    const int nv = min(geo.n[l - 1], (bqmax >> (l - 2)) + 1);
+  // Passes.  A pair pass scores levels l and l - 1 from one sweep over the tiles of level
+  // l - 2: a node's dot is the mean of its children's dots, so the sweep's products give the
+  // level-(l-1) dots (pair means, over the children that exist) and with them both levels'
+  // scores, and the level-(l - 1) candidates (children of the level-l nodes kept) are
+  // children of level-l candidates, whose scores the items pick up in the same sweep.  A
+  // single pass scores level l from the tiles of level l - 1 (the last level when the dense
+  // levels are odd in number).  Pair passes cost the tiles of every other level only.
+  auto is_pair = [&](int lv) { return lv - 1 >= l_bot && lv >= 3; };
+  auto tile_level = [&](int lv) { return is_pair(lv) ? lv - 2 : lv - 1; };
+  auto ntiles = [&](int lt) {  // tiles of the visible prefix of level lt
+    const int nv = min(geo.n[lt], (bqmax >> (lt - 1)) + 1);
     return (nv + 31) >> 5;
   };
+  // pair pass: an item keeps the scores of the level-(l-1) nodes 4 ip .. 4 ip + 3 in its two
+  // key slots (16 bytes, free until the pass's Top-K), not in registers
 
-  int l = L, t = 0, nt = ntiles(L), buf = 0;
-  dense_load_tile<D>(Rb, geo, l, 0, wave, lane, stg);
-  dense_store_tile<D>(lds, 0, wave, lane, stg);
+  int l = L, t = 0, buf = 0;
+  int nt = ntiles(tile_level(L));
+  dense_fetch_tile<D>(Rb, geo, tile_level(L) + 1, 0, wave, lane, lds, 0);
+  dense_fetch_wait();
   __syncthreads();
   for (;;) {
+    const bool pr = is_pair(l);
+    const int lt = pr ? l - 2 : l - 1;  // level of this pass's tiles
     int ln = l, tn = t + 1;
     if (tn == nt) {
-      ln = l - 1;
+      ln = l - (pr ? 2 : 1);
       tn = 0;
     }
     const bool more = ln >= l_bot;
-    // unconditional (the last step reloads its own tile): a branch here would make the
-    // compiler wait for each load in turn
-    dense_load_tile<D>(Rb, geo, more ? ln : l, more ? tn : t, wave, lane, stg);
+    const int ltn = more ? tile_level(ln) : lt;
+    // the next tile goes straight into the other buffer, which every wavefront finished
+    // reading before the previous step's barrier
+    if (more) dense_fetch_tile<D>(Rb, geo, ltn + 1, tn, wave, lane, lds, buf ^ 1);
 
-    // ---- scores of the 16 nodes of tile t for this wavefront's queries
+    // ---- products of the 32 level-lt nodes of tile t with this wavefront's queries
     const char* Tt = lds + buf * TILE;
     f32x16 acc[NCG];
 #pragma unroll
@@ -172,91 +192,117 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
         acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[cg][ks], acc[cg], 0, 0, 0);
       }
     }
-    const int nchild = geo.n[l - 1], cshift = l - 2;
-    // Epilogue.  Result row (child) 8a + 4hh + 2p (+1) sits in acc[4a + 2p] (+1); node
-    // 4a + 2hh + p of the tile owns that pair.  Per head, with d = a0 - a1: mx = a0 -
-    // min(d, 0) is the max of the pair and f = 1 + 2^-|d| lies in [1, 2]; the head
-    // reduction is sum(mx) and prod(f), so the node score sum_h LSE_h (log2 units) =
-    // sum(mx) + log2 prod(f), and the G lanes of a query split the logarithms among
-    // themselves.  A node whose first child is visible has a finite mx; other nodes are
-    // never read, so only the second child of a pair needs a mask (-inf, giving mx = a0
-    // and f = 1), and only in the tile holding the visibility boundary.  (Forming the max
-    // from the difference keeps the compiler from canonicalising the raw MFMA results.)
-    const bool full = 32 * t + 32 <= min(nchild, (bqw >> cshift) + 1);  // bqw: smallest bq
+    // Epilogue.  Result row (tile node) 8a + 4hh + v sits in acc[4a + v]: the lane holds
+    // the four nodes 8a + 4hh .. +3, i.e. the children of the two level-(lt+1) nodes
+    // 4a + 2hh + p of the tile (p = 0, 1), which are the children of level-(lt+2) node
+    // 2a + hh.  Pair LSE per head: max(y0, y1) and f = 1 + 2^-|y0 - y1| in [1, 2]; the head
+    // reduction is sum(max) and prod(f), and the node score (log2 units) = sum(max) +
+    // log2 prod(f).  The reductions are scattered over the G lanes of a query, each lane
+    // finishing a share of the values.  A node whose first child is visible has a finite
+    // max; other nodes are never read, so only second children are masked (-inf: max = y0,
+    // f = 1), and only in the tile that holds the end of the visible prefix: the others take
+    // a path without masks.  (fmed3 against +inf is the max without canonicalising the raw
+    // MFMA results first.)
+    const int base = 32 * t;
+    const int ntn = geo.n[lt];
+    const int vsh = lt - 1;  // a level-lt node c is visible to leaf block bq iff c <= bq >> vsh
+    const int lim = min(ntn - 1, bqw >> vsh) - base;  // visible rows of the wavefront's leaf block: <= lim
+    const int elim = ntn - 1 - base;                  // existing rows: <= elim
+    const int r = j % G;
+    // +inf in a register the compiler cannot see through: fmed3 against a literal +inf is
+    // rewritten into a max that canonicalises both raw MFMA results first (three operations)
+    float pinf = INFINITY;
+    asm volatile("" : "+s"(pinf));
+    auto epilogue = [&](auto maskedc) {
+      constexpr bool MASKED = decltype(maskedc)::value;
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) {
-      if (!full) {
-        const int lim = min(nchild - 1, bqc[cg] >> cshift) - 32 * t;  // visible rows: <= lim
+      for (int cg = 0; cg < NCG; ++cg) {
+        const int qi = cg * (32 / G) + j / G;
+        if (pr) {  // the 8 level-(lt+2) nodes: slots 16..23 (first: this reads acc, the values
+                   // below consume it)
+          // a level-(lt+1) node's dot is the mean of its existing children's dots; these are
+          // twice the means, the factor 1/2 is taken after the head sum.  The node's second
+          // child (level lt+1) is visible iff that child's first child is.
+          float mxs[4], prd[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int p = 0; p < 2; ++p)
-            if (8 * a + 4 * hh + 2 * p + 1 > lim) acc[cg][4 * a + 2 * p + 1] = -INFINITY;
-      }
-      float mxs[8], prd[8];
-      if constexpr (!trunc) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const float a0 = acc[cg][4 * a + 2 * p], a1 = acc[cg][4 * a + 2 * p + 1];
-            const float dd = a0 - a1;
-            mxs[2 * a + p] = a0 - fminf(dd, 0.f);
-            prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(-fabsf(dd));
+          for (int a = 0; a < 4; ++a) {
+            const int r0 = 8 * a + 4 * hh;
+            const float y0 = acc[cg][4 * a], y1 = acc[cg][4 * a + 1];
+            const float y2 = acc[cg][4 * a + 2], y3 = acc[cg][4 * a + 3];
+            float d0 = y0 + y1, d1 = y2 + y3;
+            if constexpr (MASKED) {
+              d0 = r0 + 1 <= elim ? d0 : 2.f * y0;
+              d1 = r0 + 3 <= elim ? d1 : 2.f * y2;
+              d1 = r0 + 2 <= lim ? d1 : -INFINITY;
+            }
+            if constexpr (!trunc) {
+              mxs[a] = __builtin_amdgcn_fmed3f(d0, d1, pinf);
+              prd[a] = 1.f + __builtin_amdgcn_exp2f(-fabsf(0.5f * (d0 - d1)));
+            } else {
+              mxs[a] = 2.f * pair_trunc(0.5f * d0, 0.5f * d1, 1.f, c2);
+              prd[a] = 1.f;
+            }
           }
+          group_reduce_scatter<G, 4, false>(mxs, r);
+          if constexpr (!trunc) group_reduce_scatter<G, 4, true>(prd, r);
+          constexpr int GE = G < 4 ? G : 4, VPL = 4 / GE;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          mxs[e] = group_sum<G>(mxs[e]);
-          prd[e] = group_prod<G>(prd[e]);
-        }
-      } else {  // PISA-1 / PISA-2: per-head truncated scores, summed over the heads
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            mxs[2 * a + p] = pair_trunc(acc[cg][4 * a + 2 * p], acc[cg][4 * a + 2 * p + 1], 1.f, c2);
-            prd[2 * a + p] = 1.f;
-          }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) mxs[e] = group_sum<G>(mxs[e]);
-      }
-      // lane r < GE of a query's group finishes values r*VPL .. r*VPL + VPL - 1
-      constexpr int GE = G < 8 ? G : 8, VPL = 8 / GE;
-      const int r = j % G;
-      const int qi = cg * (32 / G) + j / G;
-      float out[VPL];
-#pragma unroll
-      for (int u = 0; u < VPL; ++u) {
-        float m = mxs[u], f = prd[u];
-#pragma unroll
-        for (int k = 1; k < GE; ++k) {
-          m = r == k ? mxs[k * VPL + u] : m;
-          f = r == k ? prd[k * VPL + u] : f;
-        }
-        if constexpr (trunc)
-          out[u] = m;
-        else
-          out[u] = m + __builtin_amdgcn_logf(f);
-      }
-      if (r < GE) {
-        float* dst = Sx + qi * 16 + 2 * hh;
-        if constexpr (VPL == 1) {
-          dst[4 * (r >> 1) + (r & 1)] = out[0];
-        } else {
-#pragma unroll
-          for (int u = 0; u < VPL; u += 2) {
-            const int a = (r * VPL + u) >> 1;  // value index r*VPL + u = 2a (+1)
-            *reinterpret_cast<float2*>(dst + 4 * a) = make_float2(out[u], out[u + 1]);
+          for (int u = 0; u < VPL; ++u) {  // value e: node 2e + hh
+            const int e = (r % GE) * VPL + u;
+            const float out = trunc ? 0.5f * mxs[u] : fmaf(0.5f, mxs[u], __builtin_amdgcn_logf(prd[u]));
+            if (r < GE) Sx[qi * 24 + 16 + 2 * e + hh] = out;
           }
         }
+        {  // the 16 level-(lt+1) nodes of the tile: slots 0..15
+          float mxs[8], prd[8];
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const float y0 = acc[cg][4 * a + 2 * p];
+              float y1 = acc[cg][4 * a + 2 * p + 1];
+              if constexpr (MASKED) y1 = 8 * a + 4 * hh + 2 * p + 1 <= lim ? y1 : -INFINITY;
+              if constexpr (!trunc) {
+                mxs[2 * a + p] = __builtin_amdgcn_fmed3f(y0, y1, pinf);
+                prd[2 * a + p] = 1.f + __builtin_amdgcn_exp2f(-fabsf(y0 - y1));
+              } else {
+                mxs[2 * a + p] = pair_trunc(y0, y1, 1.f, c2);
+                prd[2 * a + p] = 1.f;
+              }
+            }
+          group_reduce_scatter<G, 8, false>(mxs, r);
+          if constexpr (!trunc) group_reduce_scatter<G, 8, true>(prd, r);
+          constexpr int GE = G < 8 ? G : 8, VPL = 8 / GE;
+#pragma unroll
+          for (int u = 0; u < VPL; ++u) {  // value e = 2a + p: node 4a + 2hh + p
+            const int e = (r % GE) * VPL + u;
+            const float out = trunc ? mxs[u] : mxs[u] + __builtin_amdgcn_logf(prd[u]);
+            if (r < GE) Sx[qi * 24 + 4 * (e >> 1) + 2 * hh + (e & 1)] = out;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one column group's epilogue at a time
       }
-    }
+    };
+    if (lim >= 31)
+      epilogue(std::false_type{});
+    else
+      epilogue(std::true_type{});
     wave_sync();
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      if (ip[m] >= 8 * t && ip[m] < 8 * t + 8) {
-        const int iq = (lane + 64 * m) / KC;
-        const float2 v = *reinterpret_cast<const float2*>(Sx + iq * 16 + 2 * (ip[m] - 8 * t));
+      const int iq = (lane + 64 * m) / KC;
+      if (pr) {
+        // candidates 2 ip, 2 ip + 1 (level l) and their children 4 ip .. 4 ip + 3 (level l - 1)
+        if (ip[m] >= 4 * t && ip[m] < 4 * t + 4) {
+          const int o = ip[m] - 4 * t;
+          const float2 v = *reinterpret_cast<const float2*>(Sx + iq * 24 + 16 + 2 * o);
+          const float4 w4 = *reinterpret_cast<const float4*>(Sx + iq * 24 + 4 * o);
+          sc[m][0] = v.x;
+          sc[m][1] = v.y;
+          *reinterpret_cast<float4*>(key + 2 * (lane + 64 * m)) = w4;
+        }
+      } else if (ip[m] >= 8 * t && ip[m] < 8 * t + 8) {
+        const float2 v = *reinterpret_cast<const float2*>(Sx + iq * 24 + 2 * (ip[m] - 8 * t));
         sc[m][0] = v.x;
         sc[m][1] = v.y;
       }
@@ -265,10 +311,24 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
 
     if (t == nt - 1) {
       // ---- Top-K of level l per query; the kept node of rank r becomes item r's parent
+      // (single pass) or opens the level-(l-1) slots 2r, 2r+1 (pair pass)
       const int nl = geo.n[l];
+      int kr[M][2];  // rank of the item's two candidates (>= K: not kept)
+      float c1[M][4];
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int it = lane + 64 * m;
+        const float4 w4 = pr && it < ITEMS ? *reinterpret_cast<const float4*>(key + 2 * it) : float4{0.f, 0.f, 0.f, 0.f};
+        c1[m][0] = w4.x;
+        c1[m][1] = w4.y;
+        c1[m][2] = w4.z;
+        c1[m][3] = w4.w;
+      }
+      wave_sync();
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int it = lane + 64 * m;
+        kr[m][0] = kr[m][1] = K;
         if (it < ITEMS) {
           // item it = (query it / KC, rank it % KC): key slots 2 it, 2 it + 1 (SLOTS = 2 KC)
           const int n0 = 2 * ip[m], n1 = n0 + 1;
@@ -293,11 +353,67 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
             r0 += (kk.x > k0) + (kk.y > k0);
             r1 += (kk.x > k1) + (kk.y > k1);
           }
-          if (k0 != 0ull && r0 < K) np[(it & ~(KC - 1)) + r0] = 2 * ip[m];
-          if (k1 != 0ull && r1 < K) np[(it & ~(KC - 1)) + r1] = 2 * ip[m] + 1;
+          if (k0 != 0ull && r0 < K) kr[m][0] = r0;
+          if (k1 != 0ull && r1 < K) kr[m][1] = r1;
+          if (!pr) {
+            if (kr[m][0] < K) np[(it & ~(KC - 1)) + r0] = 2 * ip[m];
+            if (kr[m][1] < K) np[(it & ~(KC - 1)) + r1] = 2 * ip[m] + 1;
+          }
         }
       }
       wave_sync();
+      if (pr) {
+        // ---- Top-K of level l - 1 over the kept nodes' children: kept node x of rank r
+        // fills slots 2r, 2r+1 with its children 2x, 2x+1 (keys of the level-(l-1) scores
+        // picked up during the sweep)
+        const int nc = geo.n[l - 1];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int it = lane + 64 * m;
+          if (it < ITEMS) {
+            key[2 * it] = 0ull;
+            key[2 * it + 1] = 0ull;
+          }
+        }
+        wave_sync();
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int it = lane + 64 * m;
+          if (it < ITEMS) {
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+              if (kr[m][c] < K) {
+                const int x = 2 * ip[m] + c;
+                const int ch1 = 2 * x + 1;
+                const bool vis1 = ch1 < nc && ((int64_t)ch1 << (l - 2)) <= ibq[m];
+                uint64_t* dst = key + (it & ~(KC - 1)) * 2 + 2 * kr[m][c];
+                dst[0] = cand_key(c1[m][2 * c], 2 * x);
+                dst[1] = vis1 ? cand_key(c1[m][2 * c + 1], ch1) : 0ull;
+              }
+            }
+          }
+        }
+        wave_sync();
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          const int it = lane + 64 * m;
+          if (it < ITEMS) {
+            const uint64_t* kq = key + (it & ~(KC - 1)) * 2;
+            const uint64_t k0 = key[2 * it], k1 = key[2 * it + 1];
+            int r0 = 0, r1 = 0;
+#pragma unroll 4
+            for (int s = 0; s < SLOTS; s += 2) {
+              const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(kq + s);
+              r0 += (kk.x > k0) + (kk.y > k0);
+              r1 += (kk.x > k1) + (kk.y > k1);
+            }
+            // the node of a key: its low word holds the complemented index
+            if (k0 != 0ull && r0 < K) np[(it & ~(KC - 1)) + r0] = (int)~(uint32_t)k0;
+            if (k1 != 0ull && r1 < K) np[(it & ~(KC - 1)) + r1] = (int)~(uint32_t)k1;
+          }
+        }
+        wave_sync();
+      }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int it = lane + 64 * m;
@@ -306,20 +422,25 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
       wave_sync();
     }
 
-    if (more) dense_store_tile<D>(lds, buf ^ 1, wave, lane, stg);
+    if (more) dense_fetch_wait();
     __syncthreads();
     if (!more) break;
-    if (ln != l) nt = ntiles(ln);
+    if (ln != l) nt = ntiles(ltn);
     l = ln;
     t = tn;
     buf ^= 1;
   }
+  // the passes end at level l_bot: ip holds its kept nodes
 
   // ---- level l_bot - 1 candidates: the children of each kept node, 2K slots per query
   const int lc = l_bot - 1, twoK = 2 * K;
+  // the item indices are formed again from an opaque copy of the lane: carried across the
+  // passes they would cost registers the tile loop needs
+  int lp = lane;
+  asm volatile("" : "+v"(lp));
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int it = lane + 64 * m;
+    const int it = lp + 64 * m;
     const int iq = it / KC, ir = it % KC, i = iw + iq;
     if (it < ITEMS && ir < K && i < N) {
       const int p = ip[m];
@@ -344,6 +465,7 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   ft[nft++] = 0;
   for (int f = max(1, bfirst - 1); f <= bqmax && nft < 4; ++f) ft[nft++] = f;
   const bf16* kb = k + (int64_t)bh * N * D;
+  u32x4 stg[F / kDenseWaves];
   __syncthreads();  // the staging buffers are free again
   dense_load_keys<D>(kb, N, ft[0], wave, lane, stg);
   dense_store_tile<D>(lds, 0, wave, lane, stg);

@@ -34,6 +34,23 @@ __device__ __forceinline__ void dense_load_tile(const char* Rb, const Geo& geo, 
 #pragma unroll
   for (int u = 0; u < NU; ++u) stg[u] = *reinterpret_cast<const u32x4*>(base + 512 * u);
 }
+// The same tile straight into LDS buffer buf (global_load_lds_dwordx4: each lane's 16 bytes
+// land at the wavefront-uniform fragment base + 16 lane, which is the fragment-major slot),
+// so no registers hold the tile in flight.  Completion is counted by vmcnt: wait for
+// vmcnt(0) (dense_fetch_wait) before the barrier that publishes the buffer.
+template <int D>
+__device__ __forceinline__ void dense_fetch_tile(const char* Rb, const Geo& geo, int l, int t, int wave, int lane,
+                                                 char* lds, int buf) {
+  constexpr int NU = 2 * (D / 16) / kDenseWaves, TILE = 2 * (D / 16) * 1024;
+  const int node = geo.off[l - 1] + min(32 * t + (lane & 31), geo.n[l - 1] - 1);
+  const char* base = Rb + 2 * rc_node(node, D) + 64 * (lane >> 5) + 256 * (wave >> 1) + 128 * (wave & 1);
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+    __builtin_amdgcn_global_load_lds(base + 512 * u,
+                                     (__attribute__((address_space(3))) void*)(lds + buf * TILE + (wave + kDenseWaves * u) * 1024),
+                                     16, 0, 0);
+}
+__device__ __forceinline__ void dense_fetch_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 template <int D, int NU>
 __device__ __forceinline__ void dense_store_tile(char* lds, int buf, int wave, int lane, const u32x4 (&stg)[NU]) {
   constexpr int TILE = 2 * (D / 16) * 1024;
