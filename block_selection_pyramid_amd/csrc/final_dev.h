@@ -113,9 +113,15 @@ __device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, in
 // LSE over the 64 keys of this lane's column (32 here, 32 in lane l ^ 32), in units of
 // the scaled dot product.  Masked keys hold -inf; at least one key is live.
 __device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
+  // The max: fmed3 against +inf in a register the compiler cannot see through is the max of
+  // two raw MFMA results without canonicalising each first (which fmaxf would do), then
+  // max3 over those pair maxima.
+  float pinf = INFINITY;
+  asm volatile("" : "+s"(pinf));
   float m = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) m = fmaxf(m, fmaxf(a0[v], a1[v]));
+  for (int v = 0; v < 16; v += 2)
+    m = fmaxf(m, fmaxf(__builtin_amdgcn_fmed3f(a0[v], a1[v], pinf), __builtin_amdgcn_fmed3f(a0[v + 1], a1[v + 1], pinf)));
   m = fmaxf(m, __shfl_xor(m, 32));
   // exp(s (a - m)) as 2^(a s log2(e) - m s log2(e)): one fused multiply-add per key
   const float ms = m * s_log2e;

@@ -112,14 +112,15 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   const int live1 = two ? min(kLeaf, geo.N - (2 * m + 1) * kLeaf) : 0;
   const int twoK = 2 * geo.K;
 
-  for (int u = 0; u < NCG; ++u) {
-    if (e0 + (u * 4 + wave) * CPG >= e1) break;  // uniform across the wavefront
+  // column group u scores with cur while the next group's query fragments load into nxt;
+  // two groups per iteration swap the roles, so no fragment is copied between registers
+  auto step = [&](int u, const bf16x8 (&cur)[KS], bf16x8 (&nxt)[KS]) {
+    if (e0 + (u * 4 + wave) * CPG >= e1) return false;  // uniform across the wavefront
     const int ent_n = u + 1 < NCG ? ents[((u + 1) * 4 + wave) * CPG + col / G] : -1;
-    bf16x8 bqn[KS];
-    load_bfrag_step<D>(qh + (ent_n >> 6) * qrow, ent_n >= 0, qstep, bqn);
+    load_bfrag_step<D>(qh + (ent_n >> 6) * qrow, ent_n >= 0, qstep, nxt);
 
     f32x16 acc0, acc1;
-    tile_mfma32<D>(kt, bq, lane, acc0, acc1);
+    tile_mfma32<D>(kt, cur, lane, acc0, acc1);
     if (live0 < kLeaf) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
     const float lse0 = group_sum<G>(column_lse32(acc0, acc1, geo.s, geo.s_log2e));
     float lse1 = 0.f;
     if (two) {
-      tile_mfma32<D>(kt + kLeaf * LDSR, bq, lane, acc0, acc1);
+      tile_mfma32<D>(kt + kLeaf * LDSR, cur, lane, acc0, acc1);
       if (live1 < kLeaf) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -146,8 +147,13 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
       if (two) dst[1] = lse1;
     }
     ent = ent_n;
-#pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) bq[s2] = bqn[s2];
+    return true;
+  };
+  static_assert(NCG % 2 == 0, "column groups come in pairs");
+  bf16x8 bqn[KS];
+  for (int u = 0; u < NCG; u += 2) {
+    if (!step(u, bq, bqn)) break;
+    if (!step(u + 1, bqn, bq)) break;
   }
 }
 
