@@ -122,15 +122,16 @@ __device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1
 #pragma unroll
   for (int v = 0; v < 16; v += 2)
     m = fmaxf(m, fmaxf(__builtin_amdgcn_fmed3f(a0[v], a1[v], pinf), __builtin_amdgcn_fmed3f(a0[v + 1], a1[v + 1], pinf)));
-  m = fmaxf(m, __shfl_xor(m, 32));
+  m = xor32_max(m);
   // exp(s (a - m)) as 2^(a s log2(e) - m s log2(e)): one fused multiply-add per key
   const float ms = m * s_log2e;
   float sum = 0.f;
 #pragma unroll
   for (int v = 0; v < 16; ++v)
     sum += __builtin_amdgcn_exp2f(fmaf(a0[v], s_log2e, -ms)) + __builtin_amdgcn_exp2f(fmaf(a1[v], s_log2e, -ms));
-  sum += __shfl_xor(sum, 32);
-  return s * m + logf(sum);
+  sum = xor32_sum(sum);
+  // sum >= 1 (the max key contributes 2^0), so log2 times ln 2 needs no range handling
+  return s * m + 0.6931471805599453f * __builtin_amdgcn_logf(sum);
 }
 
 // VALU score of one leaf tile for one query group: lane = key of the tile.

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
       s1[w] = (t1 <= i && t1 < N) ? s1[w] * sl : -INFINITY;
       mx = fmaxf(mx, fmaxf(s0[w], s1[w]));
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // key 64 j <= i is live for a valid pair
+    mx = xor32_max(mx);  // key 64 j <= i is live for a valid pair
     if (!valid) mx = 0.f;                // padding columns: all probabilities 0, never written
     float sum = 0.f;
     bf16x8 pa[4];
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
       pa[w >> 3][w & 7] = (__bf16)p0;
       pa[2 + (w >> 3)][w & 7] = (__bf16)p1;
     }
-    sum += __shfl_xor(sum, 32);
+    sum = xor32_sum(sum);
 
     f32x16 ao[DB];
 #pragma unroll
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict
           s1[w] = (named && t1 <= i && t1 < N) ? s1[w] * sl : -INFINITY;
           mx = fmaxf(mx, fmaxf(s0[w], s1[w]));
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = xor32_max(mx);
         const float mnew = fmaxf(mrun, mx);
         // running maximum still -inf: every key so far is masked and contributes nothing
         const float base = mnew == -INFINITY ? 0.f : mnew;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(512) void attn_forced_kernel(const bf16* __restrict
           pa[w >> 3][w & 7] = (__bf16)p0;
           pa[2 + (w >> 3)][w & 7] = (__bf16)p1;
         }
-        sum += __shfl_xor(sum, 32);
+        sum = xor32_sum(sum);
         lrun = lrun * alpha + sum;
         mrun = mnew;
 #pragma unroll
