@@ -101,12 +101,26 @@ __device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, in
     acc0[v] = 0.f;
     acc1[v] = 0.f;
   }
+  // key fragments one k-step ahead (step s + 1's reads in flight while step s's products
+  // issue), held in that order through scheduling: otherwise each product waits out its
+  // own LDS round trip
+  bf16x8 a[2][2];
+  auto rd = [&](int s, bf16x8 (&f)[2]) {
+    f[0] = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + 16 * s + 8 * hh);
+    f[1] = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + 16 * s + 8 * hh);
+  };
+  rd(0, a[0]);
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(kt + col * LDSR + 16 * s + 8 * hh);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(kt + (32 + col) * LDSR + 16 * s + 8 * hh);
-    acc0 = mfma32(a0, bq[s], acc0);
-    acc1 = mfma32(a1, bq[s], acc1);
+    if (s + 1 < KS) rd(s + 1, a[(s + 1) & 1]);
+    acc0 = mfma32(a[s & 1][0], bq[s], acc0);
+    acc1 = mfma32(a[s & 1][1], bq[s], acc1);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
 }
 

@@ -171,27 +171,48 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
     }
     const bool more = ln >= l_bot;
     const int ltn = more ? tile_level(ln) : lt;
-    // the next tile goes straight into the other buffer, which every wavefront finished
-    // reading before the previous step's barrier
-    if (more) dense_fetch_tile<D>(Rb, geo, ltn + 1, tn, wave, lane, lds, buf ^ 1);
 
     // ---- products of the 32 level-lt nodes of tile t with this wavefront's queries
+    // the level size the epilogue needs, loaded (and waited for) before the products: a
+    // scalar load in flight among the fragment reads makes every LDS wait a full drain
+    int ntn = geo.n[lt];
+    asm volatile("" : "+s"(ntn));
     const char* Tt = lds + buf * TILE;
     f32x16 acc[NCG];
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[cg][v] = 0.f;
+    // A fragments one k-step ahead: the reads of step ks + 1 are in flight while step ks's
+    // products issue, so no k-step waits out a full LDS round trip
+    bf16x8 fa[2][2];
+    auto read_a = [&](int ks, bf16x8 (&f)[2]) {
+      f[0] = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks) * 64 + lane) * 16);
+      f[1] = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks + 1) * 64 + lane) * 16);
+    };
+    read_a(0, fa[0]);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks) * 64 + lane) * 16);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(Tt + ((2 * ks + 1) * 64 + lane) * 16);
+      if (ks + 1 < KS) read_a(ks + 1, fa[(ks + 1) & 1]);
 #pragma unroll
       for (int cg = 0; cg < NCG; ++cg) {
-        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[cg][ks], acc[cg], 0, 0, 0);
-        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[cg][ks], acc[cg], 0, 0, 0);
+        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][0], qf[cg][ks], acc[cg], 0, 0, 0);
+        acc[cg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][1], qf[cg][ks], acc[cg], 0, 0, 0);
       }
     }
+    // keep that order through scheduling: step 0's two reads, then per step the next step's
+    // two reads ahead of this step's products (the register-pressure scheduler would
+    // otherwise wait for each step's reads right before its products)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * NCG, 0);
+    }
+    // the next tile goes straight into the other buffer, which every wavefront finished
+    // reading before the previous step's barrier; issued after the fragment reads, since
+    // with a transfer into LDS in flight the reads' waits can no longer be counted
+    if (more) dense_fetch_tile<D>(Rb, geo, ltn + 1, tn, wave, lane, lds, buf ^ 1);
     // Epilogue.  Result row (tile node) 8a + 4hh + v sits in acc[4a + v]: the lane holds
     // the four nodes 8a + 4hh .. +3, i.e. the children of the two level-(lt+1) nodes
     // 4a + 2hh + p of the tile (p = 0, 1), which are the children of level-(lt+2) node
@@ -204,7 +225,6 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
     // a path without masks.  (fmed3 against +inf is the max without canonicalising the raw
     // MFMA results first.)
     const int base = 32 * t;
-    const int ntn = geo.n[lt];
     const int vsh = lt - 1;  // a level-lt node c is visible to leaf block bq iff c <= bq >> vsh
     const int lim = min(ntn - 1, bqw >> vsh) - base;  // visible rows of the wavefront's leaf block: <= lim
     const int elim = ntn - 1 - base;                  // existing rows: <= elim
