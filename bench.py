@@ -36,8 +36,10 @@ import numpy as np
 METRIC = "pyramid selection latency ms @64K/256K prefill (C=64,K=8); decode µs/step"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-# exp2 / log2 issue at a quarter of the fp32 lane rate: 256 CUs x 4 SIMDs x 16 lanes / 4 x 2.4 GHz
-TRANS_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9
+# exp2 / log2 issue at a quarter of the fp32 add rate (measured with a throughput loop: 0.25
+# against 0.82 wave64 instructions per SIMD per ns); the add rate is 32 lanes per SIMD per
+# clock, the figure behind the 157.3 TFLOP/s fp32 vector peak: 256 CUs x 4 SIMDs x 8 x 2.4 GHz
+TRANS_PEAK_PER_S = 256 * 4 * 8 * 2.4e9
 
 
 def log(*a):
