@@ -718,18 +718,19 @@ __device__ __forceinline__ void score_tiles_mfma(const bf16* __restrict__ keys, 
         if (t > i || t >= N) acc[rb][v] = -INFINITY;
         mx = fmaxf(mx, acc[rb][v]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // key jC <= i is live, so mx is finite
+    // lane bits 4 and 5 hold the other keys of the column: combined in registers
+    // (v_permlane16/32_swap), not through LDS
+    mx = xor32_max(xor16_max(mx));  // key jC <= i is live, so mx is finite
     const float ms = mx * s_log2e;
     float sum = 0.f;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][v], s_log2e, -ms));
-    sum += __shfl_xor(sum, 16);
-    sum += __shfl_xor(sum, 32);
-    const float lse = group_sum<G>(s * mx + logf(sum));  // lanes 0 .. G-1: the group's heads
-    out[u] = __shfl(lse, 0);
+    sum = xor32_sum(xor16_sum(sum));
+    // sum >= 1 (the max key contributes 2^0): log2 times ln 2 needs no range handling
+    const float lse = group_sum<G>(s * mx + 0.6931471805599453f * __builtin_amdgcn_logf(sum));
+    out[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lse)));  // lanes 0 .. G-1: the group's heads
   }
 }
 
