@@ -9,13 +9,15 @@
 // kernels paragraph: a single-stage kernel for decode avoids launch overhead; rcap.io
 // explainer: one query at a time leaves no cross-query tile reuse): one workgroup of 8
 // wavefronts per (sequence, KV head).  All of them first load the query rows and stage
-// the top pyramid levels' routing copy in LDS (one parallel burst); wavefront 0 then walks
-// the pyramid for the new query at position N-1, its top levels from LDS and two levels
-// per round of gathers below them (bf16: MfmaWalk::pair_step), while wavefronts 1..3 score
-// the forced tiles (known up front); then every wavefront scores two of the <= 2K routed
-// tiles with both tiles' loads in flight together (bf16 on the matrix cores, 16 keys x 32
-// dims per MFMA against the G head columns), and wavefront 0 writes the selection.  One
-// launch per step.  With
+// the top pyramid levels' routing copy in LDS (one parallel burst).  bf16: wavefronts 0..3
+// then walk the pyramid for the new query at position N-1 together, its top levels from
+// LDS and two levels per round of gathers below them, each scoring a quarter of every
+// round's tiles (MfmaWalk::pair_step_mw; wavefront 0 runs the Top-Ks), while wavefronts
+// 4..6 hold the forced tiles' loads (known up front) and score them after the walk; fp32:
+// wavefront 0 walks alone and wavefronts 1..3 score the forced tiles.  Then every
+// wavefront scores two of the <= 2K routed tiles with both tiles' loads in flight together
+// (bf16 on the matrix cores, 16 keys x 32 dims per MFMA against the G head columns), and
+// wavefront 0 writes the selection.  One launch per step.  With
 // per-sequence lengths each workgroup first re-derives its sequence's level table in LDS
 // (node offsets stay those of the capacity layout that pisa_append_keys maintains).
 #include <type_traits>
@@ -158,31 +160,46 @@ __device__ __forceinline__ void decode_body(const T* __restrict__ q, const T* __
     }
     if (lane == 0) tsc[t] = s;
   };
-  if (wave == 0) {
-    int nx;
-    const int32_t* X;
-    if constexpr (std::is_same<T, bf16>::value) {
-      MfmaWalk<D, G, 1> mw;
-      mw.R = R;
-      mw.lds = stage;
-      mw.stage_lo = stage_lo < geo.L ? stage_lo : 1 << 30;
-      mw.stage_base = sbase;
-      mw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
-      nx = mw.walk_pairs(geo, bq, &wlm, lane);
-      X = wlm.X;
-    } else {
-      ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.Tp * D, qs};
-      nx = route_walk(geo, sc, bq, &wl, lane);
-      X = wl.X;
-    }
-    if (lane < twoK) {
-      leaf = lane < nx ? X[lane] : -1;
+  if constexpr (std::is_same<T, bf16>::value) {
+    // The walk on wavefronts 0..3 (each scoring a quarter of every step's tiles); the
+    // forced tiles, known up front, on wavefronts 4..6: their loads go out before the walk
+    // and are scored after it, so the walk's workgroup barriers never wait on them.
+    using Walk = MfmaWalk<D, G, 1>;
+    Walk mw;
+    mw.R = R;
+    mw.lds = stage;
+    mw.stage_lo = stage_lo < geo.L ? stage_lo : 1 << 30;
+    mw.stage_base = sbase;
+    mw.load_q([&](int, int r) -> const bf16* { return rows[r]; }, lane);
+    const int fw = wave - Walk::kWalkWaves;
+    const bool fmine = fw >= 0 && fw < nf;
+    const int fj[1] = {fmine ? (fw == 0 ? F[0] : (fw == 1 ? F[1] : F[2])) : -1};
+    bf16x8 fa[1][4][D / 32];
+    if (fmine) load_key_tiles<D, 1>(keys, fj, geo.N, geo.C, lane, fa);
+    const int nx = mw.walk_pairs_mw(geo, bq, &wlm, lane, wave);
+    if (wave == 0 && lane < twoK) {
+      leaf = lane < nx ? wlm.X[lane] : -1;
       if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
       tj[lane] = leaf;
     }
-  } else if (wave <= nf) {
-    // the forced tiles are known up front: wavefronts 1..nf score them during the walk
-    score_tile(twoK + wave - 1, wave == 1 ? F[0] : (wave == 2 ? F[1] : F[2]));
+    if (fmine) {
+      float fs[1];
+      score_loaded_tiles<D, G, 1>(fa, fj, i, geo.N, geo.C, mw.qb[0], lane, geo.s, geo.s_log2e, fs);
+      if (lane == 0) tsc[twoK + fw] = fs[0];
+    }
+  } else {
+    if (wave == 0) {
+      ValuScorer<D, G> sc{pyr + (int64_t)bh * geo.Tp * D, qs};
+      const int nx = route_walk(geo, sc, bq, &wl, lane);
+      if (lane < twoK) {
+        leaf = lane < nx ? wl.X[lane] : -1;
+        if (leaf >= 0 && is_forced(leaf, bq)) leaf = -1;
+        tj[lane] = leaf;
+      }
+    } else if (wave <= nf) {
+      // the forced tiles are known up front: wavefronts 1..nf score them during the walk
+      score_tile(twoK + wave - 1, wave == 1 ? F[0] : (wave == 2 ? F[1] : F[2]));
+    }
   }
   __syncthreads();
   // the routed leaf candidates (forced blocks excluded): tiles t and t + kDecodeWaves of a

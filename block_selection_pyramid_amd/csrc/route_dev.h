@@ -58,6 +58,7 @@ struct alignas(16) WalkLdsM {  // 16-byte aligned: key arrays are read two keys 
   float sc[kMaxCand], er[kMaxCand];
   int32_t cls[kMaxCand], U[kMaxCand];
   uint64_t key2[kMaxCand];
+  int32_t nx_shared;  // the walk's candidate count, for the wavefronts that share a walk
 };
 
 // |lo| <= 2^-8 (1 + 2^-8) |hi| elementwise for hi = v rounded to nearest in bf16 and
@@ -660,6 +661,154 @@ struct MfmaWalk {
     return 2 * nk;
   }
 
+  // pair_step spread over the workgroup (decode): wavefronts 0 .. kWalkWaves-1 score tiles
+  // wave, wave + kWalkWaves, ... (one tile of four candidates at a time, each wavefront with
+  // its own copy of the query fragments), so a step's products and epilogues run four at
+  // a time; wavefront 0 then runs both Top-Ks.  Every wavefront of the workgroup must call
+  // it (it holds three workgroup barriers); the returned count is the same in all of them.
+  static constexpr int kWalkWaves = 4;
+  template <bool kLds>
+  __device__ int pair_step_mw(const Geo& geo, int bq, int l, int nx, WalkLdsM<GPW>* w, int lane, int wave) const {
+    static_assert(GPW == 1, "one query group per workgroup");
+    const int K = geo.K;
+    const int lb = l - 2;  // level of the gathered nodes (>= 1)
+    const int nb = geo.n[lb];
+    const int sh = lb - 1;  // a level-lb node g covers leaf blocks from g << sh
+    const char* Lc = kLds ? lds + (int64_t)(geo.off[lb] - stage_base) * kRecLds : nullptr;
+    const int m = lane & 15, kg = lane >> 4;
+    const int rb = m >> 2, v = m & 3;
+    const float c2 = trunc_c2(geo.scorer, true);
+    const bool lse = geo.scorer == PISA_LSE;
+    auto pair = [&](float y0, float y1) {  // y0: a visible child's dot; y1: -inf if absent
+      const float a = fmaxf(y0, y1), b = fminf(y0, y1);
+      return lse ? a + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(b - a)) : pair_trunc(a, b, 1.f, c2);
+    };
+    const int ntiles = (nx + 3) >> 2;
+    if (wave < kWalkWaves) {
+      for (int t = wave; t < ntiles; t += kWalkWaves) {
+        bf16x8 hi[KS], lo[KS];
+        const int xe = 4 * t + kg;
+        const int ye = xe < nx ? w->X[xe] : -1;  // epilogue: candidate 4t + kg of this lane
+        const int x = 4 * t + rb;
+        const int y = x < nx ? w->X[x] : -1;
+        const int gc = y >= 0 ? 4 * y + v : -1;
+        const int ca = (gc >= 0 && gc < nb) ? gc : 0;  // a missing grandchild reads node 0, never used
+        if constexpr (kLds) {
+          const char* rp = Lc + (int64_t)ca * kRecLds + 16 * kg;
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            hi[s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s);
+            lo[s] = *reinterpret_cast<const bf16x8*>(rp + 128 * s + 64);
+          }
+        } else {
+          const bf16* rp = R + rc_node(geo.off[lb] + ca, D) + rc_piece(kg);  // piece 4 s + kg
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            hi[s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
+            lo[s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the tile's loads in flight before its first product
+        f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[s], qb[0][s], a, 0, 0, 0);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[s], qb[0][s], a, 0, 0, 0);
+        }
+        const int g0 = 4 * ye;
+        const bool e1 = g0 + 1 < nb, e2 = g0 + 2 < nb, e3 = g0 + 3 < nb;
+        const bool v1 = e1 && ((int64_t)(g0 + 1) << sh) <= bq;
+        const bool v2 = e2 && ((int64_t)(g0 + 2) << sh) <= bq;
+        const bool v3 = e3 && ((int64_t)(g0 + 3) << sh) <= bq;
+        // children 2y and 2y+1 of candidate y (the latter exists iff 4y+2 does, is visible
+        // iff 4y+2 is): their dots are the means of their existing children's dots
+        const float d0 = e1 ? 0.5f * (a[0] + a[1]) : a[0];
+        const float d1 = e3 ? 0.5f * (a[2] + a[3]) : a[2];
+        const float sl = group_sum<G>(pair(d0, v2 ? d1 : -INFINITY));  // y at level l
+        const float s0 = group_sum<G>(pair(a[0], v1 ? a[1] : -INFINITY));  // 2y at level l - 1
+        const float s1 = group_sum<G>(pair(a[2], v3 ? a[3] : -INFINITY));  // 2y+1 (if v2)
+        if (m == 0 && xe < nx) {
+          w->key[xe] = ye >= 0 ? cand_key(sl, ye) : 0ull;
+          w->sc[xe] = s0;
+          w->er[xe] = s1;
+        }
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      w->key2[lane] = 0ull;
+      w->U[lane] = -1;
+      wave_sync();
+      // Top-K of level l; the kept node of rank r opens level-(l-1) slots 2r, 2r+1
+      {
+        const uint64_t my = lane < nx ? w->key[lane] : 0ull;
+        int rank = 0;
+#pragma unroll 4
+        for (int y = 0; y < nx; y += 2) {
+          const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(w->key + y);
+          rank += (kk.x > my) + (y + 1 < nx && kk.y > my);
+        }
+        if (my != 0ull && rank < K) {
+          const int y = w->X[lane];
+          const bool vis1 = child_visible(2 * y + 1, geo.n[l - 1], l - 2, bq);
+          w->U[2 * rank] = 2 * y;
+          w->key2[2 * rank] = cand_key(w->sc[lane], 2 * y);
+          w->U[2 * rank + 1] = vis1 ? 2 * y + 1 : -1;
+          w->key2[2 * rank + 1] = vis1 ? cand_key(w->er[lane], 2 * y + 1) : 0ull;
+        }
+      }
+      wave_sync();
+      // Top-K of level l - 1; the kept node of rank r opens level-(l-2) slots 2r, 2r+1
+      const uint64_t my = w->key2[lane];
+      int rank = 0;
+#pragma unroll 4
+      for (int y = 0; y < 2 * K && y < kMaxCand; y += 2) {
+        const ulonglong2 kk = *reinterpret_cast<const ulonglong2*>(w->key2 + y);
+        rank += (kk.x > my) + (kk.y > my);
+      }
+      const int z = w->U[lane];
+      const int nk = min(K, (int)__popcll(__ballot(my != 0ull)));
+      w->X[lane] = -1;
+      wave_sync();
+      if (my != 0ull && rank < K) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int ch = 2 * z + c;
+          w->X[2 * rank + c] = child_visible(ch, geo.n[l - 2], l - 3, bq) ? ch : -1;
+        }
+      }
+      if (lane == 0) w->nx_shared = 2 * nk;
+    }
+    __syncthreads();
+    return w->nx_shared;
+  }
+
+  // The walk spread over the workgroup: pair_step_mw while at least two routing levels
+  // remain, the top level's set-up and a last single level on wavefront 0.  Every
+  // wavefront calls it; all of them return the count of level-1 candidates in X.
+  __device__ int walk_pairs_mw(const Geo& geo, int bq, WalkLdsM<GPW>* w, int lane, int wave) const {
+    if (wave == 0) {
+      const int n0 = init_level(geo, bq, geo.L, w, lane);
+      if (lane == 0) w->nx_shared = n0;
+    }
+    __syncthreads();
+    int nx = w->nx_shared;
+    int l = geo.L;
+    for (; l >= 3; l -= 2)
+      nx = l - 2 >= stage_lo ? pair_step_mw<true>(geo, bq, l, nx, w, lane, wave)
+                             : pair_step_mw<false>(geo, bq, l, nx, w, lane, wave);
+    if (l == 2) {
+      __syncthreads();  // every wavefront has read nx before wavefront 0 writes it again
+      if (wave == 0) {
+        const int n1 = walk_levels(geo, bq, 2, 2, nx, w, lane);
+        if (lane == 0) w->nx_shared = n1;
+      }
+      __syncthreads();
+      nx = w->nx_shared;
+    }
+    return nx;
+  }
+
   // The whole walk for one query group per wavefront, two levels per gather while at
   // least two routing levels remain (pair_step), then the last one alone.
   __device__ int walk_pairs(const Geo& geo, int bq, WalkLdsM<GPW>* w, int lane) const {
@@ -679,13 +828,11 @@ struct MfmaWalk {
 // keys t <= i (t < N) of block j[u], in natural units, in every lane (a tile with j[u] < 0
 // reads block 0 and its result is meaningless).  Every tile's loads go out before the
 // first product, so the NT tiles cost one round trip.
-template <int D, int G, int NT>
-__device__ __forceinline__ void score_tiles_mfma(const bf16* __restrict__ keys, const int (&jt)[NT], int i, int N,
-                                                 int C, const bf16x8 (&qb)[D / 32], int lane, float s, float s_log2e,
-                                                 float (&out)[NT]) {
+template <int D, int NT>
+__device__ __forceinline__ void load_key_tiles(const bf16* __restrict__ keys, const int (&jt)[NT], int N, int C, int lane,
+                                               bf16x8 (&a)[NT][4][D / 32]) {
   constexpr int KS = D / 32;
   const int m = lane & 15, kg = lane >> 4;
-  bf16x8 a[NT][4][KS];
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int j = jt[u] >= 0 ? jt[u] : 0;
@@ -696,9 +843,15 @@ __device__ __forceinline__ void score_tiles_mfma(const bf16* __restrict__ keys, 
       for (int k = 0; k < KS; ++k) a[u][rb][k] = *reinterpret_cast<const bf16x8*>(keys + (int64_t)t * D + 32 * k + 8 * kg);
     }
   }
-  // the tiles' loads in flight before the first product (G <= 4: with more heads the
-  // decode kernel would spill)
-  if constexpr (G <= 4) __builtin_amdgcn_sched_barrier(0);
+}
+
+// The scores of tiles already loaded by load_key_tiles.
+template <int D, int G, int NT>
+__device__ __forceinline__ void score_loaded_tiles(const bf16x8 (&a)[NT][4][D / 32], const int (&jt)[NT], int i, int N,
+                                                   int C, const bf16x8 (&qb)[D / 32], int lane, float s, float s_log2e,
+                                                   float (&out)[NT]) {
+  constexpr int KS = D / 32;
+  const int kg = lane >> 4;
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int j = jt[u] >= 0 ? jt[u] : 0;
@@ -732,6 +885,18 @@ __device__ __forceinline__ void score_tiles_mfma(const bf16* __restrict__ keys, 
     const float lse = group_sum<G>(s * mx + 0.6931471805599453f * __builtin_amdgcn_logf(sum));
     out[u] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(lse)));  // lanes 0 .. G-1: the group's heads
   }
+}
+
+template <int D, int G, int NT>
+__device__ __forceinline__ void score_tiles_mfma(const bf16* __restrict__ keys, const int (&jt)[NT], int i, int N,
+                                                 int C, const bf16x8 (&qb)[D / 32], int lane, float s, float s_log2e,
+                                                 float (&out)[NT]) {
+  bf16x8 a[NT][4][D / 32];
+  load_key_tiles<D, NT>(keys, jt, N, C, lane, a);
+  // the tiles' loads in flight before the first product (G <= 4: with more heads the
+  // decode kernel would spill)
+  if constexpr (G <= 4) __builtin_amdgcn_sched_barrier(0);
+  score_loaded_tiles<D, G, NT>(a, jt, i, N, C, qb, lane, s, s_log2e, out);
 }
 
 template <int D, int G>
