@@ -145,9 +145,10 @@ __global__ __launch_bounds__(256, KC <= 8 ? 3 : 2) void route_dense_kernel(const
   // level-(l-1) dots (pair means, over the children that exist) and with them both levels'
   // scores, and the level-(l - 1) candidates (children of the level-l nodes kept) are
   // children of level-l candidates, whose scores the items pick up in the same sweep.  A
-  // single pass scores level l from the tiles of level l - 1 (the last level when the dense
-  // levels are odd in number).  Pair passes cost the tiles of every other level only.
-  auto is_pair = [&](int lv) { return lv - 1 >= l_bot && lv >= 3; };
+  // single pass scores level l from the tiles of level l - 1.  Pair passes cost the tiles of
+  // every other level only; when the dense levels are odd in number the single pass is the
+  // top one, whose tiles are the fewest, and the pairs end at l_bot.
+  auto is_pair = [&](int lv) { return ((lv - l_bot) & 1) && lv >= 3; };
   auto tile_level = [&](int lv) { return is_pair(lv) ? lv - 2 : lv - 1; };
   auto ntiles = [&](int lt) {  // tiles of the visible prefix of level lt
     const int nv = min(geo.n[lt], (bqmax >> (lt - 1)) + 1);
