@@ -155,6 +155,23 @@ __device__ __forceinline__ float group_prod(float v) {
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x >> 1); }
 
+// The largest list l in [lo, hi) whose first chunk choff[l] is <= c, given choff[lo] <= c <
+// choff[hi] (choff non-decreasing: empty lists repeat an offset).  A 64-way search: every
+// lane of the wavefront probes one offset per round, so 8192 lists take three rounds of
+// loads instead of thirteen dependent ones.  Uniform across the wavefront.
+__device__ __forceinline__ int find_chunk_list(const int32_t* __restrict__ choff, int lo, int hi, int c, int lane) {
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) >> 6;
+    const int idx = lo + step * lane;
+    const bool ok = lane == 0 || (idx < hi && choff[idx] <= c);  // a prefix of the lanes
+    const unsigned long long bal = __ballot(ok);
+    const int t = 63 - __clzll(bal);
+    lo += step * t;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
 // Sum (or product) of NV values per lane over the G lanes of a query group, scattered:
 // afterwards lane r of the group holds the results for values (r % GE) VPL .. + VPL - 1 in
 // v[0 .. VPL), GE = min(G, NV), VPL = NV / GE.  The exchanges run from the highest lane bit

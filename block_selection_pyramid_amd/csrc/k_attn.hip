@@ -260,12 +260,7 @@ __global__ __launch_bounds__(256) void attn_chunk_kernel(const bf16* __restrict_
 
   const int c = choff[Mlo] + blockIdx.x;
   if (c >= choff[Mhi]) return;  // uniform: grid is an upper bound on the range's chunk count
-  int lo = Mlo, hi = Mhi;        // largest list whose first chunk is <= c
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (choff[mid] <= c) lo = mid; else hi = mid;
-  }
-  const int list = lo;
+  const int list = find_chunk_list(choff, Mlo, Mhi, c, threadIdx.x & 63);  // largest list whose first chunk is <= c
   const int bh = (list / geo.n1) % (geo.B * geo.Hkv), j = list % geo.n1;
   const int e0 = off[list] + (c - choff[list]) * QC;
   const int e1 = min(e0 + QC, off[list + 1]);

@@ -58,12 +58,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
 
   const int c = blockIdx.x;
   if (c >= choff[M]) return;  // uniform: the grid is an upper bound on the chunk count
-  int lo = 0, hi = M;  // largest list whose first chunk is <= c
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (choff[mid] <= c) lo = mid; else hi = mid;
-  }
-  const int list = lo;
+  const int list = find_chunk_list(choff, 0, M, c, threadIdx.x & 63);
   const int bh = list / geo.n1p, m = list % geo.n1p;
   const int e0 = off[list] + (c - choff[list]) * QC;
   const int e1 = min(e0 + QC, off[list + 1]);
