@@ -371,7 +371,10 @@ def gpu_decode(env, w):
     return p, op, q, k, qd, kd, pyr, idx.cpu().numpy(), sc.cpu().numpy()
 
 
-@pytest.mark.parametrize("N,B,K,G", [(16384 + 5, 4, 8, 4), (64 * 33, 2, 32, 2), (100, 3, 3, 1), (1, 2, 8, 4)])
+# the last two walk several levels with more than 16 candidates per level (several tiles
+# per walking wavefront) at G = 8 and 16
+@pytest.mark.parametrize("N,B,K,G", [(16384 + 5, 4, 8, 4), (64 * 33, 2, 32, 2), (100, 3, 3, 1), (1, 2, 8, 4),
+                                     (64 * 3000 + 7, 1, 32, 8), (64 * 777 + 33, 2, 16, 16)])
 def test_decode_parity_and_matches_prefill(env, N, B, K, G):
     torch, pisa = env
     w = synth.custom(name="decode-%d" % N, batch=B, seq_len=N, n_q_heads=2 * G, n_kv_heads=2, head_dim=128, top_k=K,
