@@ -173,6 +173,48 @@ def test_prefill_edge_cases(env, case):
     verify(op, q, k, opyr, np.arange(B * Hkv * N), idx, sc, what=name)
 
 
+def random_shape(i, decode=False):
+    """Seeded random problem shape i: head groups of 1..16, one or two KV heads, d = 64 or
+    128, K = 3..32, lengths from one token to ~20K with a bias towards multiples of the
+    leaf block (ragged tails and exact fills), bf16 mostly."""
+    rng = np.random.default_rng(4242 + i + (1000 if decode else 0))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2]))
+    d = int(rng.choice([64, 128]))
+    K = int(rng.integers(3, 33))  # K >= 3: the three forced blocks count inside K
+    if rng.random() < 0.4:
+        N = int(64 * rng.integers(1, 300) + rng.integers(-2, 3))
+    else:
+        N = int(rng.integers(1, 20000))
+    N = max(N, 1)
+    B = int(rng.choice([1, 2])) if not decode else int(rng.integers(1, 5))
+    dt = synth.F32 if (d == 64 and rng.random() < 0.2) else synth.BF16
+    return N, B, G, Hkv, d, K, dt
+
+
+@pytest.mark.parametrize("i", range(16), ids=["rand%d" % i for i in range(16)])
+def test_prefill_random_shapes(env, i):
+    N, B, G, Hkv, d, K, dt = random_shape(i)
+    name = "rand%d-N%d-B%d-G%d-H%d-d%d-K%d-%s" % (i, N, B, G, Hkv, d, K, "f32" if dt == synth.F32 else "bf16")
+    w = synth.custom(name=name, batch=B, seq_len=N, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     dtype=dt, seed=700 + i, needles=min(8, max(N // 200, 1)))
+    p, op, q, k, _, pyr, outs = gpu_prefill(env, w)
+    opyr = check_pyramid(op, k, pyr, name)
+    idx, sc = outs[0]
+    verify(op, q, k, opyr, np.arange(B * Hkv * N), idx, sc, what=name)
+
+
+@pytest.mark.parametrize("i", range(8), ids=["drand%d" % i for i in range(8)])
+def test_decode_random_shapes(env, i):
+    N, B, G, Hkv, d, K, dt = random_shape(i, decode=True)
+    name = "drand%d-N%d-B%d-G%d-H%d-d%d-K%d-%s" % (i, N, B, G, Hkv, d, K, "f32" if dt == synth.F32 else "bf16")
+    w = synth.custom(name=name, batch=B, seq_len=N, n_q_heads=G * Hkv, n_kv_heads=Hkv, head_dim=d, top_k=K,
+                     dtype=dt, seed=800 + i, needles=min(8, max(N // 200, 1)), decode=True)
+    p, op, q, k, qd, kd, pyr, idx, sc = gpu_decode(env, w)
+    opyr = check_pyramid(op, k, pyr.cpu().numpy()[0], name)
+    verify(op, q, k, opyr, np.arange(B * Hkv), idx, sc, decode=True, what=name)
+
+
 @pytest.mark.parametrize("dt,d,decode", [(synth.BF16, 64, False), (synth.BF16, 128, True), (synth.F32, 64, False)])
 def test_non_default_scale(env, dt, d, decode):
     # the routing copy carries the scale, so build and selection must both honour it
