@@ -89,6 +89,16 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// max(a, b, c) in one v_max3_f32.  fmaxf chains become max3 only where the compiler can
+// prove its inputs canonical; values that come from v_med3_f32 of raw matrix-core results
+// are not, so it would emit a v_max_f32 per pair instead.  Operands are VALU results (no
+// matrix-core read hazard to cover).
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // v combined with lane l ^ 32's v, in every lane: v_permlane32_swap exchanges the two
 // halves of the wavefront between two copies of v, so each lane then holds both values in
 // registers (no LDS crossbar round trip, unlike a shuffle).

@@ -74,18 +74,14 @@ __device__ __forceinline__ void load_bfrag(const bf16* __restrict__ qrow, bool v
 }
 
 // B fragments of one column: k-step s at p + s * step (p already at the lane's 8 dims).
+// Always loads: a caller with no row for the column points p at any valid row and
+// discards that column's results, which costs less than zeroing the fragments under a
+// branch.
 template <int D>
-__device__ __forceinline__ void load_bfrag_step(const bf16* __restrict__ p, bool valid, int step, bf16x8* bq) {
+__device__ __forceinline__ void load_bfrag_step(const bf16* __restrict__ p, int step, bf16x8* bq) {
   constexpr int KS = D / 16;
 #pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    if (valid) {
-      bq[s] = *reinterpret_cast<const bf16x8*>(p + step * s);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bq[s][e] = (__bf16)0.f;
-    }
-  }
+  for (int s = 0; s < KS; ++s) bq[s] = *reinterpret_cast<const bf16x8*>(p + step * s);
 }
 
 // 64 keys (LDS tile, two M-tiles of 32) x 32 columns: acc0/acc1[v] of lane l hold keys
@@ -128,14 +124,17 @@ __device__ __forceinline__ void tile_mfma32(const bf16* kt, const bf16x8* bq, in
 // the scaled dot product.  Masked keys hold -inf; at least one key is live.
 __device__ __forceinline__ float column_lse32(const f32x16& a0, const f32x16& a1, float s, float s_log2e) {
   // The max: fmed3 against +inf in a register the compiler cannot see through is the max of
-  // two raw MFMA results without canonicalising each first (which fmaxf would do), then
-  // max3 over those pair maxima.
+  // two raw MFMA results without canonicalising each first (which fmaxf would do), then a
+  // chain of v_max3_f32 over those 16 pair maxima (24 instructions for 32 values).
   float pinf = INFINITY;
   asm volatile("" : "+s"(pinf));
-  float m = -INFINITY;
+  float c[16];
 #pragma unroll
-  for (int v = 0; v < 16; v += 2)
-    m = fmaxf(m, fmaxf(__builtin_amdgcn_fmed3f(a0[v], a1[v], pinf), __builtin_amdgcn_fmed3f(a0[v + 1], a1[v + 1], pinf)));
+  for (int v = 0; v < 16; ++v) c[v] = __builtin_amdgcn_fmed3f(a0[v], a1[v], pinf);
+  float m = vmax3(c[0], c[1], c[2]);
+#pragma unroll
+  for (int v = 3; v < 15; v += 2) m = vmax3(m, c[v], c[v + 1]);
+  m = vmax3(m, c[15], c[15]);
   m = xor32_max(m);
   // exp(s (a - m)) as 2^(a s log2(e) - m s log2(e)): one fused multiply-add per key
   const float ms = m * s_log2e;

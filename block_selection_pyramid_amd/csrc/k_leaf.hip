@@ -74,7 +74,8 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
                       : q + ((int64_t)b * geo.Hq + h * G + r) * geo.N * D + 8 * hh;
   const int64_t qrow = qg ? G * D : D;
   const int qstep = qg ? 16 * G : 16;
-  // entry of this lane's column in column group u of the wavefront (-1: none): the first
+  // entry of this lane's column in column group u of the wavefront (-1: none; the column
+  // then scores the rows of query 0 and its results are never stored): the first
   // from global memory, the others from the chunk's copy in LDS (loaded with the key
   // tiles, so no column group waits on a global round trip for its entry index)
   auto entry = [&](int u) {
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   int ent = entry(0);
   bf16x8 bq[KS];
   // query fragments first: their latency overlaps the key-tile staging
-  load_bfrag_step<D>(qh + (ent >> 6) * qrow, ent >= 0, qstep, bq);
+  load_bfrag_step<D>(qh + max(ent >> 6, 0) * qrow, qstep, bq);
   int ev[EPT];
 #pragma unroll
   for (int x = 0; x < EPT; ++x) {
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(256) void leaf_pair_kernel(const bf16* __restrict__
   auto step = [&](int u, const bf16x8 (&cur)[KS], bf16x8 (&nxt)[KS]) {
     if (e0 + (u * 4 + wave) * CPG >= e1) return false;  // uniform across the wavefront
     const int ent_n = u + 1 < NCG ? ents[((u + 1) * 4 + wave) * CPG + col / G] : -1;
-    load_bfrag_step<D>(qh + (ent_n >> 6) * qrow, ent_n >= 0, qstep, nxt);
+    load_bfrag_step<D>(qh + max(ent_n >> 6, 0) * qrow, qstep, nxt);
 
     f32x16 acc0, acc1;
     tile_mfma32<D>(kt, cur, lane, acc0, acc1);
