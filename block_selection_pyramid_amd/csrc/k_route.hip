@@ -131,7 +131,7 @@ __global__ __launch_bounds__(256) void route_mfma_kernel(const bf16* __restrict_
 
 template <int D, int G, int GPW>
 int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
-                      int32_t* cand, int32_t* cnt, void* qg, hipEvent_t mid, hipStream_t st) {
+                      int32_t* cand, int32_t* cnt, void* qg, uint8_t* lo8, hipEvent_t mid, hipStream_t st) {
   if (g.L >= 3) {
     // every routing level dense: the dense launch writes the leaf candidates
     const bool all_dense = dense_bottom(g) == 2;
@@ -146,34 +146,34 @@ int route_mfma_launch(const Geo& g, const void* q, const void* k, const float* p
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kLowerQueries - 1) / kLowerQueries));
   const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
   const int l_x = g.L >= 3 ? dense_bottom(g) - 1 : 2;  // level of the candidates in x2
-  if (route_sub_supported(g, l_x)) return launch_route_sub(g, l_x, q, pyr, x2, cand, cnt, qg, st);
+  if (route_sub_supported(g, l_x)) return launch_route_sub(g, l_x, q, pyr, x2, cand, cnt, qg, lo8, st);
   route_mfma_kernel<D, G, GPW><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, l_x, x2, cand, cnt);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 template <int D, int G>
 int route_mfma_g(const Geo& g, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
-                 int32_t* cand, int32_t* cnt, void* qg, hipEvent_t mid, hipStream_t st) {
+                 int32_t* cand, int32_t* cnt, void* qg, uint8_t* lo8, hipEvent_t mid, hipStream_t st) {
   const int gpw = route_groups_per_wave(g.G, g.K);
   if constexpr (G <= 4) {
-    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
+    if (gpw == 4) return route_mfma_launch<D, G, 4>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
   }
   if constexpr (G <= 8) {
-    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
+    if (gpw == 2) return route_mfma_launch<D, G, 2>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
   }
-  return route_mfma_launch<D, G, 1>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
+  return route_mfma_launch<D, G, 1>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
 }
 
 template <int D>
 int route_d(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2, float* fsc,
-            int32_t* cand, int32_t* cnt, void* qg, hipEvent_t mid, hipStream_t st) {
+            int32_t* cand, int32_t* cnt, void* qg, uint8_t* lo8, hipEvent_t mid, hipStream_t st) {
   if (dtype == PISA_BF16) {
     switch (g.G) {
-      case 1: return route_mfma_g<D, 1>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
-      case 2: return route_mfma_g<D, 2>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
-      case 4: return route_mfma_g<D, 4>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
-      case 8: return route_mfma_g<D, 8>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
-      case 16: return route_mfma_g<D, 16>(g, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
+      case 1: return route_mfma_g<D, 1>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
+      case 2: return route_mfma_g<D, 2>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
+      case 4: return route_mfma_g<D, 4>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
+      case 8: return route_mfma_g<D, 8>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
+      case 16: return route_mfma_g<D, 16>(g, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
       default: return PISA_ERR_UNSUPPORTED;
     }
   }
@@ -199,9 +199,9 @@ __global__ void zero_kernel(int32_t* __restrict__ a, int64_t n) {
 }  // namespace
 
 int launch_route(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2,
-                 float* fsc, int32_t* cand, int32_t* cnt, void* qg, hipEvent_t mid, hipStream_t st) {
-  if (g.d == 128) return route_d<128>(g, dtype, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
-  if (g.d == 64) return route_d<64>(g, dtype, q, k, pyr, x2, fsc, cand, cnt, qg, mid, st);
+                 float* fsc, int32_t* cand, int32_t* cnt, void* qg, uint8_t* lo8, hipEvent_t mid, hipStream_t st) {
+  if (g.d == 128) return route_d<128>(g, dtype, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
+  if (g.d == 64) return route_d<64>(g, dtype, q, k, pyr, x2, fsc, cand, cnt, qg, lo8, mid, st);
   return PISA_ERR_UNSUPPORTED;
 }
 

@@ -21,9 +21,13 @@
 // candidates in), each of the K kept level-3 nodes contributes its four leaf means and
 // only level 2 is walked here.
 //
-// Matrix cores: v_mfma_f32_16x16x32_bf16 over the level-1 routing copy (hi and lo, so the
-// dots are the scaled scores in log2 units to ~2^-17), four query groups of one leaf block
-// per wavefront, B = their 16 (group, head) query columns.  Tile j holds in row block rb
+// Matrix cores: v_mfma_f32_16x16x32_bf16 over the level-1 routing copy's hi halves, four
+// query groups of one leaf block per wavefront, B = their 16 (group, head) query columns;
+// the lo halves' products follow at d = 128 from a compact fp8 copy (lo8_kernel: each leaf's
+// lo halves as e4m3 scaled by a power of two, undone by the E8M0 scale of
+// v_mfma_scale_f32_16x16x128_f8f6f4, against the query columns in e5m2), which leaves the
+// dots the scaled scores in log2 units to ~2^-13 of the hi product's rounding error and
+// moves 384 instead of 512 bytes per leaf; at d = 64 the bf16 lo halves as well.  Tile j holds in row block rb
 // the four leaf means of level-3 node Y[(rb + j) mod 4][j], so every lane's B operand is
 // its own query fragment and each result lane finds its own group's rows in one tile of
 // every four (mixed-row tiles; G = 4 only).
@@ -49,6 +53,61 @@ struct SubLds {
   int32_t Lf[4][2 * KC];    // leaf candidates out
 };
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// fp8 correction record of leaf n (d = 128): quads of four leaves, then the lane k-group kg,
+// then the leaf in the quad; 32 bytes, byte 8 s + e holding dim 32 s + 8 kg + e -- the dims
+// a route_sub lane holds in its query fragments, in the same order, so that four lanes of
+// one k-group read one 128-byte line.
+__device__ __forceinline__ int64_t lo8_piece(int64_t n, int kg) { return (n >> 2) * 512 + kg * 128 + (n & 3) * 32; }
+
+// Thread = (leaf n, k-group kg), four consecutive lanes per leaf: the 32 lo halves of its
+// dims from the level-1 routing copy, scaled by 2^S (S per leaf: the largest |lo| lands in
+// [128, 256), inside e4m3's range), rounded to e4m3; the leaf's E8M0 byte 127 - S follows
+// the records.  Leaves n1 .. n1q-1 get zeros (the level-2 launch never reads them).
+__global__ __launch_bounds__(256) void lo8_kernel(const float* __restrict__ pyr, Geo geo, uint8_t* __restrict__ lo8) {
+  constexpr int D = 128;
+  const int bh = blockIdx.y;
+  const int n1q = (geo.n1 + 3) & ~3;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int n = t >> 2, kg = t & 3;
+  if (n >= n1q) return;  // all four lanes of a leaf alike
+  const bf16* R1 = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * 2 * D;
+  float r[32];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    // lo half of 8-dim piece 4 s + kg (leaf 0's when n is past n1; zeroed below)
+    const uint4 u = *reinterpret_cast<const uint4*>(R1 + rc_node(n < geo.n1 ? n : 0, D) + rc_piece(4 * s + kg) + 64);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      r[8 * s + 2 * h] = n < geo.n1 ? bf2f(w[h] & 0xFFFFu) : 0.f;
+      r[8 * s + 2 * h + 1] = n < geo.n1 ? bf2f(w[h] >> 16) : 0.f;
+    }
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) mx = fmaxf(mx, fabsf(r[e]));
+  mx = fmaxf(mx, __shfl_xor(mx, 1));
+  mx = fmaxf(mx, __shfl_xor(mx, 2));
+  // mx < 2^E with E = biased exponent - 126; below 2^-100 the record stays zero
+  const uint32_t eb = __float_as_uint(mx) >> 23;
+  const bool tiny = eb < 27;
+  const int S = tiny ? 0 : 134 - (int)eb;  // 8 - E
+  int w[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const float a = tiny ? 0.f : ldexpf(r[4 * v], S), b = tiny ? 0.f : ldexpf(r[4 * v + 1], S);
+    const float c = tiny ? 0.f : ldexpf(r[4 * v + 2], S), d = tiny ? 0.f : ldexpf(r[4 * v + 3], S);
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w[v] = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, x, true);
+  }
+  uint8_t* rec = lo8 + (int64_t)bh * n1q * D + lo8_piece(n, kg);
+  reinterpret_cast<uint4*>(rec)[0] = uint4{(uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]};
+  reinterpret_cast<uint4*>(rec)[1] = uint4{(uint32_t)w[4], (uint32_t)w[5], (uint32_t)w[6], (uint32_t)w[7]};
+  if (kg == 0) lo8[(int64_t)geo.B * geo.Hkv * n1q * D + (int64_t)bh * n1q + n] = (uint8_t)(127 - S);
+}
+
 template <bool TRUNC>
 __device__ __forceinline__ float sub_pair(float y0, float y1, float c2) {
   // y0: a visible child's dot; y1: the other child's, -inf when missing or not visible
@@ -69,8 +128,9 @@ template <int D, int KC, int NLEV, bool TRUNC>
 __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
                                                         Geo geo, const int32_t* __restrict__ x2,
                                                         int32_t* __restrict__ cand, int32_t* __restrict__ cnt,
-                                                        const bf16* __restrict__ qg) {
+                                                        const bf16* __restrict__ qg, const uint8_t* __restrict__ lo8) {
   constexpr int G = 4, KS = D / 32;
+  constexpr bool LO8 = D == 128;  // lo products from the fp8 records
   using S = SubLds<KC, NLEV>;
   extern __shared__ __attribute__((aligned(16))) int hist[];
   __shared__ S sl_all[4];
@@ -88,6 +148,9 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
   // routing copy of this (b, h); level 1 comes first, so leaf c is node c
   const bf16* R1 = reinterpret_cast<const bf16*>(pyr + geo.means_floats()) + (int64_t)bh * geo.Tp * 2 * D;
   const int N = geo.N, K = geo.K, twoK = 2 * K, n1 = geo.n[1];
+  const int n1q = (n1 + 3) & ~3;
+  const uint8_t* L8 = LO8 ? lo8 + (int64_t)bh * n1q * D : nullptr;                                // records
+  const uint8_t* S8 = LO8 ? lo8 + (int64_t)geo.B * geo.Hkv * n1q * D + (int64_t)bh * n1q : nullptr;  // scales
   const int ntile = NLEV == 2 ? twoK : K;
   const float c2 = trunc_c2(geo.scorer, true);
   const int m = lane & 15, kg = lane >> 4;
@@ -138,7 +201,8 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
   // Gathers of tiles t0 .. t0+TB-1 (a batch: 2 TB KS loads per lane, all issued before the
   // first MFMA that needs them: left to itself the compiler keeps two in flight and waits
   // on each, a dependent chain of L2 round trips).
-  auto load_batch = [&](int t0, bf16x8 (&hi)[kSubTB][KS], bf16x8 (&lo)[kSubTB][KS]) {
+  auto load_batch = [&](int t0, bf16x8 (&hi)[kSubTB][KS], bf16x8 (&lo)[kSubTB][KS], v8i (&l8)[kSubTB],
+                        int (&sc)[kSubTB]) {
 #pragma unroll
     for (int u = 0; u < kSubTB; ++u) {
       const int j = t0 + u;
@@ -146,11 +210,17 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
       const int leaf = 4 * y + v;
       // a missing leaf (or an empty tile) reads leaf 0 instead; its rows are never used
       // k-step s, lane group kg <-> 8-dim piece 4 s + kg (hi, then lo 64 bf16 later)
-      const bf16* rp = R1 + rc_node((y >= 0 && leaf < n1) ? leaf : 0, D) + rc_piece(kg);
+      const int lf = (y >= 0 && leaf < n1) ? leaf : 0;
+      const bf16* rp = R1 + rc_node(lf, D) + rc_piece(kg);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
-        lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
+      for (int s = 0; s < KS; ++s) hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
+      if constexpr (LO8) {
+        // this lane's A row is leaf lf: its record piece for k-group kg and its scale
+        l8[u] = *reinterpret_cast<const v8i*>(L8 + lo8_piece(lf, kg));
+        sc[u] = S8[lf];
+      } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
       }
     }
   };
@@ -166,6 +236,20 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
     const int bq = i0 / kLeaf;   // four consecutive queries share one leaf block (C = kLeaf)
 #pragma unroll
     for (int s = 0; s < KS; ++s) qb[s] = qn[s];
+    // the query columns in e5m2 for the fp8 lo products, in the records' dim order (byte
+    // 8 s + e = dim 32 s + 8 kg + e); |q| past e5m2's largest finite value is clamped to it
+    v8i q8;
+    if constexpr (LO8) {
+#pragma unroll
+      for (int v = 0; v < 8; ++v) {
+        const int s = v >> 1, e = 4 * (v & 1);
+        float c[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) c[h] = __builtin_amdgcn_fmed3f((float)qb[s][e + h], -57344.f, 57344.f);
+        const int x = __builtin_amdgcn_cvt_pk_bf8_f32(c[0], c[1], 0, false);
+        q8[v] = __builtin_amdgcn_cvt_pk_bf8_f32(c[2], c[3], x, true);
+      }
+    }
 #pragma unroll
     for (int u = 0; u < YPL; ++u)
       if (xl + 16 * u < S::NT) w->Y[gl][xl + 16 * u] = yn[u];
@@ -184,15 +268,23 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
 #pragma unroll
       for (int t1 = 0; t1 < 4; t1 += kSubTB) {
         bf16x8 hi[kSubTB][KS], lo[kSubTB][KS];
-        load_batch(t0 + t1, hi, lo);
+        v8i l8[kSubTB];
+        int sc[kSubTB];
+        load_batch(t0 + t1, hi, lo, l8, sc);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kSubTB; ++u) {
           acc[t1 + u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < KS; ++s) {
+          for (int s = 0; s < KS; ++s)
             acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[u][s], qb[s], acc[t1 + u], 0, 0, 0);
-            acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[u][s], qb[s], acc[t1 + u], 0, 0, 0);
+          if constexpr (LO8) {
+            // A = e4m3 records (format 0) with their E8M0 scales, B = e5m2 queries (format 1)
+            acc[t1 + u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(l8[u], q8, acc[t1 + u], 0, 1, 0, sc[u], 0, 127);
+          } else {
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+              acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[u][s], qb[s], acc[t1 + u], 0, 0, 0);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -298,22 +390,28 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
 
 template <int D, int KC, int NLEV>
 int sub_launch(const Geo& g, const void* q, const float* pyr, const int32_t* x2, int32_t* cand, int32_t* cnt,
-               const void* qg, hipStream_t st) {
+               const void* qg, uint8_t* lo8, hipStream_t st) {
+  if constexpr (D == 128) {
+    if (!lo8) return PISA_ERR_INTERNAL;
+    const int n1q = (g.n1 + 3) & ~3;
+    lo8_kernel<<<dim3((unsigned)((4 * n1q + 255) / 256), (unsigned)(g.B * g.Hkv)), 256, 0, st>>>(pyr, g, lo8);
+    if (hipGetLastError() != hipSuccess) return PISA_ERR_HIP;
+  }
   const unsigned grid = (unsigned)(g.B * g.Hkv * ((g.N + kSubQueries - 1) / kSubQueries));
   const size_t hbytes = g.n1p <= kHistMaxBins ? sizeof(int) * (size_t)g.n1p : 0;
   if (g.scorer == PISA_LSE)
-    route_sub_kernel<D, KC, NLEV, false><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt, (const bf16*)qg);
+    route_sub_kernel<D, KC, NLEV, false><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt, (const bf16*)qg, lo8);
   else
-    route_sub_kernel<D, KC, NLEV, true><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt, (const bf16*)qg);
+    route_sub_kernel<D, KC, NLEV, true><<<grid, 256, hbytes, st>>>((const bf16*)q, pyr, g, x2, cand, cnt, (const bf16*)qg, lo8);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
 template <int D, int NLEV>
 int sub_k(const Geo& g, const void* q, const float* pyr, const int32_t* x2, int32_t* cand, int32_t* cnt,
-          const void* qg, hipStream_t st) {
-  if (g.K <= 8) return sub_launch<D, 8, NLEV>(g, q, pyr, x2, cand, cnt, qg, st);
-  if (g.K <= 16) return sub_launch<D, 16, NLEV>(g, q, pyr, x2, cand, cnt, qg, st);
-  return sub_launch<D, 32, NLEV>(g, q, pyr, x2, cand, cnt, qg, st);
+          const void* qg, uint8_t* lo8, hipStream_t st) {
+  if (g.K <= 8) return sub_launch<D, 8, NLEV>(g, q, pyr, x2, cand, cnt, qg, lo8, st);
+  if (g.K <= 16) return sub_launch<D, 16, NLEV>(g, q, pyr, x2, cand, cnt, qg, lo8, st);
+  return sub_launch<D, 32, NLEV>(g, q, pyr, x2, cand, cnt, qg, lo8, st);
 }
 
 }  // namespace
@@ -323,10 +421,11 @@ bool route_sub_supported(const Geo& g, int l_x) {
 }
 
 int launch_route_sub(const Geo& g, int l_x, const void* q, const float* pyr, const int32_t* x2, int32_t* cand,
-                     int32_t* cnt, const void* qg, hipStream_t st) {
+                     int32_t* cnt, const void* qg, uint8_t* lo8, hipStream_t st) {
   if (!route_sub_supported(g, l_x)) return PISA_ERR_UNSUPPORTED;
-  if (g.d == 128) return l_x == 3 ? sub_k<128, 2>(g, q, pyr, x2, cand, cnt, qg, st) : sub_k<128, 1>(g, q, pyr, x2, cand, cnt, qg, st);
-  return l_x == 3 ? sub_k<64, 2>(g, q, pyr, x2, cand, cnt, qg, st) : sub_k<64, 1>(g, q, pyr, x2, cand, cnt, qg, st);
+  if (g.d == 128)
+    return l_x == 3 ? sub_k<128, 2>(g, q, pyr, x2, cand, cnt, qg, lo8, st) : sub_k<128, 1>(g, q, pyr, x2, cand, cnt, qg, lo8, st);
+  return l_x == 3 ? sub_k<64, 2>(g, q, pyr, x2, cand, cnt, qg, lo8, st) : sub_k<64, 1>(g, q, pyr, x2, cand, cnt, qg, lo8, st);
 }
 
 }  // namespace pisa

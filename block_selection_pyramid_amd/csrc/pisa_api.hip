@@ -87,6 +87,7 @@ PrefillWs prefill_ws(const Geo& g, int dtype) {
   w.choff = o;   o = align256(o + sizeof(int32_t) * (w.M + 1));
   w.entries = o; o = align256(o + sizeof(int32_t) * w.slots);
   w.fsc = o;     o = align256(o + sizeof(float) * 3 * (size_t)g.B * g.Hkv * g.N);
+  w.lo8 = o;     o = align256(o + lo8_bytes(g));
   w.total_min = o;
   w.qg = o;
   if (route_scores_forced(g, dtype)) o = align256(o + 2 * (size_t)g.B * g.Hq * g.N * g.d);  // bf16, q's size
@@ -212,6 +213,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   int32_t* choff = (int32_t*)(ws + w.choff);
   int32_t* entries = (int32_t*)(ws + w.entries);
   float* fsc = (float*)(ws + w.fsc);
+  uint8_t* lo8 = (uint8_t*)(ws + w.lo8);
   auto mark = [&](int i) { return ev ? (hipEventRecord((hipEvent_t)ev[i], st) == hipSuccess ? PISA_OK : PISA_ERR_HIP)
                                      : PISA_OK; };
 
@@ -219,7 +221,7 @@ static int select_prefill_impl(const pisa_problem* p, const void* q, const void*
   // counters are contiguous: cnt then cursor (each 256-aligned)
   if ((rc = launch_zero(cnt, (int64_t)(w.off - w.cnt) / (int64_t)sizeof(int32_t), st)) != PISA_OK) return rc;
   // the entries region is free until the scatter: it carries the level-2 candidates
-  if ((rc = launch_route(g, p->dtype, q, k, pyramid, entries, fsc, cand, cnt, qg, ev ? (hipEvent_t)ev[1] : nullptr,
+  if ((rc = launch_route(g, p->dtype, q, k, pyramid, entries, fsc, cand, cnt, qg, lo8, ev ? (hipEvent_t)ev[1] : nullptr,
                         st)) != PISA_OK)
     return rc;
   if ((rc = mark(2)) != PISA_OK) return rc;

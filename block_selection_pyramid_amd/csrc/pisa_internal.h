@@ -34,7 +34,7 @@ struct Geo {
 // total_min does not (a workspace of at least total_min but less than total runs without
 // the copy, reading q itself).
 struct PrefillWs {
-  size_t cand, lscore, cnt, cursor, off, choff, entries, fsc, qg, total_min, total;
+  size_t cand, lscore, cnt, cursor, off, choff, entries, fsc, lo8, qg, total_min, total;
   int64_t slots;  // B*Hkv*N*2K
   int32_t M;      // B*Hkv*n1p leaf-pair lists
 };
@@ -93,8 +93,9 @@ int launch_zero(int32_t* a, int64_t n, hipStream_t st);
 // recorded between the upper-level and the level-2 launch
 // qg (may be null): the regrouped query copy, written by the dense launch and read by the
 // gather launch
+// lo8: workspace of lo8_bytes(g) for the level-2 launch's fp8 leaf corrections (d = 128)
 int launch_route(const Geo& g, int dtype, const void* q, const void* k, const float* pyr, int32_t* x2,
-                 float* fsc, int32_t* cand, int32_t* cnt, void* qg, hipEvent_t mid, hipStream_t st);
+                 float* fsc, int32_t* cand, int32_t* cnt, void* qg, uint8_t* lo8, hipEvent_t mid, hipStream_t st);
 // Levels L..dense_bottom(g) of the bf16 walk (L >= 3), scored densely per leaf block; writes x2 and the
 // forced blocks' scores fsc [B*Hkv*N*3] (ascending forced-block order).
 int launch_route_upper_dense(const Geo& g, const void* q, const float* pyr, const void* k, int32_t* x2, float* fsc,
@@ -122,7 +123,13 @@ inline int dense_bottom(const Geo& g) {
 // like the gather walk.
 bool route_sub_supported(const Geo& g, int l_x);
 int launch_route_sub(const Geo& g, int l_x, const void* q, const float* pyr, const int32_t* x2, int32_t* cand,
-                     int32_t* cnt, const void* qg, hipStream_t st);
+                     int32_t* cnt, const void* qg, uint8_t* lo8, hipStream_t st);
+// Level-1 fp8 corrections that the level-2 launch reads in place of the routing copy's lo
+// halves (d = 128): per (b, KV head) n1 rounded up to 4 leaf records of 128 e4m3 bytes,
+// then one E8M0 scale byte per leaf (workspace bytes, 0 for other d).
+inline size_t lo8_bytes(const Geo& g) {
+  return g.d == 128 ? (size_t)g.B * g.Hkv * (size_t)((g.n1 + 3) & ~3) * (g.d + 1) : 0;
+}
 int launch_scan(const int32_t* cnt, int32_t M, int32_t qc, int32_t* off, int32_t* choff, hipStream_t st);
 // histogram of the routed (query group, level-2 node) pairs of the 2K leaf slots per query
 // group into cnt [B*Hkv*n1p] (the counts the gather launch keeps when it runs)
