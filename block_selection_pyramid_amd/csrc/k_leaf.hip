@@ -261,17 +261,22 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
 }
 
 // Final selection for problems whose forced blocks the dense routing launch scored (fsc:
-// the forced blocks' scores of each query group, ascending): workgroup = the 64 queries of
-// one leaf block of one (b, h); each wavefront finalizes 16 of them, 64/SL per pass.
-template <int SL>
+// the forced blocks' scores of each query group, ascending): workgroup = 4 QW queries of
+// one leaf block of one (b, h) (64 / (4 QW) workgroups per leaf block); each wavefront
+// finalizes QW of them, 64/SL per pass.  With 2K > 16 slots a query fills SL = 32 or 64
+// lanes, so QW = 4 keeps the passes per wavefront (each an LDS round trip) few and the
+// launch wide (16K, K = 32: 74 -> 62 us).
+template <int SL, int QW>
 __global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __restrict__ cand,
                                                     const float* __restrict__ lscore, const float* __restrict__ fsc,
                                                     int32_t* __restrict__ out_idx, float* __restrict__ out_score) {
   constexpr int NQ = 64 / SL;      // query groups finalized per pass
-  constexpr int PASSES = 16 / NQ;  // passes for a wavefront's 16 queries
+  constexpr int PASSES = QW / NQ;  // passes for a wavefront's QW queries
+  constexpr int SUB = 16 / QW;     // workgroups per leaf block
+  static_assert(QW % NQ == 0 && 16 % QW == 0, "whole passes, whole leaf blocks");
   __shared__ __attribute__((aligned(16))) uint64_t kx_all[4][64];
   __shared__ __attribute__((aligned(16))) int32_t lx_all[4][64];
-  const int bq = blockIdx.x, bh = blockIdx.y;
+  const int bq = blockIdx.x / SUB, q0 = bq * kLeaf + (blockIdx.x % SUB) * 4 * QW, bh = blockIdx.y;
   int F[3];
   const int nf = forced_blocks(bq, F);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __re
   for (int p = 0; p < PASSES; ++p) {
     // the slot's candidate and score loaded together (the score is only used where the
     // slot holds a candidate; elsewhere it reads an in-bounds stale value)
-    const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
+    const int i = q0 + wave + 4 * (p * NQ + qq);
     const bool in = i < geo.N && slot < twoK;
     const int64_t e = in ? ((int64_t)bh * geo.N + i) * twoK + slot : 0;
     const int c = cand[e];
@@ -293,7 +298,7 @@ __global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __re
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int i = bq * kLeaf + wave + 4 * (p * NQ + qq);
+    const int i = q0 + wave + 4 * (p * NQ + qq);
     const bool live = i < geo.N;
     const int64_t row = (int64_t)bh * geo.N + (live ? i : 0);
     finalize_rows<SL>(cl[p], cv[p], F, nf, fsc + row * 3, geo.K, lane, live, kx_all[wave], lx_all[wave],
@@ -357,10 +362,13 @@ int launch_leaf_mfma(const Geo& g, const void* q, const void* k, const void* qg,
 
 int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const float* fsc, int32_t* out_idx,
                  float* out_score, hipStream_t st) {
-  dim3 grid(g.n1, g.B * g.Hkv);
-  if (2 * g.K <= 16) final_kernel<16><<<grid, 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
-  else if (2 * g.K <= 32) final_kernel<32><<<grid, 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
-  else final_kernel<64><<<grid, 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+  const unsigned bh = (unsigned)(g.B * g.Hkv);
+  if (2 * g.K <= 16)
+    final_kernel<16, 16><<<dim3(g.n1, bh), 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+  else if (2 * g.K <= 32)
+    final_kernel<32, 4><<<dim3(4 * g.n1, bh), 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+  else
+    final_kernel<64, 4><<<dim3(4 * g.n1, bh), 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
