@@ -125,7 +125,7 @@ __device__ __forceinline__ float sub_pair(float y0, float y1, float c2) {
 // forced blocks (-1 elsewhere; slots 2r, 2r+1 = children of the kept level-2 node of rank r)
 // and histograms the (query group, level-2 node) pairs into cnt.
 template <int D, int KC, int NLEV, bool TRUNC>
-__global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
+__global__ __launch_bounds__(256, NLEV == 2 ? 4 : 3) void route_sub_kernel(const bf16* __restrict__ q, const float* __restrict__ pyr,
                                                         Geo geo, const int32_t* __restrict__ x2,
                                                         int32_t* __restrict__ cand, int32_t* __restrict__ cnt,
                                                         const bf16* __restrict__ qg, const uint8_t* __restrict__ lo8) {
@@ -212,13 +212,15 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
       // k-step s, lane group kg <-> 8-dim piece 4 s + kg (hi, then lo 64 bf16 later)
       const int lf = (y >= 0 && leaf < n1) ? leaf : 0;
       const bf16* rp = R1 + rc_node(lf, D) + rc_piece(kg);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
       if constexpr (LO8) {
         // this lane's A row is leaf lf: its record piece for k-group kg and its scale
+        // (loaded first: the fp8 product opens the tile's accumulation)
         l8[u] = *reinterpret_cast<const v8i*>(L8 + lo8_piece(lf, kg));
         sc[u] = S8[lf];
-      } else {
+      }
+#pragma unroll
+      for (int s = 0; s < KS; ++s) hi[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s);
+      if constexpr (!LO8) {
 #pragma unroll
         for (int s = 0; s < KS; ++s) lo[u][s] = *reinterpret_cast<const bf16x8*>(rp + 256 * s + 64);
       }
@@ -275,13 +277,15 @@ __global__ __launch_bounds__(256) void route_sub_kernel(const bf16* __restrict__
 #pragma unroll
         for (int u = 0; u < kSubTB; ++u) {
           acc[t1 + u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (LO8) {
+            // the lo products first (their record registers free at once): A = e4m3
+            // records (format 0) with their E8M0 scales, B = e5m2 queries (format 1)
+            acc[t1 + u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(l8[u], q8, acc[t1 + u], 0, 1, 0, sc[u], 0, 127);
+          }
 #pragma unroll
           for (int s = 0; s < KS; ++s)
             acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi[u][s], qb[s], acc[t1 + u], 0, 0, 0);
-          if constexpr (LO8) {
-            // A = e4m3 records (format 0) with their E8M0 scales, B = e5m2 queries (format 1)
-            acc[t1 + u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(l8[u], q8, acc[t1 + u], 0, 1, 0, sc[u], 0, 127);
-          } else {
+          if constexpr (!LO8) {
 #pragma unroll
             for (int s = 0; s < KS; ++s)
               acc[t1 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo[u][s], qb[s], acc[t1 + u], 0, 0, 0);
