@@ -22,15 +22,16 @@
 // only level 2 is walked here.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16 over the level-1 routing copy's hi halves, four
-// query groups of one leaf block per wavefront, B = their 16 (group, head) query columns;
-// the lo halves' products follow at d = 128 from a compact fp8 copy (lo8_kernel: each leaf's
-// lo halves as e4m3 scaled by a power of two, undone by the E8M0 scale of
-// v_mfma_scale_f32_16x16x128_f8f6f4, against the query columns in e5m2), which leaves the
-// dots the scaled scores in log2 units to ~2^-13 of the hi product's rounding error and
-// moves 384 instead of 512 bytes per leaf; at d = 64 the bf16 lo halves as well.  Tile j holds in row block rb
-// the four leaf means of level-3 node Y[(rb + j) mod 4][j], so every lane's B operand is
-// its own query fragment and each result lane finds its own group's rows in one tile of
-// every four (mixed-row tiles; G = 4 only).
+// query groups of one leaf block per wavefront, B = their 16 (group, head) query columns.
+// At d = 128 the products of the lo halves come from a compact fp8 copy that lo8_kernel
+// writes into the workspace: each leaf's lo halves in e4m3 under a power-of-two scale that
+// the E8M0 scale operand of v_mfma_scale_f32_16x16x128_f8f6f4 undoes, against the query
+// columns in e5m2.  The lo product is itself ~2^-9 of a dot, so its fp8 rounding (~2^-4 of
+// it) leaves the dots ~1e-5 from exact in score units, and a leaf costs 384 instead of 512
+// bytes; at d = 64 the bf16 lo halves are multiplied as they are.  Tile j holds in row
+// block rb the four leaf means of level-3 node Y[(rb + j) mod 4][j], so every lane's B
+// operand is its own query fragment and each result lane finds its own group's rows in one
+// tile of every four (mixed-row tiles; G = 4 only).
 #include "route_dev.h"
 
 namespace pisa {
