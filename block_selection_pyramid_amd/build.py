@@ -60,6 +60,7 @@ RESOURCES = os.path.join(BUILD_DIR, "kernel_resources.txt")
 HEADLINE = (
     "pisa::(anonymous namespace)::route_dense_kernel<128, 4, 8, false>",
     "pisa::(anonymous namespace)::route_sub_kernel<128,",
+    "pisa::(anonymous namespace)::lo8_kernel",
     "pisa::(anonymous namespace)::route_mfma_kernel<128, 4,",
     "pisa::(anonymous namespace)::leaf_pair_kernel<128, 4>",
     "pisa::(anonymous namespace)::final_kernel",
