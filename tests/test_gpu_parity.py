@@ -304,6 +304,31 @@ def sample_rows(w, needles, n_random, seed):
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def scale_bf16(a, c):
+    """bf16 bits a times c, rounded back to bf16 (nearest, ties to even)."""
+    u = ((a.astype(np.uint32) << 16).view(np.float32) * np.float32(c)).view(np.uint32)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_level2_fp8_margin_with_doubled_inputs(env):
+    # The level-2 launch takes the leaf means' lo products in fp8, an error relative to the
+    # dots.  With q and k doubled (dots x 4, logits of standard deviation ~4) it stays
+    # inside the tie tolerance: 128K (the level-2 launch walks level 2), 100K sampled rows.
+    torch, pisa = env
+    w = synth.custom(name="128k-doubled", batch=1, seq_len=131072, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                     top_k=8, seed=11, needles=64)
+    p, op = problems(pisa, w)
+    q, k, _ = synth.make_inputs(w)
+    q, k = scale_bf16(q, 2.0), scale_bf16(k, 2.0)
+    qd, kd = dev(torch, q), dev(torch, k)
+    pyr = pisa.build_pyramid(p, kd)
+    idx, sc = pisa.select_prefill(p, qd, kd, pyr, pisa.workspace(p))
+    torch.cuda.synchronize()
+    opyr = check_pyramid(op, k, pyr.cpu().numpy()[0], w.name)
+    rows = np.sort(np.random.default_rng(3).choice(4 * 131072, 100000, replace=False))
+    verify(op, q, k, opyr, rows, idx.cpu().numpy(), sc.cpu().numpy(), what=w.name)
+
+
 @pytest.mark.parametrize("name", ["16k", "64k", "128k", "256k"])
 def test_prefill_workload_every_row(env, name):
     # the full-size workloads in bench.py's launch configuration, every query row against
