@@ -139,6 +139,8 @@ __global__ __launch_bounds__(256) void scatter_pairs_kernel(const int32_t* __res
   entries[pos] = (i << 6) | r;
 }
 
+constexpr int kScatterBatch = 8;
+
 // Workgroup = qpw consecutive queries of one (b, h), as scatter_hist_kernel, over level-2
 // nodes.
 __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* __restrict__ cand, int32_t N,
@@ -159,21 +161,41 @@ __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* 
   __syncthreads();
   const int32_t* c = cand + ((int64_t)bh * N + q0) * 2 * K;
   const int n = (q1 - q0) * K;
-  for (int t = threadIdx.x; t < n; t += 256) {
-    const int node = pair_node(c + 2 * t);
-    if (node >= 0) atomicAdd(&hist[node], 1);
+  // kScatterBatch pairs per thread at a time: their loads (and below, their returning
+  // atomics) are all in flight before the first result is used
+  for (int t0 = threadIdx.x; t0 < n; t0 += 256 * kScatterBatch) {
+    int nd[kScatterBatch];
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) nd[u] = t0 + 256 * u < n ? pair_node(c + 2 * (t0 + 256 * u)) : -1;
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u)
+      if (nd[u] >= 0) atomicAdd(&hist[nd[u]], 1);
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < n1p; t += 256) {
-    const int h = hist[t];
-    if (h) hist[t] = off[bh * n1p + t] + atomicAdd(&cursor[bh * n1p + t], h);
+  for (int t0 = threadIdx.x; t0 < n1p; t0 += 256 * kScatterBatch) {
+    int base[kScatterBatch];
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) {
+      const int t = t0 + 256 * u;
+      const int h = t < n1p ? hist[t] : 0;
+      base[u] = h ? off[bh * n1p + t] + atomicAdd(&cursor[bh * n1p + t], h) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u)
+      if (t0 + 256 * u < n1p) hist[t0 + 256 * u] = base[u];
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < n; t += 256) {
-    const int node = pair_node(c + 2 * t);
-    if (node < 0) continue;
-    const int pos = hist[node] + atomicAdd(&lcur[node], 1);
-    entries[pos] = ((q0 + t / K) << 6) | (t % K);
+  for (int t0 = threadIdx.x; t0 < n; t0 += 256 * kScatterBatch) {
+    int nd[kScatterBatch], pos[kScatterBatch];
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) nd[u] = t0 + 256 * u < n ? pair_node(c + 2 * (t0 + 256 * u)) : -1;
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) pos[u] = nd[u] >= 0 ? hist[nd[u]] + atomicAdd(&lcur[nd[u]], 1) : 0;
+#pragma unroll
+    for (int u = 0; u < kScatterBatch; ++u) {
+      const int t = t0 + 256 * u;
+      if (nd[u] >= 0) entries[pos[u]] = ((q0 + t / K) << 6) | (t % K);
+    }
   }
 }
 
