@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void scatter_pairs_kernel(const int32_t* __res
   entries[pos] = (i << 6) | r;
 }
 
-constexpr int kScatterBatch = 8;
+constexpr int kScatterBatch = 16;
 
 // Workgroup = qpw consecutive queries of one (b, h), as scatter_hist_kernel, over level-2
 // nodes.
@@ -162,7 +162,8 @@ __global__ __launch_bounds__(256) void scatter_pairs_hist_kernel(const int32_t* 
   const int32_t* c = cand + ((int64_t)bh * N + q0) * 2 * K;
   const int n = (q1 - q0) * K;
   // kScatterBatch pairs per thread at a time: their loads (and below, their returning
-  // atomics) are all in flight before the first result is used
+  // atomics) are all in flight before the first result is used (256K, batches of 1, 8,
+  // 16 and 32: 140, 119, 112 and 113 us)
   for (int t0 = threadIdx.x; t0 < n; t0 += 256 * kScatterBatch) {
     int nd[kScatterBatch];
 #pragma unroll
