@@ -264,8 +264,9 @@ __global__ __launch_bounds__(256) void forced_final_kernel(const bf16* __restric
 // the forced blocks' scores of each query group, ascending): workgroup = 4 QW queries of
 // one leaf block of one (b, h) (64 / (4 QW) workgroups per leaf block); each wavefront
 // finalizes QW of them, 64/SL per pass.  With 2K > 16 slots a query fills SL = 32 or 64
-// lanes, so QW = 4 keeps the passes per wavefront (each an LDS round trip) few and the
-// launch wide (16K, K = 32: 74 -> 62 us).
+// lanes, so QW = 4 (SL = 32) or 2 (SL = 64) keeps the passes per wavefront (each an LDS
+// round trip) few and the launch wide (16K, K = 32: 74 us at QW = 16, 62 at 4, 59 at 2,
+// 60 at 1).
 template <int SL, int QW>
 __global__ __launch_bounds__(256) void final_kernel(Geo geo, const int32_t* __restrict__ cand,
                                                     const float* __restrict__ lscore, const float* __restrict__ fsc,
@@ -368,7 +369,7 @@ int launch_final(const Geo& g, const int32_t* cand, const float* lscore, const f
   else if (2 * g.K <= 32)
     final_kernel<32, 4><<<dim3(4 * g.n1, bh), 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
   else
-    final_kernel<64, 4><<<dim3(4 * g.n1, bh), 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
+    final_kernel<64, 2><<<dim3(8 * g.n1, bh), 256, 0, st>>>(g, cand, lscore, fsc, out_idx, out_score);
   return hipGetLastError() == hipSuccess ? PISA_OK : PISA_ERR_HIP;
 }
 
